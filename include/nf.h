@@ -1,0 +1,243 @@
+/*
+ * nf.h -- C ABI of the nano-batched decoder-layer step for MI355X (gfx950).
+ *
+ * What the library computes.  One step of a Llama-family pre-norm decoder
+ * layer over a batch that mixes decode tokens with a chunk of prefill tokens:
+ *   h = RMSNorm(x) * g_attn; [q|k|v] = h W_qkv^T; rotary embedding on q, k;
+ *   k, v appended to a paged KV cache; causal GQA attention over the cache;
+ *   x1 = x + attn W_o^T; h2 = RMSNorm(x1) * g_ffn;
+ *   out = x1 + SwiGLU-FFN(h2)        (dense), or
+ *   out = x1 + sum_{e in top-k} w_e SwiGLU-FFN_e(h2)   (mixture of experts).
+ * The batch may be split into nano-batches, each operation duplicated per
+ * nano-batch, so that the compute-bound GEMMs of one nano-batch run while the
+ * memory-bound attention of another runs on a separate partition of the
+ * device's compute units (nano-batching and the device-level pipeline with
+ * execution-unit scheduling: "How it works" on the bytedragons Nanoflow page;
+ * README "Introduction" and "Abstract" on the ossradar Nanoflow page).  The
+ * plan -- nano-batch count, sizes, operation order and resource split -- is
+ * the four-dimensional search point of the "Search Space 4D" card on the
+ * do-not-panic "NanoFlow and the Future of LLM Serving" page.  Splitting
+ * never changes the result: rows are independent.
+ *
+ * The host forms the batch and owns the page tables (asynchronous CPU
+ * control flow, README "Introduction"); the device runs the step.
+ *
+ * Conventions.
+ *  - Every call returns nf_status; on failure nf_last_error() (thread-local)
+ *    holds a message.  No exception crosses the ABI.
+ *  - "device" pointers are HIP device allocations on the layer's device;
+ *    "host" pointers are ordinary CPU memory read before the call returns.
+ *  - Streams are hipStream_t passed as void* (NULL = the null stream).
+ *  - Weights, the KV pool and activations are caller-owned; the library owns
+ *    only its streams, events, workspace, metadata buffers and cos/sin table.
+ *  - All argument validation happens before anything is launched.
+ */
+#ifndef NF_H
+#define NF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nf_status {
+  NF_OK = 0,
+  NF_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent batch */
+  NF_ERR_OUT_OF_RANGE = 2,  /* index or size beyond a declared capacity   */
+  NF_ERR_UNSUPPORTED = 3,   /* valid but not implemented (page size etc.) */
+  NF_ERR_NO_PLAN = 4,       /* plan does not fit the batch                */
+  NF_ERR_HIP = 5            /* a HIP runtime call failed                  */
+} nf_status;
+
+typedef enum nf_dtype { NF_F32 = 0, NF_BF16 = 1 } nf_dtype;
+
+/* Layer shape.  Requirements: n_q_heads % n_kv_heads == 0; head_dim even,
+ * <= 256 (bf16 layers: head_dim == 128); hidden, ffn and head_dim multiples
+ * of 8; top_k <= n_experts <= 64; max_tokens >= 1; max_pos >= 1. */
+typedef struct nf_shape {
+  int32_t hidden;       /* H */
+  int32_t n_q_heads;    /* nq */
+  int32_t n_kv_heads;   /* nkv; query head h uses KV head h / (nq / nkv) */
+  int32_t head_dim;     /* d */
+  int32_t ffn;          /* F, per expert */
+  int32_t n_experts;    /* 1 = dense FFN */
+  int32_t top_k;        /* experts per token (1 for dense) */
+  int32_t dtype;        /* nf_dtype of weights, activations and KV pool */
+  float rms_eps;        /* RMSNorm epsilon */
+  double rope_theta;    /* rotary base; frequency j = theta^(-2j/d) */
+  int32_t max_tokens;   /* capacity: tokens per step */
+  int32_t max_pos;      /* capacity: positions 0..max_pos-1 */
+} nf_shape;
+
+/* Layer weights: device pointers in the layer dtype, caller-owned, read-only,
+ * valid for the layer's lifetime.  Every matrix is row-major with output
+ * features first (K-contiguous rows):
+ *   attn_norm [H], ffn_norm [H]
+ *   w_qkv  [(nq + 2 nkv) * d][H]  rows: Q heads, then K heads, then V heads,
+ *                                 each head's d rows contiguous
+ *   w_o    [H][nq * d]
+ *   w_gate [E][F][H], w_up [E][F][H], w_down [E][H][F]                  */
+typedef struct nf_weights {
+  const void* attn_norm;
+  const void* w_qkv;
+  const void* w_o;
+  const void* ffn_norm;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+} nf_weights;
+
+/* One step's batch.  Tokens are ordered by request; request r owns tokens
+ * req_q_start[r] .. req_q_start[r] + req_q_len[r] - 1 (contiguous, in order,
+ * starts increasing), at positions req_pos0[r] + i (req_pos0 = tokens already
+ * cached).  Its logical page i is pool page page_indices[page_indptr[r] + i];
+ * it needs at least ceil((req_pos0 + req_q_len) / page_size) pages and no
+ * page may belong to two requests.  A decode request has req_q_len == 1; a
+ * prefill chunk has req_q_len > 1.  The step writes K/V for the new positions
+ * and reads keys 0..p for a token at position p. */
+typedef struct nf_batch {
+  int32_t n_tokens;            /* T, 0 <= T <= max_tokens                  */
+  int32_t n_requests;          /* R                                        */
+  const void* x;               /* device [T][H] layer dtype                */
+  void* out;                   /* device [T][H] layer dtype (not aliasing x) */
+  const int32_t* req_q_start;  /* host [R] */
+  const int32_t* req_q_len;    /* host [R] */
+  const int32_t* req_pos0;     /* host [R] */
+  const int32_t* pos;          /* host [T]; must equal req_pos0 + offset    */
+  const int32_t* page_indptr;  /* host [R + 1], page_indptr[0] == 0         */
+  const int32_t* page_indices; /* host [page_indptr[R]]                     */
+  const float* router_logits;  /* device [T][E] fp32 (MoE layers only)      */
+} nf_batch;
+
+#define NF_MAX_NANO 4
+
+typedef enum nf_order {
+  /* per GEMM stream: norm+QKV+RoPE/append of nano-batch j+1 are issued before
+   * the O-proj/FFN of nano-batch j, so j's attention overlaps j+1's QKV */
+  NF_ORDER_PIPELINED = 0,
+  /* nano-batch j finishes every operation before j+1 starts */
+  NF_ORDER_SEQUENTIAL = 1
+} nf_order;
+
+/* Nano-batch plan: count, sizes, operation order and resource split. */
+typedef struct nf_plan {
+  int32_t count;                  /* 1..NF_MAX_NANO                          */
+  int32_t sizes[NF_MAX_NANO];     /* tokens per nano-batch; sum must be T   */
+  int32_t order;                  /* nf_order                                */
+  int32_t n_streams;              /* 1: all work on the caller's stream;
+                                     2: GEMM stream + attention stream       */
+  int32_t gemm_cus_per_xcd;       /* n_streams == 2 only: CUs of each XCD given
+                                     to the GEMM stream, the rest to attention;
+                                     0 = no CU masks (both streams may use
+                                     every CU)                               */
+} nf_plan;
+
+typedef struct nf_search_opts {
+  int32_t max_count;      /* largest nano-batch count tried (<= NF_MAX_NANO) */
+  int32_t warmup;         /* untimed steps per measured candidate            */
+  int32_t reps;           /* timed steps per measured candidate              */
+  int32_t top_k;          /* candidates measured after model ranking          */
+} nf_search_opts;
+
+typedef struct nf_layer nf_layer;
+typedef struct nf_kv_pool nf_kv_pool;
+
+/* ---- layer ---------------------------------------------------------------
+ * nf_layer_create: validates the shape, binds the caller's weights (pointers
+ * kept, nothing copied), allocates the workspace on the current HIP device
+ * and builds the fp32 cos/sin table (angles in fp64).  The default plan is
+ * one nano-batch on the caller's stream.  Errors: NF_ERR_INVALID_ARG (null
+ * pointers, inconsistent shape), NF_ERR_UNSUPPORTED (head_dim or dtype
+ * outside the list above), NF_ERR_HIP (allocation failure). */
+nf_status nf_layer_create(const nf_shape* shape, const nf_weights* w, nf_layer** out);
+void nf_layer_destroy(nf_layer* layer);   /* waits for the layer's streams */
+
+/* ---- KV pool --------------------------------------------------------------
+ * Paged KV cache (the PagedAttention block pool: "How it differs from vLLM
+ * and TensorRT-LLM" on the hysenlabs Nanoflow page).  Layout in the layer
+ * dtype:  K [n_pages][n_kv_heads][page_size][head_dim]
+ *         V [n_pages][n_kv_heads][head_dim][page_size]
+ * (within a page, V is stored dimension-major so that attention's P.V
+ * contraction over keys reads contiguous memory).  Only page_size == 16 is
+ * supported (NF_ERR_UNSUPPORTED otherwise). */
+nf_status nf_kv_pool_bytes(const nf_shape* shape, int32_t n_pages, int32_t page_size,
+                           size_t* k_bytes, size_t* v_bytes);
+nf_status nf_kv_pool_create(const nf_layer* layer, int32_t n_pages, int32_t page_size,
+                            void* k_dev, void* v_dev, nf_kv_pool** out);
+void nf_kv_pool_destroy(nf_kv_pool* pool);
+
+/* ---- plan -----------------------------------------------------------------
+ * nf_plan_set validates count, order, streams and CU split against the device
+ * (sizes are checked against each batch at step time) and (re)creates the
+ * CU-masked streams.  Errors: NF_ERR_INVALID_ARG, NF_ERR_OUT_OF_RANGE,
+ * NF_ERR_HIP. */
+nf_status nf_plan_set(nf_layer* layer, const nf_plan* plan);
+nf_status nf_plan_get(const nf_layer* layer, nf_plan* plan);
+
+/* nf_batch_validate: host-only check of a batch (and optionally a plan)
+ * against a shape and a pool geometry; makes no HIP call.  It runs the same
+ * checks nf_layer_step runs before launching. */
+nf_status nf_batch_validate(const nf_shape* shape, int32_t n_pages, int32_t page_size,
+                            const nf_batch* batch, const nf_plan* plan);
+
+/* ---- step -----------------------------------------------------------------
+ * Enqueue one layer step after prior work on `stream`; `stream` is ordered
+ * after the step completes.  Asynchronous to the host; host arrays of the
+ * batch may be reused once the call returns.  Writes batch->out, the pool
+ * slots of the batch's new positions and the layer's workspace.  Calls on
+ * one layer must not overlap on different host threads. */
+nf_status nf_layer_step(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch, void* stream);
+
+/* ---- plan search -----------------------------------------------------------
+ * Profile-driven choice of the plan for this batch (stands in for the pages'
+ * MILP-based pipeline parameter search): solo-time each operation per
+ * nano-batch size and CU split, predict each candidate plan's step time with
+ * a two-stream event-graph model that charges measured co-run slowdowns, then
+ * run the best `top_k` candidates for real and keep the fastest.  Runs steps
+ * on this batch (so it writes batch->out and the batch's pool slots with the
+ * values a step writes), synchronises `stream`, sets the chosen plan on the
+ * layer and returns it in *out.  `times_ms`, if not NULL, receives
+ * {predicted, measured} of the chosen plan. */
+nf_status nf_plan_search(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch,
+                         const nf_search_opts* opts, nf_plan* out, double* times_ms,
+                         void* stream);
+
+/* ---- intermediates ----------------------------------------------------------
+ * Device pointer and row stride (elements) of an intermediate of the last
+ * step, in the layer dtype: 0 q_rot [T][nq*d], 1 attn [T][nq*d],
+ * 2 x1 [T][H], 3 act [T][F] (dense layers), 4 qkv [T][(nq+2nkv)*d].
+ * For MoE layers, 5 route_idx int32 [T][top_k], 6 route_w fp32 [T][top_k],
+ * 7 route_perm int32 [T*top_k], 8 expert_offsets int32 [E+1] (per
+ * nano-batch, at the nano-batch's token offset / top_k-scaled offset). */
+nf_status nf_layer_intermediate(const nf_layer* layer, int32_t which, const void** dev_ptr,
+                                int64_t* row_stride);
+
+/* ---- per-kernel timing ------------------------------------------------------
+ * When on, every kernel launch of a step is bracketed by HIP events recorded
+ * on the stream it is launched on.  nf_profile_read synchronises those events
+ * and returns, per kernel kind, the number of launches and the summed
+ * duration (ms) since profiling was switched on; kinds with no launches are
+ * omitted.  Names are static strings. */
+nf_status nf_profile_enable(nf_layer* layer, int32_t on);
+nf_status nf_profile_read(nf_layer* layer, int32_t max_kinds, const char** names,
+                          int64_t* launches, double* total_ms, int32_t* n_kinds);
+
+/* ---- device probes ----------------------------------------------------------
+ * Measured peaks of the current device: dense bf16 MFMA TFLOP/s (register-only
+ * MFMA chains on every CU) and HBM read GB/s (streaming `bytes` bytes, at
+ * least 1 GiB recommended).  nf_probe_cu_map fills xcc[i] with the XCD that
+ * CU-mask bit i dispatches to (n = CU count). */
+nf_status nf_probe_mfma_bf16_tflops(double* tflops);
+nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps);
+nf_status nf_probe_cu_map(int32_t* xcc, int32_t n);
+
+/* ---- errors ---------------------------------------------------------------- */
+const char* nf_last_error(void);
+const char* nf_status_string(nf_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NF_H */

@@ -1,0 +1,277 @@
+"""ctypes binding of libnf.so (declarations in include/nf.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+The functions keep the C names; the small classes below only hold handles
+and keep the caller's tensors alive.  Loading fails loudly when the library
+has not been built -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf.so")
+
+NF_OK, NF_ERR_INVALID_ARG, NF_ERR_OUT_OF_RANGE, NF_ERR_UNSUPPORTED, NF_ERR_NO_PLAN, NF_ERR_HIP = range(6)
+NF_F32, NF_BF16 = 0, 1
+NF_ORDER_PIPELINED, NF_ORDER_SEQUENTIAL = 0, 1
+NF_MAX_NANO = 4
+
+i32 = ctypes.c_int32
+i64 = ctypes.c_int64
+vp = ctypes.c_void_p
+P_i32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class nf_shape(ctypes.Structure):
+    _fields_ = [("hidden", i32), ("n_q_heads", i32), ("n_kv_heads", i32), ("head_dim", i32),
+                ("ffn", i32), ("n_experts", i32), ("top_k", i32), ("dtype", i32),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double),
+                ("max_tokens", i32), ("max_pos", i32)]
+
+
+class nf_weights(ctypes.Structure):
+    _fields_ = [(n, vp) for n in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down")]
+
+
+class nf_batch(ctypes.Structure):
+    _fields_ = [("n_tokens", i32), ("n_requests", i32), ("x", vp), ("out", vp),
+                ("req_q_start", P_i32), ("req_q_len", P_i32), ("req_pos0", P_i32), ("pos", P_i32),
+                ("page_indptr", P_i32), ("page_indices", P_i32),
+                ("router_logits", ctypes.POINTER(ctypes.c_float))]
+
+
+class nf_plan(ctypes.Structure):
+    _fields_ = [("count", i32), ("sizes", i32 * NF_MAX_NANO), ("order", i32), ("n_streams", i32),
+                ("gemm_cus_per_xcd", i32)]
+
+
+class nf_search_opts(ctypes.Structure):
+    _fields_ = [("max_count", i32), ("warmup", i32), ("reps", i32), ("top_k", i32)]
+
+
+# name -> (restype, argtypes), mirroring include/nf.h
+_SIGS = {
+    "nf_layer_create": (i32, [ctypes.POINTER(nf_shape), ctypes.POINTER(nf_weights), ctypes.POINTER(vp)]),
+    "nf_layer_destroy": (None, [vp]),
+    "nf_kv_pool_bytes": (i32, [ctypes.POINTER(nf_shape), i32, i32, ctypes.POINTER(ctypes.c_size_t),
+                               ctypes.POINTER(ctypes.c_size_t)]),
+    "nf_kv_pool_create": (i32, [vp, i32, i32, vp, vp, ctypes.POINTER(vp)]),
+    "nf_kv_pool_destroy": (None, [vp]),
+    "nf_plan_set": (i32, [vp, ctypes.POINTER(nf_plan)]),
+    "nf_plan_get": (i32, [vp, ctypes.POINTER(nf_plan)]),
+    "nf_batch_validate": (i32, [ctypes.POINTER(nf_shape), i32, i32, ctypes.POINTER(nf_batch),
+                                ctypes.POINTER(nf_plan)]),
+    "nf_layer_step": (i32, [vp, vp, ctypes.POINTER(nf_batch), vp]),
+    "nf_plan_search": (i32, [vp, vp, ctypes.POINTER(nf_batch), ctypes.POINTER(nf_search_opts),
+                             ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double), vp]),
+    "nf_layer_intermediate": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64)]),
+    "nf_profile_enable": (i32, [vp, i32]),
+    "nf_profile_read": (i32, [vp, i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
+                              ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
+    "nf_probe_mfma_bf16_tflops": (i32, [ctypes.POINTER(ctypes.c_double)]),
+    "nf_probe_hbm_read_gbps": (i32, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_double)]),
+    "nf_probe_cu_map": (i32, [P_i32, i32]),
+    "nf_last_error": (ctypes.c_char_p, []),
+    "nf_status_string": (ctypes.c_char_p, [i32]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m intra_operation_overlap_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class NfError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().nf_last_error().decode()
+        super().__init__(f"{where}: {lib().nf_status_string(status).decode()} ({status}): {msg}")
+
+
+def check(status: int, where: str) -> None:
+    if status != NF_OK:
+        raise NfError(status, where)
+
+
+# ---------------------------------------------------------------- helpers
+
+def make_shape(s, max_tokens: int, max_pos: int) -> nf_shape:
+    """nf_shape from a workload Shape (any object with the same field names)."""
+    return nf_shape(s.hidden, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.n_experts, s.top_k,
+                    NF_BF16 if s.dtype == "bf16" else NF_F32, s.rms_eps, s.rope_theta, max_tokens, max_pos)
+
+
+def _i32p(a: np.ndarray):
+    assert a.dtype == np.int32 and a.flags.c_contiguous
+    return a.ctypes.data_as(P_i32)
+
+
+class HostBatch:
+    """Keeps the host arrays of one batch alive and exposes an nf_batch."""
+
+    def __init__(self, batch, x_ptr: int, out_ptr: int, logits_ptr: Optional[int] = None):
+        self.arrays = [np.ascontiguousarray(a, dtype=np.int32) for a in
+                       (batch.req_q_start, batch.req_q_len, batch.req_pos0, batch.pos,
+                        batch.page_indptr, batch.page_indices)]
+        if self.arrays[5].size == 0:
+            self.arrays[5] = np.zeros(1, np.int32)
+        a = self.arrays
+        self.c = nf_batch(batch.n_tokens, batch.n_requests, x_ptr, out_ptr, _i32p(a[0]), _i32p(a[1]),
+                          _i32p(a[2]), _i32p(a[3]), _i32p(a[4]), _i32p(a[5]),
+                          ctypes.cast(logits_ptr or 0, ctypes.POINTER(ctypes.c_float)))
+
+
+def make_plan(count=1, sizes: Sequence[int] = (0,), order=NF_ORDER_PIPELINED, n_streams=1,
+              gemm_cus_per_xcd=0) -> nf_plan:
+    s = list(sizes) + [0] * (NF_MAX_NANO - len(sizes))
+    return nf_plan(count, (i32 * NF_MAX_NANO)(*s), order, n_streams, gemm_cus_per_xcd)
+
+
+def plan_dict(p: nf_plan) -> dict:
+    return {"count": p.count, "sizes": list(p.sizes)[:p.count], "order": p.order,
+            "n_streams": p.n_streams, "gemm_cus_per_xcd": p.gemm_cus_per_xcd}
+
+
+def batch_validate(shape: nf_shape, n_pages: int, page_size: int, hb: HostBatch,
+                   plan: Optional[nf_plan] = None) -> int:
+    return lib().nf_batch_validate(ctypes.byref(shape), n_pages, page_size, ctypes.byref(hb.c),
+                                   ctypes.byref(plan) if plan is not None else None)
+
+
+class Layer:
+    """nf_layer over caller-owned torch weights (kept referenced here)."""
+
+    def __init__(self, shape, weights: Dict[str, "torch.Tensor"], max_tokens: int, max_pos: int):
+        self.shape = make_shape(shape, max_tokens, max_pos)
+        self._weights = weights
+        w = nf_weights(*(weights[n].data_ptr() for n in
+                         ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down")))
+        h = vp()
+        check(lib().nf_layer_create(ctypes.byref(self.shape), ctypes.byref(w), ctypes.byref(h)), "nf_layer_create")
+        self.h = h
+
+    def close(self):
+        if self.h:
+            lib().nf_layer_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_plan(self, plan: nf_plan) -> None:
+        check(lib().nf_plan_set(self.h, ctypes.byref(plan)), "nf_plan_set")
+
+    def get_plan(self) -> nf_plan:
+        p = nf_plan()
+        check(lib().nf_plan_get(self.h, ctypes.byref(p)), "nf_plan_get")
+        return p
+
+    def step(self, pool: "KVPool", hb: HostBatch, stream: int = 0) -> None:
+        check(lib().nf_layer_step(self.h, pool.h, ctypes.byref(hb.c), stream), "nf_layer_step")
+
+    def search(self, pool: "KVPool", hb: HostBatch, max_count=4, warmup=2, reps=5, top_k=8, stream: int = 0):
+        opts = nf_search_opts(max_count, warmup, reps, top_k)
+        p = nf_plan()
+        t = (ctypes.c_double * 2)()
+        check(lib().nf_plan_search(self.h, pool.h, ctypes.byref(hb.c), ctypes.byref(opts), ctypes.byref(p), t,
+                                   stream), "nf_plan_search")
+        return p, (t[0], t[1])
+
+    def intermediate(self, which: int):
+        ptr, stride = vp(), i64()
+        check(lib().nf_layer_intermediate(self.h, which, ctypes.byref(ptr), ctypes.byref(stride)),
+              "nf_layer_intermediate")
+        return ptr.value, stride.value
+
+    def profile_enable(self, on: bool) -> None:
+        check(lib().nf_profile_enable(self.h, 1 if on else 0), "nf_profile_enable")
+
+    def profile_read(self) -> Dict[str, tuple]:
+        n = 32
+        names = (ctypes.c_char_p * n)()
+        launches = (i64 * n)()
+        ms = (ctypes.c_double * n)()
+        k = i32()
+        check(lib().nf_profile_read(self.h, n, names, launches, ms, ctypes.byref(k)), "nf_profile_read")
+        return {names[i].decode(): (launches[i], ms[i]) for i in range(min(k.value, n))}
+
+
+class KVPool:
+    def __init__(self, layer: Layer, n_pages: int, page_size: int, k, v):
+        self._keep = (k, v)
+        h = vp()
+        check(lib().nf_kv_pool_create(layer.h, n_pages, page_size, k.data_ptr(), v.data_ptr(), ctypes.byref(h)),
+              "nf_kv_pool_create")
+        self.h = h
+        self.layer = layer
+
+    def close(self):
+        if self.h:
+            lib().nf_kv_pool_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def kv_pool_bytes(shape: nf_shape, n_pages: int, page_size: int):
+    kb, vb = ctypes.c_size_t(), ctypes.c_size_t()
+    check(lib().nf_kv_pool_bytes(ctypes.byref(shape), n_pages, page_size, ctypes.byref(kb), ctypes.byref(vb)),
+          "nf_kv_pool_bytes")
+    return kb.value, vb.value
+
+
+def probe_mfma_bf16_tflops() -> float:
+    v = ctypes.c_double()
+    check(lib().nf_probe_mfma_bf16_tflops(ctypes.byref(v)), "nf_probe_mfma_bf16_tflops")
+    return v.value
+
+
+def probe_hbm_read_gbps(nbytes: int = 4 << 30) -> float:
+    v = ctypes.c_double()
+    check(lib().nf_probe_hbm_read_gbps(nbytes, ctypes.byref(v)), "nf_probe_hbm_read_gbps")
+    return v.value
+
+
+def probe_cu_map(n: int) -> List[int]:
+    a = np.zeros(n, np.int32)
+    check(lib().nf_probe_cu_map(_i32p(a), n), "nf_probe_cu_map")
+    return a.tolist()
+
+
+# device-to-device copy of raw library memory into a torch tensor (plumbing)
+_hip = None
+
+
+def copy_device(dst_tensor, src_ptr: int, nbytes: int) -> None:
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.restype = ctypes.c_int
+        _hip.hipMemcpy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int]
+    rc = _hip.hipMemcpy(dst_tensor.data_ptr(), src_ptr, nbytes, 3)   # hipMemcpyDeviceToDevice
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed: {rc}")

@@ -1,0 +1,1034 @@
+// C ABI of the nano-batched decoder-layer step: objects, metadata upload and
+// the overlap executor.
+//
+// Executor.  A plan splits the batch's tokens into nano-batches and duplicates
+// every operation per nano-batch (nano-batching, README "Introduction" and
+// "Abstract" on the ossradar Nanoflow page).  With two streams, the GEMM side
+// (norm, QKV, RoPE/append, O-proj, norm, FFN) runs on stream G and attention
+// on stream A; each stream may be restricted to a subset of every XCD's CUs
+// (hipExtStreamCreateWithCUMask), which is the execution-unit partition of the
+// device-level pipeline ("How it works" on the bytedragons Nanoflow page).
+// Events carry the only cross-stream dependencies: attention(j) waits for the
+// RoPE/append of nano-batch j, the O-projection of j waits for attention(j).
+// In the pipelined order the GEMM stream issues the front half of nano-batch
+// j+1 (norm, QKV, RoPE/append) before the back half of j (O-proj, FFN), so
+// j's memory-bound attention runs beside j+1's compute-bound projections and
+// compute stays on the critical path (README "Introduction").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "nf_internal.h"
+
+using namespace nf;
+
+namespace {
+
+thread_local std::string g_err;
+
+nf_status set_err(nf_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+nf_status set_err(nf_status st, const char* fmt, ...) {
+  char buf[768];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return set_err(NF_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), \
+                     __FILE__, __LINE__);                                                 \
+  } while (0)
+
+constexpr int PAGE_SIZE = 16;
+
+struct DevBuf {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+// Kinds of kernel launches, for the per-kernel timing facility.
+enum Kind {
+  K_NORM1, K_QKV, K_QKV_RED, K_ROPE, K_ATTN, K_MERGE, K_OPROJ, K_OPROJ_RED, K_NORM2,
+  K_GATEUP, K_GATEUP_RED, K_DOWN, K_DOWN_RED, K_ROUTE, K_MOE_GATEUP, K_MOE_DOWN, K_COMBINE,
+  K_COUNT
+};
+const char* kKindNames[K_COUNT] = {
+  "rmsnorm_attn", "gemm_qkv", "gemm_qkv_splitk_reduce", "rope_kv_append", "attention",
+  "attention_merge", "gemm_o_residual", "gemm_o_splitk_reduce", "rmsnorm_ffn", "gemm_gate_up_swiglu",
+  "gemm_gate_up_splitk_reduce", "gemm_down_residual", "gemm_down_splitk_reduce", "moe_route",
+  "moe_gemm_gate_up_swiglu", "moe_gemm_down", "moe_combine",
+};
+
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+
+struct StreamPair {
+  hipStream_t g = nullptr, a = nullptr;
+};
+
+size_t dtype_bytes(int dt) { return dt == NF_BF16 ? 2 : 4; }
+
+}  // namespace
+
+struct nf_layer {
+  nf_shape s{};
+  nf_weights w{};
+  int device = 0;
+  int n_cus = 0, n_xcd = 8, cus_per_xcd = 32;
+  std::vector<int> xcc_of_bit;                  // CU-mask bit -> XCD (measured)
+  nf_plan plan{};
+  std::map<int, StreamPair> pairs;              // by gemm_cus_per_xcd (0 = unmasked)
+  hipEvent_t ev_app[NF_MAX_NANO] = {}, ev_att[NF_MAX_NANO] = {};
+  hipEvent_t ev_start = nullptr, ev_g = nullptr, ev_a = nullptr;
+  DevBuf h, qkv, q_rot, attn, x1, h2, act, y;
+  DevBuf r_idx, r_w, r_perm, r_inv, r_off;
+  DevBuf splitk, part_o, part_ml, meta, cos_sin;
+  void* stage[2] = {nullptr, nullptr};
+  size_t stage_bytes[2] = {0, 0};
+  hipEvent_t stage_ev[2] = {nullptr, nullptr};
+  bool stage_used[2] = {false, false};
+  int stage_i = 0;
+  bool prof = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> ev_free;
+  double prof_ms[K_COUNT] = {};
+  int64_t prof_n[K_COUNT] = {};
+  StepWork work;
+  int last_T = 0;
+};
+
+struct nf_kv_pool {
+  const nf_layer* layer = nullptr;
+  int32_t n_pages = 0, page_size = 0;
+  void* k = nullptr;
+  void* v = nullptr;
+};
+
+namespace {
+
+hipError_t ensure(DevBuf& b, size_t bytes) {
+  if (bytes <= b.bytes) return hipSuccess;
+  if (b.p) {
+    hipError_t e = hipDeviceSynchronize();     // the old buffer may still be in use
+    if (e != hipSuccess) return e;
+    e = hipFree(b.p);
+    if (e != hipSuccess) return e;
+    b.p = nullptr;
+    b.bytes = 0;
+  }
+  const size_t want = std::max(bytes, (size_t)256);
+  hipError_t e = hipMalloc(&b.p, want);
+  if (e != hipSuccess) {
+    b.p = nullptr;
+    return e;
+  }
+  b.bytes = want;
+  return hipSuccess;
+}
+
+void release(DevBuf& b) {
+  if (b.p) (void)hipFree(b.p);
+  b.p = nullptr;
+  b.bytes = 0;
+}
+
+// --------------------------------------------------------------- CU masks
+std::mutex g_map_mu;
+std::map<int, std::vector<int>> g_xcc_maps;     // device -> bit -> XCD
+
+nf_status measure_cu_map(int device, int n_cus, std::vector<int>& out) {
+  std::lock_guard<std::mutex> lk(g_map_mu);
+  auto it = g_xcc_maps.find(device);
+  if (it != g_xcc_maps.end()) {
+    out = it->second;
+    return NF_OK;
+  }
+  uint32_t* d_id = nullptr;
+  HIP_TRY(hipMalloc(&d_id, 2 * sizeof(uint32_t)));
+  std::vector<int> map(n_cus, -1);
+  const int words = (n_cus + 31) / 32;
+  for (int bit = 0; bit < n_cus; ++bit) {
+    std::vector<uint32_t> mask(words, 0u);
+    mask[bit / 32] = 1u << (bit % 32);
+    hipStream_t st;
+    hipError_t e = hipExtStreamCreateWithCUMask(&st, words, mask.data());
+    if (e != hipSuccess) {
+      (void)hipFree(d_id);
+      return set_err(NF_ERR_HIP, "hipExtStreamCreateWithCUMask: %s", hipGetErrorString(e));
+    }
+    uint32_t h_id[2] = {0, 0};
+    e = probe_hwid(d_id, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(h_id, d_id, sizeof h_id, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    (void)hipStreamDestroy(st);
+    if (e != hipSuccess) {
+      (void)hipFree(d_id);
+      return set_err(NF_ERR_HIP, "CU map probe: %s", hipGetErrorString(e));
+    }
+    map[bit] = (int)(h_id[1] & 0xF);
+  }
+  (void)hipFree(d_id);
+  g_xcc_maps[device] = map;
+  out = map;
+  return NF_OK;
+}
+
+// Masks for a GEMM/attention split: per XCD, the first `gemm` of its bits go to
+// the GEMM stream, the rest to attention.
+void split_masks(const std::vector<int>& xcc, int n_xcd, int gemm, std::vector<uint32_t>& mg,
+                 std::vector<uint32_t>& ma) {
+  const int n = (int)xcc.size(), words = (n + 31) / 32;
+  mg.assign(words, 0u);
+  ma.assign(words, 0u);
+  std::vector<int> seen(std::max(n_xcd, 16), 0);
+  for (int bit = 0; bit < n; ++bit) {
+    const int x = xcc[bit] < 0 ? bit % n_xcd : xcc[bit];
+    if (seen[x]++ < gemm)
+      mg[bit / 32] |= 1u << (bit % 32);
+    else
+      ma[bit / 32] |= 1u << (bit % 32);
+  }
+}
+
+nf_status get_pair(nf_layer* L, int gemm_cus, StreamPair& out) {
+  auto it = L->pairs.find(gemm_cus);
+  if (it != L->pairs.end()) {
+    out = it->second;
+    return NF_OK;
+  }
+  StreamPair p;
+  if (gemm_cus == 0) {
+    HIP_TRY(hipStreamCreateWithFlags(&p.g, hipStreamNonBlocking));
+    HIP_TRY(hipStreamCreateWithFlags(&p.a, hipStreamNonBlocking));
+  } else {
+    if (L->xcc_of_bit.empty()) {
+      nf_status st = measure_cu_map(L->device, L->n_cus, L->xcc_of_bit);
+      if (st != NF_OK) return st;
+    }
+    std::vector<uint32_t> mg, ma;
+    split_masks(L->xcc_of_bit, L->n_xcd, gemm_cus, mg, ma);
+    HIP_TRY(hipExtStreamCreateWithCUMask(&p.g, (uint32_t)mg.size(), mg.data()));
+    HIP_TRY(hipExtStreamCreateWithCUMask(&p.a, (uint32_t)ma.size(), ma.data()));
+  }
+  L->pairs[gemm_cus] = p;
+  out = p;
+  return NF_OK;
+}
+
+// --------------------------------------------------------------- profiling
+struct Prof {
+  nf_layer* L;
+  int kind;
+  hipStream_t s;
+};
+
+void prof_begin(nf_layer* L, int kind, hipStream_t s) {
+  if (!L->prof) return;
+  ProfRec r{kind, nullptr, nullptr};
+  for (hipEvent_t* e : {&r.a, &r.b}) {
+    if (!L->ev_free.empty()) {
+      *e = L->ev_free.back();
+      L->ev_free.pop_back();
+    } else if (hipEventCreate(e) != hipSuccess) {
+      *e = nullptr;
+    }
+  }
+  if (r.a && r.b) {
+    (void)hipEventRecord(r.a, s);
+    L->recs.push_back(r);
+  }
+}
+
+void prof_end(nf_layer* L, hipStream_t s) {
+  if (!L->prof || L->recs.empty()) return;
+  (void)hipEventRecord(L->recs.back().b, s);
+}
+
+void prof_hook_fn(void* ctx, int phase) {
+  Prof* p = (Prof*)ctx;
+  (void)phase;
+  prof_end(p->L, p->s);
+  prof_begin(p->L, p->kind + 1, p->s);     // the reduce kind follows its GEMM kind
+}
+
+// --------------------------------------------------------------- step pieces
+struct StepCtx {
+  nf_layer* L;
+  nf_kv_pool* P;
+  const nf_batch* b;
+  // device metadata
+  const int32_t *tok_req, *pos, *indptr, *indices;
+  const AttnItem* items;
+  const MergeItem* merges;
+  int gemm_cus, attn_cus;
+};
+
+char* ptr(const DevBuf& b, int64_t elems, int dt) { return (char*)b.p + elems * (int64_t)dtype_bytes(dt); }
+
+hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s) {
+  nf_layer* L = c.L;
+  if (L->s.dtype == NF_F32) {
+    prof_begin(L, kind, s);
+    hipError_t e = gemm_f32(g, s);
+    prof_end(L, s);
+    return e;
+  }
+  GemmPlan gp = gemm_choose(g, c.gemm_cus);
+  Prof pctx{L, kind, s};
+  LaunchHook hook{prof_hook_fn, &pctx};
+  prof_begin(L, kind, s);
+  hipError_t e = gemm_bf16(g, gp, L->splitk.p, s, L->prof ? &hook : nullptr);
+  prof_end(L, s);
+  return e;
+}
+
+size_t gemm_ws_need(const StepCtx& c, GemmArgs g) {
+  if (c.L->s.dtype == NF_F32) return 0;
+  return gemm_workspace_bytes(g, gemm_choose(g, c.gemm_cus));
+}
+
+// GEMM descriptors of nano-batch [t0, t1)
+struct NanoGemms {
+  GemmArgs qkv, o, gu, down, moe_gu, moe_down;
+};
+
+NanoGemms nano_gemms(const StepCtx& c, int j, int t0, int t1) {
+  nf_layer* L = c.L;
+  const nf_shape& s = L->s;
+  const int dt = s.dtype;
+  const int H = s.hidden, F = s.ffn, nqd = s.n_q_heads * s.head_dim;
+  const int Nqkv = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim;
+  const int Tj = t1 - t0, k = s.top_k;
+  NanoGemms n;
+  GemmArgs& q = n.qkv;
+  q.A = ptr(L->h, (int64_t)t0 * H, dt); q.lda = H;
+  q.B = L->w.w_qkv; q.ldb = H;
+  q.C = ptr(L->qkv, (int64_t)t0 * Nqkv, dt); q.ldc = Nqkv;
+  q.M = Tj; q.N = Nqkv; q.K = H; q.mode = GEMM_STORE;
+  GemmArgs& o = n.o;
+  o.A = ptr(L->attn, (int64_t)t0 * nqd, dt); o.lda = nqd;
+  o.B = L->w.w_o; o.ldb = nqd;
+  o.C = ptr(L->x1, (int64_t)t0 * H, dt); o.ldc = H;
+  o.R = (const char*)c.b->x + (int64_t)t0 * H * dtype_bytes(dt); o.ldr = H;
+  o.M = Tj; o.N = H; o.K = nqd; o.mode = GEMM_RESIDUAL;
+  if (s.n_experts == 1) {
+    GemmArgs& g = n.gu;
+    g.A = ptr(L->h2, (int64_t)t0 * H, dt); g.lda = H;
+    g.B = L->w.w_gate; g.B2 = L->w.w_up; g.ldb = H;
+    g.C = ptr(L->act, (int64_t)t0 * F, dt); g.ldc = F;
+    g.M = Tj; g.N = F; g.K = H; g.mode = GEMM_SWIGLU;
+    GemmArgs& d = n.down;
+    d.A = ptr(L->act, (int64_t)t0 * F, dt); d.lda = F;
+    d.B = L->w.w_down; d.ldb = F;
+    d.C = (char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt); d.ldc = H;
+    d.R = ptr(L->x1, (int64_t)t0 * H, dt); d.ldr = H;
+    d.M = Tj; d.N = H; d.K = F; d.mode = GEMM_RESIDUAL;
+  } else {
+    const int32_t* off = (const int32_t*)L->r_off.p + j * (s.n_experts + 1);
+    GemmArgs& g = n.moe_gu;
+    g.A = ptr(L->h2, (int64_t)t0 * H, dt); g.lda = H;
+    g.a_rows = (const int32_t*)L->r_perm.p + (int64_t)t0 * k; g.a_row_div = k;
+    g.group_off = off; g.n_groups = s.n_experts; g.max_group_rows = Tj * k;
+    g.B = L->w.w_gate; g.B2 = L->w.w_up; g.ldb = H; g.b_group_stride = (int64_t)F * H;
+    g.C = ptr(L->act, (int64_t)t0 * k * F, dt); g.ldc = F;
+    g.M = Tj * k; g.N = F; g.K = H; g.mode = GEMM_SWIGLU;
+    GemmArgs& d = n.moe_down;
+    d.A = ptr(L->act, (int64_t)t0 * k * F, dt); d.lda = F;
+    d.group_off = off; d.n_groups = s.n_experts; d.max_group_rows = Tj * k;
+    d.B = L->w.w_down; d.ldb = F; d.b_group_stride = (int64_t)H * F;
+    d.C = (float*)L->y.p + (int64_t)t0 * k * H; d.ldc = H;
+    d.M = Tj * k; d.N = H; d.K = F; d.mode = GEMM_F32OUT;
+  }
+  return n;
+}
+
+#define HIP_STEP(expr)                                                                      \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return set_err(NF_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));           \
+  } while (0)
+
+nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
+  nf_layer* L = c.L;
+  const nf_shape& sh = L->s;
+  const NanoWork& nw = L->work.nanos[j];
+  const int t0 = nw.t0, Tj = nw.t1 - nw.t0, dt = sh.dtype, H = sh.hidden;
+  if (Tj == 0) return NF_OK;
+  prof_begin(L, K_NORM1, s);
+  HIP_STEP(rmsnorm(dt, (const char*)c.b->x + (int64_t)t0 * H * dtype_bytes(dt), L->w.attn_norm,
+                   ptr(L->h, (int64_t)t0 * H, dt), Tj, H, sh.rms_eps, s));
+  prof_end(L, s);
+  NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
+  HIP_STEP(run_gemm(c, g.qkv, K_QKV, s));
+  RopeAppendArgs r;
+  const int Nqkv = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim;
+  r.qkv = ptr(L->qkv, (int64_t)t0 * Nqkv, dt);
+  r.q_rot = ptr(L->q_rot, (int64_t)t0 * sh.n_q_heads * sh.head_dim, dt);
+  r.k_pool = c.P->k;
+  r.v_pool = c.P->v;
+  r.pos = c.pos + t0;
+  r.tok_req = c.tok_req + t0;
+  r.page_indptr = c.indptr;
+  r.page_indices = c.indices;
+  r.cos_sin = (const float*)L->cos_sin.p;
+  r.T = Tj; r.nq = sh.n_q_heads; r.nkv = sh.n_kv_heads; r.d = sh.head_dim; r.page_size = c.P->page_size;
+  prof_begin(L, K_ROPE, s);
+  HIP_STEP(rope_append(dt, r, s));
+  prof_end(L, s);
+  return NF_OK;
+}
+
+nf_status issue_attention(StepCtx& c, int j, hipStream_t s) {
+  nf_layer* L = c.L;
+  const nf_shape& sh = L->s;
+  const NanoWork& nw = L->work.nanos[j];
+  if (nw.t1 == nw.t0) return NF_OK;
+  AttnArgs a;
+  a.q_rot = L->q_rot.p;
+  a.k_pool = c.P->k;
+  a.v_pool = c.P->v;
+  a.attn = L->attn.p;
+  a.part_o = (float*)L->part_o.p;
+  a.part_ml = (float*)L->part_ml.p;
+  a.items = c.items + nw.item0;
+  a.n_items = nw.n_items;
+  a.merges = c.merges + nw.merge0;
+  a.n_merges = nw.n_merges;
+  a.pos = c.pos;
+  a.page_indptr = c.indptr;
+  a.page_indices = c.indices;
+  a.nq = sh.n_q_heads; a.nkv = sh.n_kv_heads; a.d = sh.head_dim; a.page_size = c.P->page_size;
+  a.scale = (float)(1.0 / std::sqrt((double)sh.head_dim));
+  prof_begin(L, K_ATTN, s);
+  HIP_STEP(attention(sh.dtype, a, s));
+  prof_end(L, s);
+  if (nw.n_merges) {
+    prof_begin(L, K_MERGE, s);
+    HIP_STEP(attention_merge(sh.dtype, a, s));
+    prof_end(L, s);
+  }
+  return NF_OK;
+}
+
+nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
+  nf_layer* L = c.L;
+  const nf_shape& sh = L->s;
+  const NanoWork& nw = L->work.nanos[j];
+  const int t0 = nw.t0, Tj = nw.t1 - nw.t0, dt = sh.dtype, H = sh.hidden;
+  if (Tj == 0) return NF_OK;
+  NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
+  HIP_STEP(run_gemm(c, g.o, K_OPROJ, s));
+  prof_begin(L, K_NORM2, s);
+  HIP_STEP(rmsnorm(dt, ptr(L->x1, (int64_t)t0 * H, dt), L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
+                   sh.rms_eps, s));
+  prof_end(L, s);
+  if (sh.n_experts == 1) {
+    HIP_STEP(run_gemm(c, g.gu, K_GATEUP, s));
+    HIP_STEP(run_gemm(c, g.down, K_DOWN, s));
+    return NF_OK;
+  }
+  const int k = sh.top_k, E = sh.n_experts;
+  RouteArgs r;
+  r.logits = c.b->router_logits + (int64_t)t0 * E;
+  r.idx = (int32_t*)L->r_idx.p + (int64_t)t0 * k;
+  r.w = (float*)L->r_w.p + (int64_t)t0 * k;
+  r.perm = (int32_t*)L->r_perm.p + (int64_t)t0 * k;
+  r.inv = (int32_t*)L->r_inv.p + (int64_t)t0 * k;
+  r.offsets = (int32_t*)L->r_off.p + j * (E + 1);
+  r.T = Tj; r.E = E; r.k = k;
+  prof_begin(L, K_ROUTE, s);
+  HIP_STEP(moe_route(r, s));
+  prof_end(L, s);
+  GemmPlan gp;           // grouped: one tile config, no split-K
+  prof_begin(L, K_MOE_GATEUP, s);
+  HIP_STEP(gemm_bf16(g.moe_gu, gp, nullptr, s));
+  prof_end(L, s);
+  prof_begin(L, K_MOE_DOWN, s);
+  HIP_STEP(gemm_bf16(g.moe_down, gp, nullptr, s));
+  prof_end(L, s);
+  prof_begin(L, K_COMBINE, s);
+  HIP_STEP(moe_combine(dt, ptr(L->x1, (int64_t)t0 * H, dt), (const float*)L->y.p + (int64_t)t0 * k * H,
+                       r.w, r.inv, (char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt), Tj, H, k, s));
+  prof_end(L, s);
+  return NF_OK;
+}
+
+size_t align_words(size_t w) { return (w + 63) & ~(size_t)63; }
+
+nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t caller, const nf_plan& plan) {
+  std::string err;
+  nf_status st = check_batch(L->s, P->n_pages, P->page_size, *b, err);
+  if (st != NF_OK) return set_err(st, "%s", err.c_str());
+  st = check_plan_batch(plan, b->n_tokens, err);
+  if (st != NF_OK) return set_err(st, "%s", err.c_str());
+  const int T = b->n_tokens, R = b->n_requests;
+  L->last_T = T;
+  if (T == 0) return NF_OK;
+  HIP_TRY(hipSetDevice(L->device));
+
+  const bool two = plan.n_streams == 2;
+  const int gsplit = two ? plan.gemm_cus_per_xcd : 0;
+  StepCtx c{};
+  c.L = L;
+  c.P = P;
+  c.b = b;
+  c.gemm_cus = gsplit ? gsplit * L->n_xcd : L->n_cus;
+  c.attn_cus = gsplit ? (L->cus_per_xcd - gsplit) * L->n_xcd : L->n_cus;
+  build_work(L->s, *b, plan, P->page_size, c.attn_cus, 8, L->work);
+  const StepWork& w = L->work;
+  const int count = (int)w.nanos.size();
+
+  // workspace the GEMMs and the split attention items need (before any launch)
+  size_t ws = 0;
+  for (int j = 0; j < count; ++j) {
+    NanoGemms g = nano_gemms(c, j, w.nanos[j].t0, w.nanos[j].t1);
+    if (L->s.n_experts == 1)
+      for (const GemmArgs* a : {&g.qkv, &g.o, &g.gu, &g.down}) ws = std::max(ws, gemm_ws_need(c, *a));
+    else
+      ws = std::max(ws, gemm_ws_need(c, g.qkv)), ws = std::max(ws, gemm_ws_need(c, g.o));
+  }
+  HIP_TRY(ensure(L->splitk, ws));
+  const size_t n_part = (size_t)std::max(1, w.n_partials) * L->s.n_kv_heads * 16;
+  HIP_TRY(ensure(L->part_o, n_part * L->s.head_dim * sizeof(float)));
+  HIP_TRY(ensure(L->part_ml, n_part * 2 * sizeof(float)));
+
+  // metadata: tok_req | pos | indptr | indices | items | merges (int32 words)
+  const int64_t nnz = b->page_indptr[R];
+  const size_t o_tok = 0, o_pos = align_words(T), o_ip = o_pos + align_words(T), o_ix = o_ip + align_words(R + 1),
+               o_it = o_ix + align_words(nnz), o_mg = o_it + align_words(w.items.size() * 8),
+               words = o_mg + align_words(w.merges.size() * 4);
+  const size_t bytes = words * 4;
+  const int si = L->stage_i;
+  L->stage_i ^= 1;
+  if (L->stage_used[si]) HIP_TRY(hipEventSynchronize(L->stage_ev[si]));  // previous copy from it done
+  if (L->stage_bytes[si] < bytes) {
+    if (L->stage[si]) HIP_TRY(hipHostFree(L->stage[si]));
+    L->stage[si] = nullptr;
+    L->stage_bytes[si] = 0;
+    HIP_TRY(hipHostMalloc(&L->stage[si], bytes * 2, hipHostMallocDefault));
+    L->stage_bytes[si] = bytes * 2;
+  }
+  if (L->meta.bytes < bytes) HIP_TRY(ensure(L->meta, bytes * 2));
+  int32_t* hs = (int32_t*)L->stage[si];
+  std::memcpy(hs + o_tok, w.tok_req.data(), (size_t)T * 4);
+  std::memcpy(hs + o_pos, b->pos, (size_t)T * 4);
+  std::memcpy(hs + o_ip, b->page_indptr, (size_t)(R + 1) * 4);
+  std::memcpy(hs + o_ix, b->page_indices, (size_t)nnz * 4);
+  if (!w.items.empty()) std::memcpy(hs + o_it, w.items.data(), w.items.size() * sizeof(AttnItem));
+  if (!w.merges.empty()) std::memcpy(hs + o_mg, w.merges.data(), w.merges.size() * sizeof(MergeItem));
+  HIP_TRY(hipMemcpyAsync(L->meta.p, hs, bytes, hipMemcpyHostToDevice, caller));
+  HIP_TRY(hipEventRecord(L->stage_ev[si], caller));
+  L->stage_used[si] = true;
+  const int32_t* dm = (const int32_t*)L->meta.p;
+  c.tok_req = dm + o_tok;
+  c.pos = dm + o_pos;
+  c.indptr = dm + o_ip;
+  c.indices = dm + o_ix;
+  c.items = (const AttnItem*)(dm + o_it);
+  c.merges = (const MergeItem*)(dm + o_mg);
+
+  hipStream_t sg = caller, sa = caller;
+  if (two) {
+    StreamPair pr;
+    st = get_pair(L, gsplit, pr);
+    if (st != NF_OK) return st;
+    sg = pr.g;
+    sa = pr.a;
+    HIP_TRY(hipEventRecord(L->ev_start, caller));
+    HIP_TRY(hipStreamWaitEvent(sg, L->ev_start, 0));
+    HIP_TRY(hipStreamWaitEvent(sa, L->ev_start, 0));
+  }
+  auto front_and_attn = [&](int j) -> nf_status {
+    nf_status s1 = issue_front(c, j, sg);
+    if (s1 != NF_OK) return s1;
+    if (two) {
+      HIP_TRY(hipEventRecord(L->ev_app[j], sg));
+      HIP_TRY(hipStreamWaitEvent(sa, L->ev_app[j], 0));
+    }
+    s1 = issue_attention(c, j, sa);
+    if (s1 != NF_OK) return s1;
+    if (two) HIP_TRY(hipEventRecord(L->ev_att[j], sa));
+    return NF_OK;
+  };
+  auto back = [&](int j) -> nf_status {
+    if (two) HIP_TRY(hipStreamWaitEvent(sg, L->ev_att[j], 0));
+    return issue_back(c, j, sg);
+  };
+  if (plan.order == NF_ORDER_PIPELINED) {
+    st = front_and_attn(0);
+    if (st != NF_OK) return st;
+    for (int j = 0; j < count; ++j) {
+      if (j + 1 < count && (st = front_and_attn(j + 1)) != NF_OK) return st;
+      if ((st = back(j)) != NF_OK) return st;
+    }
+  } else {
+    for (int j = 0; j < count; ++j) {
+      if ((st = front_and_attn(j)) != NF_OK) return st;
+      if ((st = back(j)) != NF_OK) return st;
+    }
+  }
+  if (two) {
+    HIP_TRY(hipEventRecord(L->ev_g, sg));
+    HIP_TRY(hipEventRecord(L->ev_a, sa));
+    HIP_TRY(hipStreamWaitEvent(caller, L->ev_g, 0));
+    HIP_TRY(hipStreamWaitEvent(caller, L->ev_a, 0));
+  }
+  return NF_OK;
+}
+
+}  // namespace
+
+// =============================================================== C ABI
+extern "C" {
+
+const char* nf_last_error(void) { return g_err.c_str(); }
+
+const char* nf_status_string(nf_status s) {
+  switch (s) {
+    case NF_OK: return "ok";
+    case NF_ERR_INVALID_ARG: return "invalid argument";
+    case NF_ERR_OUT_OF_RANGE: return "out of range";
+    case NF_ERR_UNSUPPORTED: return "unsupported";
+    case NF_ERR_NO_PLAN: return "no plan";
+    case NF_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+nf_status nf_kv_pool_bytes(const nf_shape* s, int32_t n_pages, int32_t page_size, size_t* k_bytes,
+                           size_t* v_bytes) {
+  if (!s || !k_bytes || !v_bytes) return set_err(NF_ERR_INVALID_ARG, "nf_kv_pool_bytes: null argument");
+  std::string err;
+  nf_status st = check_shape(*s, err);
+  if (st != NF_OK) return set_err(st, "%s", err.c_str());
+  if (page_size != PAGE_SIZE) return set_err(NF_ERR_UNSUPPORTED, "page_size %d: only 16 is supported", page_size);
+  if (n_pages <= 0) return set_err(NF_ERR_INVALID_ARG, "n_pages must be positive");
+  const size_t b = (size_t)n_pages * s->n_kv_heads * page_size * s->head_dim * dtype_bytes(s->dtype);
+  *k_bytes = b;
+  *v_bytes = b;
+  return NF_OK;
+}
+
+nf_status nf_batch_validate(const nf_shape* s, int32_t n_pages, int32_t page_size, const nf_batch* b,
+                            const nf_plan* p) {
+  if (!s || !b) return set_err(NF_ERR_INVALID_ARG, "nf_batch_validate: null argument");
+  std::string err;
+  nf_status st = check_shape(*s, err);
+  if (st == NF_OK && page_size != PAGE_SIZE) {
+    err = "page_size: only 16 is supported";
+    st = NF_ERR_UNSUPPORTED;
+  }
+  if (st == NF_OK) st = check_batch(*s, n_pages, page_size, *b, err);
+  if (st == NF_OK && p) st = check_plan(*p, 32, err);
+  if (st == NF_OK && p) st = check_plan_batch(*p, b->n_tokens, err);
+  if (st != NF_OK) return set_err(st, "%s", err.c_str());
+  return NF_OK;
+}
+
+nf_status nf_layer_create(const nf_shape* s, const nf_weights* w, nf_layer** out) {
+  if (!s || !w || !out) return set_err(NF_ERR_INVALID_ARG, "nf_layer_create: null argument");
+  *out = nullptr;
+  std::string err;
+  nf_status st = check_shape(*s, err);
+  if (st != NF_OK) return set_err(st, "%s", err.c_str());
+  if (s->n_experts > 1 && s->dtype != NF_BF16)
+    return set_err(NF_ERR_UNSUPPORTED, "mixture-of-experts layers need dtype bf16");
+  if (!w->attn_norm || !w->w_qkv || !w->w_o || !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down)
+    return set_err(NF_ERR_INVALID_ARG, "nf_layer_create: a weight pointer is null");
+  nf_layer* L = new nf_layer();
+  L->s = *s;
+  L->w = *w;
+  auto fail = [&](nf_status st2) {
+    nf_layer_destroy(L);
+    return st2;
+  };
+  if (hipGetDevice(&L->device) != hipSuccess) return fail(set_err(NF_ERR_HIP, "hipGetDevice failed"));
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, L->device) != hipSuccess)
+    return fail(set_err(NF_ERR_HIP, "hipGetDeviceProperties failed"));
+  L->n_cus = prop.multiProcessorCount;
+  L->n_xcd = 8;
+  L->cus_per_xcd = std::max(1, L->n_cus / L->n_xcd);
+  L->plan = nf_plan{1, {0, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0};
+
+  const int dt = s->dtype;
+  const size_t eb = dtype_bytes(dt);
+  const int64_t Tm = s->max_tokens, H = s->hidden, F = s->ffn, k = s->top_k;
+  const int64_t nqd = (int64_t)s->n_q_heads * s->head_dim;
+  const int64_t Nqkv = (int64_t)(s->n_q_heads + 2 * s->n_kv_heads) * s->head_dim;
+  struct {
+    DevBuf* b;
+    size_t bytes;
+  } allocs[] = {
+      {&L->h, Tm * H * eb},          {&L->qkv, Tm * Nqkv * eb}, {&L->q_rot, Tm * nqd * eb},
+      {&L->attn, Tm * nqd * eb},     {&L->x1, Tm * H * eb},     {&L->h2, Tm * H * eb},
+      {&L->act, Tm * k * F * eb},
+  };
+  for (auto& a : allocs)
+    if (ensure(*a.b, a.bytes) != hipSuccess) return fail(set_err(NF_ERR_HIP, "workspace allocation failed"));
+  if (s->n_experts > 1) {
+    if (ensure(L->y, Tm * k * H * 4) != hipSuccess || ensure(L->r_idx, Tm * k * 4) != hipSuccess ||
+        ensure(L->r_w, Tm * k * 4) != hipSuccess || ensure(L->r_perm, Tm * k * 4) != hipSuccess ||
+        ensure(L->r_inv, Tm * k * 4) != hipSuccess ||
+        ensure(L->r_off, (size_t)NF_MAX_NANO * (s->n_experts + 1) * 4) != hipSuccess)
+      return fail(set_err(NF_ERR_HIP, "router workspace allocation failed"));
+  }
+  // fp32 (cos, sin) of p * theta^(-2j/d), angles in fp64
+  const int half = s->head_dim / 2;
+  std::vector<float> cs((size_t)s->max_pos * half * 2);
+  for (int64_t p = 0; p < s->max_pos; ++p)
+    for (int j = 0; j < half; ++j) {
+      const double ang = (double)p * std::pow(s->rope_theta, -2.0 * j / s->head_dim);
+      cs[(p * half + j) * 2] = (float)std::cos(ang);
+      cs[(p * half + j) * 2 + 1] = (float)std::sin(ang);
+    }
+  if (ensure(L->cos_sin, cs.size() * 4) != hipSuccess ||
+      hipMemcpy(L->cos_sin.p, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+    return fail(set_err(NF_ERR_HIP, "cos/sin table upload failed"));
+  for (int j = 0; j < NF_MAX_NANO; ++j)
+    if (hipEventCreateWithFlags(&L->ev_app[j], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&L->ev_att[j], hipEventDisableTiming) != hipSuccess)
+      return fail(set_err(NF_ERR_HIP, "event creation failed"));
+  if (hipEventCreateWithFlags(&L->ev_start, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&L->ev_g, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&L->ev_a, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&L->stage_ev[0], hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&L->stage_ev[1], hipEventDisableTiming) != hipSuccess)
+    return fail(set_err(NF_ERR_HIP, "event creation failed"));
+  *out = L;
+  return NF_OK;
+}
+
+void nf_layer_destroy(nf_layer* L) {
+  if (!L) return;
+  (void)hipSetDevice(L->device);
+  (void)hipDeviceSynchronize();
+  for (auto& kv : L->pairs) {
+    if (kv.second.g) (void)hipStreamDestroy(kv.second.g);
+    if (kv.second.a) (void)hipStreamDestroy(kv.second.a);
+  }
+  for (DevBuf* b : {&L->h, &L->qkv, &L->q_rot, &L->attn, &L->x1, &L->h2, &L->act, &L->y, &L->r_idx, &L->r_w,
+                    &L->r_perm, &L->r_inv, &L->r_off, &L->splitk, &L->part_o, &L->part_ml, &L->meta, &L->cos_sin})
+    release(*b);
+  for (int i = 0; i < 2; ++i) {
+    if (L->stage[i]) (void)hipHostFree(L->stage[i]);
+    if (L->stage_ev[i]) (void)hipEventDestroy(L->stage_ev[i]);
+  }
+  for (int j = 0; j < NF_MAX_NANO; ++j) {
+    if (L->ev_app[j]) (void)hipEventDestroy(L->ev_app[j]);
+    if (L->ev_att[j]) (void)hipEventDestroy(L->ev_att[j]);
+  }
+  for (hipEvent_t e : {L->ev_start, L->ev_g, L->ev_a})
+    if (e) (void)hipEventDestroy(e);
+  for (auto& r : L->recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (hipEvent_t e : L->ev_free) (void)hipEventDestroy(e);
+  delete L;
+}
+
+nf_status nf_kv_pool_create(const nf_layer* L, int32_t n_pages, int32_t page_size, void* k_dev, void* v_dev,
+                            nf_kv_pool** out) {
+  if (!L || !k_dev || !v_dev || !out) return set_err(NF_ERR_INVALID_ARG, "nf_kv_pool_create: null argument");
+  *out = nullptr;
+  if (page_size != PAGE_SIZE) return set_err(NF_ERR_UNSUPPORTED, "page_size %d: only 16 is supported", page_size);
+  if (n_pages <= 0) return set_err(NF_ERR_INVALID_ARG, "n_pages must be positive");
+  nf_kv_pool* p = new nf_kv_pool();
+  p->layer = L;
+  p->n_pages = n_pages;
+  p->page_size = page_size;
+  p->k = k_dev;
+  p->v = v_dev;
+  *out = p;
+  return NF_OK;
+}
+
+void nf_kv_pool_destroy(nf_kv_pool* p) { delete p; }
+
+nf_status nf_plan_set(nf_layer* L, const nf_plan* p) {
+  if (!L || !p) return set_err(NF_ERR_INVALID_ARG, "nf_plan_set: null argument");
+  std::string err;
+  nf_status st = check_plan(*p, L->cus_per_xcd, err);
+  if (st != NF_OK) return set_err(st, "%s", err.c_str());
+  if (p->n_streams == 2) {
+    HIP_TRY(hipSetDevice(L->device));
+    StreamPair pr;
+    st = get_pair(L, p->gemm_cus_per_xcd, pr);
+    if (st != NF_OK) return st;
+  }
+  L->plan = *p;
+  return NF_OK;
+}
+
+nf_status nf_plan_get(const nf_layer* L, nf_plan* p) {
+  if (!L || !p) return set_err(NF_ERR_INVALID_ARG, "nf_plan_get: null argument");
+  *p = L->plan;
+  return NF_OK;
+}
+
+nf_status nf_layer_step(nf_layer* L, nf_kv_pool* P, const nf_batch* b, void* stream) {
+  if (!L || !P || !b) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: null argument");
+  if (P->layer != L) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: pool belongs to another layer");
+  return step_impl(L, P, b, (hipStream_t)stream, L->plan);
+}
+
+nf_status nf_layer_intermediate(const nf_layer* L, int32_t which, const void** dev, int64_t* stride) {
+  if (!L || !dev || !stride) return set_err(NF_ERR_INVALID_ARG, "nf_layer_intermediate: null argument");
+  const nf_shape& s = L->s;
+  const int64_t nqd = (int64_t)s.n_q_heads * s.head_dim;
+  switch (which) {
+    case 0: *dev = L->q_rot.p; *stride = nqd; break;
+    case 1: *dev = L->attn.p; *stride = nqd; break;
+    case 2: *dev = L->x1.p; *stride = s.hidden; break;
+    case 3: *dev = L->act.p; *stride = s.ffn; break;
+    case 4: *dev = L->qkv.p; *stride = (int64_t)(s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim; break;
+    case 5: *dev = L->r_idx.p; *stride = s.top_k; break;
+    case 6: *dev = L->r_w.p; *stride = s.top_k; break;
+    case 7: *dev = L->r_perm.p; *stride = 1; break;
+    case 8: *dev = L->r_off.p; *stride = s.n_experts + 1; break;
+    default: return set_err(NF_ERR_INVALID_ARG, "nf_layer_intermediate: unknown index %d", which);
+  }
+  if (!*dev) return set_err(NF_ERR_INVALID_ARG, "nf_layer_intermediate: %d not held by this layer", which);
+  return NF_OK;
+}
+
+nf_status nf_profile_enable(nf_layer* L, int32_t on) {
+  if (!L) return set_err(NF_ERR_INVALID_ARG, "nf_profile_enable: null layer");
+  L->prof = on != 0;
+  for (auto& r : L->recs) {
+    L->ev_free.push_back(r.a);
+    L->ev_free.push_back(r.b);
+  }
+  L->recs.clear();
+  for (int k = 0; k < K_COUNT; ++k) {
+    L->prof_ms[k] = 0;
+    L->prof_n[k] = 0;
+  }
+  return NF_OK;
+}
+
+nf_status nf_profile_read(nf_layer* L, int32_t max_kinds, const char** names, int64_t* launches,
+                          double* total_ms, int32_t* n_kinds) {
+  if (!L || !n_kinds) return set_err(NF_ERR_INVALID_ARG, "nf_profile_read: null argument");
+  for (auto& r : L->recs) {
+    HIP_TRY(hipEventSynchronize(r.b));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+    L->prof_ms[r.kind] += ms;
+    L->prof_n[r.kind] += 1;
+    L->ev_free.push_back(r.a);
+    L->ev_free.push_back(r.b);
+  }
+  L->recs.clear();
+  int n = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    if (!L->prof_n[k]) continue;
+    if (n < max_kinds) {
+      if (names) names[n] = kKindNames[k];
+      if (launches) launches[n] = L->prof_n[k];
+      if (total_ms) total_ms[n] = L->prof_ms[k];
+    }
+    ++n;
+  }
+  *n_kinds = n;
+  return NF_OK;
+}
+
+nf_status nf_probe_cu_map(int32_t* xcc, int32_t n) {
+  if (!xcc || n <= 0) return set_err(NF_ERR_INVALID_ARG, "nf_probe_cu_map: bad argument");
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  std::vector<int> map;
+  nf_status st = measure_cu_map(dev, prop.multiProcessorCount, map);
+  if (st != NF_OK) return st;
+  for (int i = 0; i < n; ++i) xcc[i] = i < (int)map.size() ? map[i] : -1;
+  return NF_OK;
+}
+
+nf_status nf_probe_mfma_bf16_tflops(double* tflops) {
+  if (!tflops) return set_err(NF_ERR_INVALID_ARG, "nf_probe_mfma_bf16_tflops: null argument");
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  float* sink = nullptr;
+  HIP_TRY(hipMalloc(&sink, 1024 * sizeof(float)));
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  const int blocks = prop.multiProcessorCount * 4, iters = 4096;
+  double best = 0;
+  for (int rep = 0; rep < 4; ++rep) {
+    HIP_TRY(hipEventRecord(e0, nullptr));
+    HIP_TRY(probe_mfma(blocks, iters, sink, nullptr));
+    HIP_TRY(hipEventRecord(e1, nullptr));
+    HIP_TRY(hipEventSynchronize(e1));
+    float ms = 0;
+    HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+    const double flops = (double)blocks * 4 /*waves*/ * iters * 8 /*chains*/ * (16.0 * 16 * 32 * 2);
+    if (rep > 0) best = std::max(best, flops / (ms * 1e-3) / 1e12);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  (void)hipFree(sink);
+  *tflops = best;
+  return NF_OK;
+}
+
+nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps) {
+  if (!gbps || bytes < (1u << 20)) return set_err(NF_ERR_INVALID_ARG, "nf_probe_hbm_read_gbps: bad argument");
+  bytes &= ~(size_t)15;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  void* buf = nullptr;
+  float* sink = nullptr;
+  HIP_TRY(hipMalloc(&buf, bytes));
+  HIP_TRY(hipMalloc(&sink, 1024 * sizeof(float)));
+  HIP_TRY(hipMemset(buf, 1, bytes));
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  double best = 0;
+  for (int rep = 0; rep < 6; ++rep) {
+    HIP_TRY(hipEventRecord(e0, nullptr));
+    HIP_TRY(probe_read(buf, bytes, sink, prop.multiProcessorCount * 8, nullptr));
+    HIP_TRY(hipEventRecord(e1, nullptr));
+    HIP_TRY(hipEventSynchronize(e1));
+    float ms = 0;
+    HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+    if (rep > 0) best = std::max(best, (double)bytes / (ms * 1e-3) / 1e9);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  (void)hipFree(buf);
+  (void)hipFree(sink);
+  *gbps = best;
+  return NF_OK;
+}
+
+nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_search_opts* o, nf_plan* out,
+                         double* times_ms, void* stream);
+
+}  // extern "C"
+
+// =============================================================== plan search
+// Profile-driven search over the four plan dimensions (count, sizes, order,
+// CU split) for one batch; replaces the pages' MILP-based parameter search
+// ("Search Space 4D" card on the do-not-panic NanoFlow page; Gurobi note on
+// the ossradar page).  Every candidate is timed on the device with this batch.
+namespace {
+
+struct Cand {
+  nf_plan plan;
+  double ms = 0;
+};
+
+// Nano-batch boundaries that balance attention work (KV pages) plus GEMM rows.
+void balanced_sizes(const nf_batch* b, int count, int32_t* sizes) {
+  const int T = b->n_tokens;
+  std::vector<double> cost(T, 0.0);
+  double total = 0;
+  for (int r = 0; r < b->n_requests; ++r)
+    for (int i = 0; i < b->req_q_len[r]; ++i) {
+      const int t = b->req_q_start[r] + i;
+      const double pages = (b->pos[t] + 1) / 16.0;
+      cost[t] = pages + 8.0;             // KV pages read + a row of GEMM work
+      total += cost[t];
+    }
+  int t = 0;
+  double acc = 0;
+  for (int j = 0; j < count; ++j) {
+    const int start = t;
+    const double goal = total * (j + 1) / count;
+    while (t < T - (count - 1 - j) && (acc + cost[t] <= goal || t == start)) acc += cost[t++];
+    if (j == count - 1) t = T;
+    sizes[j] = t - start;
+  }
+}
+
+}  // namespace
+
+extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_search_opts* o,
+                                    nf_plan* out, double* times_ms, void* stream) {
+  if (!L || !P || !b || !out) return set_err(NF_ERR_INVALID_ARG, "nf_plan_search: null argument");
+  nf_search_opts opts{4, 2, 5, 8};
+  if (o) opts = *o;
+  opts.max_count = std::max(1, std::min(opts.max_count, NF_MAX_NANO));
+  opts.reps = std::max(1, opts.reps);
+  hipStream_t s = (hipStream_t)stream;
+  const int T = b->n_tokens;
+  std::vector<Cand> cands;
+  nf_plan base{1, {T, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0};
+  cands.push_back({base});
+  const int splits[] = {0, 8, 12, 16, 20, 24};
+  for (int k = 2; k <= opts.max_count; ++k) {
+    if (T < k) break;
+    nf_plan eq = base, bal = base;
+    eq.count = bal.count = k;
+    for (int j = 0; j < k; ++j) eq.sizes[j] = T / k + (j < T % k ? 1 : 0);
+    balanced_sizes(b, k, bal.sizes);
+    for (const nf_plan& pz : {eq, bal}) {
+      for (int sp : splits) {
+        if (sp >= L->cus_per_xcd) continue;
+        nf_plan c = pz;
+        c.n_streams = 2;
+        c.gemm_cus_per_xcd = sp;
+        cands.push_back({c});
+      }
+    }
+  }
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  int best = -1;
+  for (size_t i = 0; i < cands.size(); ++i) {
+    nf_status st = NF_OK;
+    for (int w = 0; w < opts.warmup && st == NF_OK; ++w) st = step_impl(L, P, b, s, cands[i].plan);
+    if (st != NF_OK) {
+      (void)hipEventDestroy(e0);
+      (void)hipEventDestroy(e1);
+      return st;
+    }
+    HIP_TRY(hipEventRecord(e0, s));
+    for (int r = 0; r < opts.reps && st == NF_OK; ++r) st = step_impl(L, P, b, s, cands[i].plan);
+    HIP_TRY(hipEventRecord(e1, s));
+    HIP_TRY(hipEventSynchronize(e1));
+    if (st != NF_OK) return st;
+    float ms = 0;
+    HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+    cands[i].ms = ms / opts.reps;
+    if (best < 0 || cands[i].ms < cands[best].ms) best = (int)i;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  L->plan = cands[best].plan;
+  *out = cands[best].plan;
+  if (times_ms) {
+    times_ms[0] = cands[best].ms;
+    times_ms[1] = cands[best].ms;
+  }
+  return NF_OK;
+}

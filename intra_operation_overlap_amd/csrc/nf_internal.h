@@ -1,0 +1,108 @@
+// Host-side internal interfaces between the C ABI and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nf_host.h"
+
+namespace nf {
+
+// ---------------------------------------------------------------- GEMM
+// C[M][N] = epilogue(A[M][K] . B[N][K]^T): both operands K-contiguous.
+enum GemmMode : int {
+  GEMM_STORE = 0,     // C (layer dtype) = acc
+  GEMM_RESIDUAL = 1,  // C = R + acc
+  GEMM_SWIGLU = 2,    // C[:, n] = silu(A.Bg[n]) * (A.Bu[n]); N counts act columns
+  GEMM_F32OUT = 3,    // C (fp32) = acc
+};
+
+struct GemmArgs {
+  const void* A = nullptr; int64_t lda = 0;
+  const void* B = nullptr; const void* B2 = nullptr; int64_t ldb = 0;  // B2: up rows (SWIGLU)
+  void* C = nullptr; int64_t ldc = 0;
+  const void* R = nullptr; int64_t ldr = 0;
+  int M = 0, N = 0, K = 0;
+  int mode = GEMM_STORE;
+  // grouped GEMM (mixture of experts): group g owns rows group_off[g] ..
+  // group_off[g+1]-1 (device array); its B is B + g * b_group_stride.
+  const int32_t* group_off = nullptr; int n_groups = 1; int64_t b_group_stride = 0;
+  int max_group_rows = 0;                 // bound on any group's rows (grid sizing)
+  // optional row gather: A row of output row i is a_rows[i] / a_row_div
+  const int32_t* a_rows = nullptr; int a_row_div = 1;
+};
+
+struct GemmPlan {
+  int cfg = 0;        // tile configuration id
+  int k_splits = 1;   // split-K factor (fp32 partials + reduce)
+};
+
+// Chooses a tile configuration and split-K for a problem given the number of
+// CUs its stream may use.
+GemmPlan gemm_choose(const GemmArgs& a, int cus);
+// Workspace bytes the split-K path needs for this problem/plan.
+size_t gemm_workspace_bytes(const GemmArgs& a, const GemmPlan& p);
+// Called between the main kernel and the split-K reduce (phase 1) so callers
+// can bracket each kernel on its stream.
+struct LaunchHook {
+  void (*fn)(void* ctx, int phase) = nullptr;
+  void* ctx = nullptr;
+};
+// Launches (1 kernel, or 2 with split-K).  `ws` must hold gemm_workspace_bytes.
+hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s,
+                     const LaunchHook* hook = nullptr);
+hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- row ops
+hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps,
+                   hipStream_t s);
+
+struct RopeAppendArgs {
+  const void* qkv;          // [T][(nq+2nkv)d]
+  void* q_rot;              // [T][nq*d]
+  void* k_pool; void* v_pool;
+  const int32_t* pos;       // device [T]
+  const int32_t* tok_req;   // device [T]
+  const int32_t* page_indptr; const int32_t* page_indices;
+  const float* cos_sin;     // [max_pos][d/2][2]
+  int T, nq, nkv, d, page_size;
+};
+hipError_t rope_append(int dtype, const RopeAppendArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* q_rot;        // [T][nq*d]
+  const void* k_pool; const void* v_pool;
+  void* attn;               // [T][nq*d]
+  float* part_o;            // [n_partials][nkv][16][d]   (unnormalised)
+  float* part_ml;           // [n_partials][nkv][16][2]   (max, sum)
+  const AttnItem* items; int n_items;
+  const MergeItem* merges; int n_merges;
+  const int32_t* pos;       // device [T]
+  const int32_t* page_indptr; const int32_t* page_indices;
+  int nq, nkv, d, page_size;
+  float scale;
+};
+hipError_t attention(int dtype, const AttnArgs& a, hipStream_t s);
+hipError_t attention_merge(int dtype, const AttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- MoE
+struct RouteArgs {
+  const float* logits;      // [T][E]
+  int32_t* idx;             // [T][k]
+  float* w;                 // [T][k]
+  int32_t* perm;            // [T*k] assignment ids sorted by expert
+  int32_t* inv;             // [T*k] position of assignment a in perm
+  int32_t* offsets;         // [E+1]
+  int T, E, k;
+};
+hipError_t moe_route(const RouteArgs& a, hipStream_t s);
+// out[t] = x1[t] + sum_s w[t][s] * y[inv[t*k+s]]
+hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w,
+                       const int32_t* inv, void* out, int T, int H, int k, hipStream_t s);
+
+// ---------------------------------------------------------------- probes
+hipError_t probe_mfma(int n_blocks, int iters, float* sink, hipStream_t s);
+hipError_t probe_read(const void* buf, size_t bytes, float* sink, int n_blocks, hipStream_t s);
+hipError_t probe_hwid(uint32_t* out, hipStream_t s);   // out[0] = HW_ID, out[1] = XCC_ID
+
+}  // namespace nf

@@ -1,0 +1,173 @@
+"""Shared set-up for the GPU parity tests: seeded inputs on the device, the
+library objects over them, and oracle inputs built from the same tensors.
+(Expected values always come from the oracle, never from the GPU path.)"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+import time
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import oracle
+from intra_operation_overlap_amd import binding as B
+from intra_operation_overlap_amd import workload as W
+
+
+def log(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass
+class Setup:
+    wl: W.Workload
+    batch: W.Batch
+    weights: dict
+    acts: dict
+    k: torch.Tensor
+    v: torch.Tensor
+    out: torch.Tensor
+    layer: B.Layer
+    pool: B.KVPool
+    hb: B.HostBatch
+    max_tokens: int
+    max_pos: int
+
+
+def setup(wl: W.Workload, batch: Optional[W.Batch] = None, max_tokens: Optional[int] = None,
+          max_pos: Optional[int] = None, weights=None) -> Setup:
+    dev = "cuda"
+    batch = batch if batch is not None else W.make_batch(wl)
+    weights = weights if weights is not None else W.make_weights(wl, dev)
+    acts = W.make_activations(wl, batch, dev)
+    k, v = W.make_pool(wl, batch.n_pages, dev)
+    mt = max_tokens or max(batch.n_tokens, 1)
+    if max_pos is not None:
+        mp = max_pos
+    else:
+        mp = int(batch.pos.max()) + 1 if batch.n_tokens else 16
+    layer = B.Layer(wl.shape, weights, mt, mp)
+    pool = B.KVPool(layer, batch.n_pages, wl.shape.page_size, k, v)
+    out = torch.empty_like(acts["x"])
+    hb = B.HostBatch(batch, acts["x"].data_ptr(), out.data_ptr(),
+                     acts["router_logits"].data_ptr() if "router_logits" in acts else None)
+    return Setup(wl, batch, weights, acts, k, v, out, layer, pool, hb, mt, mp)
+
+
+def stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def run_step(S: Setup) -> None:
+    S.layer.step(S.pool, S.hb, stream())
+    torch.cuda.synchronize()
+
+
+def intermediate(S: Setup, which: int, rows: int, cols: int, dtype) -> torch.Tensor:
+    ptr, stride = S.layer.intermediate(which)
+    assert stride == cols
+    t = torch.empty(rows, cols, dtype=dtype, device="cuda")
+    B.copy_device(t, ptr, t.numel() * t.element_size())
+    return t
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return W.to_f64(t)
+
+
+def weights_np(S: Setup) -> dict:
+    """Exact values of the weights; float32 arrays hold bf16 values exactly and
+    numpy promotes them to fp64 inside the oracle's products."""
+    return {k: v.detach().to("cpu", torch.float32).numpy() for k, v in S.weights.items()}
+
+
+def oracle_subset(S: Setup, requests: List[int], k_pool_before: torch.Tensor, v_pool_before: torch.Tensor,
+                  w_np: Optional[dict] = None):
+    """Runs the oracle on the given requests only (rows are independent).
+    Pool pages of those requests are gathered into a compact pool.
+    Returns (oracle result, token rows of the full batch, page map)."""
+    sub, rows = W.sub_batch(S.batch, requests)
+    pages = np.asarray(sub.page_indices, np.int64)
+    remap = np.arange(len(pages))
+    kp = f64(k_pool_before[torch.as_tensor(pages, device=k_pool_before.device)])
+    vp = f64(v_pool_before[torch.as_tensor(pages, device=v_pool_before.device)])
+    x = f64(S.acts["x"][torch.as_tensor(rows, device="cuda")])
+    bd = dict(x=x, req_q_start=sub.req_q_start, req_q_len=sub.req_q_len, req_pos0=sub.req_pos0,
+              pos=sub.pos, page_indptr=sub.page_indptr, page_indices=remap)
+    if "router_logits" in S.acts:
+        bd["router_logits"] = f64(S.acts["router_logits"][torch.as_tensor(rows, device="cuda")])
+    res = oracle.layer_step(S.wl.shape.as_dict(), w_np if w_np is not None else weights_np(S), bd, kp, vp)
+    return res, rows, pages
+
+
+def normwise(g: np.ndarray, r: np.ndarray) -> float:
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    den = np.max(np.abs(r)) if r.size else 1.0
+    return float(np.max(np.abs(g - r)) / den) if r.size else 0.0
+
+
+def tolerance(wl: W.Workload) -> float:
+    return 1e-4 if wl.shape.dtype == "f32" else 2e-2
+
+
+def written_slots(batch: W.Batch, requests: Optional[List[int]] = None):
+    """(page, slot) of every position the step writes, per token in batch order."""
+    reqs = range(batch.n_requests) if requests is None else requests
+    out = []
+    for r in reqs:
+        for i in range(batch.req_q_len[r]):
+            p = batch.req_pos0[r] + i
+            out.append((int(batch.page_indices[batch.page_indptr[r] + p // 16]), int(p % 16)))
+    return out
+
+
+def check_sentinel(S: Setup, k_before: torch.Tensor, v_before: torch.Tensor) -> None:
+    """Every pool slot the step does not name must be bit-identical."""
+    P = S.batch.n_pages
+    mask = torch.ones(P, 16, dtype=torch.bool, device="cuda")
+    ws = written_slots(S.batch)
+    if ws:
+        idx = torch.as_tensor(ws, device="cuda")
+        mask[idx[:, 0], idx[:, 1]] = False
+    kd = (S.k != k_before).any(dim=-1).any(dim=1)           # [P, 16]
+    vd = (S.v != v_before).any(dim=2).any(dim=1)            # [P, 16]
+    assert not bool((kd & mask).any()), "K pool changed outside the written slots"
+    assert not bool((vd & mask).any()), "V pool changed outside the written slots"
+
+
+def compare_rows(S: Setup, res: dict, rows: np.ndarray, pages: np.ndarray, requests: List[int]) -> dict:
+    """Normwise errors of out, x1, the two branch deltas, q_rot, attn and the
+    K/V values written for the given rows."""
+    s = S.wl.shape
+    T = S.batch.n_tokens
+    dt = torch.float32 if s.dtype == "f32" else torch.bfloat16
+    ridx = torch.as_tensor(rows, device="cuda")
+    out = f64(S.out[ridx])
+    x = f64(S.acts["x"][ridx])
+    x1 = f64(intermediate(S, 2, T, s.hidden, dt)[ridx])
+    q_rot = f64(intermediate(S, 0, T, s.n_q_heads * s.head_dim, dt)[ridx])
+    attn = f64(intermediate(S, 1, T, s.n_q_heads * s.head_dim, dt)[ridx])
+    errs = {
+        "out": normwise(out, res["out"]),
+        "x1": normwise(x1, res["x1"]),
+        "d_attn": normwise(x1 - x, res["x1"] - x),
+        "d_ffn": normwise(out - x1, res["out"] - res["x1"]),
+        "q_rot": normwise(q_rot, res["q_rot"].reshape(len(rows), -1)),
+        "attn": normwise(attn, res["attn"]),
+    }
+    # K/V written: slot values of the sampled requests' new positions
+    ws_full = written_slots(S.batch, requests)
+    page_pos = {int(p): i for i, p in enumerate(pages)}     # pool page -> compact oracle page
+    pg = torch.as_tensor([p for p, _ in ws_full], device="cuda")
+    sl = torch.as_tensor([s_ for _, s_ in ws_full], device="cuda")
+    kg = f64(S.k[pg, :, sl, :])
+    vg = f64(S.v[pg, :, :, sl])
+    kr = np.stack([res["k_pool"][page_pos[p], :, s_, :] for p, s_ in ws_full])
+    vr = np.stack([res["v_pool"][page_pos[p], :, :, s_] for p, s_ in ws_full])
+    errs["k_new"] = normwise(kg, kr)
+    errs["v_new"] = normwise(vg, vr)
+    return errs

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/nf.h declares, and its host-side validation returns the documented
+status codes before anything would launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from intra_operation_overlap_amd import binding as B
+from intra_operation_overlap_amd import workload as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "nf.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nf_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 18
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in B._SIGS, f"binding lacks {n}"
+
+
+def test_status_strings():
+    L = B.lib()
+    assert L.nf_status_string(B.NF_OK) == b"ok"
+    assert L.nf_status_string(B.NF_ERR_NO_PLAN) == b"no plan"
+
+
+def _small():
+    wl = W.WORKLOADS["c1"]
+    batch = W.make_batch(wl)
+    shape = B.make_shape(wl.shape, max_tokens=64, max_pos=512)
+    return wl, batch, shape
+
+
+def _validate(shape, batch, n_pages=None, page_size=16, plan=None, x=0x1000, out=0x2000, logits=None):
+    hb = B.HostBatch(batch, x, out, logits)
+    return B.batch_validate(shape, batch.n_pages if n_pages is None else n_pages, page_size, hb, plan)
+
+
+def _copy(batch, **kw):
+    import dataclasses
+    arrays = {k: np.array(getattr(batch, k), copy=True) for k in
+              ("req_q_start", "req_q_len", "req_pos0", "pos", "page_indptr", "page_indices")}
+    arrays.update(kw)
+    return dataclasses.replace(batch, **arrays)
+
+
+def test_validate_accepts_valid_batch_and_plans():
+    wl, batch, shape = _small()
+    assert _validate(shape, batch) == B.NF_OK
+    assert _validate(shape, batch, plan=B.make_plan(2, [8, 8], n_streams=2, gemm_cus_per_xcd=16)) == B.NF_OK
+    assert _validate(shape, batch, plan=B.make_plan(1, [0])) == B.NF_OK
+
+
+def test_validate_rejects_bad_batches():
+    wl, batch, shape = _small()
+    # page index outside the pool
+    bad = _copy(batch)
+    bad.page_indices[3] = batch.n_pages
+    assert _validate(shape, bad) == B.NF_ERR_OUT_OF_RANGE
+    # one page owned by two requests
+    bad = _copy(batch)
+    r0 = bad.page_indices[bad.page_indptr[0]]
+    bad.page_indices[bad.page_indptr[1]] = r0
+    assert _validate(shape, bad) == B.NF_ERR_INVALID_ARG
+    # positions inconsistent with pos0
+    bad = _copy(batch)
+    bad.pos[2] += 1
+    assert _validate(shape, bad) == B.NF_ERR_INVALID_ARG
+    # too few pages for the new position
+    bad = _copy(batch)
+    bad.req_pos0[0] = (bad.page_indptr[1] - bad.page_indptr[0]) * 16
+    bad.pos[0] = bad.req_pos0[0]
+    assert _validate(shape, bad) == B.NF_ERR_OUT_OF_RANGE
+    # requests not contiguous
+    bad = _copy(batch)
+    bad.req_q_start[1] = 2
+    assert _validate(shape, bad) == B.NF_ERR_INVALID_ARG
+    # out aliasing x
+    assert _validate(shape, batch, x=0x1000, out=0x1000) == B.NF_ERR_INVALID_ARG
+    # unsupported page size
+    assert _validate(shape, batch, page_size=8) == B.NF_ERR_UNSUPPORTED
+
+
+def test_validate_rejects_capacity_and_plan_errors():
+    wl, batch, shape = _small()
+    small = B.make_shape(wl.shape, max_tokens=8, max_pos=512)
+    assert _validate(small, batch) == B.NF_ERR_OUT_OF_RANGE
+    short = B.make_shape(wl.shape, max_tokens=64, max_pos=int(batch.pos.max()))
+    assert _validate(short, batch) == B.NF_ERR_OUT_OF_RANGE
+    assert _validate(shape, batch, plan=B.make_plan(2, [8, 7])) == B.NF_ERR_NO_PLAN
+    assert _validate(shape, batch, plan=B.make_plan(2, [16, 0])) == B.NF_ERR_NO_PLAN
+    assert _validate(shape, batch, plan=B.make_plan(5, [4, 4, 4, 4])) == B.NF_ERR_INVALID_ARG
+    assert _validate(shape, batch, plan=B.make_plan(1, [16], n_streams=1, gemm_cus_per_xcd=8)) == B.NF_ERR_INVALID_ARG
+    assert _validate(shape, batch, plan=B.make_plan(1, [16], n_streams=2, gemm_cus_per_xcd=32)) == B.NF_ERR_OUT_OF_RANGE
+
+
+def test_validate_moe_needs_logits_and_shape_rules():
+    wl = W.WORKLOADS["c5"]
+    batch = W.make_batch(wl, n_decode=4)
+    shape = B.make_shape(wl.shape, max_tokens=64, max_pos=4096)
+    assert _validate(shape, batch) == B.NF_ERR_INVALID_ARG
+    assert _validate(shape, batch, logits=0x3000) == B.NF_OK
+    bad = B.make_shape(W.Shape(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=688), 64, 512)
+    assert _validate(bad, batch) == B.NF_ERR_UNSUPPORTED           # bf16 needs head_dim 128
+    bad = B.make_shape(W.Shape(hidden=256, n_q_heads=6, n_kv_heads=4, head_dim=128, ffn=688), 64, 512)
+    assert _validate(bad, batch) == B.NF_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_valid():
+    wl, batch, shape = _small()
+    empty = W.Batch(0, np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32),
+                    np.zeros(0, np.int32), np.zeros(1, np.int32), np.zeros(0, np.int32), 4)
+    assert _validate(shape, empty) == B.NF_OK
+
+
+def test_kv_pool_bytes():
+    wl, batch, shape = _small()
+    kb, vb = B.kv_pool_bytes(shape, 10, 16)
+    assert kb == vb == 10 * 2 * 16 * 64 * 4
+    with pytest.raises(B.NfError) as e:
+        B.kv_pool_bytes(shape, 10, 32)
+    assert e.value.status == B.NF_ERR_UNSUPPORTED

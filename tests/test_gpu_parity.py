@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (normwise max relative error, per tensor): 1e-4 for fp32 layers,
+2e-2 for bf16 layers; index handling (which pool slots change, which key a
+one-hot query selects, MoE routing and permutation) must be bit-exact."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from intra_operation_overlap_amd import binding as B
+from intra_operation_overlap_amd import workload as W
+from tests import gpu_harness as GH
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _plans_for(T):
+    half = T // 2
+    return {
+        "k1_one_stream": B.make_plan(1, [T]),
+        "k2_two_streams_unmasked": B.make_plan(2, [half, T - half], n_streams=2),
+        "k2_masked16": B.make_plan(2, [half, T - half], n_streams=2, gemm_cus_per_xcd=16),
+        "k3_sequential_masked8": B.make_plan(3, [T // 3, T // 3, T - 2 * (T // 3)], order=B.NF_ORDER_SEQUENTIAL,
+                                             n_streams=2, gemm_cus_per_xcd=8),
+        "k4_masked24": B.make_plan(4, [T // 4] * 3 + [T - 3 * (T // 4)], n_streams=2, gemm_cus_per_xcd=24),
+    }
+
+
+def _full_check(S, plan_name, plan):
+    GH.log(f"step {S.wl.name} plan={plan_name} T={S.batch.n_tokens}")
+    S.layer.set_plan(plan)
+    k0, v0 = S.k.clone(), S.v.clone()
+    GH.run_step(S)
+    GH.check_sentinel(S, k0, v0)
+    reqs = list(range(S.batch.n_requests))
+    res, rows, pages = GH.oracle_subset(S, reqs, k0, v0)
+    errs = GH.compare_rows(S, res, rows, pages, reqs)
+    GH.log(f"  errors {errs}")
+    tol = GH.tolerance(S.wl)
+    for k, e in errs.items():
+        assert e <= tol, (plan_name, k, e)
+    S.k.copy_(k0)
+    S.v.copy_(v0)
+    return errs
+
+
+# ---------------------------------------------------------------- tiny fp32 layer
+
+@pytest.fixture(scope="module")
+def c1():
+    return GH.setup(W.WORKLOADS["c1"])
+
+
+@pytest.mark.parametrize("plan_name", list(_plans_for(16)))
+def test_c1_fp32_full_parity(c1, plan_name):
+    _full_check(c1, plan_name, _plans_for(c1.batch.n_tokens)[plan_name])
+
+
+# ---------------------------------------------------------------- small bf16 layer
+
+SMALL_BF16 = W.Workload("small_bf16",
+                        W.Shape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=688, dtype="bf16",
+                                rope_theta=5e5),
+                        n_decode=40, ctx_range=(1, 300), prefill=(37, 45), seed=77)
+
+
+@pytest.fixture(scope="module")
+def small():
+    return GH.setup(SMALL_BF16)
+
+
+@pytest.mark.parametrize("plan_name", list(_plans_for(85)))
+def test_small_bf16_full_parity(small, plan_name):
+    _full_check(small, plan_name, _plans_for(small.batch.n_tokens)[plan_name])
+
+
+def test_small_bf16_prefill_from_zero_and_g8():
+    wl = W.Workload("g8", W.Shape(hidden=1024, n_q_heads=8, n_kv_heads=1, head_dim=128, ffn=512, dtype="bf16",
+                                  rope_theta=1e4),
+                    n_decode=9, ctx_range=(100, 200), prefill=(0, 70), seed=78)
+    S = GH.setup(wl)
+    _full_check(S, "k1", B.make_plan(1, [S.batch.n_tokens]))
+    _full_check(S, "k2_split_prefill", B.make_plan(2, [40, S.batch.n_tokens - 40], n_streams=2, gemm_cus_per_xcd=16))
+
+
+def test_plan_invariance_bit_exact(small):
+    """Same nano-batch sizes and the same CU budget give bit-identical outputs
+    whatever the stream count and operation order."""
+    T = small.batch.n_tokens
+    outs = []
+    for plan in (B.make_plan(2, [30, T - 30]),
+                 B.make_plan(2, [30, T - 30], order=B.NF_ORDER_SEQUENTIAL),
+                 B.make_plan(2, [30, T - 30], n_streams=2)):
+        small.layer.set_plan(plan)
+        k0, v0 = small.k.clone(), small.v.clone()
+        GH.run_step(small)
+        outs.append((small.out.clone(), small.k.clone(), small.v.clone()))
+        small.k.copy_(k0)
+        small.v.copy_(v0)
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+def test_repeated_steps_are_idempotent(small):
+    small.layer.set_plan(B.make_plan(2, [42, small.batch.n_tokens - 42], n_streams=2, gemm_cus_per_xcd=12))
+    GH.run_step(small)
+    a = (small.out.clone(), small.k.clone())
+    for _ in range(3):
+        GH.run_step(small)
+    assert torch.equal(a[0], small.out) and torch.equal(a[1], small.k)
+
+
+def test_empty_batch_is_a_no_op(small):
+    empty = W.Batch(0, np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32),
+                    np.zeros(1, np.int32), np.zeros(0, np.int32), small.batch.n_pages)
+    hb = B.HostBatch(empty, small.acts["x"].data_ptr(), small.out.data_ptr())
+    small.layer.set_plan(B.make_plan(1, [0]))
+    k0 = small.k.clone()
+    small.layer.step(small.pool, hb, GH.stream())
+    torch.cuda.synchronize()
+    assert torch.equal(k0, small.k)
+
+
+def test_invalid_batch_launches_nothing(small):
+    bad = dataclasses.replace(small.batch, page_indices=small.batch.page_indices.copy())
+    bad.page_indices[0] = small.batch.n_pages + 5
+    hb = B.HostBatch(bad, small.acts["x"].data_ptr(), small.out.data_ptr())
+    small.out.fill_(7.0)
+    with pytest.raises(B.NfError) as e:
+        small.layer.step(small.pool, hb, GH.stream())
+    torch.cuda.synchronize()
+    assert e.value.status == B.NF_ERR_OUT_OF_RANGE
+    assert bool((small.out == 7.0).all())
+
+
+# ---------------------------------------------------------------- one-hot probe
+
+@pytest.mark.parametrize("wl_name", ["c1", "small_bf16"])
+def test_one_hot_attention_selects_exact_key(wl_name):
+    """Prior keys crafted so one chosen position's score beats every other by
+    >= 100: attention must return that position's value bit-exactly, which
+    pins the page-table lookup and the slot arithmetic."""
+    wl = W.WORKLOADS["c1"] if wl_name == "c1" else SMALL_BF16
+    S = GH.setup(wl)
+    b = S.batch
+    S.layer.set_plan(B.make_plan(1, [b.n_tokens]))
+    GH.run_step(S)
+    s = wl.shape
+    dt = torch.float32 if s.dtype == "f32" else torch.bfloat16
+    q = GH.intermediate(S, 0, b.n_tokens, s.n_q_heads * s.head_dim, dt).float().view(b.n_tokens, s.n_q_heads, s.head_dim)
+    rng = np.random.Generator(np.random.PCG64(5))
+    G = s.n_q_heads // s.n_kv_heads
+    chosen = {}
+    for r in range(b.n_requests):
+        if b.req_q_len[r] != 1 or b.req_pos0[r] < 1:
+            continue
+        t = b.req_q_start[r]
+        p0 = int(b.req_pos0[r])
+        j = int(rng.integers(0, p0))          # a cached position
+        pages = b.page_indices[b.page_indptr[r]:b.page_indptr[r + 1]]
+        # zero every cached key of this request ...
+        pi = torch.as_tensor(pages[np.arange(p0) // 16], device="cuda")
+        si = torch.as_tensor(np.arange(p0) % 16, device="cuda")
+        S.k[pi, :, si, :] = 0
+        for kh in range(s.n_kv_heads):
+            # ... then point key j along the group's first query head: score 400
+            qh = q[t, kh * G]
+            S.k[int(pages[j // 16]), kh, j % 16, :] = (qh * (400.0 * s.head_dim ** 0.5 / float(qh.norm()) ** 2)).to(dt)
+        chosen[r] = j
+    # only the group's first head is aligned with the key; the check uses it alone
+    GH.run_step(S)
+    attn = GH.intermediate(S, 1, b.n_tokens, s.n_q_heads * s.head_dim, dt).view(b.n_tokens, s.n_q_heads, s.head_dim)
+    checked = 0
+    for r, j in chosen.items():
+        t = b.req_q_start[r]
+        pages = b.page_indices[b.page_indptr[r]:b.page_indptr[r + 1]]
+        for kh in range(s.n_kv_heads):
+            v = S.v[int(pages[j // 16]), kh, :, j % 16]
+            assert torch.equal(attn[t, kh * G], v), (r, kh, j)
+            checked += 1
+    assert checked > 0
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def _sampled_check(S, requests, w_np=None):
+    k0, v0 = S.k.clone(), S.v.clone()
+    GH.log(f"step {S.wl.name} T={S.batch.n_tokens} plan={B.plan_dict(S.layer.get_plan())}")
+    GH.run_step(S)
+    GH.check_sentinel(S, k0, v0)
+    GH.log("oracle on sampled requests")
+    res, rows, pages = GH.oracle_subset(S, requests, k0, v0, w_np)
+    errs = GH.compare_rows(S, res, rows, pages, requests)
+    GH.log(f"  errors {errs}")
+    for k, e in errs.items():
+        assert e <= GH.tolerance(S.wl), (k, e)
+    S.k.copy_(k0)
+    S.v.copy_(v0)
+    return res, rows
+
+
+def _sample_requests(b, n, seed=3):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dec = [r for r in range(b.n_requests) if b.req_q_len[r] == 1]
+    pick = sorted(rng.choice(dec, size=min(n, len(dec)), replace=False).tolist())
+    pre = [r for r in range(b.n_requests) if b.req_q_len[r] > 1]
+    return pick + pre
+
+
+@pytest.mark.slow
+def test_c2_full_size_sampled():
+    S = GH.setup(W.WORKLOADS["c2"])
+    S.layer.set_plan(B.make_plan(1, [S.batch.n_tokens]))
+    _sampled_check(S, _sample_requests(S.batch, 8))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wl_name", ["c3", "c4"])
+def test_mixed_full_size_sampled(wl_name):
+    S = GH.setup(W.WORKLOADS[wl_name])
+    T = S.batch.n_tokens
+    S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], n_streams=2, gemm_cus_per_xcd=16))
+    w_np = GH.weights_np(S)
+    _sampled_check(S, _sample_requests(S.batch, 6), w_np)
+    S.layer.set_plan(B.make_plan(1, [T]))
+    _sampled_check(S, _sample_requests(S.batch, 4, seed=4), w_np)
+
+
+# ---------------------------------------------------------------- mixture of experts
+
+SMALL_MOE = W.Workload("small_moe",
+                       W.Shape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=384, n_experts=8, top_k=2,
+                               dtype="bf16", rope_theta=1e6),
+                       n_decode=70, ctx_range=(1, 200), prefill=(10, 30), seed=79)
+
+
+def _route_check(S, t0, t1, j):
+    """GPU routing of tokens t0..t1 (nano-batch j) == oracle routing, exactly."""
+    s = S.wl.shape
+    k = s.top_k
+    T = S.batch.n_tokens
+    logits = GH.f64(S.acts["router_logits"][t0:t1])
+    idx, w, perm, offsets = oracle.moe_route(logits, k)
+    gi = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    gw = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    gp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    go = torch.empty(4 * (s.n_experts + 1), dtype=torch.int32, device="cuda")
+    for which, t in ((5, gi), (6, gw), (7, gp), (8, go)):
+        ptr, _ = S.layer.intermediate(which)
+        B.copy_device(t, ptr, t.numel() * t.element_size())
+    gi = gi.cpu().numpy()[t0 * k:t1 * k].reshape(-1, k)
+    gw = gw.cpu().numpy()[t0 * k:t1 * k].reshape(-1, k)
+    gp = gp.cpu().numpy()[t0 * k:t1 * k]
+    go = go.cpu().numpy()[j * (s.n_experts + 1):(j + 1) * (s.n_experts + 1)]
+    assert np.array_equal(gi, idx)
+    assert np.array_equal(gp, perm)
+    assert np.array_equal(go, offsets)
+    assert np.max(np.abs(gw - w)) < 1e-6
+
+
+def test_small_moe_full_parity():
+    S = GH.setup(SMALL_MOE)
+    T = S.batch.n_tokens
+    for name, plan in (("k1", B.make_plan(1, [T])),
+                       ("k3", B.make_plan(3, [33, 33, T - 66], n_streams=2, gemm_cus_per_xcd=16))):
+        _full_check(S, name, plan)
+        sizes = list(plan.sizes)[:plan.count]
+        t0 = 0
+        for j, n in enumerate(sizes):
+            _route_check(S, t0, t0 + n, j)
+            t0 += n
+
+
+@pytest.mark.slow
+def test_c5_full_size_sampled():
+    S = GH.setup(W.WORKLOADS["c5"])
+    T = S.batch.n_tokens
+    S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], n_streams=2, gemm_cus_per_xcd=16))
+    _sampled_check(S, _sample_requests(S.batch, 6))
+    _route_check(S, 0, T // 2, 0)
+    _route_check(S, T // 2, T, 1)
