@@ -1,0 +1,280 @@
+"""Decoder-layer step throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c5]
+
+One step = one nf_layer_step of the whole layer (norm, QKV, RoPE + paged KV
+append, decode/prefill attention, O-proj, norm, FFN or experts) over one batch
+of seeded synthetic inputs that are resident in HBM before timing starts.
+Prints one JSON line: throughput (tokens/s), the fraction of the
+compute-bound optimum (peaks measured in this run), the roofline of the
+dominant kernel (its duration measured with HIP events on its own stream
+during the timed steps) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+PEAK_BF16_TFLOPS = 2500.0       # MI355X published dense bf16 MFMA
+DEFAULT_WORKLOAD = "c2"         # the Llama-3-8B-shaped decode batch (64 requests, context 512)
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic work
+def kernel_work(kind, wl, batch, plan_sizes):
+    """(bytes, flops) the method must move/compute in ONE launch of `kind`,
+    averaged over the launches of one step (one per nano-batch)."""
+    s = wl.shape
+    H, F, d = s.hidden, s.ffn, s.head_dim
+    nq, nkv = s.n_q_heads, s.n_kv_heads
+    Nqkv = (nq + 2 * nkv) * d
+    eb = 2 if s.dtype == "bf16" else 4
+    T = batch.n_tokens
+    n = max(1, len(plan_sizes))
+    if kind == "attention":
+        # each cached K and V element of every request read once per KV head,
+        # q read once, output written once
+        keys = 0
+        for r in range(batch.n_requests):
+            last = batch.req_pos0[r] + batch.req_q_len[r] - 1
+            keys += last + 1
+        kv = keys * nkv * d * 2 * eb
+        qo = 2 * T * nq * d * eb
+        flops = 0
+        for r in range(batch.n_requests):
+            for i in range(batch.req_q_len[r]):
+                flops += 4 * nq * d * (batch.req_pos0[r] + i + 1)
+        return (kv + qo) / n, flops / n
+    gemms = {
+        "gemm_qkv": (Nqkv, H, False),
+        "gemm_o_residual": (H, nq * d, True),
+        "gemm_gate_up_swiglu": (2 * F, H, False),
+        "gemm_down_residual": (H, F, True),
+    }
+    if kind in gemms:
+        N, K, res = gemms[kind]
+        M = T / n
+        out_cols = F if kind == "gemm_gate_up_swiglu" else N
+        byts = N * K * eb + M * K * eb + M * out_cols * eb + (M * N * eb if res else 0)
+        return byts, 2.0 * M * N * K
+    return None, None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--plan", default="auto", help="auto (workload default / search) or k1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None, help="JSON file with rocprofv3 FETCH/WRITE bytes per launch")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
+              "replica of the step); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from intra_operation_overlap_amd import binding as B
+    from intra_operation_overlap_amd import workload as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = W.WORKLOADS[args.workload]
+    s = wl.shape
+    log(f"workload {wl.name}: {wl.description}")
+    batch = W.make_batch(wl)
+    weights = W.make_weights(wl, "cuda")
+    acts = W.make_activations(wl, batch, "cuda")
+    k_pool, v_pool = W.make_pool(wl, batch.n_pages, "cuda")
+    out = torch.empty_like(acts["x"])
+    T = batch.n_tokens
+    layer = B.Layer(s, weights, T, int(batch.pos.max()) + 1)
+    pool = B.KVPool(layer, batch.n_pages, s.page_size, k_pool, v_pool)
+    hb = B.HostBatch(batch, acts["x"].data_ptr(), out.data_ptr(),
+                     acts["router_logits"].data_ptr() if "router_logits" in acts else None)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    log("probing peaks")
+    peak_tflops = B.probe_mfma_bf16_tflops()
+    peak_gbps = B.probe_hbm_read_gbps(4 << 30)
+    log(f"measured peaks: bf16 MFMA {peak_tflops:.0f} TFLOP/s, HBM read {peak_gbps:.0f} GB/s")
+
+    def time_steps(n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            layer.step(pool, hb, sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    comparisons = {}
+    if args.plan == "k1" or wl.plan_sizes == (T,):
+        plan = B.make_plan(1, [T])
+        layer.set_plan(plan)
+    elif wl.plan_sizes is not None:
+        plan = B.make_plan(len(wl.plan_sizes), list(wl.plan_sizes), n_streams=2)
+        layer.set_plan(plan)
+    else:
+        log("plan search")
+        plan, (pred, meas) = layer.search(pool, hb, max_count=4, warmup=2, reps=5, stream=sp)
+        log(f"searched plan {B.plan_dict(plan)} ({meas:.3f} ms)")
+        # the sequential baselines the overlap is measured against
+        layer.set_plan(B.make_plan(1, [T]))
+        for _ in range(3):
+            layer.step(pool, hb, sp)
+        comparisons["sequential_unsplit_ms"] = time_steps(10)
+        seq = B.make_plan(plan.count, list(plan.sizes)[:plan.count], order=B.NF_ORDER_SEQUENTIAL)
+        layer.set_plan(seq)
+        for _ in range(3):
+            layer.step(pool, hb, sp)
+        comparisons["sequential_split_ms"] = time_steps(10)
+        layer.set_plan(plan)
+    plan_sizes = list(plan.sizes)[:plan.count]
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        layer.step(pool, hb, sp)
+    torch.cuda.synchronize()
+
+    # dominant kernel: the kind with the largest summed time over a short pass
+    layer.profile_enable(True)
+    for _ in range(5):
+        layer.step(pool, hb, sp)
+    prof = layer.profile_read()
+    layer.profile_enable(False)
+    dominant = max(prof, key=lambda k: prof[k][1])
+    log("per-kernel (5 steps): " + ", ".join(f"{k} {v[1] / v[0] * 1e3:.1f}us x{v[0] // 5}" for k, v in prof.items()))
+
+    # timed region: events on the caller stream bracket K steps; the library
+    # brackets each launch of the dominant kernel on its own stream
+    layer.profile_enable(True, dominant)
+    log(f"timing {args.steps} steps")
+    ms = time_steps(args.steps)
+    dprof = layer.profile_read()
+    layer.profile_enable(False)
+    launches, dom_ms = dprof[dominant]
+    dom_avg_ms = dom_ms / launches
+    value = T / (ms * 1e-3)
+    if comparisons:
+        comparisons["overlapped_ms"] = ms
+
+    # roofline of the dominant kernel
+    byts, flops = kernel_work(dominant, wl, batch, plan_sizes)
+    roofline = None
+    if byts is not None:
+        intensity = flops / byts
+        ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+        if intensity < ridge:
+            ach = byts / (dom_avg_ms * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(ach / PEAK_HBM_GBPS, 4)}
+        else:
+            ach = flops / (dom_avg_ms * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        roofline["traffic"] = None
+        roofline["kernel"] = dominant
+        roofline["avg_launch_us"] = round(dom_avg_ms * 1e3, 2)
+        roofline["algorithmic_bytes_per_launch"] = int(byts)
+        tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{dominant}_{wl.name}.json")
+        if os.path.exists(tpath):
+            t = json.load(open(tpath))
+            roofline["traffic"] = t.get("bytes_per_launch")
+
+    # fraction of the compute-bound optimum: tokens/s / (peak / FLOPs per token)
+    fpt = W.layer_flops_per_token(s)
+    optimum = peak_tflops * 1e12 / fpt
+    frac_opt = value / optimum
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, batch, weights, acts, k_pool, v_pool)
+
+    line = {
+        "metric": "decoder-layer tokens/s on 1 MI355X + fraction of compute-bound optimal",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "tokens": T,
+                   "requests": batch.n_requests, "hidden": s.hidden, "q_heads": s.n_q_heads,
+                   "kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "ffn": s.ffn, "experts": s.n_experts,
+                   "plan": B.plan_dict(plan)},
+        "frac_compute_optimal": round(frac_opt, 4),
+        "peaks_measured": {"bf16_mfma_tflops": round(peak_tflops, 1), "hbm_read_gbps": round(peak_gbps, 1)},
+        "flops_per_token": fpt,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if comparisons:
+        line["comparisons"] = {k: round(v, 5) for k, v in comparisons.items()}
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, batch, weights, acts, k_pool, v_pool, budget_s=20.0):
+    """The CPU oracle, as it stands, on a bounded sample of this workload's
+    requests (rows are independent, so a subset is a fair per-token rate)."""
+    import torch
+    import oracle
+    from intra_operation_overlap_amd import workload as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    wn = {k: v.detach().to("cpu", torch.float32).numpy() for k, v in weights.items()}
+    rng = np.random.Generator(np.random.PCG64(1))
+    reqs = list(range(batch.n_requests))
+    rng.shuffle(reqs)
+    done_tokens, elapsed, used = 0, 0.0, []
+    chunk = 8
+    while reqs and elapsed < budget_s:
+        pick = sorted(reqs[:chunk])
+        reqs = reqs[chunk:]
+        sub, rows = W.sub_batch(batch, pick)
+        pages = torch.as_tensor(np.asarray(sub.page_indices, np.int64), device=k_pool.device)
+        kp, vp = W.to_f64(k_pool[pages]), W.to_f64(v_pool[pages])
+        ridx = torch.as_tensor(rows, device="cuda")
+        bd = dict(x=W.to_f64(acts["x"][ridx]), req_q_start=sub.req_q_start, req_q_len=sub.req_q_len,
+                  req_pos0=sub.req_pos0, pos=sub.pos, page_indptr=sub.page_indptr,
+                  page_indices=np.arange(len(sub.page_indices)))
+        if "router_logits" in acts:
+            bd["router_logits"] = W.to_f64(acts["router_logits"][ridx])
+        t0 = time.perf_counter()
+        oracle.layer_step(wl.shape.as_dict(), wn, bd, kp, vp)
+        elapsed += time.perf_counter() - t0
+        done_tokens += sub.n_tokens
+        used += pick
+    return {"value": round(done_tokens / elapsed, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(used)} of {batch.n_requests} requests ({done_tokens} tokens) of workload {wl.name}, "
+                      f"{elapsed:.1f} s of fp64 numpy work"}
+
+
+if __name__ == "__main__":
+    main()

@@ -215,12 +215,13 @@ nf_status nf_layer_intermediate(const nf_layer* layer, int32_t which, const void
                                 int64_t* row_stride);
 
 /* ---- per-kernel timing ------------------------------------------------------
- * When on, every kernel launch of a step is bracketed by HIP events recorded
- * on the stream it is launched on.  nf_profile_read synchronises those events
- * and returns, per kernel kind, the number of launches and the summed
- * duration (ms) since profiling was switched on; kinds with no launches are
- * omitted.  Names are static strings. */
-nf_status nf_profile_enable(nf_layer* layer, int32_t on);
+ * When on, every kernel launch of a step (or only those of kind `only_kind`,
+ * if not NULL) is bracketed by HIP events recorded on the stream it is
+ * launched on.  nf_profile_read synchronises those events and returns, per
+ * kernel kind, the number of launches and the summed duration (ms) since
+ * profiling was switched on; kinds with no launches are omitted.  Names are
+ * static strings.  Enabling resets the totals. */
+nf_status nf_profile_enable(nf_layer* layer, int32_t on, const char* only_kind);
 nf_status nf_profile_read(nf_layer* layer, int32_t max_kinds, const char** names,
                           int64_t* launches, double* total_ms, int32_t* n_kinds);
 
@@ -228,7 +229,9 @@ nf_status nf_profile_read(nf_layer* layer, int32_t max_kinds, const char** names
  * Measured peaks of the current device: dense bf16 MFMA TFLOP/s (register-only
  * MFMA chains on every CU) and HBM read GB/s (streaming `bytes` bytes, at
  * least 1 GiB recommended).  nf_probe_cu_map fills xcc[i] with the XCD that
- * CU-mask bit i dispatches to (n = CU count). */
+ * CU-mask bit i dispatches to (n = CU count), or -1 for every bit when the
+ * expected striping (bit i -> XCD i % 8) could not be confirmed.  A CU mask
+ * must leave every XCD at least one CU; the plan's split does. */
 nf_status nf_probe_mfma_bf16_tflops(double* tflops);
 nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps);
 nf_status nf_probe_cu_map(int32_t* xcc, int32_t n);

@@ -70,7 +70,7 @@ _SIGS = {
     "nf_plan_search": (i32, [vp, vp, ctypes.POINTER(nf_batch), ctypes.POINTER(nf_search_opts),
                              ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double), vp]),
     "nf_layer_intermediate": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64)]),
-    "nf_profile_enable": (i32, [vp, i32]),
+    "nf_profile_enable": (i32, [vp, i32, ctypes.c_char_p]),
     "nf_profile_read": (i32, [vp, i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
     "nf_probe_mfma_bf16_tflops": (i32, [ctypes.POINTER(ctypes.c_double)]),
@@ -203,8 +203,9 @@ class Layer:
               "nf_layer_intermediate")
         return ptr.value, stride.value
 
-    def profile_enable(self, on: bool) -> None:
-        check(lib().nf_profile_enable(self.h, 1 if on else 0), "nf_profile_enable")
+    def profile_enable(self, on: bool, only_kind: Optional[str] = None) -> None:
+        check(lib().nf_profile_enable(self.h, 1 if on else 0, only_kind.encode() if only_kind else None),
+              "nf_profile_enable")
 
     def profile_read(self) -> Dict[str, tuple]:
         n = 32

@@ -21,6 +21,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -46,12 +47,16 @@ nf_status set_err(nf_status st, const char* fmt, ...) {
   return st;
 }
 
+// On a HIP failure the runtime's last-error slot is cleared so that the
+// caller's next unrelated HIP call does not report it again.
 #define HIP_TRY(expr)                                                                     \
   do {                                                                                    \
     hipError_t e_ = (expr);                                                               \
-    if (e_ != hipSuccess)                                                                 \
+    if (e_ != hipSuccess) {                                                               \
+      (void)hipGetLastError();                                                            \
       return set_err(NF_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), \
                      __FILE__, __LINE__);                                                 \
+    }                                                                                     \
   } while (0)
 
 constexpr int PAGE_SIZE = 16;
@@ -106,6 +111,7 @@ struct nf_layer {
   bool stage_used[2] = {false, false};
   int stage_i = 0;
   bool prof = false;
+  int prof_only = -1;                           // kind filter (-1: every kind)
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> ev_free;
   double prof_ms[K_COUNT] = {};
@@ -153,38 +159,46 @@ void release(DevBuf& b) {
 std::mutex g_map_mu;
 std::map<int, std::vector<int>> g_xcc_maps;     // device -> bit -> XCD
 
-nf_status measure_cu_map(int device, int n_cus, std::vector<int>& out) {
+// Which XCD each CU-mask bit lands on.  The driver stripes mask bits over
+// the XCDs (bit i -> XCD i % n_xcd, CU i / n_xcd within it), and a mask must
+// leave every XCD at least one CU (workgroups are dealt to XCDs round-robin
+// whatever the mask).  The striping is checked with a stream masked to bits
+// 0 .. n_xcd-1 -- one CU per XCD if striped -- running many single-wave
+// workgroups that report their XCC_ID: every XCD must show up.  If it does
+// not, the bits stay -1 (unknown) and splits still use the striped guess.
+nf_status measure_cu_map(int device, int n_cus, int n_xcd, std::vector<int>& out) {
   std::lock_guard<std::mutex> lk(g_map_mu);
   auto it = g_xcc_maps.find(device);
   if (it != g_xcc_maps.end()) {
     out = it->second;
     return NF_OK;
   }
-  uint32_t* d_id = nullptr;
-  HIP_TRY(hipMalloc(&d_id, 2 * sizeof(uint32_t)));
+  constexpr int kBlocks = 256;
   std::vector<int> map(n_cus, -1);
   const int words = (n_cus + 31) / 32;
-  for (int bit = 0; bit < n_cus; ++bit) {
-    std::vector<uint32_t> mask(words, 0u);
-    mask[bit / 32] = 1u << (bit % 32);
-    hipStream_t st;
-    hipError_t e = hipExtStreamCreateWithCUMask(&st, words, mask.data());
-    if (e != hipSuccess) {
-      (void)hipFree(d_id);
-      return set_err(NF_ERR_HIP, "hipExtStreamCreateWithCUMask: %s", hipGetErrorString(e));
-    }
-    uint32_t h_id[2] = {0, 0};
-    e = probe_hwid(d_id, st);
-    if (e == hipSuccess) e = hipMemcpyAsync(h_id, d_id, sizeof h_id, hipMemcpyDeviceToHost, st);
+  std::vector<uint32_t> mask(words, 0u);
+  for (int bit = 0; bit < n_xcd && bit < n_cus; ++bit) mask[bit / 32] |= 1u << (bit % 32);
+  uint32_t* d_id = nullptr;
+  HIP_TRY(hipMalloc(&d_id, 2 * kBlocks * sizeof(uint32_t)));
+  hipStream_t st = nullptr;
+  hipError_t e = hipExtStreamCreateWithCUMask(&st, words, mask.data());
+  std::vector<uint32_t> h_id(2 * kBlocks, 0xFFFFFFFFu);
+  if (e == hipSuccess) {
+    e = probe_hwid(d_id, kBlocks, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(h_id.data(), d_id, h_id.size() * 4, hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     (void)hipStreamDestroy(st);
-    if (e != hipSuccess) {
-      (void)hipFree(d_id);
-      return set_err(NF_ERR_HIP, "CU map probe: %s", hipGetErrorString(e));
-    }
-    map[bit] = (int)(h_id[1] & 0xF);
   }
+  (void)hipGetLastError();
   (void)hipFree(d_id);
+  if (e == hipSuccess) {
+    std::vector<int> seen(16, 0);
+    for (int b = 0; b < kBlocks; ++b) seen[h_id[2 * b + 1] & 0xF] = 1;
+    int n_seen = 0;
+    for (int x = 0; x < 16; ++x) n_seen += seen[x];
+    if (n_seen == n_xcd)
+      for (int bit = 0; bit < n_cus; ++bit) map[bit] = bit % n_xcd;
+  }
   g_xcc_maps[device] = map;
   out = map;
   return NF_OK;
@@ -219,7 +233,7 @@ nf_status get_pair(nf_layer* L, int gemm_cus, StreamPair& out) {
     HIP_TRY(hipStreamCreateWithFlags(&p.a, hipStreamNonBlocking));
   } else {
     if (L->xcc_of_bit.empty()) {
-      nf_status st = measure_cu_map(L->device, L->n_cus, L->xcc_of_bit);
+      nf_status st = measure_cu_map(L->device, L->n_cus, L->n_xcd, L->xcc_of_bit);
       if (st != NF_OK) return st;
     }
     std::vector<uint32_t> mg, ma;
@@ -240,7 +254,7 @@ struct Prof {
 };
 
 void prof_begin(nf_layer* L, int kind, hipStream_t s) {
-  if (!L->prof) return;
+  if (!L->prof || (L->prof_only >= 0 && kind != L->prof_only)) return;
   ProfRec r{kind, nullptr, nullptr};
   for (hipEvent_t* e : {&r.a, &r.b}) {
     if (!L->ev_free.empty()) {
@@ -256,16 +270,17 @@ void prof_begin(nf_layer* L, int kind, hipStream_t s) {
   }
 }
 
-void prof_end(nf_layer* L, hipStream_t s) {
-  if (!L->prof || L->recs.empty()) return;
+void prof_end(nf_layer* L, int kind, hipStream_t s) {
+  if (!L->prof || L->recs.empty() || L->recs.back().kind != kind) return;
   (void)hipEventRecord(L->recs.back().b, s);
 }
 
 void prof_hook_fn(void* ctx, int phase) {
   Prof* p = (Prof*)ctx;
   (void)phase;
-  prof_end(p->L, p->s);
+  prof_end(p->L, p->kind, p->s);
   prof_begin(p->L, p->kind + 1, p->s);     // the reduce kind follows its GEMM kind
+  p->kind += 1;
 }
 
 // --------------------------------------------------------------- step pieces
@@ -287,7 +302,7 @@ hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s) {
   if (L->s.dtype == NF_F32) {
     prof_begin(L, kind, s);
     hipError_t e = gemm_f32(g, s);
-    prof_end(L, s);
+    prof_end(L, kind, s);
     return e;
   }
   GemmPlan gp = gemm_choose(g, c.gemm_cus);
@@ -295,7 +310,7 @@ hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s) {
   LaunchHook hook{prof_hook_fn, &pctx};
   prof_begin(L, kind, s);
   hipError_t e = gemm_bf16(g, gp, L->splitk.p, s, L->prof ? &hook : nullptr);
-  prof_end(L, s);
+  prof_end(L, pctx.kind, s);
   return e;
 }
 
@@ -375,7 +390,7 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
   prof_begin(L, K_NORM1, s);
   HIP_STEP(rmsnorm(dt, (const char*)c.b->x + (int64_t)t0 * H * dtype_bytes(dt), L->w.attn_norm,
                    ptr(L->h, (int64_t)t0 * H, dt), Tj, H, sh.rms_eps, s));
-  prof_end(L, s);
+  prof_end(L, K_NORM1, s);
   NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
   HIP_STEP(run_gemm(c, g.qkv, K_QKV, s));
   RopeAppendArgs r;
@@ -392,7 +407,7 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
   r.T = Tj; r.nq = sh.n_q_heads; r.nkv = sh.n_kv_heads; r.d = sh.head_dim; r.page_size = c.P->page_size;
   prof_begin(L, K_ROPE, s);
   HIP_STEP(rope_append(dt, r, s));
-  prof_end(L, s);
+  prof_end(L, K_ROPE, s);
   return NF_OK;
 }
 
@@ -419,11 +434,11 @@ nf_status issue_attention(StepCtx& c, int j, hipStream_t s) {
   a.scale = (float)(1.0 / std::sqrt((double)sh.head_dim));
   prof_begin(L, K_ATTN, s);
   HIP_STEP(attention(sh.dtype, a, s));
-  prof_end(L, s);
+  prof_end(L, K_ATTN, s);
   if (nw.n_merges) {
     prof_begin(L, K_MERGE, s);
     HIP_STEP(attention_merge(sh.dtype, a, s));
-    prof_end(L, s);
+    prof_end(L, K_MERGE, s);
   }
   return NF_OK;
 }
@@ -439,7 +454,7 @@ nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
   prof_begin(L, K_NORM2, s);
   HIP_STEP(rmsnorm(dt, ptr(L->x1, (int64_t)t0 * H, dt), L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
                    sh.rms_eps, s));
-  prof_end(L, s);
+  prof_end(L, K_NORM2, s);
   if (sh.n_experts == 1) {
     HIP_STEP(run_gemm(c, g.gu, K_GATEUP, s));
     HIP_STEP(run_gemm(c, g.down, K_DOWN, s));
@@ -456,18 +471,18 @@ nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
   r.T = Tj; r.E = E; r.k = k;
   prof_begin(L, K_ROUTE, s);
   HIP_STEP(moe_route(r, s));
-  prof_end(L, s);
+  prof_end(L, K_ROUTE, s);
   GemmPlan gp;           // grouped: one tile config, no split-K
   prof_begin(L, K_MOE_GATEUP, s);
   HIP_STEP(gemm_bf16(g.moe_gu, gp, nullptr, s));
-  prof_end(L, s);
+  prof_end(L, K_MOE_GATEUP, s);
   prof_begin(L, K_MOE_DOWN, s);
   HIP_STEP(gemm_bf16(g.moe_down, gp, nullptr, s));
-  prof_end(L, s);
+  prof_end(L, K_MOE_DOWN, s);
   prof_begin(L, K_COMBINE, s);
   HIP_STEP(moe_combine(dt, ptr(L->x1, (int64_t)t0 * H, dt), (const float*)L->y.p + (int64_t)t0 * k * H,
                        r.w, r.inv, (char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt), Tj, H, k, s));
-  prof_end(L, s);
+  prof_end(L, K_COMBINE, s);
   return NF_OK;
 }
 
@@ -811,8 +826,14 @@ nf_status nf_layer_intermediate(const nf_layer* L, int32_t which, const void** d
   return NF_OK;
 }
 
-nf_status nf_profile_enable(nf_layer* L, int32_t on) {
+nf_status nf_profile_enable(nf_layer* L, int32_t on, const char* only_kind) {
   if (!L) return set_err(NF_ERR_INVALID_ARG, "nf_profile_enable: null layer");
+  L->prof_only = -1;
+  if (only_kind) {
+    for (int k = 0; k < K_COUNT; ++k)
+      if (std::strcmp(kKindNames[k], only_kind) == 0) L->prof_only = k;
+    if (L->prof_only < 0) return set_err(NF_ERR_INVALID_ARG, "nf_profile_enable: unknown kind %s", only_kind);
+  }
   L->prof = on != 0;
   for (auto& r : L->recs) {
     L->ev_free.push_back(r.a);
@@ -860,7 +881,7 @@ nf_status nf_probe_cu_map(int32_t* xcc, int32_t n) {
   hipDeviceProp_t prop;
   HIP_TRY(hipGetDeviceProperties(&prop, dev));
   std::vector<int> map;
-  nf_status st = measure_cu_map(dev, prop.multiProcessorCount, map);
+  nf_status st = measure_cu_map(dev, prop.multiProcessorCount, 8, map);
   if (st != NF_OK) return st;
   for (int i = 0; i < n; ++i) xcc[i] = i < (int)map.size() ? map[i] : -1;
   return NF_OK;
@@ -879,15 +900,22 @@ nf_status nf_probe_mfma_bf16_tflops(double* tflops) {
   HIP_TRY(hipEventCreate(&e1));
   const int blocks = prop.multiProcessorCount * 4, iters = 4096;
   double best = 0;
-  for (int rep = 0; rep < 4; ++rep) {
-    HIP_TRY(hipEventRecord(e0, nullptr));
-    HIP_TRY(probe_mfma(blocks, iters, sink, nullptr));
-    HIP_TRY(hipEventRecord(e1, nullptr));
-    HIP_TRY(hipEventSynchronize(e1));
-    float ms = 0;
-    HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
-    const double flops = (double)blocks * 4 /*waves*/ * iters * 8 /*chains*/ * (16.0 * 16 * 32 * 2);
-    if (rep > 0) best = std::max(best, flops / (ms * 1e-3) / 1e12);
+  for (int shape = 0; shape < 2; ++shape) {
+    double best_shape = 0;
+    for (int rep = 0; rep < 4; ++rep) {
+      HIP_TRY(hipEventRecord(e0, nullptr));
+      HIP_TRY(probe_mfma(shape, blocks, iters, sink, nullptr));
+      HIP_TRY(hipEventRecord(e1, nullptr));
+      HIP_TRY(hipEventSynchronize(e1));
+      float ms = 0;
+      HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+      // per wave and iteration: 8 x 16x16x32 or 4 x 32x32x16, both 131072 FLOP
+      const double flops = (double)blocks * 4 /*waves*/ * iters * 131072.0;
+      if (rep > 0) best_shape = std::max(best_shape, flops / (ms * 1e-3) / 1e12);
+    }
+    if (std::getenv("NF_PROBE_VERBOSE"))
+      std::fprintf(stderr, "nf probe: mfma %s %.1f TFLOP/s\n", shape ? "32x32x16" : "16x16x32", best_shape);
+    best = std::max(best, best_shape);
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);

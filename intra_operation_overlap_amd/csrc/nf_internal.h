@@ -101,8 +101,10 @@ hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w
                        const int32_t* inv, void* out, int T, int H, int k, hipStream_t s);
 
 // ---------------------------------------------------------------- probes
-hipError_t probe_mfma(int n_blocks, int iters, float* sink, hipStream_t s);
+// shape 0: v_mfma_f32_16x16x32_bf16 (8 chains), 1: v_mfma_f32_32x32x16_bf16 (4 chains)
+hipError_t probe_mfma(int shape, int n_blocks, int iters, float* sink, hipStream_t s);
 hipError_t probe_read(const void* buf, size_t bytes, float* sink, int n_blocks, hipStream_t s);
-hipError_t probe_hwid(uint32_t* out, hipStream_t s);   // out[0] = HW_ID, out[1] = XCC_ID
+// out[2*b] = HW_ID, out[2*b+1] = XCC_ID of workgroup b
+hipError_t probe_hwid(uint32_t* out, int n_blocks, hipStream_t s);
 
 }  // namespace nf

@@ -6,8 +6,10 @@
 namespace nf {
 namespace {
 
-// Eight independent accumulator chains of v_mfma_f32_16x16x32_bf16 per wave,
-// operands in registers only.
+// Eight independent accumulator chains of one bf16 MFMA shape per wave,
+// operands in registers only.  SHAPE 0: 16x16x32, SHAPE 1: 32x32x16.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <int SHAPE>
 __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* sink) {
   bf16x8 a, b;
 #pragma unroll
@@ -15,16 +17,30 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* sink)
     a[e] = (bf16)(float)((threadIdx.x + e) & 3);
     b[e] = (bf16)(float)((threadIdx.x * 3 + e) & 3);
   }
-  f32x4 acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
-  }
   float s = 0.f;
+  if (SHAPE == 0) {
+    f32x4 acc[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  } else {
+    f32x16 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s += acc[c][0] + acc[c][5] + acc[c][10] + acc[c][15];
+  }
   if (s == 12345.678f) sink[threadIdx.x] = s;     // keeps the chains live
 }
 
@@ -44,18 +60,21 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
   if (x == 0x9e3779b9u) sink[threadIdx.x] = (float)x;
 }
 
-// HW_ID (hwreg 4) and XCC_ID (hwreg 20) of the wave that runs it.
+// HW_ID (hwreg 4) and XCC_ID (hwreg 20) of the first wave of each workgroup.
 __global__ void probe_hwid_kernel(uint32_t* out) {
   if (threadIdx.x == 0) {
-    out[0] = __builtin_amdgcn_s_getreg((4) | (0 << 6) | ((32 - 1) << 11));
-    out[1] = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((16 - 1) << 11));
+    out[2 * blockIdx.x] = __builtin_amdgcn_s_getreg((4) | (0 << 6) | ((32 - 1) << 11));
+    out[2 * blockIdx.x + 1] = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((16 - 1) << 11));
   }
 }
 
 }  // namespace
 
-hipError_t probe_mfma(int n_blocks, int iters, float* sink, hipStream_t s) {
-  probe_mfma_kernel<<<n_blocks, 256, 0, s>>>(iters, sink);
+hipError_t probe_mfma(int shape, int n_blocks, int iters, float* sink, hipStream_t s) {
+  if (shape == 0)
+    probe_mfma_kernel<0><<<n_blocks, 256, 0, s>>>(iters, sink);
+  else
+    probe_mfma_kernel<1><<<n_blocks, 256, 0, s>>>(iters, sink);
   return hipGetLastError();
 }
 
@@ -64,8 +83,8 @@ hipError_t probe_read(const void* buf, size_t bytes, float* sink, int n_blocks, 
   return hipGetLastError();
 }
 
-hipError_t probe_hwid(uint32_t* out, hipStream_t s) {
-  probe_hwid_kernel<<<1, 64, 0, s>>>(out);
+hipError_t probe_hwid(uint32_t* out, int n_blocks, hipStream_t s) {
+  probe_hwid_kernel<<<n_blocks, 64, 0, s>>>(out);
   return hipGetLastError();
 }
 

