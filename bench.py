@@ -48,14 +48,13 @@ def kernel_work(kind, wl, batch, plan_sizes):
         # q read once, output written once
         keys = 0
         for r in range(batch.n_requests):
-            last = batch.req_pos0[r] + batch.req_q_len[r] - 1
-            keys += last + 1
+            keys += int(batch.req_pos0[r]) + int(batch.req_q_len[r])
         kv = keys * nkv * d * 2 * eb
         qo = 2 * T * nq * d * eb
         flops = 0
         for r in range(batch.n_requests):
-            for i in range(batch.req_q_len[r]):
-                flops += 4 * nq * d * (batch.req_pos0[r] + i + 1)
+            for i in range(int(batch.req_q_len[r])):
+                flops += 4 * nq * d * (int(batch.req_pos0[r]) + i + 1)
         return (kv + qo) / n, flops / n
     gemms = {
         "gemm_qkv": (Nqkv, H, False),

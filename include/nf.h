@@ -53,9 +53,10 @@ typedef enum nf_status {
 
 typedef enum nf_dtype { NF_F32 = 0, NF_BF16 = 1 } nf_dtype;
 
-/* Layer shape.  Requirements: n_q_heads % n_kv_heads == 0; head_dim even,
- * <= 256 (bf16 layers: head_dim == 128); hidden, ffn and head_dim multiples
- * of 8; top_k <= n_experts <= 64; max_tokens >= 1; max_pos >= 1. */
+/* Layer shape.  Requirements: n_q_heads % n_kv_heads == 0 with at most 16
+ * query heads per KV head; head_dim a multiple of 32, <= 256 (bf16 layers:
+ * head_dim == 128); hidden and ffn multiples of 8; top_k <= n_experts <= 64,
+ * top_k <= 8; max_tokens >= 1; max_pos >= 1. */
 typedef struct nf_shape {
   int32_t hidden;       /* H */
   int32_t n_q_heads;    /* nq */
@@ -128,10 +129,22 @@ typedef struct nf_plan {
   int32_t order;                  /* nf_order                                */
   int32_t n_streams;              /* 1: all work on the caller's stream;
                                      2: GEMM stream + attention stream       */
-  int32_t gemm_cus_per_xcd;       /* n_streams == 2 only: CUs of each XCD given
-                                     to the GEMM stream, the rest to attention;
-                                     0 = no CU masks (both streams may use
-                                     every CU)                               */
+  int32_t gemm_cus_per_xcd;       /* n_streams == 2 only: the GEMM stream may use
+                                     the first gemm_cus_per_xcd CUs of every
+                                     XCD; 0 = every CU                       */
+  int32_t attn_cus_per_xcd;       /* n_streams == 2 only: the attention stream
+                                     may use the last attn_cus_per_xcd CUs of
+                                     every XCD; 0 = the CUs the GEMM stream
+                                     does not have (every CU if it has all).
+                                     The two ranges may overlap: waves of both
+                                     streams then share those CUs (matrix
+                                     cores vs memory pipes).                 */
+  int32_t attn_waves_per_cu;      /* 0: one attention workgroup per work item;
+                                     1..16: a persistent attention grid of
+                                     that many single-wave workgroups per CU
+                                     of its budget, each looping over work
+                                     items, so attention leaves room on every
+                                     CU for the GEMM's workgroups            */
 } nf_plan;
 
 typedef struct nf_search_opts {
@@ -156,12 +169,17 @@ void nf_layer_destroy(nf_layer* layer);   /* waits for the layer's streams */
 
 /* ---- KV pool --------------------------------------------------------------
  * Paged KV cache (the PagedAttention block pool: "How it differs from vLLM
- * and TensorRT-LLM" on the hysenlabs Nanoflow page).  Layout in the layer
- * dtype:  K [n_pages][n_kv_heads][page_size][head_dim]
- *         V [n_pages][n_kv_heads][head_dim][page_size]
- * (within a page, V is stored dimension-major so that attention's P.V
- * contraction over keys reads contiguous memory).  Only page_size == 16 is
- * supported (NF_ERR_UNSUPPORTED otherwise). */
+ * and TensorRT-LLM" on the hysenlabs Nanoflow page).  K and V each hold
+ * [n_pages][n_kv_heads] blocks of page_size * head_dim elements in the layer
+ * dtype.  page_size must be 16 (NF_ERR_UNSUPPORTED otherwise) and head_dim a
+ * multiple of 32.  Inside a block, key slot s (0..15) and dimension d sit at
+ *   K: (d / 32) * 512 + (16 * ((d % 32) / 8) + s) * 8 + d % 8
+ *   V: (d / 32) * 512 + ((d % 16) + 16 * (s / 4)) * 8 + 4 * ((d / 16) % 2) + s % 4
+ * i.e. in the operand order of the attention kernel's matrix-core
+ * instructions: every 512-element run is what the 64 lanes of a wavefront
+ * load with one contiguous 16-byte-per-lane read (8 elements each), which on
+ * gfx950 roughly doubles the bandwidth one CU can draw compared with
+ * row-major pages. */
 nf_status nf_kv_pool_bytes(const nf_shape* shape, int32_t n_pages, int32_t page_size,
                            size_t* k_bytes, size_t* v_bytes);
 nf_status nf_kv_pool_create(const nf_layer* layer, int32_t n_pages, int32_t page_size,
@@ -234,6 +252,14 @@ nf_status nf_profile_read(nf_layer* layer, int32_t max_kinds, const char** names
  * must leave every XCD at least one CU; the plan's split does. */
 nf_status nf_probe_mfma_bf16_tflops(double* tflops);
 nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps);
+/* Average time (ms) of the layer's bf16 GEMM kernel on an M x N x K problem
+ * (C = A B^T, mode 0 plain, 1 residual, 2 SwiGLU with N act columns), on
+ * library-allocated constant-filled buffers.  tile_cfg < 0 and k_splits <= 0
+ * let the library choose for a stream that may use `cus` CUs; out_cfg and
+ * out_splits (may be NULL) return what ran. */
+nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int32_t mode, int32_t tile_cfg,
+                                int32_t k_splits, int32_t cus, int32_t reps, double* ms,
+                                int32_t* out_cfg, int32_t* out_splits);
 nf_status nf_probe_cu_map(int32_t* xcc, int32_t n);
 
 /* ---- errors ---------------------------------------------------------------- */

@@ -47,7 +47,7 @@ class nf_batch(ctypes.Structure):
 
 class nf_plan(ctypes.Structure):
     _fields_ = [("count", i32), ("sizes", i32 * NF_MAX_NANO), ("order", i32), ("n_streams", i32),
-                ("gemm_cus_per_xcd", i32)]
+                ("gemm_cus_per_xcd", i32), ("attn_cus_per_xcd", i32), ("attn_waves_per_cu", i32)]
 
 
 class nf_search_opts(ctypes.Structure):
@@ -76,6 +76,8 @@ _SIGS = {
     "nf_probe_mfma_bf16_tflops": (i32, [ctypes.POINTER(ctypes.c_double)]),
     "nf_probe_hbm_read_gbps": (i32, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_double)]),
     "nf_probe_cu_map": (i32, [P_i32, i32]),
+    "nf_probe_gemm_bf16_ms": (i32, [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double),
+                                    P_i32, P_i32]),
     "nf_last_error": (ctypes.c_char_p, []),
     "nf_status_string": (ctypes.c_char_p, [i32]),
 }
@@ -139,14 +141,16 @@ class HostBatch:
 
 
 def make_plan(count=1, sizes: Sequence[int] = (0,), order=NF_ORDER_PIPELINED, n_streams=1,
-              gemm_cus_per_xcd=0) -> nf_plan:
+              gemm_cus_per_xcd=0, attn_cus_per_xcd=0, attn_waves_per_cu=0) -> nf_plan:
     s = list(sizes) + [0] * (NF_MAX_NANO - len(sizes))
-    return nf_plan(count, (i32 * NF_MAX_NANO)(*s), order, n_streams, gemm_cus_per_xcd)
+    return nf_plan(count, (i32 * NF_MAX_NANO)(*s), order, n_streams, gemm_cus_per_xcd, attn_cus_per_xcd,
+                   attn_waves_per_cu)
 
 
 def plan_dict(p: nf_plan) -> dict:
     return {"count": p.count, "sizes": list(p.sizes)[:p.count], "order": p.order,
-            "n_streams": p.n_streams, "gemm_cus_per_xcd": p.gemm_cus_per_xcd}
+            "n_streams": p.n_streams, "gemm_cus_per_xcd": p.gemm_cus_per_xcd,
+            "attn_cus_per_xcd": p.attn_cus_per_xcd, "attn_waves_per_cu": p.attn_waves_per_cu}
 
 
 def batch_validate(shape: nf_shape, n_pages: int, page_size: int, hb: HostBatch,
@@ -261,6 +265,15 @@ def probe_cu_map(n: int) -> List[int]:
     a = np.zeros(n, np.int32)
     check(lib().nf_probe_cu_map(_i32p(a), n), "nf_probe_cu_map")
     return a.tolist()
+
+
+def probe_gemm_bf16_ms(M, N, K, mode=0, tile_cfg=-1, k_splits=0, cus=256, reps=20):
+    """(ms, cfg, splits) of one GEMM launch on library-owned buffers."""
+    v = ctypes.c_double()
+    c, s = i32(), i32()
+    check(lib().nf_probe_gemm_bf16_ms(M, N, K, mode, tile_cfg, k_splits, cus, reps, ctypes.byref(v),
+                                      ctypes.byref(c), ctypes.byref(s)), "nf_probe_gemm_bf16_ms")
+    return v.value, c.value, s.value
 
 
 # device-to-device copy of raw library memory into a torch tensor (plumbing)

@@ -99,7 +99,7 @@ struct nf_layer {
   int n_cus = 0, n_xcd = 8, cus_per_xcd = 32;
   std::vector<int> xcc_of_bit;                  // CU-mask bit -> XCD (measured)
   nf_plan plan{};
-  std::map<int, StreamPair> pairs;              // by gemm_cus_per_xcd (0 = unmasked)
+  std::map<std::pair<int, int>, StreamPair> pairs;   // by (GEMM CUs, attention CUs) per XCD
   hipEvent_t ev_app[NF_MAX_NANO] = {}, ev_att[NF_MAX_NANO] = {};
   hipEvent_t ev_start = nullptr, ev_g = nullptr, ev_a = nullptr;
   DevBuf h, qkv, q_rot, attn, x1, h2, act, y;
@@ -118,6 +118,7 @@ struct nf_layer {
   int64_t prof_n[K_COUNT] = {};
   StepWork work;
   int last_T = 0;
+  int attn_variant = 0;                         // bf16 attention kernel variant (NF_ATTN_VARIANT)
 };
 
 struct nf_kv_pool {
@@ -204,44 +205,49 @@ nf_status measure_cu_map(int device, int n_cus, int n_xcd, std::vector<int>& out
   return NF_OK;
 }
 
-// Masks for a GEMM/attention split: per XCD, the first `gemm` of its bits go to
-// the GEMM stream, the rest to attention.
-void split_masks(const std::vector<int>& xcc, int n_xcd, int gemm, std::vector<uint32_t>& mg,
-                 std::vector<uint32_t>& ma) {
+// CU budgets per XCD -> masks: the GEMM stream gets the first g CUs of each
+// XCD, the attention stream the last a (g or a == 0: see nf_plan).  Whole-
+// chip budgets use ordinary streams; a mask always leaves every XCD a CU.
+int attn_budget(int g, int a, int per_xcd) { return a ? a : (g ? per_xcd - g : 0); }
+
+void make_mask(const std::vector<int>& xcc, int n_xcd, int lo, int hi, std::vector<uint32_t>& m) {
   const int n = (int)xcc.size(), words = (n + 31) / 32;
-  mg.assign(words, 0u);
-  ma.assign(words, 0u);
+  m.assign(words, 0u);
   std::vector<int> seen(std::max(n_xcd, 16), 0);
   for (int bit = 0; bit < n; ++bit) {
     const int x = xcc[bit] < 0 ? bit % n_xcd : xcc[bit];
-    if (seen[x]++ < gemm)
-      mg[bit / 32] |= 1u << (bit % 32);
-    else
-      ma[bit / 32] |= 1u << (bit % 32);
+    const int k = seen[x]++;                    // k-th CU of XCD x
+    if (k >= lo && k < hi) m[bit / 32] |= 1u << (bit % 32);
   }
 }
 
-nf_status get_pair(nf_layer* L, int gemm_cus, StreamPair& out) {
-  auto it = L->pairs.find(gemm_cus);
+nf_status get_pair(nf_layer* L, int g, int a, StreamPair& out) {
+  const int ab = attn_budget(g, a, L->cus_per_xcd);
+  auto key = std::make_pair(g, ab);
+  auto it = L->pairs.find(key);
   if (it != L->pairs.end()) {
     out = it->second;
     return NF_OK;
   }
+  if ((g || ab) && L->xcc_of_bit.empty()) {
+    nf_status st = measure_cu_map(L->device, L->n_cus, L->n_xcd, L->xcc_of_bit);
+    if (st != NF_OK) return st;
+  }
   StreamPair p;
-  if (gemm_cus == 0) {
+  std::vector<uint32_t> m;
+  if (g == 0) {
     HIP_TRY(hipStreamCreateWithFlags(&p.g, hipStreamNonBlocking));
+  } else {
+    make_mask(L->xcc_of_bit, L->n_xcd, 0, g, m);
+    HIP_TRY(hipExtStreamCreateWithCUMask(&p.g, (uint32_t)m.size(), m.data()));
+  }
+  if (ab == 0) {
     HIP_TRY(hipStreamCreateWithFlags(&p.a, hipStreamNonBlocking));
   } else {
-    if (L->xcc_of_bit.empty()) {
-      nf_status st = measure_cu_map(L->device, L->n_cus, L->n_xcd, L->xcc_of_bit);
-      if (st != NF_OK) return st;
-    }
-    std::vector<uint32_t> mg, ma;
-    split_masks(L->xcc_of_bit, L->n_xcd, gemm_cus, mg, ma);
-    HIP_TRY(hipExtStreamCreateWithCUMask(&p.g, (uint32_t)mg.size(), mg.data()));
-    HIP_TRY(hipExtStreamCreateWithCUMask(&p.a, (uint32_t)ma.size(), ma.data()));
+    make_mask(L->xcc_of_bit, L->n_xcd, L->cus_per_xcd - ab, L->cus_per_xcd, m);
+    HIP_TRY(hipExtStreamCreateWithCUMask(&p.a, (uint32_t)m.size(), m.data()));
   }
-  L->pairs[gemm_cus] = p;
+  L->pairs[key] = p;
   out = p;
   return NF_OK;
 }
@@ -293,6 +299,7 @@ struct StepCtx {
   const AttnItem* items;
   const MergeItem* merges;
   int gemm_cus, attn_cus;
+  int attn_waves_per_cu;
 };
 
 char* ptr(const DevBuf& b, int64_t elems, int dt) { return (char*)b.p + elems * (int64_t)dtype_bytes(dt); }
@@ -432,6 +439,8 @@ nf_status issue_attention(StepCtx& c, int j, hipStream_t s) {
   a.page_indices = c.indices;
   a.nq = sh.n_q_heads; a.nkv = sh.n_kv_heads; a.d = sh.head_dim; a.page_size = c.P->page_size;
   a.scale = (float)(1.0 / std::sqrt((double)sh.head_dim));
+  a.variant = L->attn_variant;
+  a.max_blocks = c.attn_waves_per_cu > 0 ? c.attn_waves_per_cu * c.attn_cus : 0;
   prof_begin(L, K_ATTN, s);
   HIP_STEP(attention(sh.dtype, a, s));
   prof_end(L, K_ATTN, s);
@@ -501,13 +510,19 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
 
   const bool two = plan.n_streams == 2;
   const int gsplit = two ? plan.gemm_cus_per_xcd : 0;
+  const int asplit = two ? attn_budget(plan.gemm_cus_per_xcd, plan.attn_cus_per_xcd, L->cus_per_xcd) : 0;
   StepCtx c{};
   c.L = L;
   c.P = P;
   c.b = b;
   c.gemm_cus = gsplit ? gsplit * L->n_xcd : L->n_cus;
-  c.attn_cus = gsplit ? (L->cus_per_xcd - gsplit) * L->n_xcd : L->n_cus;
-  build_work(L->s, *b, plan, P->page_size, c.attn_cus, 8, L->work);
+  c.attn_cus = asplit ? asplit * L->n_xcd : L->n_cus;
+  c.attn_waves_per_cu = two ? plan.attn_waves_per_cu : 0;
+  // attention work items: one wave each for the LDS-free kernel (many, short),
+  // a four-wave workgroup each otherwise
+  const bool wave_items = L->s.dtype == NF_BF16 && L->s.head_dim == 128 && L->attn_variant != 1;
+  build_work(L->s, *b, plan, P->page_size, wave_items ? 8 * c.attn_cus : 2 * c.attn_cus, 8,
+             wave_items ? 32 : 0, L->work);
   const StepWork& w = L->work;
   const int count = (int)w.nanos.size();
 
@@ -560,16 +575,23 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
   c.items = (const AttnItem*)(dm + o_it);
   c.merges = (const MergeItem*)(dm + o_mg);
 
+  // Streams: the GEMM side runs on the caller's stream unless it is CU-masked;
+  // attention runs on the pair's attention stream.  Cross-stream waits cost
+  // ~20 us each on this runtime, so only the necessary ones are issued:
+  // attention(j) waits for RoPE/append(j), the O-projection of j waits for
+  // attention(j).  The last of those also orders every attention kernel
+  // before the end of the step on the GEMM stream.
   hipStream_t sg = caller, sa = caller;
   if (two) {
     StreamPair pr;
-    st = get_pair(L, gsplit, pr);
+    st = get_pair(L, gsplit, plan.attn_cus_per_xcd, pr);
     if (st != NF_OK) return st;
-    sg = pr.g;
     sa = pr.a;
-    HIP_TRY(hipEventRecord(L->ev_start, caller));
-    HIP_TRY(hipStreamWaitEvent(sg, L->ev_start, 0));
-    HIP_TRY(hipStreamWaitEvent(sa, L->ev_start, 0));
+    if (gsplit) {
+      sg = pr.g;
+      HIP_TRY(hipEventRecord(L->ev_start, caller));
+      HIP_TRY(hipStreamWaitEvent(sg, L->ev_start, 0));
+    }
   }
   auto front_and_attn = [&](int j) -> nf_status {
     nf_status s1 = issue_front(c, j, sg);
@@ -600,11 +622,9 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
       if ((st = back(j)) != NF_OK) return st;
     }
   }
-  if (two) {
+  if (two && sg != caller) {
     HIP_TRY(hipEventRecord(L->ev_g, sg));
-    HIP_TRY(hipEventRecord(L->ev_a, sa));
     HIP_TRY(hipStreamWaitEvent(caller, L->ev_g, 0));
-    HIP_TRY(hipStreamWaitEvent(caller, L->ev_a, 0));
   }
   return NF_OK;
 }
@@ -682,7 +702,8 @@ nf_status nf_layer_create(const nf_shape* s, const nf_weights* w, nf_layer** out
   L->n_cus = prop.multiProcessorCount;
   L->n_xcd = 8;
   L->cus_per_xcd = std::max(1, L->n_cus / L->n_xcd);
-  L->plan = nf_plan{1, {0, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0};
+  L->plan = nf_plan{1, {0, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0, 0, 0};
+  if (const char* v = std::getenv("NF_ATTN_VARIANT")) L->attn_variant = std::atoi(v);
 
   const int dt = s->dtype;
   const size_t eb = dtype_bytes(dt);
@@ -787,7 +808,7 @@ nf_status nf_plan_set(nf_layer* L, const nf_plan* p) {
   if (p->n_streams == 2) {
     HIP_TRY(hipSetDevice(L->device));
     StreamPair pr;
-    st = get_pair(L, p->gemm_cus_per_xcd, pr);
+    st = get_pair(L, p->gemm_cus_per_xcd, p->attn_cus_per_xcd, pr);
     if (st != NF_OK) return st;
   }
   L->plan = *p;
@@ -1006,57 +1027,134 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
   if (o) opts = *o;
   opts.max_count = std::max(1, std::min(opts.max_count, NF_MAX_NANO));
   opts.reps = std::max(1, opts.reps);
+  opts.top_k = std::max(1, opts.top_k);
   hipStream_t s = (hipStream_t)stream;
   const int T = b->n_tokens;
+  if (T == 0) {
+    *out = nf_plan{1, {0, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0, 0, 0};
+    L->plan = *out;
+    return NF_OK;
+  }
+
+  // candidate grid over the four plan dimensions
   std::vector<Cand> cands;
-  nf_plan base{1, {T, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0};
+  const nf_plan base{1, {T, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0, 0, 0};
   cands.push_back({base});
-  const int splits[] = {0, 8, 12, 16, 20, 24};
-  for (int k = 2; k <= opts.max_count; ++k) {
-    if (T < k) break;
+  struct Split { int g, a, w; };
+  const Split splits[] = {{0, 0, 0}, {0, 0, 4}, {0, 24, 0}, {16, 16, 0}, {20, 12, 0}, {24, 8, 0}};
+  for (int k = 2; k <= opts.max_count && k <= T; ++k) {
     nf_plan eq = base, bal = base;
     eq.count = bal.count = k;
     for (int j = 0; j < k; ++j) eq.sizes[j] = T / k + (j < T % k ? 1 : 0);
     balanced_sizes(b, k, bal.sizes);
     for (const nf_plan& pz : {eq, bal}) {
-      for (int sp : splits) {
-        if (sp >= L->cus_per_xcd) continue;
+      cands.push_back({pz});                      // split, one stream
+      for (const Split& sp : splits) {
+        if (sp.g >= L->cus_per_xcd || sp.a >= L->cus_per_xcd) continue;
         nf_plan c = pz;
         c.n_streams = 2;
-        c.gemm_cus_per_xcd = sp;
+        c.gemm_cus_per_xcd = sp.g;
+        c.attn_cus_per_xcd = sp.a;
+        c.attn_waves_per_cu = sp.w;
         cands.push_back({c});
       }
     }
   }
+
   hipEvent_t e0, e1;
   HIP_TRY(hipEventCreate(&e0));
   HIP_TRY(hipEventCreate(&e1));
-  int best = -1;
-  for (size_t i = 0; i < cands.size(); ++i) {
+  auto measure = [&](Cand& c, int warm, int reps) -> nf_status {
     nf_status st = NF_OK;
-    for (int w = 0; w < opts.warmup && st == NF_OK; ++w) st = step_impl(L, P, b, s, cands[i].plan);
-    if (st != NF_OK) {
-      (void)hipEventDestroy(e0);
-      (void)hipEventDestroy(e1);
-      return st;
-    }
+    for (int w = 0; w < warm && st == NF_OK; ++w) st = step_impl(L, P, b, s, c.plan);
+    if (st != NF_OK) return st;
     HIP_TRY(hipEventRecord(e0, s));
-    for (int r = 0; r < opts.reps && st == NF_OK; ++r) st = step_impl(L, P, b, s, cands[i].plan);
+    for (int r = 0; r < reps && st == NF_OK; ++r) st = step_impl(L, P, b, s, c.plan);
     HIP_TRY(hipEventRecord(e1, s));
     HIP_TRY(hipEventSynchronize(e1));
     if (st != NF_OK) return st;
     float ms = 0;
     HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
-    cands[i].ms = ms / opts.reps;
-    if (best < 0 || cands[i].ms < cands[best].ms) best = (int)i;
+    c.ms = ms / reps;
+    return NF_OK;
+  };
+  // stage 1: every candidate, briefly; stage 2: the top_k again, longer
+  nf_status st = NF_OK;
+  for (Cand& c : cands)
+    if ((st = measure(c, 1, 2)) != NF_OK) break;
+  std::vector<Cand> top;
+  if (st == NF_OK) {
+    std::stable_sort(cands.begin(), cands.end(), [](const Cand& x, const Cand& y) { return x.ms < y.ms; });
+    top.assign(cands.begin(), cands.begin() + std::min<size_t>(cands.size(), opts.top_k));
+    for (Cand& c : top) {
+      const double quick = c.ms;
+      if ((st = measure(c, opts.warmup, opts.reps)) != NF_OK) break;
+      if (std::getenv("NF_SEARCH_VERBOSE")) {
+        const nf_plan& q = c.plan;
+        std::fprintf(stderr,
+                     "nf search: count %d sizes %d/%d/%d/%d streams %d cus/xcd gemm %2d attn %2d waves %d -> %.3f ms "
+                     "(first pass %.3f)\n",
+                     q.count, q.sizes[0], q.sizes[1], q.sizes[2], q.sizes[3], q.n_streams, q.gemm_cus_per_xcd,
+                     q.attn_cus_per_xcd, q.attn_waves_per_cu, c.ms, quick);
+      }
+    }
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
-  L->plan = cands[best].plan;
-  *out = cands[best].plan;
+  if (st != NF_OK) return st;
+  int best = 0;
+  for (size_t i = 1; i < top.size(); ++i)
+    if (top[i].ms < top[best].ms) best = (int)i;
   if (times_ms) {
-    times_ms[0] = cands[best].ms;
-    times_ms[1] = cands[best].ms;
+    times_ms[0] = top[best].ms;
+    times_ms[1] = cands.empty() ? 0 : (double)cands.size();
   }
+  L->plan = top[best].plan;
+  *out = top[best].plan;
+  return NF_OK;
+}
+
+extern "C" nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int32_t mode, int32_t tile_cfg,
+                                           int32_t k_splits, int32_t cus, int32_t reps, double* ms,
+                                           int32_t* out_cfg, int32_t* out_splits) {
+  if (!ms || M <= 0 || N <= 0 || K <= 0 || K % 8 || mode < 0 || mode > 2 || reps <= 0)
+    return set_err(NF_ERR_INVALID_ARG, "nf_probe_gemm_bf16_ms: bad argument");
+  const int64_t nb = mode == GEMM_SWIGLU ? 2 : 1;
+  void *A = nullptr, *Bm = nullptr, *C = nullptr, *R = nullptr;
+  HIP_TRY(hipMalloc(&A, (size_t)M * K * 2));
+  HIP_TRY(hipMalloc(&Bm, (size_t)nb * N * K * 2));
+  HIP_TRY(hipMalloc(&C, (size_t)M * N * 2));
+  HIP_TRY(hipMalloc(&R, (size_t)M * N * 2));
+  HIP_TRY(hipMemset(A, 0x3c, (size_t)M * K * 2));       // small finite bf16 values
+  HIP_TRY(hipMemset(Bm, 0x3c, (size_t)nb * N * K * 2));
+  HIP_TRY(hipMemset(R, 0, (size_t)M * N * 2));
+  GemmArgs g;
+  g.A = A; g.lda = K;
+  g.B = Bm; g.B2 = (char*)Bm + (size_t)N * K * 2; g.ldb = K;
+  g.C = C; g.ldc = N; g.R = R; g.ldr = N;
+  g.M = M; g.N = N; g.K = K; g.mode = mode;
+  GemmPlan p = gemm_choose(g, cus);
+  if (tile_cfg >= 0) p.cfg = tile_cfg;
+  if (k_splits > 0) p.k_splits = k_splits;
+  void* ws = nullptr;
+  const size_t wsb = gemm_workspace_bytes(g, p);
+  if (wsb) HIP_TRY(hipMalloc(&ws, wsb));
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  for (int i = 0; i < 3; ++i) HIP_TRY(gemm_bf16(g, p, ws, nullptr));
+  HIP_TRY(hipEventRecord(e0, nullptr));
+  for (int i = 0; i < reps; ++i) HIP_TRY(gemm_bf16(g, p, ws, nullptr));
+  HIP_TRY(hipEventRecord(e1, nullptr));
+  HIP_TRY(hipEventSynchronize(e1));
+  float t = 0;
+  HIP_TRY(hipEventElapsedTime(&t, e0, e1));
+  *ms = t / reps;
+  if (out_cfg) *out_cfg = p.cfg;
+  if (out_splits) *out_splits = p.k_splits;
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  for (void* q : {A, Bm, C, R, ws})
+    if (q) (void)hipFree(q);
   return NF_OK;
 }

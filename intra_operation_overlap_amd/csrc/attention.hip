@@ -5,25 +5,24 @@
 // head, a range of the request's logical pages).  Its 16 "rows" are the
 // (token, query head) pairs that share the KV head, so a decode token fills G
 // rows and a prefill item packs 16/G tokens.  Each row r has its own causal
-// limit: keys 0..pos(row).  A 256-thread workgroup (four wave64s) takes the
-// item's pages round-robin across its waves; each wave keeps an online
-// softmax (running max, running sum, unnormalised output) and the four are
-// combined through LDS at the end.  Items whose page range was split write
+// limit: keys 0..pos(row).  Items whose page range was split write
 // unnormalised partials + (max, sum) for a merge kernel.
 //
 // bf16, d = 128 path on matrix cores, per 16-key page:
 //   S^T[key][row] = K_page[key][:] . Q[row][:]   4 x v_mfma_f32_16x16x32_bf16
-//       (A = K page rows straight from the pool, B = Q held in registers)
+//       (A = K page straight from the pool, B = Q held in registers)
 //   the C layout of S^T puts keys 4*(lane/16)+i of row lane%16 in each lane,
 //   which is exactly the B-operand layout of the next product, so the softmax
 //   probabilities never leave registers:
 //   O^T[dim][row] += V^T_page[dim][key] . P^T[key][row]
 //                                       8 x v_mfma_f32_16x16x16_bf16
-//       (A = V page, stored dimension-major in the pool, 8 contiguous bytes
-//        per lane, each 16-dim block a contiguous 512-byte run)
-// The running max and sum are per row, i.e. per lane%16 column in both
-// products, so the rescale needs no data movement; row maxima are reduced
-// over the four lanes that share a column with two xor-shuffles.
+// The pool stores every (page, KV head) block in exactly these operand
+// layouts (kv_k_off / kv_v_off), so a page arrives with eight linear
+// 16-byte-per-lane loads (1 KB per instruction), the access pattern that lets
+// one CU draw the most HBM bandwidth.  The running max and sum are per row,
+// i.e. per lane%16 column in both products, so the rescale needs no data
+// movement; row maxima are reduced over the four lanes that share a column
+// with two xor-shuffles.
 #include "nf_device.h"
 #include "nf_internal.h"
 
@@ -31,9 +30,12 @@ namespace nf {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int ROWS = 16;
+constexpr int DH = 128;
+constexpr int BLOCK = 16 * DH;                 // elements of one (page, KV head) block
 
 __device__ __forceinline__ void row_info(const AttnArgs& a, const AttnItem& it, int row, int G, int kh,
                                          int& limit, int64_t& qoff) {
@@ -91,11 +93,94 @@ __device__ void finish_item(const AttnArgs& a, const AttnItem& it, int G, int kh
   }
 }
 
-// ---------------------------------------------------------------- bf16, d = 128
+// One page's operand fragments for this lane.
+struct PageRegs {
+  bf16x8 k[4];      // K operand fragments, dims 32c .. 32c+31 (c = 0..3)
+  s16x8 v[4];       // V operand fragments of dim blocks 2c (first 4) and 2c+1 (last 4)
+};
+
+__device__ __forceinline__ void load_page(const bf16* kb, const bf16* vb, int lane, PageRegs& r) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.k[c] = __builtin_nontemporal_load((const bf16x8*)(kb + c * 512 + lane * 8));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.v[c] = __builtin_nontemporal_load((const s16x8*)(vb + c * 512 + lane * 8));
+}
+
+struct RowState {
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[8];
+};
+
+// One 16-key page: scores, online softmax, P.V.  `key0` is this lane's first
+// key, `limit` its row's causal limit, `max_limit` the largest limit of the
+// item (keys at or past it may be unwritten, so their V values are zeroed).
+__device__ __forceinline__ void page_step(const bf16x8 (&qf)[4], PageRegs& r, int key0, int limit, int max_limit,
+                                          bool tail, float sl2, RowState& st) {
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[c], qf[c], s, 0, 0, 0);
+  float sv[4];
+  float pm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (key0 + i < limit) ? s[i] * sl2 : -INFINITY;
+    pm = fmaxf(pm, sv[i]);
+  }
+  pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+  pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+  const float m_new = fmaxf(st.m, pm);
+  const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = exp2f(st.m - mu);
+  float ps = 0.f;
+  bf16x4 pb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float pv = exp2f(sv[i] - mu);
+    ps += pv;
+    pb[i] = (bf16)pv;
+  }
+  st.l = st.l * alpha + ps;
+  st.m = m_new;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) st.o[b] *= alpha;
+  if (tail) {
+    // keys past every row's limit may be unwritten (or being written):
+    // zero them so 0 * garbage cannot reach the sum
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (key0 + i >= max_limit)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          r.v[c][i] = 0;
+          r.v[c][4 + i] = 0;
+        }
+  }
+  const s16x4 pbs = __builtin_bit_cast(s16x4, pb);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const s16x4 lo = {r.v[c][0], r.v[c][1], r.v[c][2], r.v[c][3]};
+    const s16x4 hi = {r.v[c][4], r.v[c][5], r.v[c][6], r.v[c][7]};
+    st.o[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, pbs, st.o[2 * c], 0, 0, 0);
+    st.o[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, pbs, st.o[2 * c + 1], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void load_q(const AttnArgs& a, int64_t qoff, int grp, bf16x8 (&qf)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (qoff >= 0)
+      qf[c] = *(const bf16x8*)((const bf16*)a.q_rot + qoff + 32 * c + 8 * grp);
+    else
+      qf[c] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+// ---------------------------------------------------------------- four waves per item
+// A 256-thread workgroup takes the item's pages round-robin across its four
+// waves and merges the four online-softmax states through LDS.
 __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(AttnArgs a) {
-  constexpr int D = 128;
   __shared__ float m_s[4 * ROWS], l_s[4 * ROWS];
-  __shared__ float O_s[4 * ROWS * D];
+  __shared__ float O_s[4 * ROWS * DH];
 
   const AttnItem it = a.items[blockIdx.x];
   const int kh = blockIdx.y;
@@ -109,99 +194,122 @@ __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(AttnArgs a) {
   row_info(a, it, col, G, kh, limit, qoff);
   int max_limit = 0;                // largest causal limit over the item's rows
   for (int t = 0; t < it.ntok; ++t) max_limit = max(max_limit, a.pos[it.tok0 + t] + 1);
-
-  // Q^T fragments (B operand of S^T = K Q^T): row `col`, dims 32c + 8*grp .. +7
   bf16x8 qf[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (qoff >= 0)
-      qf[c] = *(const bf16x8*)((const bf16*)a.q_rot + qoff + 32 * c + 8 * grp);
-    else
-      qf[c] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-
+  load_q(a, qoff, grp, qf);
   const float sl2 = a.scale * LOG2E;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 oacc[8];
+  RowState st;
 #pragma unroll
-  for (int b = 0; b < 8; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < 8; ++b) st.o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* ptab = a.page_indices + a.page_indptr[it.req];
-  const bf16* kpool = (const bf16*)a.k_pool;
-  const bf16* vpool = (const bf16*)a.v_pool;
-
   for (int lp = it.page_begin + wave; lp < it.page_end; lp += 4) {
-    const int64_t blk = (int64_t)ptab[lp] * a.nkv + kh;     // (page, kv head) block
-    const bf16* kb = kpool + blk * (16 * D);
-    const bf16* vb = vpool + blk * (16 * D);
-    bf16x8 kf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kf[c] = *(const bf16x8*)(kb + col * D + 32 * c + 8 * grp);
-    s16x4 vf[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) vf[b] = *(const s16x4*)(vb + (16 * b + col) * 16 + 4 * grp);
-
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[c], s, 0, 0, 0);
-
-    const int key0 = lp * 16 + 4 * grp;   // keys key0 .. key0+3 in this lane
-    float sv[4];
-    float pm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (key0 + i < limit) ? s[i] * sl2 : -INFINITY;
-      pm = fmaxf(pm, sv[i]);
-    }
-    pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-    pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
-    const float m_new = fmaxf(m_run, pm);
-    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - mu);
-    float ps = 0.f;
-    bf16x4 pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = exp2f(sv[i] - mu);
-      ps += pv;
-      pb[i] = (bf16)pv;
-    }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) oacc[b] *= alpha;
-    if (lp * 16 + 16 > max_limit) {
-      // keys past every row's limit may be unwritten (or being written):
-      // zero them so 0 * garbage cannot reach the sum
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (key0 + i >= max_limit)
-#pragma unroll
-          for (int b = 0; b < 8; ++b) vf[b][i] = 0;
-    }
-    const s16x4 pbs = __builtin_bit_cast(s16x4, pb);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[b], pbs, oacc[b], 0, 0, 0);
+    const int64_t blk = (int64_t)ptab[lp] * a.nkv + kh;
+    PageRegs r;
+    load_page((const bf16*)a.k_pool + blk * BLOCK, (const bf16*)a.v_pool + blk * BLOCK, lane, r);
+    page_step(qf, r, lp * 16 + 4 * grp, limit, max_limit, lp * 16 + 16 > max_limit, sl2, st);
   }
 
   // this wave's (m, l, O^T) -> LDS; O^T lane layout: dim 16b + 4*grp + i, row col
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  st.l += __shfl_xor(st.l, 16, 64);
+  st.l += __shfl_xor(st.l, 32, 64);
   if (grp == 0) {
-    m_s[wave * ROWS + col] = m_run;
-    l_s[wave * ROWS + col] = l_run;
+    m_s[wave * ROWS + col] = st.m;
+    l_s[wave * ROWS + col] = st.l;
   }
 #pragma unroll
   for (int b = 0; b < 8; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) O_s[(wave * ROWS + col) * D + 16 * b + 4 * grp + i] = oacc[b][i];
+    for (int i = 0; i < 4; ++i) O_s[(wave * ROWS + col) * DH + 16 * b + 4 * grp + i] = st.o[b][i];
   __syncthreads();
   finish_item<bf16>(a, it, G, kh, m_s, l_s, O_s);
 }
 
+// ---------------------------------------------------------------- one wave per item
+// One wave64 per work item, no LDS and no barrier: the wave walks its page
+// range with the next page's K and V already in flight while the current one
+// feeds the matrix cores, and writes either the normalised output or an
+// unnormalised partial.  Small and LDS-free, these waves also fit beside the
+// GEMM's LDS-heavy workgroups on a CU.
+__device__ __forceinline__ void wave_item(const AttnArgs& a, const AttnItem& it, int kh) {
+  const int G = a.nq / a.nkv;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+
+  int limit;
+  int64_t qoff;
+  row_info(a, it, col, G, kh, limit, qoff);
+  int max_limit = 0;
+  for (int t = 0; t < it.ntok; ++t) max_limit = max(max_limit, a.pos[it.tok0 + t] + 1);
+  bf16x8 qf[4];
+  load_q(a, qoff, grp, qf);
+  const float sl2 = a.scale * LOG2E;
+  RowState st;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) st.o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* ptab = a.page_indices + a.page_indptr[it.req];
+  const bf16* kpool = (const bf16*)a.k_pool;
+  const bf16* vpool = (const bf16*)a.v_pool;
+  PageRegs r[2];
+  auto load = [&](int lp, int set) {
+    const int64_t blk = (int64_t)ptab[lp] * a.nkv + kh;
+    load_page(kpool + blk * BLOCK, vpool + blk * BLOCK, lane, r[set]);
+  };
+  auto step = [&](int lp, int set) {
+    page_step(qf, r[set], lp * 16 + 4 * grp, limit, max_limit, lp * 16 + 16 > max_limit, sl2, st);
+  };
+  const int b0 = it.page_begin, n = it.page_end - it.page_begin;
+  int i = 0;
+  if (n > 0) load(b0, 0);
+  for (; i + 1 < n; i += 2) {
+    load(b0 + i + 1, 1);
+    step(b0 + i, 0);
+    if (i + 2 < n) load(b0 + i + 2, 0);
+    step(b0 + i + 1, 1);
+  }
+  if (i < n) step(b0 + i, 0);
+
+  // row totals: sum the four lane groups that share a column
+  st.l += __shfl_xor(st.l, 16, 64);
+  st.l += __shfl_xor(st.l, 32, 64);
+  const int valid_rows = min(ROWS / G, it.ntok) * G;
+  if (col >= valid_rows) return;
+  const int t = it.tok0 + col / G;
+  const int head = kh * G + col % G;
+  // O^T lane layout: dim 16 b + 4 grp + i of row `col`
+  if (it.partial < 0) {
+    const float invL = st.l > 0.f ? 1.f / st.l : 0.f;
+    bf16* o = (bf16*)a.attn + (int64_t)t * a.nq * DH + (int64_t)head * DH;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      bf16x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = (bf16)(st.o[b][q] * invL);
+      *(bf16x4*)(o + 16 * b + 4 * grp) = v;
+    }
+  } else {
+    const int64_t base = ((int64_t)it.partial * a.nkv + kh) * ROWS + col;
+    float* po = a.part_o + base * DH;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) *(f32x4*)(po + 16 * b + 4 * grp) = st.o[b];
+    if (grp == 0) {
+      a.part_ml[base * 2 + 0] = st.m;
+      a.part_ml[base * 2 + 1] = st.l;
+    }
+  }
+}
+
+// Work index w = item * nkv + kv head; with a capped grid each wave strides
+// over the work list (items are longest first, so the stride balances).
+__global__ __launch_bounds__(64) void attn_bf16_d128_wave_kernel(AttnArgs a) {
+  const int n_work = a.n_items * a.nkv;
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) wave_item(a, a.items[w / a.nkv], w % a.nkv);
+}
+
 // ---------------------------------------------------------------- generic
-// Any dtype, any even d <= 256: one wave per row at a time, keys walked one
-// by one with an online softmax; lanes split the head dimension.
+// Any dtype, any head_dim multiple of 32 up to 256: one wave per row at a
+// time, keys walked one by one with an online softmax; lanes split the head
+// dimension.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   constexpr int DMAX = 256;
@@ -229,14 +337,15 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
     float m = -INFINITY, l = 0.f;
     for (int lp = it.page_begin + wave; lp < it.page_end; lp += 4) {
       const int64_t blk = (int64_t)ptab[lp] * a.nkv + kh;
+      const T* kb = (const T*)a.k_pool + blk * S * d;
+      const T* vb = (const T*)a.v_pool + blk * S * d;
       for (int sl = 0; sl < S; ++sl) {
         const int key = lp * S + sl;
         if (key >= limit) break;
-        const T* kr = (const T*)a.k_pool + (blk * S + sl) * d;
         float part = 0.f;
         for (int u = 0; u < DMAX / 64; ++u) {
           const int e = lane + 64 * u;
-          if (e < d) part += q[u] * to_f32(kr[e]);
+          if (e < d) part += q[u] * to_f32(kb[kv_k_off(sl, e)]);
         }
         const float sc = wave_sum(part) * a.scale;
         const float mn = fmaxf(m, sc);
@@ -245,7 +354,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
         l = l * al + p;
         for (int u = 0; u < DMAX / 64; ++u) {
           const int e = lane + 64 * u;
-          const float v = e < d ? to_f32(((const T*)a.v_pool)[(blk * d + e) * S + sl]) : 0.f;
+          const float v = e < d ? to_f32(vb[kv_v_off(sl, e)]) : 0.f;
           o[u] = o[u] * al + p * v;
         }
         m = mn;
@@ -307,12 +416,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 hipError_t attention(int dtype, const AttnArgs& a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
   dim3 grid(a.n_items, a.nkv);
-  if (dtype == 1 && a.d == 128 && a.page_size == 16)
-    attn_bf16_d128_kernel<<<grid, 256, 0, s>>>(a);
-  else if (dtype == 1)
+  if (dtype == 1 && a.d == 128 && a.page_size == 16) {
+    if (a.variant == 1) {
+      attn_bf16_d128_kernel<<<grid, 256, 0, s>>>(a);
+    } else {
+      int blocks = a.n_items * a.nkv;
+      if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
+      attn_bf16_d128_wave_kernel<<<blocks, 64, 0, s>>>(a);
+    }
+  } else if (dtype == 1) {
     attn_generic_kernel<bf16><<<grid, 256, 0, s>>>(a);
-  else
+  } else {
     attn_generic_kernel<float><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -25,22 +25,52 @@ constexpr int BK = 64;
 constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (144 B: breaks bank aliasing)
 constexpr int NXCD = 8;
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int MS_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int MS = MS_;                    // MFMA block: 16x16x32 or 32x32x16
+  static constexpr int KSTEP = MS == 16 ? 32 : 16;  // K per MFMA
+  static constexpr int NACC = MS == 16 ? 4 : 16;    // accumulators per lane per block
   static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  static constexpr int FM = WTM / MS, FN = WTN / MS;
   static constexpr int A_LOADS = BM * 8 / 256, B_LOADS = BN * 8 / 256;
   static_assert(WM * WN == 4, "four waves");
+  static_assert(MS == 16 || MS == 32, "mfma shape");
   static_assert(FM >= 1 && FN >= 2 && FN % 2 == 0, "wave tile");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "loads");
 };
 
-using Cfg0 = Cfg<128, 128, 2, 2>;
-using Cfg1 = Cfg<64, 128, 1, 4>;
-using Cfg2 = Cfg<256, 128, 2, 2>;
-using Cfg3 = Cfg<32, 128, 1, 4>;
-using Cfg4 = Cfg<128, 256, 2, 2>;
+// 16x16x32 configs for decode-sized M (weight-streaming); 32x32x16 configs,
+// which run at twice the rate on gfx950, for compute-bound M.
+using Cfg0 = Cfg<128, 128, 2, 2, 32>;
+using Cfg1 = Cfg<64, 128, 1, 4, 16>;
+using Cfg2 = Cfg<256, 128, 2, 2, 32>;
+using Cfg3 = Cfg<32, 128, 1, 4, 16>;
+using Cfg4 = Cfg<128, 256, 2, 2, 32>;
+using Cfg5 = Cfg<256, 256, 2, 2, 32>;
+using Cfg6 = Cfg<64, 128, 2, 2, 32>;
+
+template <int MS> struct Acc;
+template <> struct Acc<16> { typedef f32x4 T; };
+template <> struct Acc<32> { typedef f32x16 T; };
+
+template <int MS>
+__device__ __forceinline__ typename Acc<MS>::T mfma(const bf16x8& a, const bf16x8& b, const typename Acc<MS>::T& c) {
+  if constexpr (MS == 16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of accumulator element r (within an MS x MS block) held by `lane`;
+// the column is lane % MS.
+template <int MS>
+__device__ __forceinline__ int acc_row(int lane, int r) {
+  if constexpr (MS == 16)
+    return 4 * (lane >> 4) + r;
+  else
+    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
 
 struct KParams {
   GemmArgs a;
@@ -55,6 +85,8 @@ __device__ __forceinline__ int xcd_logical(int L, int total) {
   const int q = total / NXCD, r = total % NXCD;
   return xcd * q + min(xcd, r) + slot;
 }
+
+
 
 template <class C, int MODE, bool PARTIAL>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(KParams p) {
@@ -148,62 +180,65 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(KParams p) {
     }
   };
 
-  f32x4 acc[C::FM][C::FN];
+  typedef typename Acc<C::MS>::T AccT;
+  AccT acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < C::NACC; ++e) acc[i][j][e] = 0.f;
 
   // LDS row of B fragment j for this wave
   auto b_row = [&](int j) {
     if (MODE == GEMM_SWIGLU) {
       constexpr int HF = C::FN / 2;
-      return j < HF ? wn * (C::WTN / 2) + j * 16 : C::BN / 2 + wn * (C::WTN / 2) + (j - HF) * 16;
+      return j < HF ? wn * (C::WTN / 2) + j * C::MS : C::BN / 2 + wn * (C::WTN / 2) + (j - HF) * C::MS;
     }
-    return wn * C::WTN + j * 16;
+    return wn * C::WTN + j * C::MS;
   };
 
   const int nk = (k_hi - k_lo + BK - 1) / BK;
   load_slab(k_lo);
   store_slab(0);
   __syncthreads();
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  // fragment of lane: row lane % MS of the block, 8 consecutive k at 8 * (lane / MS)
+  const int fr = lane % C::MS, fk = (lane / C::MS) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) load_slab(k_lo + (kt + 1) * BK);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < BK / C::KSTEP; ++s) {
       bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
-        af[i] = *(const bf16x8*)&As[buf][(wm * C::WTM + i * 16 + fr) * LDS_STRIDE + s * 32 + fk];
+        af[i] = *(const bf16x8*)&As[buf][(wm * C::WTM + i * C::MS + fr) * LDS_STRIDE + s * C::KSTEP + fk];
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        bfr[j] = *(const bf16x8*)&Bs[buf][(b_row(j) + fr) * LDS_STRIDE + s * 32 + fk];
+        bfr[j] = *(const bf16x8*)&Bs[buf][(b_row(j) + fr) * LDS_STRIDE + s * C::KSTEP + fk];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma<C::MS>(af[i], bfr[j], acc[i][j]);
     }
     if (kt + 1 < nk) store_slab(buf ^ 1);
     __syncthreads();
   }
 
-  // epilogue: lane holds D[m = 4*(lane/16) + r][n = lane % 16] of each 16x16 block
-  const int er = (lane >> 4) * 4, ec = lane & 15;
+  // epilogue: lane holds D[acc_row(lane, r)][lane % MS] of each block
+  const int ec = lane % C::MS;
   constexpr int NJ = (MODE == GEMM_SWIGLU) ? C::FN / 2 : C::FN;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int local = m0 + wm * C::WTM + i * 16 + er + r;
+    for (int r = 0; r < C::NACC; ++r) {
+      const int local = m0 + wm * C::WTM + i * C::MS + acc_row<C::MS>(lane, r);
       if (local >= rows) continue;
       const int64_t orow = m_begin + local;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         if (MODE == GEMM_SWIGLU) {
-          const int col = n_tile * (C::BN / 2) + wn * (C::WTN / 2) + j * 16 + ec;
+          const int col = n_tile * (C::BN / 2) + wn * (C::WTN / 2) + j * C::MS + ec;
           if (col >= a.N) continue;
           const float g = acc[i][j][r], u = acc[i][j + C::FN / 2][r];
           if (PARTIAL) {
@@ -214,7 +249,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(KParams p) {
             ((bf16*)a.C)[orow * a.ldc + col] = (bf16)(silu_f(g) * u);
           }
         } else {
-          const int col = n_tile * C::BN + wn * C::WTN + j * 16 + ec;
+          const int col = n_tile * C::BN + wn * C::WTN + j * C::MS + ec;
           if (col >= a.N) continue;
           const float v = acc[i][j][r];
           if (PARTIAL) {
@@ -233,33 +268,50 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(KParams p) {
   }
 }
 
-// Sum of split-K partials + the mode's epilogue; 4 consecutive columns per thread.
+// Sum of split-K partials + the mode's epilogue; 4 consecutive columns per
+// thread, 16-byte partial loads (N % 4 == 0: hidden, ffn and head_dim are
+// multiples of 8).
 template <int MODE>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, const float* part,
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, const float* __restrict__ part,
                                                             int64_t part_ld, int splits) {
-  const int cols4 = (a.N + 3) / 4;
+  const int cols4 = a.N / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)a.M * cols4) return;
   const int row = (int)(idx / cols4);
-  const int c0 = (int)(idx % cols4) * 4;
-  for (int c = c0; c < min(c0 + 4, a.N); ++c) {
-    float v = 0.f, u = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float* P = part + (int64_t)s * a.M * part_ld + (int64_t)row * part_ld;
-      v += P[c];
-      if (MODE == GEMM_SWIGLU) u += P[a.N + c];
-    }
-    if (MODE == GEMM_SWIGLU) {
-      ((bf16*)a.C)[(int64_t)row * a.ldc + c] = (bf16)(silu_f(v) * u);
-    } else if (MODE == GEMM_STORE) {
-      ((bf16*)a.C)[(int64_t)row * a.ldc + c] = (bf16)v;
-    } else if (MODE == GEMM_RESIDUAL) {
-      const float res = (float)((const bf16*)a.R)[(int64_t)row * a.ldr + c];
-      ((bf16*)a.C)[(int64_t)row * a.ldc + c] = (bf16)(v + res);
-    } else {
-      ((float*)a.C)[(int64_t)row * a.ldc + c] = v;
-    }
+  const int c = (int)(idx % cols4) * 4;
+  const int64_t zstride = (int64_t)a.M * part_ld;
+  const float* P = part + (int64_t)row * part_ld + c;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) {
+    v += *(const f32x4*)(P + s * zstride);
+    if (MODE == GEMM_SWIGLU) u += *(const f32x4*)(P + s * zstride + a.N);
   }
+  const int64_t o = (int64_t)row * a.ldc + c;
+  if (MODE == GEMM_F32OUT) {
+    *(f32x4*)((float*)a.C + o) = v;
+    return;
+  }
+  bf16x4 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r = v[q];
+    if (MODE == GEMM_SWIGLU) r = silu_f(v[q]) * u[q];
+    if (MODE == GEMM_RESIDUAL) r += (float)((const bf16*)a.R)[(int64_t)row * a.ldr + c + q];
+    out[q] = (bf16)r;
+  }
+  *(bf16x4*)((bf16*)a.C + o) = out;
+}
+
+hipError_t splitk_reduce(const GemmArgs& a, const float* part, int64_t part_ld, int splits, hipStream_t s) {
+  const int64_t work = (int64_t)a.M * (a.N / 4);
+  const int blocks = (int)((work + 255) / 256);
+  switch (a.mode) {
+    case GEMM_STORE: splitk_reduce_kernel<GEMM_STORE><<<blocks, 256, 0, s>>>(a, part, part_ld, splits); break;
+    case GEMM_RESIDUAL: splitk_reduce_kernel<GEMM_RESIDUAL><<<blocks, 256, 0, s>>>(a, part, part_ld, splits); break;
+    case GEMM_SWIGLU: splitk_reduce_kernel<GEMM_SWIGLU><<<blocks, 256, 0, s>>>(a, part, part_ld, splits); break;
+    default: splitk_reduce_kernel<GEMM_F32OUT><<<blocks, 256, 0, s>>>(a, part, part_ld, splits); break;
+  }
+  return hipGetLastError();
 }
 
 template <class C>
@@ -276,9 +328,9 @@ hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream
   const int rows = a.group_off ? a.max_group_rows : a.M;
   p.m_tiles = (rows + C::BM - 1) / C::BM;
   p.n_tiles = tiles_n<C>(a);
-  p.part = (float*)ws;
   p.part_ld = a.mode == GEMM_SWIGLU ? 2 * (int64_t)a.N : a.N;
   const bool split = pl.k_splits > 1 && !a.group_off;
+  p.part = split ? (float*)ws : nullptr;
   if (split) {
     const int kb = (a.K + BK - 1) / BK;
     p.k_per = ((kb + pl.k_splits - 1) / pl.k_splits) * BK;
@@ -305,15 +357,7 @@ hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hook && hook->fn) hook->fn(hook->ctx, 1);
-  const int64_t work = (int64_t)a.M * ((a.N + 3) / 4);
-  const int blocks = (int)((work + 255) / 256);
-  switch (a.mode) {
-    case GEMM_STORE: splitk_reduce_kernel<GEMM_STORE><<<blocks, 256, 0, s>>>(a, p.part, p.part_ld, p.z_count); break;
-    case GEMM_RESIDUAL: splitk_reduce_kernel<GEMM_RESIDUAL><<<blocks, 256, 0, s>>>(a, p.part, p.part_ld, p.z_count); break;
-    case GEMM_SWIGLU: splitk_reduce_kernel<GEMM_SWIGLU><<<blocks, 256, 0, s>>>(a, p.part, p.part_ld, p.z_count); break;
-    default: splitk_reduce_kernel<GEMM_F32OUT><<<blocks, 256, 0, s>>>(a, p.part, p.part_ld, p.z_count); break;
-  }
-  return hipGetLastError();
+  return splitk_reduce(a, p.part, p.part_ld, p.z_count, s);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -368,46 +412,361 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- pipelined path
+// For K % 64 == 0.  Slabs go global -> LDS with gfx950's direct 16-byte loads
+// (global_load_lds_dwordx4), with no VGPR staging, so STAGES-1 slabs are in
+// flight while the matrix cores work on the oldest; the wait is an explicit
+// vmcnt on this wave's own loads followed by a workgroup barrier.  LDS rows
+// are 128 bytes (64 bf16) with their 16-byte chunks XOR-swizzled by
+// (row / 2) % 8: a DMA instruction still writes 8 whole rows (1 KB,
+// contiguous), and the 16 lanes of a fragment read (16 rows, one chunk) hit 64
+// distinct banks.  Split-K stores fp32 partials; a vectorised reduce kernel
+// applies the epilogue (a last-arriving-workgroup reduction would need
+// device-scope fences, which on a multi-XCD part write back the L2).
+template <int BM_, int BN_, int WM_, int WN_, int MS_, int ST_>
+struct PCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MS = MS_, STAGES = ST_;
+  static constexpr int KSTEP = MS == 16 ? 32 : 16;
+  static constexpr int NACC = MS == 16 ? 4 : 16;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int FM = WTM / MS, FN = WTN / MS;
+  static constexpr int A_IN = BM / 32, B_IN = BN / 32;   // DMA instructions per thread per slab
+  static constexpr int X = A_IN + B_IN;
+  static constexpr int SLAB = (BM + BN) * 128;           // LDS bytes per stage
+  static_assert(WM * WN == 4 && FM >= 1 && FN >= 2 && FN % 2 == 0 && A_IN >= 1 && B_IN >= 1, "cfg");
+  static_assert(STAGES >= 2 && STAGES <= 4 && (STAGES - 2) * X <= 63, "vmcnt range");
+};
+
+using P10 = PCfg<256, 256, 2, 2, 32, 2>;
+using P11 = PCfg<256, 128, 2, 2, 32, 3>;
+using P12 = PCfg<128, 256, 2, 2, 32, 3>;
+using P13 = PCfg<128, 128, 2, 2, 32, 3>;
+using P14 = PCfg<128, 128, 2, 2, 32, 2>;
+using P15 = PCfg<64, 128, 1, 4, 16, 4>;
+using P16 = PCfg<32, 128, 1, 4, 16, 4>;
+using P17 = PCfg<64, 256, 1, 4, 16, 3>;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// wait until at most `after` slabs issued after the current one are pending
+template <class C>
+__device__ __forceinline__ void wait_slab(int after) {
+  if constexpr (C::STAGES >= 4) {
+    if (after >= 2) { wait_vmcnt<2 * C::X>(); return; }
+  }
+  if constexpr (C::STAGES >= 3) {
+    if (after >= 1) { wait_vmcnt<C::X>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+template <class C, int MODE, bool PARTIAL>
+__global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[C::STAGES * C::SLAB];
+  const GemmArgs& a = p.a;
+  const int total = p.m_tiles * p.n_tiles * p.z_count;
+  const int logical = xcd_logical(blockIdx.x, total);
+  const int m_tile = logical % p.m_tiles;
+  const int rest = logical / p.m_tiles;
+  const int n_tile = rest % p.n_tiles;
+  const int z = rest / p.n_tiles;
+
+  int m_begin = 0, rows = a.M;
+  if (a.group_off) {
+    m_begin = a.group_off[z];
+    rows = a.group_off[z + 1] - m_begin;
+  }
+  const int m0 = m_tile * C::BM;
+  if (m0 >= rows) return;                       // whole workgroup exits together
+  int k_lo = 0, k_hi = a.K;
+  if (PARTIAL) {
+    k_lo = z * p.k_per;
+    k_hi = min(a.K, k_lo + p.k_per);
+  }
+  const bf16* Bbase = (const bf16*)a.B;
+  const bf16* B2base = (const bf16*)a.B2;
+  if (a.group_off) {
+    Bbase += (int64_t)z * a.b_group_stride;
+    if (B2base) B2base += (int64_t)z * a.b_group_stride;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  // DMA sources: instruction i of this wave fills slab rows (4i + wave)*8 .. +7;
+  // lane l takes row +l/8 and physical chunk l%8 (logical chunk = l%8 ^ swz)
+  const bf16* srcA[C::A_IN];
+  const bf16* srcB[C::B_IN];
+  const int lrow = lane >> 3, pch = lane & 7;
+#pragma unroll
+  for (int i = 0; i < C::A_IN; ++i) {
+    const int row = (4 * i + wave) * 8 + lrow;
+    const int local = min(m0 + row, rows - 1);            // clamp: rows past M are never stored
+    int src = m_begin + local;
+    if (a.a_rows) src = a.a_rows[src] / a.a_row_div;
+    srcA[i] = (const bf16*)a.A + (int64_t)src * a.lda + k_lo + 8 * (pch ^ swz(row));
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_IN; ++i) {
+    const int row = (4 * i + wave) * 8 + lrow;
+    int n;
+    const bf16* base;
+    if (MODE == GEMM_SWIGLU) {
+      constexpr int half = C::BN / 2;
+      n = n_tile * half + (row < half ? row : row - half);
+      base = row < half ? Bbase : B2base;
+    } else {
+      n = n_tile * C::BN + row;
+      base = Bbase;
+    }
+    n = min(n, a.N - 1);
+    srcB[i] = base + (int64_t)n * a.ldb + k_lo + 8 * (pch ^ swz(row));
+  }
+  auto issue = [&](int t, int buf) {
+    const int koff = t * 64;
+    char* sA = smem + buf * C::SLAB;
+    char* sB = sA + C::BM * 128;
+#pragma unroll
+    for (int i = 0; i < C::A_IN; ++i) dma16(srcA[i] + koff, sA + (4 * i + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::B_IN; ++i) dma16(srcB[i] + koff, sB + (4 * i + wave) * 1024);
+  };
+
+  typedef typename Acc<C::MS>::T AccT;
+  AccT acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < C::NACC; ++e) acc[i][j][e] = 0.f;
+
+  auto b_row = [&](int j) {
+    if (MODE == GEMM_SWIGLU) {
+      constexpr int HF = C::FN / 2;
+      return j < HF ? wn * (C::WTN / 2) + j * C::MS : C::BN / 2 + wn * (C::WTN / 2) + (j - HF) * C::MS;
+    }
+    return wn * C::WTN + j * C::MS;
+  };
+
+  const int nk = (k_hi - k_lo) / 64;
+#pragma unroll
+  for (int t = 0; t < C::STAGES - 1; ++t)
+    if (t < nk) issue(t, t);
+  const int fr = lane % C::MS, fq = lane / C::MS;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_slab<C>(min(C::STAGES - 2, nk - 1 - kt));
+    barrier_lds();
+    if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
+    const char* sA = smem + (kt % C::STAGES) * C::SLAB;
+    const char* sB = sA + C::BM * 128;
+    // fragments of k-step s+1 are read while the MFMAs of k-step s run
+    constexpr int KS = 64 / C::KSTEP;
+    bf16x8 af[2][C::FM], bfr[2][C::FN];
+    auto load_frags = [&](int s, int set) {
+      const int c = s * (C::KSTEP / 8) + fq;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int r = wm * C::WTM + i * C::MS + fr;
+        af[set][i] = *(const bf16x8*)(sA + r * 128 + ((c ^ swz(r)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int r = b_row(j) + fr;
+        bfr[set][j] = *(const bf16x8*)(sB + r * 128 + ((c ^ swz(r)) << 4));
+      }
+    };
+    load_frags(0, 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) load_frags(s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma<C::MS>(af[s & 1][i], bfr[s & 1][j], acc[i][j]);
+    }
+  }
+
+  const int ec = lane % C::MS;
+  constexpr int NJ = (MODE == GEMM_SWIGLU) ? C::FN / 2 : C::FN;
+  constexpr int BNO = (MODE == GEMM_SWIGLU) ? C::BN / 2 : C::BN;    // output columns per tile
+  const int n0 = n_tile * BNO;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < C::NACC; ++r) {
+      const int local = m0 + wm * C::WTM + i * C::MS + acc_row<C::MS>(lane, r);
+      if (local >= rows) continue;
+      const int64_t orow = m_begin + local;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (MODE == GEMM_SWIGLU) {
+          const int col = n0 + wn * (C::WTN / 2) + j * C::MS + ec;
+          if (col >= a.N) continue;
+          const float g = acc[i][j][r], u = acc[i][j + C::FN / 2][r];
+          if (PARTIAL) {
+            float* P = p.part + (int64_t)z * a.M * p.part_ld + orow * p.part_ld;
+            P[col] = g;
+            P[a.N + col] = u;
+          } else {
+            ((bf16*)a.C)[orow * a.ldc + col] = (bf16)(silu_f(g) * u);
+          }
+        } else {
+          const int col = n0 + wn * C::WTN + j * C::MS + ec;
+          if (col >= a.N) continue;
+          const float v = acc[i][j][r];
+          if (PARTIAL) {
+            p.part[(int64_t)z * a.M * p.part_ld + orow * p.part_ld + col] = v;
+          } else if (MODE == GEMM_STORE) {
+            ((bf16*)a.C)[orow * a.ldc + col] = (bf16)v;
+          } else if (MODE == GEMM_RESIDUAL) {
+            const float res = (float)((const bf16*)a.R)[orow * a.ldr + col];
+            ((bf16*)a.C)[orow * a.ldc + col] = (bf16)(v + res);
+          } else {
+            ((float*)a.C)[orow * a.ldc + col] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class C>
+hipError_t launch_pipe(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream_t s,
+                       const LaunchHook* hook) {
+  KParams p;
+  p.a = a;
+  const int rows = a.group_off ? a.max_group_rows : a.M;
+  p.m_tiles = (rows + C::BM - 1) / C::BM;
+  p.n_tiles = (a.N + (a.mode == GEMM_SWIGLU ? C::BN / 2 : C::BN) - 1) / (a.mode == GEMM_SWIGLU ? C::BN / 2 : C::BN);
+  p.part_ld = a.mode == GEMM_SWIGLU ? 2 * (int64_t)a.N : a.N;
+  const bool split = pl.k_splits > 1 && !a.group_off;
+  if (split) {
+    const int kb = a.K / 64;
+    p.k_per = ((kb + pl.k_splits - 1) / pl.k_splits) * 64;
+    p.z_count = (a.K + p.k_per - 1) / p.k_per;
+      p.part = (float*)ws;
+  } else {
+    p.k_per = a.K;
+    p.z_count = a.group_off ? a.n_groups : 1;
+      p.part = nullptr;
+  }
+  const int total = p.m_tiles * p.n_tiles * p.z_count;
+  if (total == 0) return hipSuccess;
+  if (split && p.z_count > 1) {
+    if (a.mode == GEMM_SWIGLU)
+      gemm_pipe_kernel<C, GEMM_SWIGLU, true><<<total, 256, 0, s>>>(p);
+    else
+      gemm_pipe_kernel<C, GEMM_STORE, true><<<total, 256, 0, s>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (hook && hook->fn) hook->fn(hook->ctx, 1);
+    return splitk_reduce(a, p.part, p.part_ld, p.z_count, s);
+  }
+  switch (a.mode) {
+    case GEMM_STORE: gemm_pipe_kernel<C, GEMM_STORE, false><<<total, 256, 0, s>>>(p); break;
+    case GEMM_RESIDUAL: gemm_pipe_kernel<C, GEMM_RESIDUAL, false><<<total, 256, 0, s>>>(p); break;
+    case GEMM_SWIGLU: gemm_pipe_kernel<C, GEMM_SWIGLU, false><<<total, 256, 0, s>>>(p); break;
+    default: gemm_pipe_kernel<C, GEMM_F32OUT, false><<<total, 256, 0, s>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
+namespace {
+// (BM, BN of the B slab) of each tile configuration id
+void tile_dims(int cfg, int& bm, int& bn) {
+  switch (cfg) {
+    case 1: bm = 64; bn = 128; return;
+    case 2: bm = 256; bn = 128; return;
+    case 3: bm = 32; bn = 128; return;
+    case 4: bm = 128; bn = 256; return;
+    case 5: bm = 256; bn = 256; return;
+    case 6: bm = 64; bn = 128; return;
+    case 10: bm = 256; bn = 256; return;
+    case 11: bm = 256; bn = 128; return;
+    case 12: bm = 128; bn = 256; return;
+    case 13: case 14: bm = 128; bn = 128; return;
+    case 15: bm = 64; bn = 128; return;
+    case 16: bm = 32; bn = 128; return;
+    case 17: bm = 64; bn = 256; return;
+    default: bm = 128; bn = 128; return;
+  }
+}
+int n_tiles_of(const GemmArgs& a, int bn) {
+  const int c = a.mode == GEMM_SWIGLU ? bn / 2 : bn;
+  return (a.N + c - 1) / c;
+}
+}  // namespace
+
+// Tile choice (from sweeps on MI355X).  K % 64 == 0 problems use the
+// pipelined kernel: decode-sized M streams weights with 32- or 64-row tiles;
+// larger M uses 128 x 128 tiles, two workgroups per CU.  When the tiles
+// cannot give every CU about two workgroups, K is split (up to 8 ways for
+// weight streaming, 4 otherwise, keeping >= 512 of K per piece) and a reduce
+// kernel applies the epilogue.
 GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   GemmPlan p;
   if (cus <= 0) cus = 256;
+  const bool pipe = a.K % 64 == 0;
   if (a.group_off) {            // grouped (experts): rows per group ~ tokens*k/E
-    p.cfg = 0;
+    p.cfg = pipe ? 14 : 0;
     return p;
   }
   const int M = a.M;
-  auto ntile = [&](int bn) { return (a.N + (a.mode == GEMM_SWIGLU ? bn / 2 : bn) - 1) / (a.mode == GEMM_SWIGLU ? bn / 2 : bn); };
-  int bm;
-  if (M <= 32) { p.cfg = 3; bm = 32; }
-  else if (M <= 64) { p.cfg = 1; bm = 64; }
-  else if (M >= 1024 && ((M + 255) / 256) * ntile(128) >= cus) { p.cfg = 2; bm = 256; }
-  else { p.cfg = 0; bm = 128; }
-  const int tiles = ((M + bm - 1) / bm) * ntile(128);
-  if (tiles < cus) {
-    int ks = (cus + tiles - 1) / tiles;
-    const int max_ks = a.K / 512;           // keep >= 512 of K per split
-    if (ks > max_ks) ks = max_ks;
-    if (ks > 8) ks = 8;
-    if (ks > 1) p.k_splits = ks;
-  }
+  const bool stream_w = M <= 64;
+  if (stream_w)
+    p.cfg = pipe ? (M <= 32 ? 16 : 15) : (M <= 32 ? 3 : 1);
+  else
+    p.cfg = pipe ? 14 : 0;
+  int bm, bn;
+  tile_dims(p.cfg, bm, bn);
+  const int tiles = ((M + bm - 1) / bm) * n_tiles_of(a, bn);
+  const int want = stream_w ? cus : 2 * cus;      // workgroups that keep every CU busy
+  int ks = 1;
+  while (ks * 2 * tiles <= want && ks < (stream_w ? 8 : 4) && a.K / (ks * 2) >= 512) ks *= 2;
+  p.k_splits = ks;
   return p;
 }
 
 size_t gemm_workspace_bytes(const GemmArgs& a, const GemmPlan& p) {
   if (p.k_splits <= 1 || a.group_off) return 0;
   const int64_t ld = a.mode == GEMM_SWIGLU ? 2 * (int64_t)a.N : a.N;
+  int bm, bn;
+  tile_dims(p.cfg, bm, bn);
+  const int tiles = ((a.M + bm - 1) / bm) * n_tiles_of(a, bn);
+  (void)tiles;
   return (size_t)p.k_splits * a.M * ld * sizeof(float);
 }
 
 hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (p.cfg >= 10 && a.K % 64 != 0) return hipErrorInvalidValue;
   switch (p.cfg) {
     case 1: return launch_cfg<Cfg1>(a, p, ws, s, hook);
     case 2: return launch_cfg<Cfg2>(a, p, ws, s, hook);
     case 3: return launch_cfg<Cfg3>(a, p, ws, s, hook);
     case 4: return launch_cfg<Cfg4>(a, p, ws, s, hook);
+    case 5: return launch_cfg<Cfg5>(a, p, ws, s, hook);
+    case 6: return launch_cfg<Cfg6>(a, p, ws, s, hook);
+    case 10: return launch_pipe<P10>(a, p, ws, s, hook);
+    case 11: return launch_pipe<P11>(a, p, ws, s, hook);
+    case 12: return launch_pipe<P12>(a, p, ws, s, hook);
+    case 13: return launch_pipe<P13>(a, p, ws, s, hook);
+    case 14: return launch_pipe<P14>(a, p, ws, s, hook);
+    case 15: return launch_pipe<P15>(a, p, ws, s, hook);
+    case 16: return launch_pipe<P16>(a, p, ws, s, hook);
+    case 17: return launch_pipe<P17>(a, p, ws, s, hook);
     default: return launch_cfg<Cfg0>(a, p, ws, s, hook);
   }
 }

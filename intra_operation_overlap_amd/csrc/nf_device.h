@@ -7,6 +7,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -30,3 +31,19 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// Element offsets inside one (page, KV head) block of 16 key slots x D dims
+// (D % 32 == 0): the KV pool stores each block in the operand order of the
+// attention MFMAs, so a wavefront fetches a 512-element run with one linear
+// 16-byte-per-lane load.
+//   K: chunk c = d / 32 holds, for lane l = 16 * ((d % 32) / 8) + s, the 8
+//      dims 32c + 8 (l / 16) .. of key s (the A operand of S^T = K Q^T).
+//   V: chunk c = d / 32 holds, for lane l = (d % 16) + 16 * (s / 4), keys
+//      4 (l / 16) .. +3 of dim 32c + l % 16 and then of dim 32c + 16 + l % 16
+//      (A operands of O^T = V^T P^T for two 16-dim blocks).
+__device__ __forceinline__ int kv_k_off(int s, int d) {
+  return (d >> 5) * 512 + ((((d & 31) >> 3) << 4) + s) * 8 + (d & 7);
+}
+__device__ __forceinline__ int kv_v_off(int s, int d) {
+  return (d >> 5) * 512 + ((d & 15) + ((s >> 2) << 4)) * 8 + ((d >> 4) & 1) * 4 + (s & 3);
+}

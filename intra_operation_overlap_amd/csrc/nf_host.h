@@ -52,10 +52,11 @@ nf_status check_plan(const nf_plan& p, int cus_per_xcd, std::string& err);
 nf_status check_plan_batch(const nf_plan& p, int n_tokens, std::string& err);
 
 // Splits the batch per the plan into nano-batches and builds the attention
-// items.  `attn_cus` is the number of CUs the attention stream may use; a
-// nano-batch whose items are too few to fill them gets its page ranges split
-// (min_split_pages pages at least per piece; 0 disables splitting).
-void build_work(const nf_shape& s, const nf_batch& b, const nf_plan& p, int page_size, int attn_cus,
-                int min_split_pages, StepWork& w);
+// items.  A nano-batch with fewer (token group, KV head) items than
+// `target_items` gets its page ranges split (min_split_pages pages at least
+// per piece; 0 disables splitting); no item holds more than max_item_pages
+// pages (0: no cap).  Split pieces write partials merged by a later kernel.
+void build_work(const nf_shape& s, const nf_batch& b, const nf_plan& p, int page_size, int target_items,
+                int min_split_pages, int max_item_pages, StepWork& w);
 
 }  // namespace nf

@@ -81,6 +81,8 @@ struct AttnArgs {
   const int32_t* page_indptr; const int32_t* page_indices;
   int nq, nkv, d, page_size;
   float scale;
+  int variant = 0;          // bf16 d=128: 0 one wave per item, 1 four waves per item
+  int max_blocks = 0;       // variant 0: > 0 caps the grid; each wave then loops over items
 };
 hipError_t attention(int dtype, const AttnArgs& a, hipStream_t s);
 hipError_t attention_merge(int dtype, const AttnArgs& a, hipStream_t s);

@@ -8,7 +8,6 @@ namespace {
 
 // Eight independent accumulator chains of one bf16 MFMA shape per wave,
 // operands in registers only.  SHAPE 0: 16x16x32, SHAPE 1: 32x32x16.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 template <int SHAPE>
 __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* sink) {
   bf16x8 a, b;

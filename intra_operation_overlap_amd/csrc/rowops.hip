@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16x8_kernel(const bf16* __restr
 // ---------------------------------------------------------------- RoPE + append
 // One block per token.  Q heads: rotate-half rotation by the token's angle
 // table row, written to q_rot.  K heads: rotated and written to the K pool at
-// (page of the position, slot); V heads written to the V pool (dimension-major
-// inside the page).  Pairs (j, j + d/2) turn by the angle p * theta^(-2j/d).
+// (page of the position, slot); V heads written to the V pool (both in the
+// pool's MFMA-operand block order).  Pairs (j, j + d/2) turn by the angle p * theta^(-2j/d).
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   const int t = blockIdx.x;
@@ -88,16 +88,16 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
       q[j + half] = from_f32<T>(y1);
     } else {
       const int kh = head - a.nq;
-      T* k = (T*)a.k_pool + (((int64_t)page * a.nkv + kh) * a.page_size + slot) * d;
-      k[j] = from_f32<T>(y0);
-      k[j + half] = from_f32<T>(y1);
+      T* k = (T*)a.k_pool + ((int64_t)page * a.nkv + kh) * a.page_size * d;
+      k[kv_k_off(slot, j)] = from_f32<T>(y0);
+      k[kv_k_off(slot, j + half)] = from_f32<T>(y1);
     }
   }
   const T* vrow = row + (a.nq + a.nkv) * d;
   for (int i = threadIdx.x; i < a.nkv * d; i += blockDim.x) {
     const int kh = i / d, e = i % d;
-    T* v = (T*)a.v_pool + (((int64_t)page * a.nkv + kh) * d + e) * a.page_size + slot;
-    *v = vrow[i];
+    T* v = (T*)a.v_pool + ((int64_t)page * a.nkv + kh) * a.page_size * d;
+    v[kv_v_off(slot, e)] = vrow[i];
   }
 }
 

@@ -35,8 +35,8 @@ nf_status check_shape(const nf_shape& s, std::string& err) {
   const int G = s.n_q_heads / s.n_kv_heads;
   if (G > 16)
     return fail(err, NF_ERR_UNSUPPORTED, "shape: more than 16 query heads per KV head (%d)", G);
-  if (s.head_dim % 2 || s.head_dim > 256)
-    return fail(err, NF_ERR_UNSUPPORTED, "shape: head_dim %d must be even and <= 256", s.head_dim);
+  if (s.head_dim % 32 || s.head_dim > 256)
+    return fail(err, NF_ERR_UNSUPPORTED, "shape: head_dim %d must be a multiple of 32, at most 256", s.head_dim);
   if (s.dtype == NF_BF16 && s.head_dim != 128)
     return fail(err, NF_ERR_UNSUPPORTED, "shape: bf16 layers need head_dim 128 (got %d)", s.head_dim);
   if (s.hidden % 8 || s.ffn % 8 || s.head_dim % 8)
@@ -122,7 +122,12 @@ nf_status check_plan(const nf_plan& p, int cus_per_xcd, std::string& err) {
   if (p.gemm_cus_per_xcd < 0 || p.gemm_cus_per_xcd >= cus_per_xcd)
     return fail(err, NF_ERR_OUT_OF_RANGE, "plan: gemm_cus_per_xcd %d outside 0..%d", p.gemm_cus_per_xcd,
                 cus_per_xcd - 1);
-  if (p.n_streams == 1 && p.gemm_cus_per_xcd != 0)
+  if (p.attn_cus_per_xcd < 0 || p.attn_cus_per_xcd >= cus_per_xcd)
+    return fail(err, NF_ERR_OUT_OF_RANGE, "plan: attn_cus_per_xcd %d outside 0..%d", p.attn_cus_per_xcd,
+                cus_per_xcd - 1);
+  if (p.attn_waves_per_cu < 0 || p.attn_waves_per_cu > 16)
+    return fail(err, NF_ERR_OUT_OF_RANGE, "plan: attn_waves_per_cu %d outside 0..16", p.attn_waves_per_cu);
+  if (p.n_streams == 1 && (p.gemm_cus_per_xcd != 0 || p.attn_cus_per_xcd != 0))
     return fail(err, NF_ERR_INVALID_ARG, "plan: a CU split needs two streams");
   for (int j = 0; j < p.count; ++j)
     if (p.sizes[j] < 0) return fail(err, NF_ERR_INVALID_ARG, "plan: negative nano-batch size");
@@ -142,8 +147,8 @@ nf_status check_plan_batch(const nf_plan& p, int n_tokens, std::string& err) {
   return NF_OK;
 }
 
-void build_work(const nf_shape& s, const nf_batch& b, const nf_plan& p, int page_size, int attn_cus,
-                int min_split_pages, StepWork& w) {
+void build_work(const nf_shape& s, const nf_batch& b, const nf_plan& p, int page_size, int target_items,
+                int min_split_pages, int max_item_pages, StepWork& w) {
   const int T = b.n_tokens, R = b.n_requests;
   const int G = s.n_q_heads / s.n_kv_heads;
   const int qg = std::max(1, 16 / G);               // query tokens per item
@@ -175,13 +180,15 @@ void build_work(const nf_shape& s, const nf_batch& b, const nf_plan& p, int page
       total_pages += pages;
       t += n;
     }
-    // split page ranges only when the groups cannot fill the attention CUs
+    // split page ranges when the groups cannot fill the attention CUs, and cap
+    // the pages of one item
     int per = 1 << 30;
-    const int64_t target_wg = 2LL * std::max(1, attn_cus);
+    const int64_t target_wg = std::max(1, target_items);
     if (min_split_pages > 0 && (int64_t)groups.size() * s.n_kv_heads < target_wg && total_pages > 0) {
       const int64_t want = (total_pages * s.n_kv_heads + target_wg - 1) / target_wg;
       per = (int)std::max<int64_t>(min_split_pages, want);
     }
+    if (max_item_pages > 0) per = std::min(per, max_item_pages);
     // longest groups first so the long tails start early
     std::stable_sort(groups.begin(), groups.end(), [](const Group& x, const Group& y) { return x.pages > y.pages; });
     nw.item0 = (int)w.items.size();

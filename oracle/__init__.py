@@ -5,4 +5,4 @@ leg may import this package; the product library never does.
 """
 from .layer import (layer_step, layer_step_split, rmsnorm, rope, rope_cos_sin, silu,
                     swiglu_ffn, paged_attention, attention_weights, kv_append, moe_route,
-                    round_to_bf16, round_to_f32, store_round, page_slots)
+                    round_to_bf16, round_to_f32, store_round, page_slots, k_offset, v_offset, PAGE)

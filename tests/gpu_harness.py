@@ -14,6 +14,7 @@ import torch
 import oracle
 from intra_operation_overlap_amd import binding as B
 from intra_operation_overlap_amd import workload as W
+from tests import kv_layout as KV
 
 
 def log(msg: str) -> None:
@@ -151,8 +152,11 @@ def check_sentinel(S: Setup, k_before: torch.Tensor, v_before: torch.Tensor) -> 
     if ws:
         idx = torch.as_tensor(ws, device="cuda")
         mask[idx[:, 0], idx[:, 1]] = False
-    kd = (S.k != k_before).any(dim=-1).any(dim=1)           # [P, 16]
-    vd = (S.v != v_before).any(dim=2).any(dim=1)            # [P, 16]
+    kmap, vmap = KV.maps(S.wl.shape.head_dim)
+    km = torch.as_tensor(kmap, device="cuda")
+    vm = torch.as_tensor(vmap, device="cuda")
+    kd = (S.k != k_before).any(dim=1)[:, km].any(dim=-1)     # [P, 16]
+    vd = (S.v != v_before).any(dim=1)[:, vm].any(dim=-1)     # [P, 16]
     assert not bool((kd & mask).any()), "K pool changed outside the written slots"
     assert not bool((vd & mask).any()), "V pool changed outside the written slots"
 
@@ -182,12 +186,14 @@ def compare_rows(S: Setup, res: dict, rows: np.ndarray, pages: np.ndarray, reque
     # K/V written: slot values of the sampled requests' new positions
     ws_full = written_slots(S.batch, requests)
     page_pos = {int(p): i for i, p in enumerate(pages)}     # pool page -> compact oracle page
+    kmap, vmap = KV.maps(s.head_dim)
     pg = torch.as_tensor([p for p, _ in ws_full], device="cuda")
-    sl = torch.as_tensor([s_ for _, s_ in ws_full], device="cuda")
-    kg = f64(S.k[pg, :, sl, :])
-    vg = f64(S.v[pg, :, :, sl])
-    kr = np.stack([res["k_pool"][page_pos[p], :, s_, :] for p, s_ in ws_full])
-    vr = np.stack([res["v_pool"][page_pos[p], :, :, s_] for p, s_ in ws_full])
+    ki = torch.as_tensor(np.stack([kmap[s_] for _, s_ in ws_full]), device="cuda")   # [n, d]
+    vi = torch.as_tensor(np.stack([vmap[s_] for _, s_ in ws_full]), device="cuda")
+    kg = f64(torch.stack([S.k[pg[i]][:, ki[i]] for i in range(len(ws_full))]))       # [n, nkv, d]
+    vg = f64(torch.stack([S.v[pg[i]][:, vi[i]] for i in range(len(ws_full))]))
+    kr = np.stack([res["k_pool"][page_pos[p]][:, kmap[s_]] for p, s_ in ws_full])
+    vr = np.stack([res["v_pool"][page_pos[p]][:, vmap[s_]] for p, s_ in ws_full])
     errs["k_new"] = normwise(kg, kr)
     errs["v_new"] = normwise(vg, vr)
     return errs

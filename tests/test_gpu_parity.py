@@ -13,6 +13,7 @@ import oracle
 from intra_operation_overlap_amd import binding as B
 from intra_operation_overlap_amd import workload as W
 from tests import gpu_harness as GH
+from tests import kv_layout as KV
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +89,16 @@ def test_small_bf16_prefill_from_zero_and_g8():
     S = GH.setup(wl)
     _full_check(S, "k1", B.make_plan(1, [S.batch.n_tokens]))
     _full_check(S, "k2_split_prefill", B.make_plan(2, [40, S.batch.n_tokens - 40], n_streams=2, gemm_cus_per_xcd=16))
+
+
+def test_split_k_small_batch_parity():
+    """Decode-sized nano-batches take the split-K GEMM path (fused reduction)."""
+    wl = W.Workload("splitk", W.Shape(hidden=2048, n_q_heads=8, n_kv_heads=4, head_dim=128, ffn=1536,
+                                      dtype="bf16", rope_theta=5e5),
+                    n_decode=20, ctx_range=(5, 90), prefill=None, seed=80)
+    S = GH.setup(wl)
+    _full_check(S, "k1", B.make_plan(1, [20]))
+    _full_check(S, "k2_masked", B.make_plan(2, [7, 13], n_streams=2, gemm_cus_per_xcd=20))
 
 
 def test_plan_invariance_bit_exact(small):
@@ -166,14 +177,15 @@ def test_one_hot_attention_selects_exact_key(wl_name):
         p0 = int(b.req_pos0[r])
         j = int(rng.integers(0, p0))          # a cached position
         pages = b.page_indices[b.page_indptr[r]:b.page_indptr[r + 1]]
-        # zero every cached key of this request ...
-        pi = torch.as_tensor(pages[np.arange(p0) // 16], device="cuda")
-        si = torch.as_tensor(np.arange(p0) % 16, device="cuda")
-        S.k[pi, :, si, :] = 0
+        kmap, vmap = KV.maps(s.head_dim)
         for kh in range(s.n_kv_heads):
+            # zero every cached key of this request ...
+            for i in range(p0):
+                S.k[int(pages[i // 16]), kh, torch.as_tensor(kmap[i % 16], device="cuda")] = 0
             # ... then point key j along the group's first query head: score 400
             qh = q[t, kh * G]
-            S.k[int(pages[j // 16]), kh, j % 16, :] = (qh * (400.0 * s.head_dim ** 0.5 / float(qh.norm()) ** 2)).to(dt)
+            S.k[int(pages[j // 16]), kh, torch.as_tensor(kmap[j % 16], device="cuda")] = \
+                (qh * (400.0 * s.head_dim ** 0.5 / float(qh.norm()) ** 2)).to(dt)
         chosen[r] = j
     # only the group's first head is aligned with the key; the check uses it alone
     GH.run_step(S)
@@ -182,8 +194,9 @@ def test_one_hot_attention_selects_exact_key(wl_name):
     for r, j in chosen.items():
         t = b.req_q_start[r]
         pages = b.page_indices[b.page_indptr[r]:b.page_indptr[r + 1]]
+        kmap, vmap = KV.maps(s.head_dim)
         for kh in range(s.n_kv_heads):
-            v = S.v[int(pages[j // 16]), kh, :, j % 16]
+            v = S.v[int(pages[j // 16]), kh, torch.as_tensor(vmap[j % 16], device="cuda")]
             assert torch.equal(attn[t, kh * G], v), (r, kh, j)
             checked += 1
     assert checked > 0

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from oracle import layer as L
+from tests import kv_layout as KV
 
 
 RNG = np.random.Generator(np.random.PCG64(7))
@@ -133,12 +134,27 @@ def _contiguous_attention(q, K, V):
 
 
 def _fill_pool(P, nkv, S, d, rng):
-    return rng.standard_normal((P, nkv, S, d)), rng.standard_normal((P, nkv, d, S))
+    return rng.standard_normal((P, nkv, S * d)), rng.standard_normal((P, nkv, S * d))
+
+
+def _kv(kp, vp, page, kh, slot, d):
+    """Key and value vectors of one pool slot, addressed through the layout
+    enumerated from the kernel's operand loads (tests/kv_layout.py)."""
+    kmap, vmap = KV.maps(d)
+    return kp[page, kh, kmap[slot]], vp[page, kh, vmap[slot]]
+
+
+def test_pool_layout_offsets_match_operand_enumeration():
+    for d in (32, 64, 128):
+        kmap, vmap = KV.maps(d)
+        s, j = np.meshgrid(np.arange(16), np.arange(d), indexing="ij")
+        assert np.array_equal(L.k_offset(s, j), kmap)
+        assert np.array_equal(L.v_offset(s, j), vmap)
 
 
 def test_paged_attention_equals_contiguous_brute_force():
-    S, d, nkv, nq = 4, 8, 2, 4
-    lengths = [1, 5, 9, 4]                 # keys per decode request (position + 1)
+    S, d, nkv, nq = 16, 32, 2, 4
+    lengths = [1, 17, 40, 16]              # keys per decode request (position + 1)
     rng = np.random.Generator(np.random.PCG64(3))
     P, indptr, indices = _random_pages(lengths, S, rng)
     kp, vp = _fill_pool(P, nkv, S, d, rng)
@@ -150,15 +166,15 @@ def test_paged_attention_equals_contiguous_brute_force():
         pages = [indices[indptr[r] + j // S] for j in range(n)]
         for h in range(nq):
             kh = h // (nq // nkv)
-            K = np.array([kp[pages[j], kh, j % S, :] for j in range(n)])
-            V = np.array([vp[pages[j], kh, :, j % S] for j in range(n)])
+            K = np.array([_kv(kp, vp, pages[j], kh, j % S, d)[0] for j in range(n)])
+            V = np.array([_kv(kp, vp, pages[j], kh, j % S, d)[1] for j in range(n)])
             assert np.allclose(got[r, h], _contiguous_attention(q[r, h], K, V), rtol=1e-12, atol=1e-13)
 
 
 def test_paged_attention_page_permutation_invariance_and_gqa():
-    S, d, nkv, G = 4, 8, 2, 3
+    S, d, nkv, G = 16, 32, 2, 3
     nq = nkv * G
-    lengths = [7, 13]
+    lengths = [7, 45]
     rng = np.random.Generator(np.random.PCG64(5))
     P, indptr, indices = _random_pages(lengths, S, rng)
     kp, vp = _fill_pool(P, nkv, S, d, rng)
@@ -191,9 +207,9 @@ def test_attention_special_cases():
 
 
 def test_kv_append_rebuild_and_sentinel():
-    S, d, nkv = 4, 6, 2
-    pos0 = [3, 0, 9]
-    qlen = [1, 5, 2]
+    S, d, nkv = 16, 32, 2
+    pos0 = [3, 0, 30]
+    qlen = [1, 20, 2]
     lengths = [p + q for p, q in zip(pos0, qlen)]
     rng = np.random.Generator(np.random.PCG64(11))
     P, indptr, indices = _random_pages(lengths, S, rng)
@@ -209,17 +225,23 @@ def test_kv_append_rebuild_and_sentinel():
         r, p = tok_req[t], pos[t]
         pg = indices[indptr[r] + p // S]
         touched[pg, p % S] = True
-        assert np.array_equal(kp[pg, :, p % S, :], oracle.round_to_bf16(kn[t]))
-        assert np.array_equal(vp[pg, :, :, p % S], oracle.round_to_bf16(vn[t]))
+        for kh in range(nkv):
+            kg, vg = _kv(kp, vp, pg, kh, p % S, d)
+            assert np.array_equal(kg, oracle.round_to_bf16(kn[t, kh]))
+            assert np.array_equal(vg, oracle.round_to_bf16(vn[t, kh]))
     # every slot no (page table, position) pair names is bit-identical
-    assert np.array_equal(kp.transpose(0, 2, 1, 3)[~touched], kp0.transpose(0, 2, 1, 3)[~touched])
-    assert np.array_equal(vp.transpose(0, 3, 1, 2)[~touched], vp0.transpose(0, 3, 1, 2)[~touched])
+    kmap, vmap = KV.maps(d)
+    for pg in range(P):
+        for sl in range(S):
+            if not touched[pg, sl]:
+                assert np.array_equal(kp[pg][:, kmap[sl]], kp0[pg][:, kmap[sl]])
+                assert np.array_equal(vp[pg][:, vmap[sl]], vp0[pg][:, vmap[sl]])
 
 
 # ---------------------------------------------------------------- whole layer
 
-def _tiny_problem(rng, nq=4, nkv=2, d=8, H=16, F=12, E=1, top_k=1, S=4,
-                  pos0=(5, 0, 2), qlen=(1, 6, 1), dtype="f32", theta=1e4):
+def _tiny_problem(rng, nq=4, nkv=2, d=32, H=16, F=12, E=1, top_k=1, S=16,
+                  pos0=(19, 0, 2), qlen=(1, 6, 1), dtype="f32", theta=1e4):
     shape = dict(hidden=H, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=F, n_experts=E,
                  top_k=top_k, dtype=dtype, rms_eps=1e-5, rope_theta=theta, page_size=S)
     w = dict(attn_norm=rng.uniform(0.5, 1.5, H), w_qkv=rng.standard_normal(((nq + 2 * nkv) * d, H)) * 0.3,
@@ -276,17 +298,19 @@ def _brute_force_layer(shape, w, batch, kp, vp):
         for kh in range(nkv):
             kv = rot(col[(nq + kh) * d:(nq + kh + 1) * d], p)
             vv = col[(nq + nkv + kh) * d:(nq + nkv + kh + 1) * d]
+            kmap, vmap = KV.maps(d)
             for i in range(d):
-                kp[pg, kh, p % S, i] = kv[i]
-                vp[pg, kh, i, p % S] = vv[i]
+                kp[pg, kh, kmap[p % S, i]] = kv[i]
+                vp[pg, kh, vmap[p % S, i]] = vv[i]
     out = np.zeros((T, H))
     for t in range(T):
         r, p = req_of[t], int(batch["pos"][t])
         att = []
         for hq in range(nq):
             kh = hq // G
-            keys = [kp[batch["page_indices"][batch["page_indptr"][r] + j // S], kh, j % S, :] for j in range(p + 1)]
-            vals = [vp[batch["page_indices"][batch["page_indptr"][r] + j // S], kh, :, j % S] for j in range(p + 1)]
+            slots = [(batch["page_indices"][batch["page_indptr"][r] + j // S], j % S) for j in range(p + 1)]
+            keys = [_kv(kp, vp, pg_, kh, sl_, d)[0] for pg_, sl_ in slots]
+            vals = [_kv(kp, vp, pg_, kh, sl_, d)[1] for pg_, sl_ in slots]
             att += list(_contiguous_attention(np.array(qs[t][hq]), np.array(keys), np.array(vals)))
         x1 = [x[t, j] + sum(att[c] * w["w_o"][j, c] for c in range(nq * d)) for j in range(H)]
         h2 = norm(x1, w["ffn_norm"])
