@@ -79,7 +79,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--plan", default="auto", help="auto (workload default / search) or k1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None, help="JSON file with rocprofv3 FETCH/WRITE bytes per launch")
+    ap.add_argument("--traffic", default=None, help="text file with the rocprofv3 FETCH/WRITE bytes per launch")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 5 times (counter calibration) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -94,6 +96,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
     wl = W.WORKLOADS[args.workload]
     s = wl.shape
     log(f"workload {wl.name}: {wl.description}")
@@ -115,12 +120,16 @@ def main():
     peak_gbps = B.probe_hbm_read_gbps(4 << 30)
     log(f"measured peaks: bf16 MFMA {peak_tflops:.0f} TFLOP/s, HBM read {peak_gbps:.0f} GB/s")
 
+    host_us = []
+
     def time_steps(n):
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
+        h0 = time.perf_counter()
         for _ in range(n):
             layer.step(pool, hb, sp)
+        host_us.append((time.perf_counter() - h0) / n * 1e6)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
@@ -134,18 +143,19 @@ def main():
         layer.set_plan(plan)
     else:
         log("plan search")
-        plan, (pred, meas) = layer.search(pool, hb, max_count=4, warmup=2, reps=5, stream=sp)
-        log(f"searched plan {B.plan_dict(plan)} ({meas:.3f} ms)")
-        # the sequential baselines the overlap is measured against
-        layer.set_plan(B.make_plan(1, [T]))
-        for _ in range(3):
-            layer.step(pool, hb, sp)
-        comparisons["sequential_unsplit_ms"] = time_steps(10)
-        seq = B.make_plan(plan.count, list(plan.sizes)[:plan.count], order=B.NF_ORDER_SEQUENTIAL)
-        layer.set_plan(seq)
-        for _ in range(3):
-            layer.step(pool, hb, sp)
-        comparisons["sequential_split_ms"] = time_steps(10)
+        plan, (best_ms, n_cands) = layer.search(pool, hb, max_count=4, warmup=2, reps=5, stream=sp)
+        log(f"searched plan {B.plan_dict(plan)} ({best_ms:.3f} ms, {int(n_cands)} candidates)")
+        # the baselines the searched plan is compared with: the unsplit step,
+        # two nano-batches one after the other on one stream, and the same two
+        # nano-batches overlapped on two streams without CU masks
+        half = [T - T // 2, T // 2]
+        for key, p in (("sequential_unsplit_ms", B.make_plan(1, [T])),
+                       ("sequential_split2_ms", B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL)),
+                       ("overlapped_split2_two_streams_ms", B.make_plan(2, half, n_streams=2))):
+            layer.set_plan(p)
+            for _ in range(3):
+                layer.step(pool, hb, sp)
+            comparisons[key] = time_steps(20)
         layer.set_plan(plan)
     plan_sizes = list(plan.sizes)[:plan.count]
 
@@ -163,18 +173,23 @@ def main():
     dominant = max(prof, key=lambda k: prof[k][1])
     log("per-kernel (5 steps): " + ", ".join(f"{k} {v[1] / v[0] * 1e3:.1f}us x{v[0] // 5}" for k, v in prof.items()))
 
-    # timed region: events on the caller stream bracket K steps; the library
-    # brackets each launch of the dominant kernel on its own stream
-    layer.profile_enable(True, dominant)
+    # timed region: events on the caller stream bracket K steps
     log(f"timing {args.steps} steps")
     ms = time_steps(args.steps)
+    log(f"{ms * 1e3:.1f} us per step on the GPU, {host_us[-1]:.1f} us per step to enqueue on the host")
+    # the same K steps again, with the dominant kernel's own start/end
+    # timestamps recorded into HIP events on the stream it runs on (kept out
+    # of the throughput pass: the event packets add a few microseconds of
+    # queue time around that kernel in every step)
+    layer.profile_enable(True, dominant)
+    ms_events = time_steps(args.steps)
     dprof = layer.profile_read()
     layer.profile_enable(False)
     launches, dom_ms = dprof[dominant]
     dom_avg_ms = dom_ms / launches
     value = T / (ms * 1e-3)
     if comparisons:
-        comparisons["overlapped_ms"] = ms
+        comparisons["searched_plan_ms"] = ms
 
     # roofline of the dominant kernel
     byts, flops = kernel_work(dominant, wl, batch, plan_sizes)
@@ -193,11 +208,11 @@ def main():
         roofline["traffic"] = None
         roofline["kernel"] = dominant
         roofline["avg_launch_us"] = round(dom_avg_ms * 1e3, 2)
+        roofline["launches"] = int(launches)
+        roofline["ms_per_step_with_kernel_events"] = round(ms_events, 5)
         roofline["algorithmic_bytes_per_launch"] = int(byts)
-        tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{dominant}_{wl.name}.json")
-        if os.path.exists(tpath):
-            t = json.load(open(tpath))
-            roofline["traffic"] = t.get("bytes_per_launch")
+        roofline["traffic"] = measured_traffic(args.traffic or os.path.join(
+            ROOT, "profiles", f"traffic_{dominant}_{wl.name}.txt"), dominant)
 
     # fraction of the compute-bound optimum: tokens/s / (peak / FLOPs per token)
     fpt = W.layer_flops_per_token(s)
@@ -234,6 +249,58 @@ def main():
     if comparisons:
         line["comparisons"] = {k: round(v, 5) for k, v in comparisons.items()}
     print(json.dumps(line), flush=True)
+
+
+# Sources that decide the HBM traffic of each kernel kind; a counter summary
+# records their hash and is ignored once any of them changes.
+_CSRC = os.path.join(ROOT, "intra_operation_overlap_amd", "csrc")
+_COMMON = ["nf_device.h"]
+KERNEL_SOURCES = {
+    "attention": ["attention.hip"] + _COMMON,
+    "gemm_qkv": ["gemm.hip"] + _COMMON,
+    "gemm_o_residual": ["gemm.hip"] + _COMMON,
+    "gemm_gate_up_swiglu": ["gemm.hip"] + _COMMON,
+    "gemm_down_residual": ["gemm.hip"] + _COMMON,
+}
+
+
+def source_hash(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kind, []):
+        with open(os.path.join(_CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path, kind):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by the copy-kernel calibration factor), or None
+    when there is none or the kernel's sources changed since it was taken."""
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for ln in open(path):
+        if ":" in ln and not ln.lstrip().startswith("#"):
+            k, v = ln.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_hash(kind) or "bytes_per_launch" not in fields:
+        return None
+    return int(float(fields["bytes_per_launch"]))
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
 
 
 def cpu_baseline(wl, batch, weights, acts, k_pool, v_pool, budget_s=20.0):

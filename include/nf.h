@@ -151,7 +151,7 @@ typedef struct nf_search_opts {
   int32_t max_count;      /* largest nano-batch count tried (<= NF_MAX_NANO) */
   int32_t warmup;         /* untimed steps per measured candidate            */
   int32_t reps;           /* timed steps per measured candidate              */
-  int32_t top_k;          /* candidates measured after model ranking          */
+  int32_t top_k;          /* candidates timed again after the first pass      */
 } nf_search_opts;
 
 typedef struct nf_layer nf_layer;
@@ -209,15 +209,22 @@ nf_status nf_batch_validate(const nf_shape* shape, int32_t n_pages, int32_t page
 nf_status nf_layer_step(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch, void* stream);
 
 /* ---- plan search -----------------------------------------------------------
- * Profile-driven choice of the plan for this batch (stands in for the pages'
- * MILP-based pipeline parameter search): solo-time each operation per
- * nano-batch size and CU split, predict each candidate plan's step time with
- * a two-stream event-graph model that charges measured co-run slowdowns, then
- * run the best `top_k` candidates for real and keep the fastest.  Runs steps
- * on this batch (so it writes batch->out and the batch's pool slots with the
- * values a step writes), synchronises `stream`, sets the chosen plan on the
- * layer and returns it in *out.  `times_ms`, if not NULL, receives
- * {predicted, measured} of the chosen plan. */
+ * Profile-driven choice of the plan for this batch.  It stands in for the
+ * automatic search of nano-batch number, size, order and resource split in
+ * the abstract on the codewithpapers NanoFlow page, whose four dimensions the
+ * "Search Space" card of the do-not-panic NanoFlow page lists, and for the
+ * Gurobi-based solver of the ossradar Nanoflow page.  The candidates are the unsplit plan and, for every
+ * count 2..opts->max_count, equal and attention-balanced sizes, each on one
+ * stream and on two streams with several (GEMM, attention) CU budgets and
+ * attention residency limits.  Every candidate is timed on this batch for two
+ * steps; the `top_k` fastest are timed again with `warmup` + `reps` steps and
+ * the fastest of those is kept.  Runs steps on this batch (so it writes
+ * batch->out and the batch's pool slots with the values a step writes),
+ * synchronises `stream`, sets the chosen plan on the layer and returns it in
+ * *out.  `times_ms`, if not NULL, receives {measured ms per step of the
+ * chosen plan, number of candidates}.  An empty batch returns the unsplit
+ * plan without running anything.  Errors: NF_ERR_INVALID_ARG for a null
+ * argument, any error of nf_layer_step. */
 nf_status nf_plan_search(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch,
                          const nf_search_opts* opts, nf_plan* out, double* times_ms,
                          void* stream);
@@ -234,8 +241,10 @@ nf_status nf_layer_intermediate(const nf_layer* layer, int32_t which, const void
 
 /* ---- per-kernel timing ------------------------------------------------------
  * When on, every kernel launch of a step (or only those of kind `only_kind`,
- * if not NULL) is bracketed by HIP events recorded on the stream it is
- * launched on.  nf_profile_read synchronises those events and returns, per
+ * if not NULL) records the kernel's own start and end timestamps into a pair
+ * of HIP events (hipExtLaunchKernel), on the stream it is launched on, so the
+ * duration holds no marker packet or queue gap.  nf_profile_read
+ * synchronises those events and returns, per
  * kernel kind, the number of launches and the summed duration (ms) since
  * profiling was switched on; kinds with no launches are omitted.  Names are
  * static strings.  Enabling resets the totals. */

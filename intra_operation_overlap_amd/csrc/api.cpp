@@ -105,7 +105,8 @@ struct nf_layer {
   DevBuf h, qkv, q_rot, attn, x1, h2, act, y;
   DevBuf r_idx, r_w, r_perm, r_inv, r_off;
   DevBuf splitk, part_o, part_ml, meta, cos_sin;
-  void* stage[2] = {nullptr, nullptr};
+  void* stage[2] = {nullptr, nullptr};       // pinned, coherent host staging
+  void* stage_dev[2] = {nullptr, nullptr};   // their device addresses
   size_t stage_bytes[2] = {0, 0};
   hipEvent_t stage_ev[2] = {nullptr, nullptr};
   bool stage_used[2] = {false, false};
@@ -118,7 +119,7 @@ struct nf_layer {
   int64_t prof_n[K_COUNT] = {};
   StepWork work;
   int last_T = 0;
-  int attn_variant = 0;                         // bf16 attention kernel variant (NF_ATTN_VARIANT)
+  int attn_variant = -1;   // bf16 d=128 attention kernel: -1 chosen per step, 0 one-wave items, 1 four-wave items
 };
 
 struct nf_kv_pool {
@@ -271,14 +272,23 @@ void prof_begin(nf_layer* L, int kind, hipStream_t s) {
     }
   }
   if (r.a && r.b) {
-    (void)hipEventRecord(r.a, s);
+    // the next launch on this thread records its own start and end
+    kernel_timer() = KernelTimer{r.a, r.b};
     L->recs.push_back(r);
   }
+  (void)s;
 }
 
 void prof_end(nf_layer* L, int kind, hipStream_t s) {
+  (void)s;
   if (!L->prof || L->recs.empty() || L->recs.back().kind != kind) return;
-  (void)hipEventRecord(L->recs.back().b, s);
+  KernelTimer& t = kernel_timer();
+  if (t.start) {          // nothing was launched for this kind: drop the record
+    L->ev_free.push_back(L->recs.back().a);
+    L->ev_free.push_back(L->recs.back().b);
+    L->recs.pop_back();
+    t = KernelTimer{};
+  }
 }
 
 void prof_hook_fn(void* ctx, int phase) {
@@ -300,12 +310,16 @@ struct StepCtx {
   const MergeItem* merges;
   int gemm_cus, attn_cus;
   int attn_waves_per_cu;
+  int attn_variant;        // 0: one-wave work items (any grid), 1: four-wave workgroups
 };
 
 char* ptr(const DevBuf& b, int64_t elems, int dt) { return (char*)b.p + elems * (int64_t)dtype_bytes(dt); }
 
-hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s) {
+// `partials` != nullptr: when the GEMM splits K, its reduce is left to the
+// consumer, and *partials receives the slice count (1: C was written).
+hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s, int* partials = nullptr) {
   nf_layer* L = c.L;
+  if (partials) *partials = 1;
   if (L->s.dtype == NF_F32) {
     prof_begin(L, kind, s);
     hipError_t e = gemm_f32(g, s);
@@ -313,6 +327,10 @@ hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s) {
     return e;
   }
   GemmPlan gp = gemm_choose(g, c.gemm_cus);
+  if (partials) {
+    *partials = gemm_partials(g, gp);
+    g.defer_reduce = *partials > 1;
+  }
   Prof pctx{L, kind, s};
   LaunchHook hook{prof_hook_fn, &pctx};
   prof_begin(L, kind, s);
@@ -399,9 +417,16 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
                    ptr(L->h, (int64_t)t0 * H, dt), Tj, H, sh.rms_eps, s));
   prof_end(L, K_NORM1, s);
   NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
-  HIP_STEP(run_gemm(c, g.qkv, K_QKV, s));
+  int qkv_parts = 1;
+  HIP_STEP(run_gemm(c, g.qkv, K_QKV, s, &qkv_parts));
   RopeAppendArgs r;
   const int Nqkv = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim;
+  if (qkv_parts > 1) {          // RoPE reduces the split-K partials itself
+    r.part = (const float*)L->splitk.p;
+    r.part_ld = Nqkv;
+    r.zstride = (int64_t)Tj * Nqkv;
+    r.splits = qkv_parts;
+  }
   r.qkv = ptr(L->qkv, (int64_t)t0 * Nqkv, dt);
   r.q_rot = ptr(L->q_rot, (int64_t)t0 * sh.n_q_heads * sh.head_dim, dt);
   r.k_pool = c.P->k;
@@ -439,7 +464,7 @@ nf_status issue_attention(StepCtx& c, int j, hipStream_t s) {
   a.page_indices = c.indices;
   a.nq = sh.n_q_heads; a.nkv = sh.n_kv_heads; a.d = sh.head_dim; a.page_size = c.P->page_size;
   a.scale = (float)(1.0 / std::sqrt((double)sh.head_dim));
-  a.variant = L->attn_variant;
+  a.variant = c.attn_variant;
   a.max_blocks = c.attn_waves_per_cu > 0 ? c.attn_waves_per_cu * c.attn_cus : 0;
   prof_begin(L, K_ATTN, s);
   HIP_STEP(attention(sh.dtype, a, s));
@@ -459,10 +484,17 @@ nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
   const int t0 = nw.t0, Tj = nw.t1 - nw.t0, dt = sh.dtype, H = sh.hidden;
   if (Tj == 0) return NF_OK;
   NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
-  HIP_STEP(run_gemm(c, g.o, K_OPROJ, s));
+  const bool fuse = dt == NF_BF16 && H % 8 == 0;
+  int o_parts = 1;
+  HIP_STEP(run_gemm(c, g.o, K_OPROJ, s, fuse ? &o_parts : nullptr));
   prof_begin(L, K_NORM2, s);
-  HIP_STEP(rmsnorm(dt, ptr(L->x1, (int64_t)t0 * H, dt), L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
-                   sh.rms_eps, s));
+  if (o_parts > 1)              // O-projection split-K reduce + residual + FFN norm in one kernel
+    HIP_STEP(residual_rmsnorm_partials((const float*)L->splitk.p, H, (int64_t)Tj * H, o_parts, g.o.R, g.o.ldr,
+                                       g.o.C, g.o.ldc, L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
+                                       sh.rms_eps, s));
+  else
+    HIP_STEP(rmsnorm(dt, ptr(L->x1, (int64_t)t0 * H, dt), L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
+                     sh.rms_eps, s));
   prof_end(L, K_NORM2, s);
   if (sh.n_experts == 1) {
     HIP_STEP(run_gemm(c, g.gu, K_GATEUP, s));
@@ -481,12 +513,12 @@ nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
   prof_begin(L, K_ROUTE, s);
   HIP_STEP(moe_route(r, s));
   prof_end(L, K_ROUTE, s);
-  GemmPlan gp;           // grouped: one tile config, no split-K
+  // grouped: the tile choice depends on the mean rows per expert; no split-K
   prof_begin(L, K_MOE_GATEUP, s);
-  HIP_STEP(gemm_bf16(g.moe_gu, gp, nullptr, s));
+  HIP_STEP(gemm_bf16(g.moe_gu, gemm_choose(g.moe_gu, c.gemm_cus), nullptr, s));
   prof_end(L, K_MOE_GATEUP, s);
   prof_begin(L, K_MOE_DOWN, s);
-  HIP_STEP(gemm_bf16(g.moe_down, gp, nullptr, s));
+  HIP_STEP(gemm_bf16(g.moe_down, gemm_choose(g.moe_down, c.gemm_cus), nullptr, s));
   prof_end(L, K_MOE_DOWN, s);
   prof_begin(L, K_COMBINE, s);
   HIP_STEP(moe_combine(dt, ptr(L->x1, (int64_t)t0 * H, dt), (const float*)L->y.p + (int64_t)t0 * k * H,
@@ -518,9 +550,12 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
   c.gemm_cus = gsplit ? gsplit * L->n_xcd : L->n_cus;
   c.attn_cus = asplit ? asplit * L->n_xcd : L->n_cus;
   c.attn_waves_per_cu = two ? plan.attn_waves_per_cu : 0;
-  // attention work items: one wave each for the LDS-free kernel (many, short),
-  // a four-wave workgroup each otherwise
-  const bool wave_items = L->s.dtype == NF_BF16 && L->s.head_dim == 128 && L->attn_variant != 1;
+  // attention work items: a four-wave workgroup each (fastest when attention
+  // has the whole chip), or one wave each (many short items) when the plan
+  // asks for a persistent attention grid that leaves room for GEMM waves
+  c.attn_variant = L->attn_variant >= 0 ? L->attn_variant : (c.attn_waves_per_cu > 0 ? 0 : 1);
+  if (c.attn_waves_per_cu > 0) c.attn_variant = 0;
+  const bool wave_items = L->s.dtype == NF_BF16 && L->s.head_dim == 128 && c.attn_variant == 0;
   build_work(L->s, *b, plan, P->page_size, wave_items ? 8 * c.attn_cus : 2 * c.attn_cus, 8,
              wave_items ? 32 : 0, L->work);
   const StepWork& w = L->work;
@@ -553,7 +588,8 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
     if (L->stage[si]) HIP_TRY(hipHostFree(L->stage[si]));
     L->stage[si] = nullptr;
     L->stage_bytes[si] = 0;
-    HIP_TRY(hipHostMalloc(&L->stage[si], bytes * 2, hipHostMallocDefault));
+    HIP_TRY(hipHostMalloc(&L->stage[si], bytes * 2, hipHostMallocMapped | hipHostMallocCoherent));
+    HIP_TRY(hipHostGetDevicePointer(&L->stage_dev[si], L->stage[si], 0));
     L->stage_bytes[si] = bytes * 2;
   }
   if (L->meta.bytes < bytes) HIP_TRY(ensure(L->meta, bytes * 2));
@@ -564,7 +600,7 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
   std::memcpy(hs + o_ix, b->page_indices, (size_t)nnz * 4);
   if (!w.items.empty()) std::memcpy(hs + o_it, w.items.data(), w.items.size() * sizeof(AttnItem));
   if (!w.merges.empty()) std::memcpy(hs + o_mg, w.merges.data(), w.merges.size() * sizeof(MergeItem));
-  HIP_TRY(hipMemcpyAsync(L->meta.p, hs, bytes, hipMemcpyHostToDevice, caller));
+  HIP_TRY(meta_copy(L->stage_dev[si], L->meta.p, bytes, caller));
   HIP_TRY(hipEventRecord(L->stage_ev[si], caller));
   L->stage_used[si] = true;
   const int32_t* dm = (const int32_t*)L->meta.p;
@@ -960,15 +996,18 @@ nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps) {
   hipEvent_t e0, e1;
   HIP_TRY(hipEventCreate(&e0));
   HIP_TRY(hipEventCreate(&e1));
+  // best of a few occupancies (workgroups per CU) of a streaming read
   double best = 0;
-  for (int rep = 0; rep < 6; ++rep) {
-    HIP_TRY(hipEventRecord(e0, nullptr));
-    HIP_TRY(probe_read(buf, bytes, sink, prop.multiProcessorCount * 8, nullptr));
-    HIP_TRY(hipEventRecord(e1, nullptr));
-    HIP_TRY(hipEventSynchronize(e1));
-    float ms = 0;
-    HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
-    if (rep > 0) best = std::max(best, (double)bytes / (ms * 1e-3) / 1e9);
+  for (int per_cu : {2, 4, 8}) {
+    for (int rep = 0; rep < 4; ++rep) {
+      HIP_TRY(hipEventRecord(e0, nullptr));
+      HIP_TRY(probe_read(buf, bytes, sink, prop.multiProcessorCount * per_cu, nullptr));
+      HIP_TRY(hipEventRecord(e1, nullptr));
+      HIP_TRY(hipEventSynchronize(e1));
+      float ms = 0;
+      HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+      if (rep > 0) best = std::max(best, (double)bytes / (ms * 1e-3) / 1e9);
+    }
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);

@@ -418,16 +418,16 @@ hipError_t attention(int dtype, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_items, a.nkv);
   if (dtype == 1 && a.d == 128 && a.page_size == 16) {
     if (a.variant == 1) {
-      attn_bf16_d128_kernel<<<grid, 256, 0, s>>>(a);
+      launch(attn_bf16_d128_kernel, grid, 256, 0, s, a);
     } else {
       int blocks = a.n_items * a.nkv;
       if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
-      attn_bf16_d128_wave_kernel<<<blocks, 64, 0, s>>>(a);
+      launch(attn_bf16_d128_wave_kernel, blocks, 64, 0, s, a);
     }
   } else if (dtype == 1) {
-    attn_generic_kernel<bf16><<<grid, 256, 0, s>>>(a);
+    launch(attn_generic_kernel<bf16>, grid, 256, 0, s, a);
   } else {
-    attn_generic_kernel<float><<<grid, 256, 0, s>>>(a);
+    launch(attn_generic_kernel<float>, grid, 256, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -436,9 +436,9 @@ hipError_t attention_merge(int dtype, const AttnArgs& a, hipStream_t s) {
   if (a.n_merges == 0) return hipSuccess;
   dim3 grid(a.n_merges, a.nkv);
   if (dtype == 1)
-    attn_merge_kernel<bf16><<<grid, 256, 0, s>>>(a);
+    launch(attn_merge_kernel<bf16>, grid, 256, 0, s, a);
   else
-    attn_merge_kernel<float><<<grid, 256, 0, s>>>(a);
+    launch(attn_merge_kernel<float>, grid, 256, 0, s, a);
   return hipGetLastError();
 }
 

@@ -306,10 +306,10 @@ hipError_t splitk_reduce(const GemmArgs& a, const float* part, int64_t part_ld, 
   const int64_t work = (int64_t)a.M * (a.N / 4);
   const int blocks = (int)((work + 255) / 256);
   switch (a.mode) {
-    case GEMM_STORE: splitk_reduce_kernel<GEMM_STORE><<<blocks, 256, 0, s>>>(a, part, part_ld, splits); break;
-    case GEMM_RESIDUAL: splitk_reduce_kernel<GEMM_RESIDUAL><<<blocks, 256, 0, s>>>(a, part, part_ld, splits); break;
-    case GEMM_SWIGLU: splitk_reduce_kernel<GEMM_SWIGLU><<<blocks, 256, 0, s>>>(a, part, part_ld, splits); break;
-    default: splitk_reduce_kernel<GEMM_F32OUT><<<blocks, 256, 0, s>>>(a, part, part_ld, splits); break;
+    case GEMM_STORE: launch(splitk_reduce_kernel<GEMM_STORE>, blocks, 256, 0, s, a, part, part_ld, splits); break;
+    case GEMM_RESIDUAL: launch(splitk_reduce_kernel<GEMM_RESIDUAL>, blocks, 256, 0, s, a, part, part_ld, splits); break;
+    case GEMM_SWIGLU: launch(splitk_reduce_kernel<GEMM_SWIGLU>, blocks, 256, 0, s, a, part, part_ld, splits); break;
+    default: launch(splitk_reduce_kernel<GEMM_F32OUT>, blocks, 256, 0, s, a, part, part_ld, splits); break;
   }
   return hipGetLastError();
 }
@@ -329,33 +329,35 @@ hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream
   p.m_tiles = (rows + C::BM - 1) / C::BM;
   p.n_tiles = tiles_n<C>(a);
   p.part_ld = a.mode == GEMM_SWIGLU ? 2 * (int64_t)a.N : a.N;
-  const bool split = pl.k_splits > 1 && !a.group_off;
-  p.part = split ? (float*)ws : nullptr;
+  bool split = pl.k_splits > 1 && !a.group_off;
   if (split) {
     const int kb = (a.K + BK - 1) / BK;
     p.k_per = ((kb + pl.k_splits - 1) / pl.k_splits) * BK;
     p.z_count = (a.K + p.k_per - 1) / p.k_per;
-  } else {
+    split = p.z_count > 1;
+  }
+  if (!split) {
     p.k_per = a.K;
     p.z_count = a.group_off ? a.n_groups : 1;
   }
+  p.part = split ? (float*)ws : nullptr;
   const int total = p.m_tiles * p.n_tiles * p.z_count;
   if (total == 0) return hipSuccess;
   if (!split) {
     switch (a.mode) {
-      case GEMM_STORE: gemm_bf16_kernel<C, GEMM_STORE, false><<<total, 256, 0, s>>>(p); break;
-      case GEMM_RESIDUAL: gemm_bf16_kernel<C, GEMM_RESIDUAL, false><<<total, 256, 0, s>>>(p); break;
-      case GEMM_SWIGLU: gemm_bf16_kernel<C, GEMM_SWIGLU, false><<<total, 256, 0, s>>>(p); break;
-      default: gemm_bf16_kernel<C, GEMM_F32OUT, false><<<total, 256, 0, s>>>(p); break;
+      case GEMM_STORE: launch(gemm_bf16_kernel<C, GEMM_STORE, false>, total, 256, 0, s, p); break;
+      case GEMM_RESIDUAL: launch(gemm_bf16_kernel<C, GEMM_RESIDUAL, false>, total, 256, 0, s, p); break;
+      case GEMM_SWIGLU: launch(gemm_bf16_kernel<C, GEMM_SWIGLU, false>, total, 256, 0, s, p); break;
+      default: launch(gemm_bf16_kernel<C, GEMM_F32OUT, false>, total, 256, 0, s, p); break;
     }
     return hipGetLastError();
   }
   if (a.mode == GEMM_SWIGLU)
-    gemm_bf16_kernel<C, GEMM_SWIGLU, true><<<total, 256, 0, s>>>(p);
+    launch(gemm_bf16_kernel<C, GEMM_SWIGLU, true>, total, 256, 0, s, p);
   else
-    gemm_bf16_kernel<C, GEMM_STORE, true><<<total, 256, 0, s>>>(p);
+    launch(gemm_bf16_kernel<C, GEMM_STORE, true>, total, 256, 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.defer_reduce) return e;
   if (hook && hook->fn) hook->fn(hook->ctx, 1);
   return splitk_reduce(a, p.part, p.part_ld, p.z_count, s);
 }
@@ -434,7 +436,8 @@ struct PCfg {
   static constexpr int X = A_IN + B_IN;
   static constexpr int SLAB = (BM + BN) * 128;           // LDS bytes per stage
   static_assert(WM * WN == 4 && FM >= 1 && FN >= 2 && FN % 2 == 0 && A_IN >= 1 && B_IN >= 1, "cfg");
-  static_assert(STAGES >= 2 && STAGES <= 4 && (STAGES - 2) * X <= 63, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 8 && (STAGES - 2) * X <= 63, "vmcnt range");
+  static_assert(STAGES * SLAB <= 160 * 1024, "LDS");
 };
 
 using P10 = PCfg<256, 256, 2, 2, 32, 2>;
@@ -445,6 +448,9 @@ using P14 = PCfg<128, 128, 2, 2, 32, 2>;
 using P15 = PCfg<64, 128, 1, 4, 16, 4>;
 using P16 = PCfg<32, 128, 1, 4, 16, 4>;
 using P17 = PCfg<64, 256, 1, 4, 16, 3>;
+using P18 = PCfg<64, 128, 1, 4, 16, 6>;
+using P19 = PCfg<32, 128, 1, 4, 16, 6>;
+using P20 = PCfg<32, 128, 1, 4, 16, 8>;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -453,15 +459,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // wait until at most `after` slabs issued after the current one are pending
-template <class C>
+// (each slab is X loads of this thread, and loads retire in order)
+template <class C, int A = C::STAGES - 2>
 __device__ __forceinline__ void wait_slab(int after) {
-  if constexpr (C::STAGES >= 4) {
-    if (after >= 2) { wait_vmcnt<2 * C::X>(); return; }
+  if constexpr (A > 0) {
+    if (after >= A) {
+      wait_vmcnt<A * C::X>();
+      return;
+    }
+    wait_slab<C, A - 1>(after);
+  } else {
+    wait_vmcnt<0>();
   }
-  if constexpr (C::STAGES >= 3) {
-    if (after >= 1) { wait_vmcnt<C::X>(); return; }
-  }
-  wait_vmcnt<0>();
 }
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
@@ -559,6 +568,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
   };
 
   const int nk = (k_hi - k_lo) / 64;
+  // row fragments of this wave that hold at least one live row (wave-uniform);
+  // the rest skip their fragment loads and MFMAs (ragged groups, M % BM)
+  const int live = min(C::FM, max(0, (rows - m0 - wm * C::WTM + C::MS - 1) / C::MS));
 #pragma unroll
   for (int t = 0; t < C::STAGES - 1; ++t)
     if (t < nk) issue(t, t);
@@ -576,6 +588,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
       const int c = s * (C::KSTEP / 8) + fq;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
+        if (i >= live) break;
         const int r = wm * C::WTM + i * C::MS + fr;
         af[set][i] = *(const bf16x8*)(sA + r * 128 + ((c ^ swz(r)) << 4));
       }
@@ -590,9 +603,11 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
     for (int s = 0; s < KS; ++s) {
       if (s + 1 < KS) load_frags(s + 1, (s + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < C::FM; ++i) {
+        if (i >= live) break;
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma<C::MS>(af[s & 1][i], bfr[s & 1][j], acc[i][j]);
+      }
     }
   }
 
@@ -664,19 +679,19 @@ hipError_t launch_pipe(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStrea
   if (total == 0) return hipSuccess;
   if (split && p.z_count > 1) {
     if (a.mode == GEMM_SWIGLU)
-      gemm_pipe_kernel<C, GEMM_SWIGLU, true><<<total, 256, 0, s>>>(p);
+      launch(gemm_pipe_kernel<C, GEMM_SWIGLU, true>, total, 256, 0, s, p);
     else
-      gemm_pipe_kernel<C, GEMM_STORE, true><<<total, 256, 0, s>>>(p);
+      launch(gemm_pipe_kernel<C, GEMM_STORE, true>, total, 256, 0, s, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.defer_reduce) return e;
     if (hook && hook->fn) hook->fn(hook->ctx, 1);
     return splitk_reduce(a, p.part, p.part_ld, p.z_count, s);
   }
   switch (a.mode) {
-    case GEMM_STORE: gemm_pipe_kernel<C, GEMM_STORE, false><<<total, 256, 0, s>>>(p); break;
-    case GEMM_RESIDUAL: gemm_pipe_kernel<C, GEMM_RESIDUAL, false><<<total, 256, 0, s>>>(p); break;
-    case GEMM_SWIGLU: gemm_pipe_kernel<C, GEMM_SWIGLU, false><<<total, 256, 0, s>>>(p); break;
-    default: gemm_pipe_kernel<C, GEMM_F32OUT, false><<<total, 256, 0, s>>>(p); break;
+    case GEMM_STORE: launch(gemm_pipe_kernel<C, GEMM_STORE, false>, total, 256, 0, s, p); break;
+    case GEMM_RESIDUAL: launch(gemm_pipe_kernel<C, GEMM_RESIDUAL, false>, total, 256, 0, s, p); break;
+    case GEMM_SWIGLU: launch(gemm_pipe_kernel<C, GEMM_SWIGLU, false>, total, 256, 0, s, p); break;
+    default: launch(gemm_pipe_kernel<C, GEMM_F32OUT, false>, total, 256, 0, s, p); break;
   }
   return hipGetLastError();
 }
@@ -700,6 +715,8 @@ void tile_dims(int cfg, int& bm, int& bn) {
     case 15: bm = 64; bn = 128; return;
     case 16: bm = 32; bn = 128; return;
     case 17: bm = 64; bn = 256; return;
+    case 18: bm = 64; bn = 128; return;
+    case 19: case 20: bm = 32; bn = 128; return;
     default: bm = 128; bn = 128; return;
   }
 }
@@ -720,6 +737,8 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   if (cus <= 0) cus = 256;
   const bool pipe = a.K % 64 == 0;
   if (a.group_off) {            // grouped (experts): rows per group ~ tokens*k/E
+    // 128 x 128 tiles (measured best of the pipelined configurations on the
+    // 8-expert workload); fragments past a group's rows do no work
     p.cfg = pipe ? 14 : 0;
     return p;
   }
@@ -737,6 +756,14 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   while (ks * 2 * tiles <= want && ks < (stream_w ? 8 : 4) && a.K / (ks * 2) >= 512) ks *= 2;
   p.k_splits = ks;
   return p;
+}
+
+int gemm_partials(const GemmArgs& a, const GemmPlan& p) {
+  if (p.k_splits <= 1 || a.group_off || a.M == 0 || a.N == 0) return 1;
+  // both kernels split K in whole 64-wide blocks, as launch_cfg / launch_pipe do
+  const int kb = (a.K + 63) / 64;
+  const int k_per = ((kb + p.k_splits - 1) / p.k_splits) * 64;
+  return (a.K + k_per - 1) / k_per;
 }
 
 size_t gemm_workspace_bytes(const GemmArgs& a, const GemmPlan& p) {
@@ -767,6 +794,9 @@ hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t
     case 15: return launch_pipe<P15>(a, p, ws, s, hook);
     case 16: return launch_pipe<P16>(a, p, ws, s, hook);
     case 17: return launch_pipe<P17>(a, p, ws, s, hook);
+    case 18: return launch_pipe<P18>(a, p, ws, s, hook);
+    case 19: return launch_pipe<P19>(a, p, ws, s, hook);
+    case 20: return launch_pipe<P20>(a, p, ws, s, hook);
     default: return launch_cfg<Cfg0>(a, p, ws, s, hook);
   }
 }
@@ -775,9 +805,9 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
   switch (a.mode) {
-    case GEMM_RESIDUAL: gemm_f32_kernel<GEMM_RESIDUAL><<<grid, 256, 0, s>>>(a); break;
-    case GEMM_SWIGLU: gemm_f32_kernel<GEMM_SWIGLU><<<grid, 256, 0, s>>>(a); break;
-    default: gemm_f32_kernel<GEMM_STORE><<<grid, 256, 0, s>>>(a); break;
+    case GEMM_RESIDUAL: launch(gemm_f32_kernel<GEMM_RESIDUAL>, grid, 256, 0, s, a); break;
+    case GEMM_SWIGLU: launch(gemm_f32_kernel<GEMM_SWIGLU>, grid, 256, 0, s, a); break;
+    default: launch(gemm_f32_kernel<GEMM_STORE>, grid, 256, 0, s, a); break;
   }
   return hipGetLastError();
 }

@@ -1,11 +1,34 @@
 // Host-side internal interfaces between the C ABI and the kernel launchers.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "nf_host.h"
 
 namespace nf {
+
+// Kernel timing without marker packets: when the calling thread's timer holds
+// two events, the next kernel launched through launch() records its own start
+// and end into them (hipExtLaunchKernel), and the timer is cleared.
+struct KernelTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline KernelTimer& kernel_timer() {
+  static thread_local KernelTimer t;
+  return t;
+}
+template <typename... KArgs, typename... Args>
+inline void launch(void (*k)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  KernelTimer& t = kernel_timer();
+  if (t.start) {
+    const KernelTimer use = t;
+    t = KernelTimer{};
+    hipExtLaunchKernelGGL(k, grid, block, shmem, s, use.start, use.stop, 0u, args...);
+  } else {
+    k<<<grid, block, shmem, s>>>(args...);
+  }
+}
 
 // ---------------------------------------------------------------- GEMM
 // C[M][N] = epilogue(A[M][K] . B[N][K]^T): both operands K-contiguous.
@@ -29,6 +52,9 @@ struct GemmArgs {
   int max_group_rows = 0;                 // bound on any group's rows (grid sizing)
   // optional row gather: A row of output row i is a_rows[i] / a_row_div
   const int32_t* a_rows = nullptr; int a_row_div = 1;
+  // split-K only: leave the fp32 partials for the consumer to reduce (no
+  // reduce kernel); see gemm_partials
+  bool defer_reduce = false;
 };
 
 struct GemmPlan {
@@ -51,6 +77,10 @@ struct LaunchHook {
 hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s,
                      const LaunchHook* hook = nullptr);
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
+// Number of fp32 partial slices a split-K launch of this problem writes to
+// its workspace (1: no split, the epilogue writes C).  Slice z starts at
+// z * M * part_ld floats; rows have stride part_ld = N (2N for SWIGLU).
+int gemm_partials(const GemmArgs& a, const GemmPlan& p);
 
 // ---------------------------------------------------------------- row ops
 hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps,
@@ -65,8 +95,18 @@ struct RopeAppendArgs {
   const int32_t* page_indptr; const int32_t* page_indices;
   const float* cos_sin;     // [max_pos][d/2][2]
   int T, nq, nkv, d, page_size;
+  // splits > 1: qkv is not written yet; each value is the rounded sum of
+  // `splits` fp32 partial slices (zstride floats apart, row stride part_ld),
+  // which this kernel also stores to qkv
+  const float* part = nullptr; int64_t part_ld = 0, zstride = 0; int splits = 1;
 };
 hipError_t rope_append(int dtype, const RopeAppendArgs& a, hipStream_t s);
+// bf16, H % 8 == 0: x1 = round(sum of `splits` split-K partial slices + x),
+// then y = RMSNorm(x1) * g, in one kernel; bit-identical to the split-K
+// reduce (residual epilogue) followed by rmsnorm.
+hipError_t residual_rmsnorm_partials(const float* part, int64_t part_ld, int64_t zstride, int splits,
+                                     const void* x, int64_t ldx, void* x1, int64_t ldx1, const void* g, void* y,
+                                     int T, int H, float eps, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
@@ -99,6 +139,10 @@ struct RouteArgs {
 };
 hipError_t moe_route(const RouteArgs& a, hipStream_t s);
 // out[t] = x1[t] + sum_s w[t][s] * y[inv[t*k+s]]
+// Copies `bytes` (a multiple of 16) from device-visible pinned host memory
+// to device memory with a kernel on `s` (no DMA engine, so no cross-engine
+// dependency enters the stream).
+hipError_t meta_copy(const void* host_src, void* dst, size_t bytes, hipStream_t s);
 hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w,
                        const int32_t* inv, void* out, int T, int H, int k, hipStream_t s);
 

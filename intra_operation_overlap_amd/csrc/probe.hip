@@ -44,13 +44,17 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* sink)
 }
 
 // Streams the buffer once, 16 bytes per lane per load, grid-strided.
+template <int U>
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ buf, size_t n16, float* sink) {
   uint32_t x = 0;
   const size_t stride = (size_t)gridDim.x * 256;
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 v0 = buf[i], v1 = buf[i + stride], v2 = buf[i + 2 * stride], v3 = buf[i + 3 * stride];
-    x ^= v0[0] ^ v0[3] ^ v1[1] ^ v1[2] ^ v2[0] ^ v2[2] ^ v3[1] ^ v3[3];
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][3];
   }
   for (; i < n16; i += stride) {
     const u32x4 v = buf[i];
@@ -78,7 +82,7 @@ hipError_t probe_mfma(int shape, int n_blocks, int iters, float* sink, hipStream
 }
 
 hipError_t probe_read(const void* buf, size_t bytes, float* sink, int n_blocks, hipStream_t s) {
-  probe_read_kernel<<<n_blocks, 256, 0, s>>>((const u32x4*)buf, bytes / 16, sink);
+  probe_read_kernel<8><<<n_blocks, 256, 0, s>>>((const u32x4*)buf, bytes / 16, sink);
   return hipGetLastError();
 }
 

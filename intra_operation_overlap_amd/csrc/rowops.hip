@@ -59,46 +59,114 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16x8_kernel(const bf16* __restr
   }
 }
 
+// Split-K reduce of the O-projection (residual epilogue) fused with the FFN
+// RMSNorm: x1 = round(sum_z partial_z + x) is stored, then y = RMSNorm(x1) * g.
+// Same thread-to-chunk mapping and summation order as splitk_reduce_kernel
+// followed by rmsnorm_bf16x8_kernel, so the result is bit-identical.
+__global__ __launch_bounds__(256) void residual_rmsnorm_partials_kernel(
+    const float* __restrict__ part, int64_t part_ld, int64_t zstride, int splits, const bf16* __restrict__ x,
+    int64_t ldx, bf16* __restrict__ x1, int64_t ldx1, const bf16* __restrict__ g, bf16* __restrict__ y, int H,
+    float eps) {
+  const int64_t row = blockIdx.x;
+  const int n8 = H / 8;
+  const float* P = part + row * part_ld;
+  const bf16x8* xr = (const bf16x8*)(x + row * ldx);
+  bf16x8* x1r = (bf16x8*)(x1 + row * ldx1);
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z) {
+      lo += *(const f32x4*)(P + (int64_t)z * zstride + 8 * i);
+      hi += *(const f32x4*)(P + (int64_t)z * zstride + 8 * i + 4);
+    }
+    const bf16x8 r = xr[i];
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float a0 = lo[e], a1 = hi[e];
+      a0 += (float)r[e];
+      a1 += (float)r[e + 4];
+      o[e] = (bf16)a0;
+      o[e + 4] = (bf16)a1;
+    }
+    x1r[i] = o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += (float)o[e] * (float)o[e];
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  const bf16x8* gr = (const bf16x8*)g;
+  bf16x8* yr = (bf16x8*)(y + row * H);
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const bf16x8 v = x1r[i], w = gr[i];
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[e] * inv * (float)w[e]);
+    yr[i] = o;
+  }
+}
+
 // ---------------------------------------------------------------- RoPE + append
-// One block per token.  Q heads: rotate-half rotation by the token's angle
-// table row, written to q_rot.  K heads: rotated and written to the K pool at
-// (page of the position, slot); V heads written to the V pool (both in the
-// pool's MFMA-operand block order).  Pairs (j, j + d/2) turn by the angle p * theta^(-2j/d).
+// Grid (token, head group): each block takes 256 / (d/2) heads of one token,
+// one thread per rotation pair (j, j + d/2).  Q heads are rotated into q_rot;
+// K heads are rotated and written to the K pool at (page of the position,
+// slot); V heads are copied to the V pool (both pools in the attention
+// kernel's MFMA-operand block order).  Pair j turns by p * theta^(-2j/d).
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   const int t = blockIdx.x;
   const int d = a.d, half = d / 2;
+  const int hpb = 256 / half;
+  const int head = blockIdx.y * hpb + threadIdx.x / half;
+  const int j = threadIdx.x % half;
+  if (threadIdx.x >= hpb * half || head >= a.nq + 2 * a.nkv) return;
   const int p = a.pos[t];
   const int r = a.tok_req[t];
-  const int page = a.page_indices[a.page_indptr[r] + p / a.page_size];
-  const int slot = p % a.page_size;
   const int ncols = (a.nq + 2 * a.nkv) * d;
-  const T* row = (const T*)a.qkv + (int64_t)t * ncols;
-  const float2* cs = (const float2*)a.cos_sin + (int64_t)p * half;
-  const int rot_pairs = (a.nq + a.nkv) * half;
-  for (int i = threadIdx.x; i < rot_pairs; i += blockDim.x) {
-    const int head = i / half, j = i % half;
-    const float x0 = to_f32(row[head * d + j]), x1 = to_f32(row[head * d + j + half]);
-    const float2 c = cs[j];
+  T v0, v1;
+  if (a.splits > 1) {           // reduce the QKV GEMM's split-K partials here
+    const float* P = a.part + (int64_t)t * a.part_ld + (int64_t)head * d + j;
+    float s0 = 0.f, s1 = 0.f;
+    for (int z = 0; z < a.splits; ++z) {
+      s0 += P[(int64_t)z * a.zstride];
+      s1 += P[(int64_t)z * a.zstride + half];
+    }
+    v0 = from_f32<T>(s0);
+    v1 = from_f32<T>(s1);
+    T* out = (T*)a.qkv + (int64_t)t * ncols + (int64_t)head * d;
+    out[j] = v0;
+    out[j + half] = v1;
+  } else {
+    const T* row = (const T*)a.qkv + (int64_t)t * ncols + (int64_t)head * d;
+    v0 = row[j];
+    v1 = row[j + half];
+  }
+  if (head < a.nq + a.nkv) {
+    const float2 c = ((const float2*)a.cos_sin)[(int64_t)p * half + j];
+    const float x0 = to_f32(v0), x1 = to_f32(v1);
     const float y0 = x0 * c.x - x1 * c.y;
     const float y1 = x0 * c.y + x1 * c.x;
     if (head < a.nq) {
-      T* q = (T*)a.q_rot + (int64_t)t * a.nq * d + head * d;
+      T* q = (T*)a.q_rot + (int64_t)t * a.nq * d + (int64_t)head * d;
       q[j] = from_f32<T>(y0);
       q[j + half] = from_f32<T>(y1);
-    } else {
-      const int kh = head - a.nq;
-      T* k = (T*)a.k_pool + ((int64_t)page * a.nkv + kh) * a.page_size * d;
-      k[kv_k_off(slot, j)] = from_f32<T>(y0);
-      k[kv_k_off(slot, j + half)] = from_f32<T>(y1);
+      return;
     }
+    const int page = a.page_indices[a.page_indptr[r] + p / a.page_size];
+    const int slot = p % a.page_size;
+    T* k = (T*)a.k_pool + ((int64_t)page * a.nkv + (head - a.nq)) * a.page_size * d;
+    k[kv_k_off(slot, j)] = from_f32<T>(y0);
+    k[kv_k_off(slot, j + half)] = from_f32<T>(y1);
+    return;
   }
-  const T* vrow = row + (a.nq + a.nkv) * d;
-  for (int i = threadIdx.x; i < a.nkv * d; i += blockDim.x) {
-    const int kh = i / d, e = i % d;
-    T* v = (T*)a.v_pool + ((int64_t)page * a.nkv + kh) * a.page_size * d;
-    v[kv_v_off(slot, e)] = vrow[i];
-  }
+  const int page = a.page_indices[a.page_indptr[r] + p / a.page_size];
+  const int slot = p % a.page_size;
+  T* v = (T*)a.v_pool + ((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * a.page_size * d;
+  v[kv_v_off(slot, j)] = v0;
+  v[kv_v_off(slot, j + half)] = v1;
 }
 
 // ---------------------------------------------------------------- MoE router
@@ -188,33 +256,51 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const T* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- metadata
+__global__ __launch_bounds__(256) void meta_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) dst[i] = src[i];
+}
+
 }  // namespace
 
 hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps,
                    hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 1 && H % 8 == 0)
-    rmsnorm_bf16x8_kernel<<<T, 256, 0, s>>>((const bf16*)x, (const bf16*)g, (bf16*)y, H, eps);
+    launch(rmsnorm_bf16x8_kernel, T, 256, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps);
   else if (dtype == 1)
-    rmsnorm_kernel<bf16><<<T, 256, 0, s>>>((const bf16*)x, (const bf16*)g, (bf16*)y, H, eps);
+    launch(rmsnorm_kernel<bf16>, T, 256, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps);
   else
-    rmsnorm_kernel<float><<<T, 256, 0, s>>>((const float*)x, (const float*)g, (float*)y, H, eps);
+    launch(rmsnorm_kernel<float>, T, 256, 0, s, (const float*)x, (const float*)g, (float*)y, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t residual_rmsnorm_partials(const float* part, int64_t part_ld, int64_t zstride, int splits,
+                                     const void* x, int64_t ldx, void* x1, int64_t ldx1, const void* g, void* y,
+                                     int T, int H, float eps, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (H % 8 != 0) return hipErrorInvalidValue;
+  launch(residual_rmsnorm_partials_kernel, T, 256, 0, s, part, part_ld, zstride, splits, (const bf16*)x, ldx,
+         (bf16*)x1, ldx1, (const bf16*)g, (bf16*)y, H, eps);
   return hipGetLastError();
 }
 
 hipError_t rope_append(int dtype, const RopeAppendArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  const int hpb = 256 / (a.d / 2);                      // head_dim in [32, 256]: 2..16 heads per block
+  const dim3 grid(a.T, (a.nq + 2 * a.nkv + hpb - 1) / hpb);
   if (dtype == 1)
-    rope_append_kernel<bf16><<<a.T, 256, 0, s>>>(a);
+    launch(rope_append_kernel<bf16>, grid, 256, 0, s, a);
   else
-    rope_append_kernel<float><<<a.T, 256, 0, s>>>(a);
+    launch(rope_append_kernel<float>, grid, 256, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t moe_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.E > ROUTE_MAX_E || a.k > 8) return hipErrorInvalidValue;
-  moe_route_kernel<<<1, ROUTE_THREADS, 0, s>>>(a);
+  launch(moe_route_kernel, 1, ROUTE_THREADS, 0, s, a);
   return hipGetLastError();
 }
 
@@ -222,9 +308,17 @@ hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w
                        void* out, int T, int H, int k, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 1)
-    moe_combine_kernel<bf16><<<T, 256, 0, s>>>((const bf16*)x1, y, w, inv, (bf16*)out, H, k);
+    launch(moe_combine_kernel<bf16>, T, 256, 0, s, (const bf16*)x1, y, w, inv, (bf16*)out, H, k);
   else
-    moe_combine_kernel<float><<<T, 256, 0, s>>>((const float*)x1, y, w, inv, (float*)out, H, k);
+    launch(moe_combine_kernel<float>, T, 256, 0, s, (const float*)x1, y, w, inv, (float*)out, H, k);
+  return hipGetLastError();
+}
+
+hipError_t meta_copy(const void* host_src, void* dst, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((n16 + 255) / 256, 256);
+  launch(meta_copy_kernel, blocks, 256, 0, s, (const u32x4*)host_src, (u32x4*)dst, n16);
   return hipGetLastError();
 }
 
