@@ -159,8 +159,11 @@ typedef struct nf_kv_pool nf_kv_pool;
 
 /* ---- layer ---------------------------------------------------------------
  * nf_layer_create: validates the shape, binds the caller's weights (pointers
- * kept, nothing copied), allocates the workspace on the current HIP device
- * and builds the fp32 cos/sin table (angles in fp64).  The default plan is
+ * kept), allocates the workspace on the current HIP device and builds the
+ * fp32 cos/sin table (angles in fp64).  For bf16 mixture-of-experts layers
+ * it also copies the expert weights once into the MFMA operand order of the
+ * weight-streaming expert GEMMs (E * 3 * F * H * 2 bytes, owned by the
+ * layer), so weights must not change while the layer exists.  The default plan is
  * one nano-batch on the caller's stream.  Errors: NF_ERR_INVALID_ARG (null
  * pointers, inconsistent shape), NF_ERR_UNSUPPORTED (head_dim or dtype
  * outside the list above), NF_ERR_HIP (allocation failure). */

@@ -105,6 +105,9 @@ struct nf_layer {
   DevBuf h, qkv, q_rot, attn, x1, h2, act, y;
   DevBuf r_idx, r_w, r_perm, r_inv, r_off;
   DevBuf splitk, part_o, part_ml, meta, cos_sin;
+  // expert weights in MFMA operand order for the weight-streaming kernels
+  // (bf16 mixture-of-experts layers; empty otherwise)
+  DevBuf wp_qkv, wp_o, wp_gu, wp_down;
   void* stage[2] = {nullptr, nullptr};       // pinned, coherent host staging
   void* stage_dev[2] = {nullptr, nullptr};   // their device addresses
   size_t stage_bytes[2] = {0, 0};
@@ -359,24 +362,24 @@ NanoGemms nano_gemms(const StepCtx& c, int j, int t0, int t1) {
   NanoGemms n;
   GemmArgs& q = n.qkv;
   q.A = ptr(L->h, (int64_t)t0 * H, dt); q.lda = H;
-  q.B = L->w.w_qkv; q.ldb = H;
+  q.B = L->w.w_qkv; q.ldb = H; q.Bp = L->wp_qkv.p;
   q.C = ptr(L->qkv, (int64_t)t0 * Nqkv, dt); q.ldc = Nqkv;
   q.M = Tj; q.N = Nqkv; q.K = H; q.mode = GEMM_STORE;
   GemmArgs& o = n.o;
   o.A = ptr(L->attn, (int64_t)t0 * nqd, dt); o.lda = nqd;
-  o.B = L->w.w_o; o.ldb = nqd;
+  o.B = L->w.w_o; o.ldb = nqd; o.Bp = L->wp_o.p;
   o.C = ptr(L->x1, (int64_t)t0 * H, dt); o.ldc = H;
   o.R = (const char*)c.b->x + (int64_t)t0 * H * dtype_bytes(dt); o.ldr = H;
   o.M = Tj; o.N = H; o.K = nqd; o.mode = GEMM_RESIDUAL;
   if (s.n_experts == 1) {
     GemmArgs& g = n.gu;
     g.A = ptr(L->h2, (int64_t)t0 * H, dt); g.lda = H;
-    g.B = L->w.w_gate; g.B2 = L->w.w_up; g.ldb = H;
+    g.B = L->w.w_gate; g.B2 = L->w.w_up; g.ldb = H; g.Bp = L->wp_gu.p;
     g.C = ptr(L->act, (int64_t)t0 * F, dt); g.ldc = F;
     g.M = Tj; g.N = F; g.K = H; g.mode = GEMM_SWIGLU;
     GemmArgs& d = n.down;
     d.A = ptr(L->act, (int64_t)t0 * F, dt); d.lda = F;
-    d.B = L->w.w_down; d.ldb = F;
+    d.B = L->w.w_down; d.ldb = F; d.Bp = L->wp_down.p;
     d.C = (char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt); d.ldc = H;
     d.R = ptr(L->x1, (int64_t)t0 * H, dt); d.ldr = H;
     d.M = Tj; d.N = H; d.K = F; d.mode = GEMM_RESIDUAL;
@@ -387,12 +390,14 @@ NanoGemms nano_gemms(const StepCtx& c, int j, int t0, int t1) {
     g.a_rows = (const int32_t*)L->r_perm.p + (int64_t)t0 * k; g.a_row_div = k;
     g.group_off = off; g.n_groups = s.n_experts; g.max_group_rows = Tj * k;
     g.B = L->w.w_gate; g.B2 = L->w.w_up; g.ldb = H; g.b_group_stride = (int64_t)F * H;
+    g.Bp = L->wp_gu.p; g.bp_group_stride = 2 * (int64_t)F * H;
     g.C = ptr(L->act, (int64_t)t0 * k * F, dt); g.ldc = F;
     g.M = Tj * k; g.N = F; g.K = H; g.mode = GEMM_SWIGLU;
     GemmArgs& d = n.moe_down;
     d.A = ptr(L->act, (int64_t)t0 * k * F, dt); d.lda = F;
     d.group_off = off; d.n_groups = s.n_experts; d.max_group_rows = Tj * k;
     d.B = L->w.w_down; d.ldb = F; d.b_group_stride = (int64_t)H * F;
+    d.Bp = L->wp_down.p; d.bp_group_stride = (int64_t)H * F;
     d.C = (float*)L->y.p + (int64_t)t0 * k * H; d.ldc = H;
     d.M = Tj * k; d.N = H; d.K = F; d.mode = GEMM_F32OUT;
   }
@@ -513,12 +518,13 @@ nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
   prof_begin(L, K_ROUTE, s);
   HIP_STEP(moe_route(r, s));
   prof_end(L, K_ROUTE, s);
-  // grouped: the tile choice depends on the mean rows per expert; no split-K
+  // grouped: the tile choice depends on the mean rows per expert; the
+  // streaming kernels may split K (partials in the split-K workspace)
   prof_begin(L, K_MOE_GATEUP, s);
-  HIP_STEP(gemm_bf16(g.moe_gu, gemm_choose(g.moe_gu, c.gemm_cus), nullptr, s));
+  HIP_STEP(gemm_bf16(g.moe_gu, gemm_choose(g.moe_gu, c.gemm_cus), L->splitk.p, s));
   prof_end(L, K_MOE_GATEUP, s);
   prof_begin(L, K_MOE_DOWN, s);
-  HIP_STEP(gemm_bf16(g.moe_down, gemm_choose(g.moe_down, c.gemm_cus), nullptr, s));
+  HIP_STEP(gemm_bf16(g.moe_down, gemm_choose(g.moe_down, c.gemm_cus), L->splitk.p, s));
   prof_end(L, K_MOE_DOWN, s);
   prof_begin(L, K_COMBINE, s);
   HIP_STEP(moe_combine(dt, ptr(L->x1, (int64_t)t0 * H, dt), (const float*)L->y.p + (int64_t)t0 * k * H,
@@ -528,6 +534,28 @@ nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
 }
 
 size_t align_words(size_t w) { return (w + 63) & ~(size_t)63; }
+
+// Copies of the expert weights in MFMA operand order for the weight-streaming
+// expert GEMMs (made once; the caller's weights must not change after
+// nf_layer_create).  Dense layers keep only the caller's copy: their GEMMs use
+// the LDS-tiled kernels, which measured faster there.  Expert matrices whose
+// output features are not a multiple of 32 or whose K is not a multiple of 16
+// get no copy either.
+hipError_t pack_weights(nf_layer* L) {
+  const nf_shape& s = L->s;
+  const int64_t H = s.hidden, F = s.ffn, E = s.n_experts;
+  if (E == 1 || F % 32 || H % 32) return hipSuccess;
+  hipError_t e;
+  if ((e = ensure(L->wp_gu, E * 2 * F * H * 2)) != hipSuccess) return e;
+  if ((e = pack_b(L->w.w_gate, H, F * H, (int)F, (int)H, (int)E, L->wp_gu.p, 2, 0, 2 * F * H, nullptr)) != hipSuccess)
+    return e;
+  if ((e = pack_b(L->w.w_up, H, F * H, (int)F, (int)H, (int)E, L->wp_gu.p, 2, 1, 2 * F * H, nullptr)) != hipSuccess)
+    return e;
+  if ((e = ensure(L->wp_down, E * H * F * 2)) != hipSuccess) return e;
+  if ((e = pack_b(L->w.w_down, F, H * F, (int)H, (int)F, (int)E, L->wp_down.p, 1, 0, H * F, nullptr)) != hipSuccess)
+    return e;
+  return hipDeviceSynchronize();
+}
 
 nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t caller, const nf_plan& plan) {
   std::string err;
@@ -568,7 +596,7 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
     if (L->s.n_experts == 1)
       for (const GemmArgs* a : {&g.qkv, &g.o, &g.gu, &g.down}) ws = std::max(ws, gemm_ws_need(c, *a));
     else
-      ws = std::max(ws, gemm_ws_need(c, g.qkv)), ws = std::max(ws, gemm_ws_need(c, g.o));
+      for (const GemmArgs* a : {&g.qkv, &g.o, &g.moe_gu, &g.moe_down}) ws = std::max(ws, gemm_ws_need(c, *a));
   }
   HIP_TRY(ensure(L->splitk, ws));
   const size_t n_part = (size_t)std::max(1, w.n_partials) * L->s.n_kv_heads * 16;
@@ -772,6 +800,8 @@ nf_status nf_layer_create(const nf_shape* s, const nf_weights* w, nf_layer** out
       cs[(p * half + j) * 2] = (float)std::cos(ang);
       cs[(p * half + j) * 2 + 1] = (float)std::sin(ang);
     }
+  if (dt == NF_BF16 && pack_weights(L) != hipSuccess)
+    return fail(set_err(NF_ERR_HIP, "weight packing failed"));
   if (ensure(L->cos_sin, cs.size() * 4) != hipSuccess ||
       hipMemcpy(L->cos_sin.p, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
     return fail(set_err(NF_ERR_HIP, "cos/sin table upload failed"));
@@ -798,7 +828,8 @@ void nf_layer_destroy(nf_layer* L) {
     if (kv.second.a) (void)hipStreamDestroy(kv.second.a);
   }
   for (DevBuf* b : {&L->h, &L->qkv, &L->q_rot, &L->attn, &L->x1, &L->h2, &L->act, &L->y, &L->r_idx, &L->r_w,
-                    &L->r_perm, &L->r_inv, &L->r_off, &L->splitk, &L->part_o, &L->part_ml, &L->meta, &L->cos_sin})
+                    &L->r_perm, &L->r_inv, &L->r_off, &L->splitk, &L->part_o, &L->part_ml, &L->meta, &L->cos_sin,
+                    &L->wp_qkv, &L->wp_o, &L->wp_gu, &L->wp_down})
     release(*b);
   for (int i = 0; i < 2; ++i) {
     if (L->stage[i]) (void)hipHostFree(L->stage[i]);
@@ -1172,6 +1203,13 @@ extern "C" nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int3
   g.B = Bm; g.B2 = (char*)Bm + (size_t)N * K * 2; g.ldb = K;
   g.C = C; g.ldc = N; g.R = R; g.ldr = N;
   g.M = M; g.N = N; g.K = K; g.mode = mode;
+  void* Bp = nullptr;
+  if (N % 32 == 0 && K % 16 == 0) {             // operand-order copy for the streaming kernels
+    HIP_TRY(hipMalloc(&Bp, (size_t)nb * N * K * 2));
+    HIP_TRY(pack_b(g.B, K, 0, N, K, 1, Bp, (int)nb, 0, 0, nullptr));
+    if (nb == 2) HIP_TRY(pack_b(g.B2, K, 0, N, K, 1, Bp, 2, 1, 0, nullptr));
+    g.Bp = Bp;
+  }
   GemmPlan p = gemm_choose(g, cus);
   if (tile_cfg >= 0) p.cfg = tile_cfg;
   if (k_splits > 0) p.k_splits = k_splits;
@@ -1193,7 +1231,7 @@ extern "C" nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int3
   if (out_splits) *out_splits = p.k_splits;
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
-  for (void* q : {A, Bm, C, R, ws})
+  for (void* q : {A, Bm, C, R, ws, Bp})
     if (q) (void)hipFree(q);
   return NF_OK;
 }

@@ -23,7 +23,6 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (144 B: breaks bank aliasing)
-constexpr int NXCD = 8;
 
 template <int BM_, int BN_, int WM_, int WN_, int MS_>
 struct Cfg {
@@ -80,11 +79,6 @@ struct KParams {
   int64_t part_ld;                  // row stride of partials
 };
 
-__device__ __forceinline__ int xcd_logical(int L, int total) {
-  const int xcd = L % NXCD, slot = L / NXCD;
-  const int q = total / NXCD, r = total % NXCD;
-  return xcd * q + min(xcd, r) + slot;
-}
 
 
 
@@ -302,7 +296,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, const fl
   *(bf16x4*)((bf16*)a.C + o) = out;
 }
 
-hipError_t splitk_reduce(const GemmArgs& a, const float* part, int64_t part_ld, int splits, hipStream_t s) {
+hipError_t splitk_reduce_impl(const GemmArgs& a, const float* part, int64_t part_ld, int splits, hipStream_t s) {
   const int64_t work = (int64_t)a.M * (a.N / 4);
   const int blocks = (int)((work + 255) / 256);
   switch (a.mode) {
@@ -341,6 +335,7 @@ hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream
     p.z_count = a.group_off ? a.n_groups : 1;
   }
   p.part = split ? (float*)ws : nullptr;
+  if (split && !ws) return hipErrorInvalidValue;            // split-K needs the workspace
   const int total = p.m_tiles * p.n_tiles * p.z_count;
   if (total == 0) return hipSuccess;
   if (!split) {
@@ -452,11 +447,6 @@ using P18 = PCfg<64, 128, 1, 4, 16, 6>;
 using P19 = PCfg<32, 128, 1, 4, 16, 6>;
 using P20 = PCfg<32, 128, 1, 4, 16, 8>;
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // wait until at most `after` slabs issued after the current one are pending
 // (each slab is X loads of this thread, and loads retire in order)
@@ -475,9 +465,6 @@ __device__ __forceinline__ void wait_slab(int after) {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-__device__ __forceinline__ void dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
 
 template <class C, int MODE, bool PARTIAL>
 __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
@@ -570,7 +557,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
   const int nk = (k_hi - k_lo) / 64;
   // row fragments of this wave that hold at least one live row (wave-uniform);
   // the rest skip their fragment loads and MFMAs (ragged groups, M % BM)
-  const int live = min(C::FM, max(0, (rows - m0 - wm * C::WTM + C::MS - 1) / C::MS));
+  const int live = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (rows - m0 - wm * C::WTM + C::MS - 1) / C::MS)));
 #pragma unroll
   for (int t = 0; t < C::STAGES - 1; ++t)
     if (t < nk) issue(t, t);
@@ -670,6 +657,7 @@ hipError_t launch_pipe(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStrea
     p.k_per = ((kb + pl.k_splits - 1) / pl.k_splits) * 64;
     p.z_count = (a.K + p.k_per - 1) / p.k_per;
       p.part = (float*)ws;
+    if (!ws && p.z_count > 1) return hipErrorInvalidValue;  // split-K needs the workspace
   } else {
     p.k_per = a.K;
     p.z_count = a.group_off ? a.n_groups : 1;
@@ -732,9 +720,52 @@ int n_tiles_of(const GemmArgs& a, int bn) {
 // cannot give every CU about two workgroups, K is split (up to 8 ways for
 // weight streaming, 4 otherwise, keeping >= 512 of K per piece) and a reduce
 // kernel applies the epilogue.
+namespace {
+// Split count of a weight-streaming launch from a time model fitted on
+// MI355X: a workgroup streams at most kWgGBps, at most two workgroups share a
+// CU, and the chip at most kHbmGBps; split-K adds its fp32 partial slices
+// (written, then read again by the reduce).
+constexpr double kWgGBps = 20.0, kHbmGBps = 6000.0;
+int stream_splits(const GemmArgs& a, int cfg, int cus) {
+  const bool sw = a.mode == GEMM_SWIGLU;
+  const int nbw = (cfg == 42 || cfg == 43 || cfg == 45) ? 2 : 1;
+  const int nbt = (sw ? 2 : 1) * (a.N / 32);
+  const int n_wg = (nbt + 4 * nbw - 1) / (4 * nbw);
+  const int nch = a.K / 16 / stream_kc(cfg);
+  const double wbytes = (double)nbt * 32 * a.K * 2 * a.n_groups;
+  const double pld = sw ? 2.0 * a.N : a.N;
+  int best = 1;
+  double best_t = 1e30;
+  for (int want = 1; want <= std::min(nch, 16); ++want) {
+    const int ch_per = (nch + want - 1) / want;
+    const int z = (nch + ch_per - 1) / ch_per;
+    const double wgs = (double)n_wg * z * a.n_groups;
+    const double bw = std::min(kHbmGBps, std::min(wgs, 2.0 * cus) * kWgGBps) * 1e9;
+    const double t = (wbytes + (z > 1 ? 2.0 * z * a.M * pld * 4 : 0.0)) / bw;
+    if (t < best_t * 0.98) {
+      best_t = t;
+      best = z;
+    }
+  }
+  return best;
+}
+}  // namespace
+
 GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   GemmPlan p;
   if (cus <= 0) cus = 256;
+  if (a.Bp) {                   // packed weights: stream them for expert groups
+    // (measured: for dense decode-sized M the pipelined LDS kernel below is
+    // faster, so configurations 40..43 are chosen only on request)
+    const bool sw = a.mode == GEMM_SWIGLU;
+    int cfg = 0;
+    if (a.group_off && a.max_group_rows / std::max(1, a.n_groups) <= 160) cfg = sw ? 45 : 44;
+    if (cfg && a.N % 32 == 0 && a.K % (16 * stream_kc(cfg)) == 0) {
+      p.cfg = cfg;
+      p.k_splits = stream_splits(a, cfg, cus);
+      return p;
+    }
+  }
   const bool pipe = a.K % 64 == 0;
   if (a.group_off) {            // grouped (experts): rows per group ~ tokens*k/E
     // 128 x 128 tiles (measured best of the pipelined configurations on the
@@ -758,7 +789,18 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   return p;
 }
 
+hipError_t splitk_reduce(const GemmArgs& a, const float* part, int64_t part_ld, int splits, hipStream_t s) {
+  return splitk_reduce_impl(a, part, part_ld, splits, s);
+}
+
 int gemm_partials(const GemmArgs& a, const GemmPlan& p) {
+  if (p.cfg >= 40) {            // streaming kernels split K in whole chunks
+    const int kc = stream_kc(p.cfg);
+    const int nch = a.K / 16 / kc;
+    if (p.k_splits <= 1 || nch <= 1) return 1;
+    const int ch_per = (nch + std::min(p.k_splits, nch) - 1) / std::min(p.k_splits, nch);
+    return (nch + ch_per - 1) / ch_per;
+  }
   if (p.k_splits <= 1 || a.group_off || a.M == 0 || a.N == 0) return 1;
   // both kernels split K in whole 64-wide blocks, as launch_cfg / launch_pipe do
   const int kb = (a.K + 63) / 64;
@@ -767,6 +809,10 @@ int gemm_partials(const GemmArgs& a, const GemmPlan& p) {
 }
 
 size_t gemm_workspace_bytes(const GemmArgs& a, const GemmPlan& p) {
+  if (p.cfg >= 40) {
+    const int z = gemm_partials(a, p);
+    return z > 1 ? (size_t)z * a.M * (a.mode == GEMM_SWIGLU ? 2 * (int64_t)a.N : a.N) * sizeof(float) : 0;
+  }
   if (p.k_splits <= 1 || a.group_off) return 0;
   const int64_t ld = a.mode == GEMM_SWIGLU ? 2 * (int64_t)a.N : a.N;
   int bm, bn;
@@ -778,6 +824,7 @@ size_t gemm_workspace_bytes(const GemmArgs& a, const GemmPlan& p) {
 
 hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (p.cfg >= 40) return a.Bp ? gemm_stream(a, p, ws, s, hook) : hipErrorInvalidValue;
   if (p.cfg >= 10 && a.K % 64 != 0) return hipErrorInvalidValue;
   switch (p.cfg) {
     case 1: return launch_cfg<Cfg1>(a, p, ws, s, hook);

@@ -1,0 +1,287 @@
+// Weight-streaming bf16 GEMM for the decode-sized GEMMs of a step (M up to
+// 64 rows) and for the per-expert GEMMs of a mixture-of-experts layer (about
+// 128 rows per expert).  At these M the GEMM reads every weight byte once
+// and does little arithmetic per byte, so its time is the HBM stream of the
+// weights, and what matters is how many weight bytes each CU keeps in flight.
+//
+// The weights are copied once, at layer creation, into the operand order of
+// v_mfma_f32_32x32x16_bf16: block (n-block b of 32 output features, k-step
+// s of 16) is 1 KB holding, for lane l, the 8 K-consecutive values
+// W[32 b + l % 32][16 s + 8 (l / 32) ..].  A wavefront then fetches its B
+// operand for one k-step with one linear 16-byte-per-lane load straight into
+// registers (no LDS), and it issues a whole chunk of k-steps ahead.  The
+// activations (A) are small and shared by the four waves of a workgroup:
+// they are staged in LDS through registers, one K-chunk at a time, and the
+// chunk's B loads stay in flight while the A part is written and the
+// workgroup synchronises.
+//
+// Split-K writes fp32 partial slices in the same layout as the pipelined
+// GEMM's, so the same reduce kernel (or a fused consumer) finishes them.
+#include "nf_device.h"
+#include "nf_internal.h"
+
+namespace nf {
+namespace {
+
+constexpr int SB = 32;   // rows / columns of one MFMA block
+constexpr int SK = 16;   // K of one MFMA
+
+struct SParams {
+  GemmArgs a;
+  int nbt;          // packed n-blocks per group (SWIGLU: gate and up blocks interleaved)
+  int kbt;          // K / 16
+  int n_wg;         // workgroups along N
+  int splits;       // K pieces
+  int ks_per;       // k-steps per piece (a multiple of the chunk)
+  float* part;      // partial slices [splits][M][part_ld] (split-K only)
+  int64_t part_ld;
+};
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (within a 32 x 32 block) of accumulator element r held by `lane`; the
+// column is lane % 32.
+__device__ __forceinline__ int acc_row32(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// MB m-blocks of 32 rows per pass, NBW packed n-blocks per wave, KC k-steps
+// per A chunk.  MODE as in GemmMode; PARTIAL writes fp32 partial slices.
+template <int MB, int NBW, int KC, int MODE, bool PARTIAL>
+__global__ __launch_bounds__(256, 2) void gemm_stream_kernel(SParams p) {
+  constexpr int ROWS = MB * SB;
+  constexpr int PR = KC * 2;                 // 16-byte pieces of one A row in a chunk
+  constexpr int CH = ROWS * PR * 16;         // bytes of one A chunk
+  constexpr int NA = CH / 4096;              // 16-byte A loads per lane per chunk
+  constexpr int NB = KC * NBW;               // B loads per wave per chunk
+  static_assert(CH % 4096 == 0 && NA >= 1, "chunk");
+  static_assert(NA + NB <= 63, "vmcnt range");
+  static_assert((MODE == GEMM_SWIGLU) == (NBW == 2), "SWIGLU pairs a gate and an up block per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[CH];
+
+  const GemmArgs& a = p.a;
+  const int total = p.n_wg * p.splits * a.n_groups;
+  const int logical = xcd_logical(blockIdx.x, total);
+  const int wg_n = logical % p.n_wg;
+  const int rest = logical / p.n_wg;
+  const int z = rest % p.splits;
+  const int grp = rest / p.splits;
+  int m_begin = 0, rows = a.M;
+  if (a.group_off) {
+    m_begin = a.group_off[grp];
+    rows = a.group_off[grp + 1] - m_begin;
+  }
+  if (rows <= 0) return;                                   // whole workgroup exits together
+  const int ks0 = z * p.ks_per;
+  const int nch = min(p.ks_per, p.kbt - ks0) / KC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // B sources: this wave's packed n-blocks, clamped into range so that every
+  // wave issues the same number of loads (the vmcnt arithmetic relies on it)
+  const bf16x8* bsrc[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int nb = min((wg_n * 4 + wave) * NBW + j, p.nbt - 1);
+    bsrc[j] = (const bf16x8*)((const bf16*)a.Bp + (int64_t)grp * a.bp_group_stride +
+                              ((int64_t)nb * p.kbt + ks0) * 512) + lane;
+  }
+
+  for (int m0 = 0; m0 < rows; m0 += ROWS) {
+    const int live_mb = min(MB, (rows - m0 + SB - 1) / SB);
+    // A sources: load i of this wave fills chunk bytes [(wave NA + i) KB, +1 KB):
+    // piece (row r, physical slot sl) holds logical piece sl ^ (r % PR), so
+    // fragment reads (32 rows, one piece) spread over the LDS banks
+    const bf16* asrc[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int piece = (wave * NA + i) * 64 + lane;
+      const int r = piece / PR, q = (piece % PR) ^ (r % PR);
+      int src = m_begin + min(m0 + r, rows - 1);          // rows past the group repeat its last row
+      if (a.a_rows) src = a.a_rows[src] / a.a_row_div;
+      asrc[i] = (const bf16*)a.A + (int64_t)src * a.lda + (int64_t)ks0 * SK + q * 8;
+    }
+
+    f32x16 acc[MB][NBW];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[m][j][e] = 0.f;
+
+    // Per chunk: the chunk's A is loaded to registers and all KC * NBW of its
+    // weight loads are issued at once; A goes to LDS as soon as it lands and
+    // the MFMAs consume the weights in issue order (the compiler waits per
+    // register).  Only register loads are used, and a chunk's loads are
+    // consumed in the same iteration, so the compiler's in-order counting
+    // stays exact; the other waves of the CU keep HBM busy while one wave
+    // computes.
+    bf16x8 br[KC][NBW], ar[NA];
+    for (int c = 0; c < nch; ++c) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) ar[i] = *(const bf16x8*)(asrc[i] + (int64_t)c * KC * SK);
+#pragma unroll
+      for (int s = 0; s < KC; ++s)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) br[s][j] = __builtin_nontemporal_load(bsrc[j] + (int64_t)(c * KC + s) * 64);
+#pragma unroll
+      for (int i = 0; i < NA; ++i) *(bf16x8*)(smem + ((wave * NA + i) * 64 + lane) * 16) = ar[i];
+      barrier_lds();                  // every wave's part of the chunk's A is in LDS
+#pragma unroll
+      for (int s = 0; s < KC; ++s) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          const int r = m * SB + (lane & 31);
+          const int sl = (2 * s + (lane >> 5)) ^ (r % PR);
+          const bf16x8 af = *(const bf16x8*)(smem + r * PR * 16 + sl * 16);
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) acc[m][j] = mfma32(af, br[s][j], acc[m][j]);
+        }
+      }
+      barrier_lds();                  // LDS may take the next chunk
+    }
+
+    // epilogue: lane holds D[acc_row32(lane, r)][lane % 32] of each block
+    constexpr int NOUT = MODE == GEMM_SWIGLU ? 1 : NBW;     // output blocks per wave
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m >= live_mb) break;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int local = m0 + m * SB + acc_row32(lane, r);
+        if (local >= rows) continue;
+        const int64_t orow = m_begin + local;
+#pragma unroll
+        for (int j = 0; j < NOUT; ++j) {
+          const int ob = MODE == GEMM_SWIGLU ? wg_n * 4 + wave : (wg_n * 4 + wave) * NBW + j;
+          const int col = ob * SB + (lane & 31);
+          if (col >= a.N) continue;
+          if (MODE == GEMM_SWIGLU) {
+            const float g = acc[m][0][r], u = acc[m][1][r];
+            if (PARTIAL) {
+              float* P = p.part + (int64_t)z * a.M * p.part_ld + orow * p.part_ld;
+              P[col] = g;
+              P[a.N + col] = u;
+            } else {
+              ((bf16*)a.C)[orow * a.ldc + col] = (bf16)(silu_f(g) * u);
+            }
+          } else {
+            const float v = acc[m][j][r];
+            if (PARTIAL) {
+              p.part[(int64_t)z * a.M * p.part_ld + orow * p.part_ld + col] = v;
+            } else if (MODE == GEMM_STORE) {
+              ((bf16*)a.C)[orow * a.ldc + col] = (bf16)v;
+            } else if (MODE == GEMM_RESIDUAL) {
+              const float res = (float)((const bf16*)a.R)[orow * a.ldr + col];
+              ((bf16*)a.C)[orow * a.ldc + col] = (bf16)(v + res);
+            } else {
+              ((float*)a.C)[orow * a.ldc + col] = v;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Packs W [groups][N][K] (row stride ldw, group stride gs) into operand
+// order: block (n-block b, k-step s) of group g goes to packed n-block
+// b * nb_stride + nb_offset.  One thread per 16-byte piece.
+__global__ __launch_bounds__(256) void pack_b_kernel(const bf16* __restrict__ W, int64_t ldw, int64_t gs, int N,
+                                                     int K, int groups, bf16* __restrict__ P, int nb_stride,
+                                                     int nb_offset, int nbt_packed, int64_t pgs) {
+  const int kbt = K / SK, nbt = N / SB;
+  const int64_t pieces = (int64_t)groups * nbt * kbt * 64;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(i % 64);
+    const int64_t blk = i / 64;
+    const int s = (int)(blk % kbt);
+    const int64_t gb = blk / kbt;
+    const int b = (int)(gb % nbt);
+    const int g = (int)(gb / nbt);
+    const bf16x8 v = *(const bf16x8*)(W + g * gs + (int64_t)(b * SB + (lane & 31)) * ldw + s * SK + 8 * (lane >> 5));
+    const int64_t pb = (int64_t)b * nb_stride + nb_offset;
+    *(bf16x8*)(P + g * pgs + ((pb * kbt + s) * 64 + lane) * 8) = v;
+    (void)nbt_packed;
+  }
+}
+
+template <int MB, int NBW, int KC>
+hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream_t s, const LaunchHook* hook) {
+  if (a.N % SB || a.K % (KC * SK)) return hipErrorInvalidValue;
+  SParams p;
+  p.a = a;
+  const bool sw = a.mode == GEMM_SWIGLU;
+  p.kbt = a.K / SK;
+  p.nbt = (sw ? 2 : 1) * (a.N / SB);
+  p.n_wg = (p.nbt + 4 * NBW - 1) / (4 * NBW);
+  const int nch = p.kbt / KC;
+  const int want = std::max(1, std::min(pl.k_splits, nch));
+  const int ch_per = (nch + want - 1) / want;
+  p.ks_per = ch_per * KC;
+  p.splits = (nch + ch_per - 1) / ch_per;
+  p.part_ld = sw ? 2 * (int64_t)a.N : a.N;
+  p.part = p.splits > 1 ? (float*)ws : nullptr;
+  if (p.splits > 1 && !ws) return hipErrorInvalidValue;     // split-K needs the workspace
+  const int total = p.n_wg * p.splits * a.n_groups;
+  if (total == 0) return hipSuccess;
+  if (sw != (NBW == 2)) return hipErrorInvalidValue;    // SWIGLU configurations pair gate and up blocks
+  if (p.splits > 1) {
+    if constexpr (NBW == 2)
+      launch(gemm_stream_kernel<MB, NBW, KC, GEMM_SWIGLU, true>, total, 256, 0, s, p);
+    else
+      launch(gemm_stream_kernel<MB, NBW, KC, GEMM_STORE, true>, total, 256, 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.defer_reduce) return e;
+    if (hook && hook->fn) hook->fn(hook->ctx, 1);
+    return splitk_reduce(a, p.part, p.part_ld, p.splits, s);
+  }
+  if constexpr (NBW == 2) {
+    launch(gemm_stream_kernel<MB, NBW, KC, GEMM_SWIGLU, false>, total, 256, 0, s, p);
+  } else {
+    switch (a.mode) {
+      case GEMM_STORE: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_STORE, false>, total, 256, 0, s, p); break;
+      case GEMM_RESIDUAL: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_RESIDUAL, false>, total, 256, 0, s, p); break;
+      default: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_F32OUT, false>, total, 256, 0, s, p); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Configurations: (rows per pass, packed n-blocks per wave, k-steps per chunk)
+//   40: 32 rows,  1 block, 16    41: 64 rows, 1 block, 16
+//   42: 32 rows,  2 blocks, 16   43: 64 rows, 2 blocks, 16  (SWIGLU)
+//   44: 128 rows, 1 block, 16    45: 128 rows, 2 blocks, 8  (expert groups)
+hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook) {
+  switch (p.cfg) {
+    case 40: return launch_stream<1, 1, 16>(a, p, ws, s, hook);
+    case 41: return launch_stream<2, 1, 16>(a, p, ws, s, hook);
+    case 42: return launch_stream<1, 2, 16>(a, p, ws, s, hook);
+    case 43: return launch_stream<2, 2, 16>(a, p, ws, s, hook);
+    case 44: return launch_stream<4, 1, 16>(a, p, ws, s, hook);
+    case 45: return launch_stream<4, 2, 8>(a, p, ws, s, hook);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int stream_kc(int cfg) {
+  switch (cfg) {
+    case 40: case 41: case 42: case 43: case 44: return 16;
+    case 45: return 8;
+    default: return 0;
+  }
+}
+
+hipError_t pack_b(const void* W, int64_t ldw, int64_t group_stride, int N, int K, int groups, void* P,
+                  int nb_stride, int nb_offset, int64_t packed_group_stride, hipStream_t s) {
+  if (N % SB || K % SK) return hipErrorInvalidValue;
+  const int64_t pieces = (int64_t)groups * (N / SB) * (K / SK) * 64;
+  const int blocks = (int)std::min<int64_t>((pieces + 255) / 256, 4096);
+  launch(pack_b_kernel, blocks, 256, 0, s, (const bf16*)W, ldw, group_stride, N, K, groups, (bf16*)P, nb_stride,
+         nb_offset, 0, packed_group_stride);
+  return hipGetLastError();
+}
+
+}  // namespace nf

@@ -47,3 +47,32 @@ __device__ __forceinline__ int kv_k_off(int s, int d) {
 __device__ __forceinline__ int kv_v_off(int s, int d) {
   return (d >> 5) * 512 + ((d & 15) + ((s >> 2) << 4)) * 8 + ((d >> 4) & 1) * 4 + (s & 3);
 }
+
+// ---------------------------------------------------------------- launch and memory helpers
+
+// The dispatcher deals workgroups round-robin over the 8 XCDs; this maps the
+// hardware order to a logical tile index such that each XCD is handed one
+// contiguous range of tiles (so neighbouring tiles share that XCD's L2).
+constexpr int NXCD = 8;
+__device__ __forceinline__ int xcd_logical(int hw, int total) {
+  const int xcd = hw % NXCD, slot = hw / NXCD;
+  const int q = total / NXCD, r = total % NXCD;
+  return xcd * q + min(xcd, r) + slot;
+}
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l writes lds + 16 l, so one instruction fills 1 KB.
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (loads retire in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its global loads still in flight.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -55,6 +55,9 @@ struct GemmArgs {
   // split-K only: leave the fp32 partials for the consumer to reduce (no
   // reduce kernel); see gemm_partials
   bool defer_reduce = false;
+  // B (B2 interleaved for SWIGLU) packed in MFMA operand order by pack_b
+  // (optional; enables the weight-streaming kernels), group stride in elements
+  const void* Bp = nullptr; int64_t bp_group_stride = 0;
 };
 
 struct GemmPlan {
@@ -77,6 +80,17 @@ struct LaunchHook {
 hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s,
                      const LaunchHook* hook = nullptr);
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
+// Sum of `splits` fp32 partial slices (M x part_ld each) plus the mode's
+// epilogue, written to C.
+hipError_t splitk_reduce(const GemmArgs& a, const float* part, int64_t part_ld, int splits, hipStream_t s);
+// Weight-streaming kernels (tile configurations 40..45; need a.Bp).
+hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook);
+int stream_kc(int cfg);   // k-steps (of 16) per A chunk of a streaming configuration, 0 if none
+// Packs W [groups][N][K] (row stride ldw, group stride group_stride; N % 32 ==
+// 0, K % 16 == 0) into 1 KB operand blocks (32 rows x 16 k); source n-block b
+// becomes packed n-block b * nb_stride + nb_offset (gate/up interleave: 2, 0/1).
+hipError_t pack_b(const void* W, int64_t ldw, int64_t group_stride, int N, int K, int groups, void* P,
+                  int nb_stride, int nb_offset, int64_t packed_group_stride, hipStream_t s);
 // Number of fp32 partial slices a split-K launch of this problem writes to
 // its workspace (1: no split, the epilogue writes C).  Slice z starts at
 // z * M * part_ld floats; rows have stride part_ld = N (2N for SWIGLU).
