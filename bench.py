@@ -33,7 +33,7 @@ def log(msg):
 
 
 # ------------------------------------------------------------------ algorithmic work
-def kernel_work(kind, wl, batch, plan_sizes):
+def kernel_work(kind, wl, batch, plan_sizes, logits=None):
     """(bytes, flops) the method must move/compute in ONE launch of `kind`,
     averaged over the launches of one step (one per nano-batch)."""
     s = wl.shape
@@ -56,6 +56,16 @@ def kernel_work(kind, wl, batch, plan_sizes):
             for i in range(int(batch.req_q_len[r])):
                 flops += 4 * nq * d * (int(batch.req_pos0[r]) + i + 1)
         return (kv + qo) / n, flops / n
+    if kind in ("moe_gemm_gate_up_swiglu", "moe_gemm_down"):
+        # every expert that receives a token has its weights read once
+        k, E = s.top_k, s.n_experts
+        touched = E if logits is None else len(np.unique(np.argsort(-logits, axis=1, kind="stable")[:, :k]))
+        A = T * k / n
+        if kind == "moe_gemm_gate_up_swiglu":
+            byts = touched * 2 * F * H * eb + A * H * eb + A * F * eb
+            return byts, 2.0 * A * 2 * F * H
+        byts = touched * H * F * eb + A * F * eb + A * H * 4
+        return byts, 2.0 * A * H * F
     gemms = {
         "gemm_qkv": (Nqkv, H, False),
         "gemm_o_residual": (H, nq * d, True),
@@ -192,7 +202,8 @@ def main():
         comparisons["searched_plan_ms"] = ms
 
     # roofline of the dominant kernel
-    byts, flops = kernel_work(dominant, wl, batch, plan_sizes)
+    logits = acts["router_logits"].float().cpu().numpy() if "router_logits" in acts else None
+    byts, flops = kernel_work(dominant, wl, batch, plan_sizes, logits)
     roofline = None
     if byts is not None:
         intensity = flops / byts
