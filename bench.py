@@ -272,6 +272,8 @@ KERNEL_SOURCES = {
     "gemm_o_residual": ["gemm.hip"] + _COMMON,
     "gemm_gate_up_swiglu": ["gemm.hip"] + _COMMON,
     "gemm_down_residual": ["gemm.hip"] + _COMMON,
+    "moe_gemm_gate_up_swiglu": ["gemm_stream.hip"] + _COMMON,
+    "moe_gemm_down": ["gemm_stream.hip"] + _COMMON,
 }
 
 
@@ -295,7 +297,7 @@ def measured_traffic(path, kind):
         if ":" in ln and not ln.lstrip().startswith("#"):
             k, v = ln.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != source_hash(kind) or "bytes_per_launch" not in fields:
+    if kind not in KERNEL_SOURCES or fields.get("source_sha256") != source_hash(kind) or "bytes_per_launch" not in fields:
         return None
     return int(float(fields["bytes_per_launch"]))
 

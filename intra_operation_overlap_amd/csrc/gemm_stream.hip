@@ -48,7 +48,7 @@ __device__ __forceinline__ int acc_row32(int lane, int r) { return 8 * (r >> 2) 
 // MB m-blocks of 32 rows per pass, NBW packed n-blocks per wave, KC k-steps
 // per A chunk.  MODE as in GemmMode; PARTIAL writes fp32 partial slices.
 template <int MB, int NBW, int KC, int MODE, bool PARTIAL>
-__global__ __launch_bounds__(256, 2) void gemm_stream_kernel(SParams p) {
+__global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SParams p) {
   constexpr int ROWS = MB * SB;
   constexpr int PR = KC * 2;                 // 16-byte pieces of one A row in a chunk
   constexpr int CH = ROWS * PR * 16;         // bytes of one A chunk
@@ -253,23 +253,23 @@ hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStr
 // Configurations: (rows per pass, packed n-blocks per wave, k-steps per chunk)
 //   40: 32 rows,  1 block, 16    41: 64 rows, 1 block, 16
 //   42: 32 rows,  2 blocks, 16   43: 64 rows, 2 blocks, 16  (SWIGLU)
-//   44: 128 rows, 1 block, 16    45: 128 rows, 2 blocks, 8  (expert groups)
+//   44: 160 rows, 1 block, 16    45: 160 rows, 2 blocks, 16 (expert groups; one
+//   workgroup per CU, so that an expert of up to 160 rows streams its weights once)
 hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook) {
   switch (p.cfg) {
     case 40: return launch_stream<1, 1, 16>(a, p, ws, s, hook);
     case 41: return launch_stream<2, 1, 16>(a, p, ws, s, hook);
     case 42: return launch_stream<1, 2, 16>(a, p, ws, s, hook);
     case 43: return launch_stream<2, 2, 16>(a, p, ws, s, hook);
-    case 44: return launch_stream<4, 1, 16>(a, p, ws, s, hook);
-    case 45: return launch_stream<4, 2, 8>(a, p, ws, s, hook);
+    case 44: return launch_stream<5, 1, 16>(a, p, ws, s, hook);
+    case 45: return launch_stream<5, 2, 16>(a, p, ws, s, hook);
     default: return hipErrorInvalidValue;
   }
 }
 
 int stream_kc(int cfg) {
   switch (cfg) {
-    case 40: case 41: case 42: case 43: case 44: return 16;
-    case 45: return 8;
+    case 40: case 41: case 42: case 43: case 44: case 45: return 16;
     default: return 0;
   }
 }
