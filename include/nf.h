@@ -219,9 +219,10 @@ nf_status nf_layer_step(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch
  * Gurobi-based solver of the ossradar Nanoflow page.  The candidates are the unsplit plan and, for every
  * count 2..opts->max_count, equal and attention-balanced sizes, each on one
  * stream and on two streams with several (GEMM, attention) CU budgets and
- * attention residency limits.  Every candidate is timed on this batch for two
- * steps; the `top_k` fastest are timed again with `warmup` + `reps` steps and
- * the fastest of those is kept.  Runs steps on this batch (so it writes
+ * attention residency limits.  After three untimed steps of the unsplit
+ * plan, every candidate is timed on this batch for two steps; the `top_k`
+ * fastest, and the unsplit plan, are timed again with `warmup` + `reps` steps
+ * and the fastest of those is kept.  Runs steps on this batch (so it writes
  * batch->out and the batch's pool slots with the values a step writes),
  * synchronises `stream`, sets the chosen plan on the layer and returns it in
  * *out.  `times_ms`, if not NULL, receives {measured ms per step of the

@@ -420,17 +420,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 // distinct banks.  Split-K stores fp32 partials; a vectorised reduce kernel
 // applies the epilogue (a last-arriving-workgroup reduction would need
 // device-scope fences, which on a multi-XCD part write back the L2).
-template <int BM_, int BN_, int WM_, int WN_, int MS_, int ST_>
+template <int BM_, int BN_, int WM_, int WN_, int MS_, int ST_, int BK_ = 64>
 struct PCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MS = MS_, STAGES = ST_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MS = MS_, STAGES = ST_, BK = BK_;
   static constexpr int KSTEP = MS == 16 ? 32 : 16;
+  static constexpr int KS = BK / KSTEP;                  // MFMA k-steps per slab
   static constexpr int NACC = MS == 16 ? 4 : 16;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / MS, FN = WTN / MS;
-  static constexpr int A_IN = BM / 32, B_IN = BN / 32;   // DMA instructions per thread per slab
+  static constexpr int ROWB = BK * 2;                    // LDS bytes per slab row
+  static constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROWB;                // rows one DMA instruction fills
+  static constexpr int A_IN = BM / (4 * RPI), B_IN = BN / (4 * RPI);   // DMA instructions per thread per slab
   static constexpr int X = A_IN + B_IN;
-  static constexpr int SLAB = (BM + BN) * 128;           // LDS bytes per stage
-  static_assert(WM * WN == 4 && FM >= 1 && FN >= 2 && FN % 2 == 0 && A_IN >= 1 && B_IN >= 1, "cfg");
+  static constexpr int SLAB = (BM + BN) * ROWB;          // LDS bytes per stage
+  static_assert(BK == 64 || BK == 32, "slab K");
+  static_assert(WM * WN == 4 && FM >= 1 && FN >= 2 && FN % 2 == 0 && A_IN >= 1 && B_IN >= 1 && KS >= 1, "cfg");
   static_assert(STAGES >= 2 && STAGES <= 8 && (STAGES - 2) * X <= 63, "vmcnt range");
   static_assert(STAGES * SLAB <= 160 * 1024, "LDS");
 };
@@ -446,6 +451,9 @@ using P17 = PCfg<64, 256, 1, 4, 16, 3>;
 using P18 = PCfg<64, 128, 1, 4, 16, 6>;
 using P19 = PCfg<32, 128, 1, 4, 16, 6>;
 using P20 = PCfg<32, 128, 1, 4, 16, 8>;
+// 32-wide K slabs (more slabs in flight for the same LDS; measured slower
+// than P14 on the large shapes, kept as a probe configuration)
+using P21 = PCfg<256, 256, 2, 2, 32, 4, 32>;
 
 
 // wait until at most `after` slabs issued after the current one are pending
@@ -463,7 +471,16 @@ __device__ __forceinline__ void wait_slab(int after) {
   }
 }
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// XOR swizzle of a row's 16-byte chunks: the 16 rows of a fragment read land
+// on 16 distinct 16-byte bank groups (2 rows per 256-byte bank window for
+// 128-byte rows, 4 for 64-byte rows)
+template <class C>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (C::BK == 64)
+    return (row >> 1) & 7;
+  else
+    return (row >> 2) & 3;
+}
 
 
 template <class C, int MODE, bool PARTIAL>
@@ -498,22 +515,23 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // DMA sources: instruction i of this wave fills slab rows (4i + wave)*8 .. +7;
-  // lane l takes row +l/8 and physical chunk l%8 (logical chunk = l%8 ^ swz)
+  // DMA sources: instruction i of this wave fills slab rows (4i + wave) RPI ..
+  // + RPI - 1; lane l takes row + l / CPR and physical chunk l % CPR (logical
+  // chunk = physical ^ swz)
   const bf16* srcA[C::A_IN];
   const bf16* srcB[C::B_IN];
-  const int lrow = lane >> 3, pch = lane & 7;
+  const int lrow = lane / C::CPR, pch = lane % C::CPR;
 #pragma unroll
   for (int i = 0; i < C::A_IN; ++i) {
-    const int row = (4 * i + wave) * 8 + lrow;
+    const int row = (4 * i + wave) * C::RPI + lrow;
     const int local = min(m0 + row, rows - 1);            // clamp: rows past M are never stored
     int src = m_begin + local;
     if (a.a_rows) src = a.a_rows[src] / a.a_row_div;
-    srcA[i] = (const bf16*)a.A + (int64_t)src * a.lda + k_lo + 8 * (pch ^ swz(row));
+    srcA[i] = (const bf16*)a.A + (int64_t)src * a.lda + k_lo + 8 * (pch ^ swz<C>(row));
   }
 #pragma unroll
   for (int i = 0; i < C::B_IN; ++i) {
-    const int row = (4 * i + wave) * 8 + lrow;
+    const int row = (4 * i + wave) * C::RPI + lrow;
     int n;
     const bf16* base;
     if (MODE == GEMM_SWIGLU) {
@@ -525,12 +543,12 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
       base = Bbase;
     }
     n = min(n, a.N - 1);
-    srcB[i] = base + (int64_t)n * a.ldb + k_lo + 8 * (pch ^ swz(row));
+    srcB[i] = base + (int64_t)n * a.ldb + k_lo + 8 * (pch ^ swz<C>(row));
   }
   auto issue = [&](int t, int buf) {
-    const int koff = t * 64;
+    const int koff = t * C::BK;
     char* sA = smem + buf * C::SLAB;
-    char* sB = sA + C::BM * 128;
+    char* sB = sA + C::BM * C::ROWB;
 #pragma unroll
     for (int i = 0; i < C::A_IN; ++i) dma16(srcA[i] + koff, sA + (4 * i + wave) * 1024);
 #pragma unroll
@@ -554,7 +572,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
     return wn * C::WTN + j * C::MS;
   };
 
-  const int nk = (k_hi - k_lo) / 64;
+  const int nk = (k_hi - k_lo) / C::BK;
   // row fragments of this wave that hold at least one live row (wave-uniform);
   // the rest skip their fragment loads and MFMAs (ragged groups, M % BM)
   const int live = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (rows - m0 - wm * C::WTM + C::MS - 1) / C::MS)));
@@ -567,9 +585,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
     barrier_lds();
     if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
     const char* sA = smem + (kt % C::STAGES) * C::SLAB;
-    const char* sB = sA + C::BM * 128;
+    const char* sB = sA + C::BM * C::ROWB;
     // fragments of k-step s+1 are read while the MFMAs of k-step s run
-    constexpr int KS = 64 / C::KSTEP;
+    constexpr int KS = C::KS;
     bf16x8 af[2][C::FM], bfr[2][C::FN];
     auto load_frags = [&](int s, int set) {
       const int c = s * (C::KSTEP / 8) + fq;
@@ -577,12 +595,12 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
       for (int i = 0; i < C::FM; ++i) {
         if (i >= live) break;
         const int r = wm * C::WTM + i * C::MS + fr;
-        af[set][i] = *(const bf16x8*)(sA + r * 128 + ((c ^ swz(r)) << 4));
+        af[set][i] = *(const bf16x8*)(sA + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
         const int r = b_row(j) + fr;
-        bfr[set][j] = *(const bf16x8*)(sB + r * 128 + ((c ^ swz(r)) << 4));
+        bfr[set][j] = *(const bf16x8*)(sB + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
       }
     };
     load_frags(0, 0);
@@ -705,6 +723,7 @@ void tile_dims(int cfg, int& bm, int& bn) {
     case 17: bm = 64; bn = 256; return;
     case 18: bm = 64; bn = 128; return;
     case 19: case 20: bm = 32; bn = 128; return;
+    case 21: bm = 256; bn = 256; return;
     default: bm = 128; bn = 128; return;
   }
 }
@@ -844,6 +863,7 @@ hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t
     case 18: return launch_pipe<P18>(a, p, ws, s, hook);
     case 19: return launch_pipe<P19>(a, p, ws, s, hook);
     case 20: return launch_pipe<P20>(a, p, ws, s, hook);
+    case 21: return launch_pipe<P21>(a, p, ws, s, hook);
     default: return launch_cfg<Cfg0>(a, p, ws, s, hook);
   }
 }

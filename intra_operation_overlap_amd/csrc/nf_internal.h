@@ -97,8 +97,15 @@ hipError_t pack_b(const void* W, int64_t ldw, int64_t group_stride, int N, int K
 int gemm_partials(const GemmArgs& a, const GemmPlan& p);
 
 // ---------------------------------------------------------------- row ops
-hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps,
-                   hipStream_t s);
+// Copy of a step's metadata (16-byte units) from device-visible pinned host
+// memory, done by extra blocks of the first kernel of a step.
+struct MetaCopy {
+  const void* src = nullptr;
+  void* dst = nullptr;
+  int64_t n16 = 0;
+};
+hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps, hipStream_t s,
+                   const MetaCopy* mc = nullptr);
 
 struct RopeAppendArgs {
   const void* qkv;          // [T][(nq+2nkv)d]
@@ -153,10 +160,6 @@ struct RouteArgs {
 };
 hipError_t moe_route(const RouteArgs& a, hipStream_t s);
 // out[t] = x1[t] + sum_s w[t][s] * y[inv[t*k+s]]
-// Copies `bytes` (a multiple of 16) from device-visible pinned host memory
-// to device memory with a kernel on `s` (no DMA engine, so no cross-engine
-// dependency enters the stream).
-hipError_t meta_copy(const void* host_src, void* dst, size_t bytes, hipStream_t s);
 hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w,
                        const int32_t* inv, void* out, int T, int H, int k, hipStream_t s);
 

@@ -9,9 +9,20 @@ namespace {
 
 // ---------------------------------------------------------------- RMSNorm
 // y = x / sqrt(mean(x^2) + eps) * g, one 256-thread block per row, fp32 math.
+// Blocks past the last row copy the step's metadata instead (see MetaCopy).
+__device__ __forceinline__ bool meta_copy_block(const MetaCopy& mc, int rows) {
+  if ((int)blockIdx.x < rows) return false;
+  const u32x4* src = (const u32x4*)mc.src;
+  u32x4* dst = (u32x4*)mc.dst;
+  const int64_t nb = gridDim.x - rows;
+  for (int64_t i = (int64_t)(blockIdx.x - rows) * 256 + threadIdx.x; i < mc.n16; i += nb * 256) dst[i] = src[i];
+  return true;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, const T* __restrict__ g,
-                                                      T* __restrict__ y, int H, float eps) {
+                                                      T* __restrict__ y, int H, float eps, MetaCopy mc, int rows) {
+  if (meta_copy_block(mc, rows)) return;
   const int64_t row = blockIdx.x;
   const T* xr = x + row * H;
   T* yr = y + row * H;
@@ -33,7 +44,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
 // bf16 rows, 8 elements (16 bytes) per access; requires H % 8 == 0.
 __global__ __launch_bounds__(256) void rmsnorm_bf16x8_kernel(const bf16* __restrict__ x,
                                                              const bf16* __restrict__ g,
-                                                             bf16* __restrict__ y, int H, float eps) {
+                                                             bf16* __restrict__ y, int H, float eps, MetaCopy mc,
+                                                             int rows) {
+  if (meta_copy_block(mc, rows)) return;
   const int64_t row = blockIdx.x;
   const bf16x8* xr = (const bf16x8*)(x + row * H);
   const bf16x8* gr = (const bf16x8*)g;
@@ -256,23 +269,21 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const T* __restrict__ 
   }
 }
 
-// ---------------------------------------------------------------- metadata
-__global__ __launch_bounds__(256) void meta_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                        int64_t n16) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) dst[i] = src[i];
-}
-
 }  // namespace
 
-hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps,
-                   hipStream_t s) {
+hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps, hipStream_t s,
+                   const MetaCopy* mc) {
   if (T == 0) return hipSuccess;
+  MetaCopy m;
+  if (mc) m = *mc;
+  const int extra = m.n16 > 0 ? (int)std::min<int64_t>((m.n16 + 255) / 256, 64) : 0;
+  const int grid = T + extra;
   if (dtype == 1 && H % 8 == 0)
-    launch(rmsnorm_bf16x8_kernel, T, 256, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps);
+    launch(rmsnorm_bf16x8_kernel, grid, 256, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps, m, T);
   else if (dtype == 1)
-    launch(rmsnorm_kernel<bf16>, T, 256, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps);
+    launch(rmsnorm_kernel<bf16>, grid, 256, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps, m, T);
   else
-    launch(rmsnorm_kernel<float>, T, 256, 0, s, (const float*)x, (const float*)g, (float*)y, H, eps);
+    launch(rmsnorm_kernel<float>, grid, 256, 0, s, (const float*)x, (const float*)g, (float*)y, H, eps, m, T);
   return hipGetLastError();
 }
 
@@ -314,12 +325,5 @@ hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w
   return hipGetLastError();
 }
 
-hipError_t meta_copy(const void* host_src, void* dst, size_t bytes, hipStream_t s) {
-  const int64_t n16 = (int64_t)(bytes / 16);
-  if (n16 == 0) return hipSuccess;
-  const int blocks = (int)std::min<int64_t>((n16 + 255) / 256, 256);
-  launch(meta_copy_kernel, blocks, 256, 0, s, (const u32x4*)host_src, (u32x4*)dst, n16);
-  return hipGetLastError();
-}
 
 }  // namespace nf
