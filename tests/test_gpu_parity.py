@@ -293,6 +293,31 @@ def test_small_moe_full_parity():
             t0 += n
 
 
+SKEWED_MOE = W.Workload("skewed_moe",
+                        W.Shape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=384, n_experts=8,
+                                top_k=2, dtype="bf16", rope_theta=1e6),
+                        n_decode=200, ctx_range=(1, 64), prefill=(10, 30), seed=83)
+
+
+def test_skewed_moe_routing_multi_pass_and_empty_expert():
+    """Router logits biased so that one expert receives every token (230
+    rows: more than one 160-row pass of the expert GEMMs) and another expert
+    none (an empty group), under one and two nano-batches."""
+    S = GH.setup(SKEWED_MOE)
+    logits = S.acts["router_logits"]
+    logits[:, 3] += 8.0
+    logits[:, 5] -= 8.0
+    torch.cuda.synchronize()
+    T = S.batch.n_tokens
+    assert T > 160
+    for name, plan in (("k1", B.make_plan(1, [T])), ("k2", B.make_plan(2, [T // 2, T - T // 2]))):
+        _full_check(S, name, plan)
+        t0 = 0
+        for j, n in enumerate(list(plan.sizes)[:plan.count]):
+            _route_check(S, t0, t0 + n, j)
+            t0 += n
+
+
 @pytest.mark.slow
 def test_c5_full_size_sampled():
     S = GH.setup(W.WORKLOADS["c5"])
