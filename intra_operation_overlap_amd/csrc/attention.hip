@@ -165,6 +165,41 @@ __device__ __forceinline__ void page_step(const bf16x8 (&qf)[4], PageRegs& r, in
   }
 }
 
+// Walks n pages of request `req` (logical pages first, first + stride, ...)
+// with the next page's K and V in flight while the current one feeds the
+// matrix cores.  The pool page numbers of up to 64 pages are fetched at once,
+// one per lane, and read back with readlane: a page-table load issued behind
+// the K/V loads would otherwise make every next-page address wait for them.
+__device__ __forceinline__ void walk_pages(const AttnArgs& a, int req, int first, int stride, int n, int kh,
+                                           int lane, int grp, const bf16x8 (&qf)[4], int limit, int max_limit,
+                                           float sl2, RowState& st) {
+  const int32_t* ptab = a.page_indices + a.page_indptr[req];
+  const bf16* kpool = (const bf16*)a.k_pool;
+  const bf16* vpool = (const bf16*)a.v_pool;
+  PageRegs r[2];
+  for (int cb = 0; cb < n; cb += 64) {
+    const int cn = min(64, n - cb);
+    const int mine = lane < cn ? ptab[first + stride * (cb + lane)] : 0;
+    auto load = [&](int j, int set) {
+      const int64_t blk = (int64_t)__builtin_amdgcn_readlane(mine, j) * a.nkv + kh;
+      load_page(kpool + blk * BLOCK, vpool + blk * BLOCK, lane, r[set]);
+    };
+    auto step = [&](int j, int set) {
+      const int lp = first + stride * (cb + j);
+      page_step(qf, r[set], lp * 16 + 4 * grp, limit, max_limit, lp * 16 + 16 > max_limit, sl2, st);
+    };
+    int j = 0;
+    load(0, 0);
+    for (; j + 1 < cn; j += 2) {
+      load(j + 1, 1);
+      step(j, 0);
+      if (j + 2 < cn) load(j + 2, 0);
+      step(j + 1, 1);
+    }
+    if (j < cn) step(j, 0);
+  }
+}
+
 __device__ __forceinline__ void load_q(const AttnArgs& a, int64_t qoff, int grp, bf16x8 (&qf)[4]) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -201,13 +236,10 @@ __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(AttnArgs a) {
 #pragma unroll
   for (int b = 0; b < 8; ++b) st.o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* ptab = a.page_indices + a.page_indptr[it.req];
-  for (int lp = it.page_begin + wave; lp < it.page_end; lp += 4) {
-    const int64_t blk = (int64_t)ptab[lp] * a.nkv + kh;
-    PageRegs r;
-    load_page((const bf16*)a.k_pool + blk * BLOCK, (const bf16*)a.v_pool + blk * BLOCK, lane, r);
-    page_step(qf, r, lp * 16 + 4 * grp, limit, max_limit, lp * 16 + 16 > max_limit, sl2, st);
-  }
+  // this wave's pages: page_begin + wave, + 4, ...
+  const int first = it.page_begin + wave;
+  const int n = first < it.page_end ? (it.page_end - first + 3) / 4 : 0;
+  walk_pages(a, it.req, first, 4, n, kh, lane, grp, qf, limit, max_limit, sl2, st);
 
   // this wave's (m, l, O^T) -> LDS; O^T lane layout: dim 16b + 4*grp + i, row col
   st.l += __shfl_xor(st.l, 16, 64);
@@ -247,27 +279,8 @@ __device__ __forceinline__ void wave_item(const AttnArgs& a, const AttnItem& it,
 #pragma unroll
   for (int b = 0; b < 8; ++b) st.o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* ptab = a.page_indices + a.page_indptr[it.req];
-  const bf16* kpool = (const bf16*)a.k_pool;
-  const bf16* vpool = (const bf16*)a.v_pool;
-  PageRegs r[2];
-  auto load = [&](int lp, int set) {
-    const int64_t blk = (int64_t)ptab[lp] * a.nkv + kh;
-    load_page(kpool + blk * BLOCK, vpool + blk * BLOCK, lane, r[set]);
-  };
-  auto step = [&](int lp, int set) {
-    page_step(qf, r[set], lp * 16 + 4 * grp, limit, max_limit, lp * 16 + 16 > max_limit, sl2, st);
-  };
-  const int b0 = it.page_begin, n = it.page_end - it.page_begin;
-  int i = 0;
-  if (n > 0) load(b0, 0);
-  for (; i + 1 < n; i += 2) {
-    load(b0 + i + 1, 1);
-    step(b0 + i, 0);
-    if (i + 2 < n) load(b0 + i + 2, 0);
-    step(b0 + i + 1, 1);
-  }
-  if (i < n) step(b0 + i, 0);
+  walk_pages(a, it.req, it.page_begin, 1, it.page_end - it.page_begin, kh, lane, grp, qf, limit, max_limit, sl2,
+             st);
 
   // row totals: sum the four lane groups that share a column
   st.l += __shfl_xor(st.l, 16, 64);
