@@ -87,7 +87,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--plan", default="auto", help="auto (workload default / search) or k1")
+    ap.add_argument("--plan", default="auto",
+                    help="auto (workload default / search), k1 (unsplit), overlap2 (two nano-batches on two "
+                         "streams), or overlap2:G:A (the same with G GEMM and A attention CUs per XCD)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None, help="text file with the rocprofv3 FETCH/WRITE bytes per launch")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -145,7 +147,12 @@ def main():
         return e0.elapsed_time(e1) / n
 
     comparisons = {}
-    if args.plan == "k1" or wl.plan_sizes == (T,):
+    if args.plan.startswith("overlap2"):
+        parts = args.plan.split(":")
+        g, a = (int(parts[1]), int(parts[2])) if len(parts) == 3 else (0, 0)
+        plan = B.make_plan(2, [T - T // 2, T // 2], n_streams=2, gemm_cus_per_xcd=g, attn_cus_per_xcd=a)
+        layer.set_plan(plan)
+    elif args.plan == "k1" or wl.plan_sizes == (T,):
         plan = B.make_plan(1, [T])
         layer.set_plan(plan)
     elif wl.plan_sizes is not None:
