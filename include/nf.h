@@ -56,7 +56,10 @@ typedef enum nf_dtype { NF_F32 = 0, NF_BF16 = 1 } nf_dtype;
 /* Layer shape.  Requirements: n_q_heads % n_kv_heads == 0 with at most 16
  * query heads per KV head; head_dim a multiple of 32, <= 256 (bf16 layers:
  * head_dim == 128); hidden and ffn multiples of 8; top_k <= n_experts <= 64,
- * top_k <= 8; max_tokens >= 1; max_pos >= 1. */
+ * top_k <= 8; max_tokens >= 1; max_pos >= 1.  bf16 layers: every GEMM
+ * operand (max_tokens * top_k rows of the widest activation, and each weight
+ * matrix) stays under 4 GiB, since the GEMMs address operands with 32-bit byte
+ * offsets (NF_ERR_OUT_OF_RANGE otherwise). */
 typedef struct nf_shape {
   int32_t hidden;       /* H */
   int32_t n_q_heads;    /* nq */
@@ -267,13 +270,33 @@ nf_status nf_probe_mfma_bf16_tflops(double* tflops);
 nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps);
 /* Average time (ms) of the layer's bf16 GEMM kernel on an M x N x K problem
  * (C = A B^T, mode 0 plain, 1 residual, 2 SwiGLU with N act columns), on
- * library-allocated constant-filled buffers.  tile_cfg < 0 and k_splits <= 0
+ * library-allocated buffers filled with pseudo-random values (A uniform in
+ * [-1, 1), B with standard deviation 0.02).  tile_cfg < 0 and k_splits <= 0
  * let the library choose for a stream that may use `cus` CUs; out_cfg and
- * out_splits (may be NULL) return what ran. */
+ * out_splits (may be NULL) return what ran.  max(M, N) * K * 2 bytes must stay
+ * under 4 GiB (NF_ERR_OUT_OF_RANGE). */
 nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int32_t mode, int32_t tile_cfg,
                                 int32_t k_splits, int32_t cus, int32_t reps, double* ms,
                                 int32_t* out_cfg, int32_t* out_splits);
 nf_status nf_probe_cu_map(int32_t* xcc, int32_t n);
+
+/* ---- one GEMM ------------------------------------------------------------------
+ * One bf16 GEMM exactly as the layer runs its projections, on caller device
+ * buffers, for verification and tuning (not the layer's hot path):
+ *   mode 0: C = A B^T;  mode 1: C = A B^T + R;  mode 2: C = silu(A B^T) * (A B2^T)
+ * with A [M][K] (row stride lda), B and B2 [N][K] (ldb), R and C [M][N] (ldr,
+ * ldc), strides in elements, fp32 accumulation, one bf16 rounding of C.
+ * tile_cfg < 0 and k_splits <= 0 let the library choose for a stream that
+ * may use `cus` CUs (cus <= 0: all); a given tile_cfg must be one of the
+ * layer's LDS-tiled configurations (0..6, or 10..29 with K % 64 == 0).  The
+ * split-K workspace is allocated and freed inside, and the call returns after
+ * the GEMM finished on `stream` (NULL: the null stream).  out_cfg and
+ * out_splits (may be NULL) return what ran.  Operands must stay under 4 GiB
+ * (NF_ERR_OUT_OF_RANGE); NF_ERR_INVALID_ARG for other bad arguments. */
+nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode, const void* A, int64_t lda,
+                       const void* B, const void* B2, int64_t ldb, const void* R, int64_t ldr, void* C,
+                       int64_t ldc, int32_t tile_cfg, int32_t k_splits, int32_t cus, void* stream,
+                       int32_t* out_cfg, int32_t* out_splits);
 
 /* ---- errors ---------------------------------------------------------------- */
 const char* nf_last_error(void);

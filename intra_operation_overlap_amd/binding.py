@@ -78,6 +78,8 @@ _SIGS = {
     "nf_probe_cu_map": (i32, [P_i32, i32]),
     "nf_probe_gemm_bf16_ms": (i32, [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double),
                                     P_i32, P_i32]),
+    "nf_gemm_bf16": (i32, [i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, vp,
+                           P_i32, P_i32]),
     "nf_last_error": (ctypes.c_char_p, []),
     "nf_status_string": (ctypes.c_char_p, [i32]),
 }
@@ -274,6 +276,14 @@ def probe_gemm_bf16_ms(M, N, K, mode=0, tile_cfg=-1, k_splits=0, cus=256, reps=2
     check(lib().nf_probe_gemm_bf16_ms(M, N, K, mode, tile_cfg, k_splits, cus, reps, ctypes.byref(v),
                                       ctypes.byref(c), ctypes.byref(s)), "nf_probe_gemm_bf16_ms")
     return v.value, c.value, s.value
+
+
+def gemm_bf16(M, N, K, mode, A, lda, B, B2, ldb, R, ldr, C, ldc, tile_cfg=-1, k_splits=0, cus=0, stream=None):
+    """One layer GEMM on caller device pointers; returns (cfg, splits) that ran."""
+    c, s = i32(), i32()
+    check(lib().nf_gemm_bf16(M, N, K, mode, A, lda, B, B2, ldb, R, ldr, C, ldc, tile_cfg, k_splits, cus, stream,
+                             ctypes.byref(c), ctypes.byref(s)), "nf_gemm_bf16")
+    return c.value, s.value
 
 
 # device-to-device copy of raw library memory into a torch tensor (plumbing)

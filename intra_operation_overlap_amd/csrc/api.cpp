@@ -1211,19 +1211,55 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
   return NF_OK;
 }
 
+extern "C" nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode, const void* A, int64_t lda,
+                                  const void* Bw, const void* B2, int64_t ldb, const void* R, int64_t ldr, void* C,
+                                  int64_t ldc, int32_t tile_cfg, int32_t k_splits, int32_t cus, void* stream,
+                                  int32_t* out_cfg, int32_t* out_splits) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 8 || N % 8 || mode < 0 || mode > 2 || !A || !Bw || !C ||
+      (mode == GEMM_RESIDUAL && !R) || (mode == GEMM_SWIGLU && !B2) || lda < K || ldb < K || ldc < N ||
+      (mode == GEMM_RESIDUAL && ldr < N))
+    return set_err(NF_ERR_INVALID_ARG, "nf_gemm_bf16: bad argument");
+  if (tile_cfg >= 0 && !((tile_cfg <= 6) || (tile_cfg >= 10 && tile_cfg <= 29 && K % 64 == 0)))
+    return set_err(NF_ERR_INVALID_ARG, "nf_gemm_bf16: tile_cfg %d not available for K %d", tile_cfg, K);
+  if ((int64_t)M * lda * 2 >= (int64_t(1) << 32) || (int64_t)N * ldb * 2 >= (int64_t(1) << 32))
+    return set_err(NF_ERR_OUT_OF_RANGE, "nf_gemm_bf16: an operand would exceed 4 GiB");
+  GemmArgs g;
+  g.A = A; g.lda = lda;
+  g.B = Bw; g.B2 = B2; g.ldb = ldb;
+  g.C = C; g.ldc = ldc; g.R = R; g.ldr = ldr;
+  g.M = M; g.N = N; g.K = K; g.mode = mode;
+  GemmPlan p = gemm_choose(g, cus > 0 ? cus : 256);
+  if (tile_cfg >= 0) p.cfg = tile_cfg;
+  if (k_splits > 0) p.k_splits = k_splits;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  const size_t wsb = gemm_workspace_bytes(g, p);
+  if (wsb) HIP_TRY(hipMalloc(&ws, wsb));
+  hipError_t e = gemm_bf16(g, p, ws, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (ws) (void)hipFree(ws);
+  if (e != hipSuccess) return set_err(NF_ERR_HIP, "nf_gemm_bf16: %s", hipGetErrorString(e));
+  if (out_cfg) *out_cfg = p.cfg;
+  if (out_splits) *out_splits = p.k_splits;
+  return NF_OK;
+}
+
 extern "C" nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int32_t mode, int32_t tile_cfg,
                                            int32_t k_splits, int32_t cus, int32_t reps, double* ms,
                                            int32_t* out_cfg, int32_t* out_splits) {
   if (!ms || M <= 0 || N <= 0 || K <= 0 || K % 8 || mode < 0 || mode > 2 || reps <= 0)
     return set_err(NF_ERR_INVALID_ARG, "nf_probe_gemm_bf16_ms: bad argument");
+  if ((int64_t)std::max(M, N) * K * 2 >= (int64_t(1) << 32))
+    return set_err(NF_ERR_OUT_OF_RANGE, "nf_probe_gemm_bf16_ms: an operand would exceed 4 GiB");
   const int64_t nb = mode == GEMM_SWIGLU ? 2 : 1;
   void *A = nullptr, *Bm = nullptr, *C = nullptr, *R = nullptr;
   HIP_TRY(hipMalloc(&A, (size_t)M * K * 2));
   HIP_TRY(hipMalloc(&Bm, (size_t)nb * N * K * 2));
   HIP_TRY(hipMalloc(&C, (size_t)M * N * 2));
   HIP_TRY(hipMalloc(&R, (size_t)M * N * 2));
-  HIP_TRY(hipMemset(A, 0x3c, (size_t)M * K * 2));       // small finite bf16 values
-  HIP_TRY(hipMemset(Bm, 0x3c, (size_t)nb * N * K * 2));
+  // activations ~ unit scale, weights uniform with standard deviation 0.02
+  HIP_TRY(probe_fill_bf16(A, (int64_t)M * K, 1u, 1.0f, nullptr));
+  HIP_TRY(probe_fill_bf16(Bm, nb * N * K, 2u, 0.0346f, nullptr));
   HIP_TRY(hipMemset(R, 0, (size_t)M * N * 2));
   GemmArgs g;
   g.A = A; g.lda = K;

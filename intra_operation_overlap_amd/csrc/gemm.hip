@@ -2,19 +2,22 @@
 //
 // C[M][N] = epilogue(A[M][K] . B[N][K]^T) with both operands K-contiguous
 // (activations row-major, weights stored output-feature-major), fp32
-// accumulation in v_mfma_f32_16x16x32_bf16.  One 256-thread workgroup (four
-// wave64s) owns a BM x BN output tile; K is walked in 64-wide slabs staged
-// through LDS, double-buffered, with the next slab's global loads in flight
-// while the current slab feeds the matrix cores.  Epilogues fuse the layer's
-// elementwise work into the producing GEMM: residual add (O and down
-// projections), SwiGLU (gate and up rows of one tile come from the two weight
-// matrices so each output column gets both dot products in registers), fp32
-// output for the expert path.  Small-M problems (decode-heavy nano-batches)
-// use split-K with fp32 partials and a reduce kernel that applies the same
-// epilogue.  Workgroups are mapped to tiles XCD-aware: the dispatcher deals
-// workgroups round-robin over the 8 XCDs, so each XCD is handed a contiguous
-// range of tiles (M fastest) and the weight rows of one N tile stay in one
-// XCD's L2.
+// accumulation in v_mfma_f32_32x32x16_bf16 (large tiles) or
+// v_mfma_f32_16x16x32_bf16 (decode-sized tiles).  One 256-thread workgroup
+// (four wave64s) owns a BM x BN output tile; K is walked in slabs that the
+// buffer unit writes straight into LDS (buffer_load ... lds), several slabs
+// in flight, while the current slab feeds the matrix cores.  Epilogues fuse
+// the layer's elementwise work into the producing GEMM: residual add (O and
+// down projections), SwiGLU (gate and up rows of one tile come from the two
+// weight matrices so each output column gets both dot products in
+// registers), fp32 output for the expert path.  Small-M problems
+// (decode-heavy nano-batches) use split-K with fp32 partials and a reduce
+// kernel that applies the same epilogue.  Workgroups are mapped to tiles
+// XCD-aware: the dispatcher deals workgroups round-robin over the 8 XCDs, so
+// each XCD is handed a contiguous range of tiles (M fastest) and the weight
+// rows of one N tile stay in one XCD's L2.
+#include <type_traits>
+
 #include "nf_device.h"
 #include "nf_internal.h"
 
@@ -77,6 +80,7 @@ struct KParams {
   int k_per;                        // K per split (multiple of BK)
   float* part;                      // split-K partials
   int64_t part_ld;                  // row stride of partials
+  int vec_epi = 0;                  // C (and R) rows 16-byte aligned, N % 8 == 0
 };
 
 
@@ -436,7 +440,7 @@ struct PCfg {
   static constexpr int SLAB = (BM + BN) * ROWB;          // LDS bytes per stage
   static_assert(BK == 64 || BK == 32, "slab K");
   static_assert(WM * WN == 4 && FM >= 1 && FN >= 2 && FN % 2 == 0 && A_IN >= 1 && B_IN >= 1 && KS >= 1, "cfg");
-  static_assert(STAGES >= 2 && STAGES <= 8 && (STAGES - 2) * X <= 63, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 10 && (STAGES - 2) * X <= 63, "vmcnt range");
   static_assert(STAGES * SLAB <= 160 * 1024, "LDS");
 };
 
@@ -454,6 +458,14 @@ using P20 = PCfg<32, 128, 1, 4, 16, 8>;
 // 32-wide K slabs (more slabs in flight for the same LDS; measured slower
 // than P14 on the large shapes, kept as a probe configuration)
 using P21 = PCfg<256, 256, 2, 2, 32, 4, 32>;
+using P22 = PCfg<128, 128, 2, 2, 32, 4, 32>;
+using P23 = PCfg<128, 128, 2, 2, 32, 5, 32>;
+using P24 = PCfg<256, 128, 2, 2, 32, 4, 32>;
+using P25 = PCfg<128, 256, 2, 2, 32, 4, 32>;
+using P26 = PCfg<256, 256, 2, 2, 32, 3, 32>;
+using P27 = PCfg<256, 256, 2, 2, 32, 5, 32>;
+using P28 = PCfg<256, 128, 2, 2, 32, 5, 32>;
+using P29 = PCfg<128, 128, 2, 2, 32, 9, 32>;
 
 
 // wait until at most `after` slabs issued after the current one are pending
@@ -512,14 +524,19 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
     Bbase += (int64_t)z * a.b_group_stride;
     if (B2base) B2base += (int64_t)z * a.b_group_stride;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
 
   // DMA sources: instruction i of this wave fills slab rows (4i + wave) RPI ..
   // + RPI - 1; lane l takes row + l / CPR and physical chunk l % CPR (logical
-  // chunk = physical ^ swz)
-  const bf16* srcA[C::A_IN];
-  const bf16* srcB[C::B_IN];
+  // chunk = physical ^ swz).  Byte offsets from the operand's base (32-bit:
+  // the shape check keeps every operand under 4 GiB); the slab's K offset is
+  // the scalar offset of each load.
+  const __amdgpu_buffer_rsrc_t rA = buf_rsrc(a.A);
+  const __amdgpu_buffer_rsrc_t rB = buf_rsrc(Bbase);
+  const __amdgpu_buffer_rsrc_t rB2 = buf_rsrc(MODE == GEMM_SWIGLU ? B2base : Bbase);
+  uint32_t offA[C::A_IN], offB[C::B_IN];
   const int lrow = lane / C::CPR, pch = lane % C::CPR;
 #pragma unroll
   for (int i = 0; i < C::A_IN; ++i) {
@@ -527,32 +544,33 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
     const int local = min(m0 + row, rows - 1);            // clamp: rows past M are never stored
     int src = m_begin + local;
     if (a.a_rows) src = a.a_rows[src] / a.a_row_div;
-    srcA[i] = (const bf16*)a.A + (int64_t)src * a.lda + k_lo + 8 * (pch ^ swz<C>(row));
+    offA[i] = (uint32_t)(((int64_t)src * a.lda + k_lo + 8 * (pch ^ swz<C>(row))) * 2);
   }
 #pragma unroll
   for (int i = 0; i < C::B_IN; ++i) {
     const int row = (4 * i + wave) * C::RPI + lrow;
     int n;
-    const bf16* base;
     if (MODE == GEMM_SWIGLU) {
+      // an instruction's RPI rows lie in one half (gate rows, then up rows)
       constexpr int half = C::BN / 2;
       n = n_tile * half + (row < half ? row : row - half);
-      base = row < half ? Bbase : B2base;
     } else {
       n = n_tile * C::BN + row;
-      base = Bbase;
     }
     n = min(n, a.N - 1);
-    srcB[i] = base + (int64_t)n * a.ldb + k_lo + 8 * (pch ^ swz<C>(row));
+    offB[i] = (uint32_t)(((int64_t)n * a.ldb + k_lo + 8 * (pch ^ swz<C>(row))) * 2);
   }
   auto issue = [&](int t, int buf) {
-    const int koff = t * C::BK;
+    const uint32_t koff = (uint32_t)(t * C::BK * 2);
     char* sA = smem + buf * C::SLAB;
     char* sB = sA + C::BM * C::ROWB;
 #pragma unroll
-    for (int i = 0; i < C::A_IN; ++i) dma16(srcA[i] + koff, sA + (4 * i + wave) * 1024);
+    for (int i = 0; i < C::A_IN; ++i) dma16_buf(rA, offA[i], koff, sA + (4 * i + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < C::B_IN; ++i) dma16(srcB[i] + koff, sB + (4 * i + wave) * 1024);
+    for (int i = 0; i < C::B_IN; ++i) {
+      const bool up = MODE == GEMM_SWIGLU && (4 * i + wave) * C::RPI >= C::BN / 2;   // wave-uniform
+      dma16_buf(up ? rB2 : rB, offB[i], koff, sB + (4 * i + wave) * 1024);
+    }
   };
 
   typedef typename Acc<C::MS>::T AccT;
@@ -580,46 +598,136 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
   for (int t = 0; t < C::STAGES - 1; ++t)
     if (t < nk) issue(t, t);
   const int fr = lane % C::MS, fq = lane / C::MS;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_slab<C>(min(C::STAGES - 2, nk - 1 - kt));
-    barrier_lds();
-    if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
-    const char* sA = smem + (kt % C::STAGES) * C::SLAB;
-    const char* sB = sA + C::BM * C::ROWB;
-    // fragments of k-step s+1 are read while the MFMAs of k-step s run
-    constexpr int KS = C::KS;
-    bf16x8 af[2][C::FM], bfr[2][C::FN];
-    auto load_frags = [&](int s, int set) {
-      const int c = s * (C::KSTEP / 8) + fq;
+  // The k loop is instantiated twice: without the live-row checks when every
+  // row fragment of the wave is live (straight-line code, so the LDS reads of
+  // k-step s+1 are waited on only where the MFMAs of s+1 need them), and with
+  // them for the ragged tiles.
+  auto k_loop = [&](auto checked) {
+    constexpr bool CHECK = decltype(checked)::value;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_slab<C>(min(C::STAGES - 2, nk - 1 - kt));
+      barrier_lds();
+      if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
+      const char* sA = smem + (kt % C::STAGES) * C::SLAB;
+      const char* sB = sA + C::BM * C::ROWB;
+      // fragments of k-step s+1 are read while the MFMAs of k-step s run
+      constexpr int KS = C::KS;
+      bf16x8 af[2][C::FM], bfr[2][C::FN];
+      auto load_frags = [&](int s, int set) {
+        const int c = s * (C::KSTEP / 8) + fq;
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        if (i >= live) break;
-        const int r = wm * C::WTM + i * C::MS + fr;
-        af[set][i] = *(const bf16x8*)(sA + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
+        for (int i = 0; i < C::FM; ++i) {
+          if (CHECK && i >= live) break;
+          const int r = wm * C::WTM + i * C::MS + fr;
+          af[set][i] = *(const bf16x8*)(sA + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const int r = b_row(j) + fr;
+          bfr[set][j] = *(const bf16x8*)(sB + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
+        }
+      };
+      load_frags(0, 0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) load_frags(s + 1, (s + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          if (CHECK && i >= live) break;
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma<C::MS>(af[s & 1][i], bfr[s & 1][j], acc[i][j]);
+        }
       }
+      if constexpr (!CHECK) {
+        // issue order in the slab: reads of k-steps 0 and 1, then for each
+        // k-step s its MFMAs followed by the reads of step s + 2
+        constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
+        __builtin_amdgcn_sched_group_barrier(0x100, KS > 1 ? 2 * NR : NR, 0);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int r = b_row(j) + fr;
-        bfr[set][j] = *(const bf16x8*)(sB + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
-      }
-    };
-    load_frags(0, 0);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) load_frags(s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        if (i >= live) break;
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma<C::MS>(af[s & 1][i], bfr[s & 1][j], acc[i][j]);
+        for (int s = 0; s < KS; ++s) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+          if (s + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+        }
       }
     }
-  }
+  };
+  if (live == C::FM)
+    k_loop(std::false_type{});
+  else
+    k_loop(std::true_type{});
 
   const int ec = lane % C::MS;
   constexpr int NJ = (MODE == GEMM_SWIGLU) ? C::FN / 2 : C::FN;
   constexpr int BNO = (MODE == GEMM_SWIGLU) ? C::BN / 2 : C::BN;    // output columns per tile
   const int n0 = n_tile * BNO;
+
+  if constexpr (!PARTIAL && MODE != GEMM_F32OUT) {
+    if (p.vec_epi) {
+      // The tile leaves through LDS: waves write their accumulators (after
+      // SwiGLU, rounded to bf16; fp32 for the residual add so it rounds
+      // once), then every thread moves 16-byte row chunks to C, adding 16
+      // bytes of R for the residual.  Rows are padded so the rows 4 apart
+      // that one accumulator write covers fall on different banks.
+      constexpr bool F32S = MODE == GEMM_RESIDUAL;
+      constexpr int ES = F32S ? 4 : 2;
+      constexpr int ROWB_O = BNO * ES + (F32S ? 32 : 16);
+      constexpr int FIT = (C::STAGES * C::SLAB) / ROWB_O;
+      constexpr int RP = FIT >= C::BM ? C::BM : FIT >= 128 ? 128 : FIT >= 64 ? 64 : 32;   // rows per pass
+      static_assert(FIT >= 32 && C::BM % RP == 0, "staging");
+      constexpr int CH = BNO / 8;                          // 16-byte output chunks per row
+#pragma unroll
+      for (int pass = 0; pass < C::BM / RP; ++pass) {
+        __syncthreads();                                   // LDS free (slabs, or the previous pass)
+        const int r_lo = pass * RP;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          // wave-uniform: this fragment row block lies in the pass or not
+          const int blk = wm * C::WTM + i * C::MS;
+          if (blk + C::MS <= r_lo || blk >= r_lo + RP) continue;
+#pragma unroll
+          for (int r = 0; r < C::NACC; ++r) {
+            const int rt = blk + acc_row<C::MS>(lane, r) - r_lo;
+            char* row = smem + rt * ROWB_O;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              if (MODE == GEMM_SWIGLU) {
+                const int ct = wn * (C::WTN / 2) + j * C::MS + ec;
+                const float g = acc[i][j][r], u = acc[i][j + C::FN / 2][r];
+                *(bf16*)(row + ct * 2) = (bf16)(silu_f(g) * u);
+              } else if (F32S) {
+                *(float*)(row + (wn * C::WTN + j * C::MS + ec) * 4) = acc[i][j][r];
+              } else {
+                *(bf16*)(row + (wn * C::WTN + j * C::MS + ec) * 2) = (bf16)acc[i][j][r];
+              }
+            }
+          }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < RP * CH; idx += 256) {
+          const int rr = idx / CH, ch = idx % CH;
+          const int local = m0 + r_lo + rr;
+          const int col = n0 + ch * 8;
+          if (local >= rows || col >= a.N) continue;
+          const int64_t orow = m_begin + local;
+          bf16x8 out;
+          if constexpr (F32S) {
+            const f32x4 v0 = *(const f32x4*)(smem + rr * ROWB_O + ch * 32);
+            const f32x4 v1 = *(const f32x4*)(smem + rr * ROWB_O + ch * 32 + 16);
+            const bf16x8 res = *(const bf16x8*)((const bf16*)a.R + orow * a.ldr + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              out[e] = (bf16)(v0[e] + (float)res[e]);
+              out[e + 4] = (bf16)(v1[e] + (float)res[e + 4]);
+            }
+          } else {
+            out = *(const bf16x8*)(smem + rr * ROWB_O + ch * 16);
+          }
+          *(bf16x8*)((bf16*)a.C + orow * a.ldc + col) = out;
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
@@ -683,6 +791,9 @@ hipError_t launch_pipe(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStrea
   }
   const int total = p.m_tiles * p.n_tiles * p.z_count;
   if (total == 0) return hipSuccess;
+  auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+  p.vec_epi = a.N % 8 == 0 && a.ldc % 8 == 0 && al16(a.C) &&
+              (a.mode != GEMM_RESIDUAL || (a.ldr % 8 == 0 && al16(a.R)));
   if (split && p.z_count > 1) {
     if (a.mode == GEMM_SWIGLU)
       launch(gemm_pipe_kernel<C, GEMM_SWIGLU, true>, total, 256, 0, s, p);
@@ -724,6 +835,12 @@ void tile_dims(int cfg, int& bm, int& bn) {
     case 18: bm = 64; bn = 128; return;
     case 19: case 20: bm = 32; bn = 128; return;
     case 21: bm = 256; bn = 256; return;
+    case 22: case 23: bm = 128; bn = 128; return;
+    case 24: bm = 256; bn = 128; return;
+    case 25: bm = 128; bn = 256; return;
+    case 26: case 27: bm = 256; bn = 256; return;
+    case 28: bm = 256; bn = 128; return;
+    case 29: bm = 128; bn = 128; return;
     default: bm = 128; bn = 128; return;
   }
 }
@@ -733,9 +850,12 @@ int n_tiles_of(const GemmArgs& a, int bn) {
 }
 }  // namespace
 
-// Tile choice (from sweeps on MI355X).  K % 64 == 0 problems use the
-// pipelined kernel: decode-sized M streams weights with 32- or 64-row tiles;
-// larger M uses 128 x 128 tiles, two workgroups per CU.  When the tiles
+// Tile choice (from sweeps on MI355X, timed inside the layer step: a GEMM
+// timed back to back on its own runs up to 20% faster than between the
+// step's other kernels, and ranks the tiles differently).  K % 64 == 0
+// problems use the pipelined kernel: decode-sized M streams weights with 32-
+// or 64-row tiles; larger M uses 128 x 128 tiles, two workgroups per CU, or
+// 256 x 256 tiles (one per CU) when there are enough of them.  When the tiles
 // cannot give every CU about two workgroups, K is split (up to 8 ways for
 // weight streaming, 4 otherwise, keeping >= 512 of K per piece) and a reduce
 // kernel applies the epilogue.
@@ -798,6 +918,32 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
     p.cfg = pipe ? (M <= 32 ? 16 : 15) : (M <= 32 ? 3 : 1);
   else
     p.cfg = pipe ? 14 : 0;
+  // 256 x 256 tiles halve the operand traffic per FLOP of 128 x 128 ones
+  // but run one workgroup per CU.  Timed inside the layer step (1024- and
+  // 2048-token batches of the Llama-3-8B and Llama-2-70B-shard layers) they
+  // win once there are about 0.75 of them per CU with K >= 2048, and, for
+  // K >= 8192, when split-K brings them there with >= 2048 of K per piece
+  // (shorter K, or fewer tiles: 128 x 128 tiles, whose split partials the
+  // consumers reduce more cheaply)
+  if (p.cfg == 14 && a.K >= 2048) {
+    const int64_t t256 = (int64_t)((M + 255) / 256) * n_tiles_of(a, 256);
+    const int64_t enough = (3 * (int64_t)cus + 3) / 4;
+    int ks = 0;
+    if (t256 >= enough) {
+      ks = 1;
+    } else if (a.K >= 8192) {
+      for (int k = 2; k <= 8 && a.K / k >= 2048; k *= 2)
+        if (t256 * k >= enough) {
+          ks = k;
+          break;
+        }
+    }
+    if (ks) {
+      p.cfg = 10;
+      p.k_splits = ks;
+      return p;
+    }
+  }
   int bm, bn;
   tile_dims(p.cfg, bm, bn);
   const int tiles = ((M + bm - 1) / bm) * n_tiles_of(a, bn);
@@ -864,6 +1010,14 @@ hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t
     case 19: return launch_pipe<P19>(a, p, ws, s, hook);
     case 20: return launch_pipe<P20>(a, p, ws, s, hook);
     case 21: return launch_pipe<P21>(a, p, ws, s, hook);
+    case 22: return launch_pipe<P22>(a, p, ws, s, hook);
+    case 23: return launch_pipe<P23>(a, p, ws, s, hook);
+    case 24: return launch_pipe<P24>(a, p, ws, s, hook);
+    case 25: return launch_pipe<P25>(a, p, ws, s, hook);
+    case 26: return launch_pipe<P26>(a, p, ws, s, hook);
+    case 27: return launch_pipe<P27>(a, p, ws, s, hook);
+    case 28: return launch_pipe<P28>(a, p, ws, s, hook);
+    case 29: return launch_pipe<P29>(a, p, ws, s, hook);
     default: return launch_cfg<Cfg0>(a, p, ws, s, hook);
   }
 }

@@ -60,10 +60,20 @@ __device__ __forceinline__ int xcd_logical(int hw, int total) {
   return xcd * q + min(xcd, r) + slot;
 }
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
-// lane l writes lds + 16 l, so one instruction fills 1 KB.
-__device__ __forceinline__ void dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// Raw buffer resource over `base`: byte offsets up to 4 GiB, no range check
+// (word 3 is the gfx9-family data format for untyped dword access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)0xffffffff, 0x00020000);
+}
+
+// 16 bytes per lane from base + soff + voff straight into LDS through the
+// buffer unit (buffer_load_dwordx4 ... lds): lane l writes lds + 16 l, so one
+// instruction fills 1 KB.  The global form (global_load_lds) would do the
+// same, but as a FLAT-family instruction it makes the compiler wait for all
+// LDS reads (lgkmcnt(0)) wherever fragment reads are in flight.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff,
+                                           (int)soff, 0, 0);
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding

@@ -169,5 +169,6 @@ hipError_t probe_mfma(int shape, int n_blocks, int iters, float* sink, hipStream
 hipError_t probe_read(const void* buf, size_t bytes, float* sink, int n_blocks, hipStream_t s);
 // out[2*b] = HW_ID, out[2*b+1] = XCC_ID of workgroup b
 hipError_t probe_hwid(uint32_t* out, int n_blocks, hipStream_t s);
+hipError_t probe_fill_bf16(void* p, int64_t n, uint32_t seed, float scale, hipStream_t s);
 
 }  // namespace nf

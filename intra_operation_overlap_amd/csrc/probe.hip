@@ -1,5 +1,7 @@
 // Device probes: dense bf16 matrix-core peak, HBM read bandwidth, and the
 // hardware identity (XCC / CU) a workgroup lands on.
+#include <algorithm>
+
 #include "nf_device.h"
 #include "nf_internal.h"
 
@@ -41,6 +43,23 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* sink)
     for (int c = 0; c < 4; ++c) s += acc[c][0] + acc[c][5] + acc[c][10] + acc[c][15];
   }
   if (s == 12345.678f) sink[threadIdx.x] = s;     // keeps the chains live
+}
+
+// Deterministic pseudo-random bf16 fill: element i gets scale * u, with u
+// uniform in [-1, 1) taken from the MurmurHash3 32-bit finaliser of i ^ seed.
+// Constant operands would understate the matrix cores' switching power and so
+// overstate the clock a GEMM holds on real data.
+__global__ __launch_bounds__(256) void probe_fill_bf16_kernel(bf16* p, int64_t n, uint32_t seed, float scale) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    uint32_t h = (uint32_t)i ^ (uint32_t)(i >> 32) * 0x9e3779b9u ^ seed;
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    p[i] = (bf16)(scale * ((float)(h >> 8) * (1.0f / 8388608.0f) - 1.0f));
+  }
 }
 
 // Streams the buffer once, 16 bytes per lane per load, grid-strided.
@@ -88,6 +107,13 @@ hipError_t probe_read(const void* buf, size_t bytes, float* sink, int n_blocks, 
 
 hipError_t probe_hwid(uint32_t* out, int n_blocks, hipStream_t s) {
   probe_hwid_kernel<<<n_blocks, 64, 0, s>>>(out);
+  return hipGetLastError();
+}
+
+hipError_t probe_fill_bf16(void* p, int64_t n, uint32_t seed, float scale, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  launch(probe_fill_bf16_kernel, blocks, 256, 0, s, (bf16*)p, n, seed, scale);
   return hipGetLastError();
 }
 

@@ -49,6 +49,16 @@ nf_status check_shape(const nf_shape& s, std::string& err) {
     return fail(err, NF_ERR_INVALID_ARG, "shape: rms_eps must be >= 0 and rope_theta > 0");
   if ((int64_t)s.max_tokens * s.top_k > (1 << 24))
     return fail(err, NF_ERR_OUT_OF_RANGE, "shape: max_tokens too large");
+  if (s.dtype == NF_BF16) {
+    // the bf16 GEMMs address each operand with 32-bit byte offsets
+    const int64_t rows = (int64_t)s.max_tokens * s.top_k;
+    const int64_t qkv = (int64_t)(s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim;
+    const int64_t qd = (int64_t)s.n_q_heads * s.head_dim;
+    const int64_t widest = std::max(std::max((int64_t)s.hidden, (int64_t)s.ffn), std::max(qkv, qd));
+    const int64_t weight = std::max(std::max(qkv, qd), (int64_t)s.ffn) * s.hidden;
+    if (std::max(rows * widest, weight) * 2 >= (int64_t(1) << 32))
+      return fail(err, NF_ERR_OUT_OF_RANGE, "shape: a GEMM operand would exceed 4 GiB");
+  }
   return NF_OK;
 }
 

@@ -105,6 +105,32 @@ def test_validate_rejects_capacity_and_plan_errors():
     assert _validate(shape, batch, plan=B.make_plan(1, [16], n_streams=2, gemm_cus_per_xcd=32)) == B.NF_ERR_OUT_OF_RANGE
 
 
+def test_validate_rejects_gemm_operands_over_4gib():
+    """bf16 GEMMs address operands with 32-bit byte offsets: a capacity whose
+    widest activation (T x ffn bf16) reaches 4 GiB is refused up front."""
+    wl = W.WORKLOADS["c2"]
+    batch = W.make_batch(wl)
+    ok = B.make_shape(wl.shape, max_tokens=(1 << 32) // (2 * wl.shape.ffn) - 1, max_pos=4096)
+    assert _validate(ok, batch) == B.NF_OK
+    big = B.make_shape(wl.shape, max_tokens=(1 << 32) // (2 * wl.shape.ffn) + 1, max_pos=4096)
+    assert _validate(big, batch) == B.NF_ERR_OUT_OF_RANGE
+
+
+def test_gemm_rejects_bad_arguments_before_launching():
+    with pytest.raises(B.NfError) as e:
+        B.gemm_bf16(64, 64, 96, 0, 1, 96, 1, None, 96, None, 64, 1, 64, 14, 1)    # cfg 14 needs K % 64
+    assert e.value.status == B.NF_ERR_INVALID_ARG
+    with pytest.raises(B.NfError) as e:
+        B.gemm_bf16(64, 60, 64, 0, 1, 64, 1, None, 64, None, 60, 1, 60)           # N % 8
+    assert e.value.status == B.NF_ERR_INVALID_ARG
+    with pytest.raises(B.NfError) as e:
+        B.gemm_bf16(64, 64, 64, 2, 1, 64, 1, None, 64, None, 64, 1, 64)           # SwiGLU without B2
+    assert e.value.status == B.NF_ERR_INVALID_ARG
+    with pytest.raises(B.NfError) as e:
+        B.gemm_bf16(64, 64, 64, 0, 1, 64, 1, None, 64, None, 64, 1, 64, 40, 1)    # streaming tiles need packing
+    assert e.value.status == B.NF_ERR_INVALID_ARG
+
+
 def test_validate_moe_needs_logits_and_shape_rules():
     wl = W.WORKLOADS["c5"]
     batch = W.make_batch(wl, n_decode=4)
