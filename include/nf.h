@@ -288,7 +288,7 @@ nf_status nf_probe_cu_map(int32_t* xcc, int32_t n);
  * ldc), strides in elements, fp32 accumulation, one bf16 rounding of C.
  * tile_cfg < 0 and k_splits <= 0 let the library choose for a stream that
  * may use `cus` CUs (cus <= 0: all); a given tile_cfg must be one of the
- * layer's LDS-tiled configurations (0..6, or 10..29 with K % 64 == 0).  The
+ * layer's LDS-tiled configurations (0..6, or 10..30 with K % 64 == 0).  The
  * split-K workspace is allocated and freed inside, and the call returns after
  * the GEMM finished on `stream` (NULL: the null stream).  out_cfg and
  * out_splits (may be NULL) return what ran.  Operands must stay under 4 GiB

@@ -1219,7 +1219,7 @@ extern "C" nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode,
       (mode == GEMM_RESIDUAL && !R) || (mode == GEMM_SWIGLU && !B2) || lda < K || ldb < K || ldc < N ||
       (mode == GEMM_RESIDUAL && ldr < N))
     return set_err(NF_ERR_INVALID_ARG, "nf_gemm_bf16: bad argument");
-  if (tile_cfg >= 0 && !((tile_cfg <= 6) || (tile_cfg >= 10 && tile_cfg <= 29 && K % 64 == 0)))
+  if (tile_cfg >= 0 && !((tile_cfg <= 6) || (tile_cfg >= 10 && tile_cfg <= 30 && K % 64 == 0)))
     return set_err(NF_ERR_INVALID_ARG, "nf_gemm_bf16: tile_cfg %d not available for K %d", tile_cfg, K);
   if ((int64_t)M * lda * 2 >= (int64_t(1) << 32) || (int64_t)N * ldb * 2 >= (int64_t(1) << 32))
     return set_err(NF_ERR_OUT_OF_RANGE, "nf_gemm_bf16: an operand would exceed 4 GiB");

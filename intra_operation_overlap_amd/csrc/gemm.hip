@@ -466,7 +466,19 @@ using P26 = PCfg<256, 256, 2, 2, 32, 3, 32>;
 using P27 = PCfg<256, 256, 2, 2, 32, 5, 32>;
 using P28 = PCfg<256, 128, 2, 2, 32, 5, 32>;
 using P29 = PCfg<128, 128, 2, 2, 32, 9, 32>;
+// expert groups of up to 160 rows: one m-tile per group, three 52 KB stages
+using P30 = PCfg<160, 256, 1, 4, 32, 3>;
 
+
+// Output rows staged through LDS per epilogue pass: the whole tile if it
+// fits, else the largest power of two (>= 32, so fragment blocks never
+// straddle passes) that fits and divides the tile.
+constexpr int stage_rows(int bm, int fit) {
+  if (fit >= bm) return bm;
+  for (int p = 128; p >= 32; p /= 2)
+    if (p <= fit && bm % p == 0) return p;
+  return 0;
+}
 
 // wait until at most `after` slabs issued after the current one are pending
 // (each slab is X loads of this thread, and loads retire in order)
@@ -651,7 +663,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
       }
     }
   };
-  if (live == C::FM)
+  // grouped GEMMs stream weights: their MFMAs on clamped rows past a
+  // group's end cost nothing, the checked loop's waits would
+  if (live == C::FM || a.group_off)
     k_loop(std::false_type{});
   else
     k_loop(std::true_type{});
@@ -672,8 +686,8 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
       constexpr int ES = F32S ? 4 : 2;
       constexpr int ROWB_O = BNO * ES + (F32S ? 32 : 16);
       constexpr int FIT = (C::STAGES * C::SLAB) / ROWB_O;
-      constexpr int RP = FIT >= C::BM ? C::BM : FIT >= 128 ? 128 : FIT >= 64 ? 64 : 32;   // rows per pass
-      static_assert(FIT >= 32 && C::BM % RP == 0, "staging");
+      constexpr int RP = stage_rows(C::BM, FIT);          // rows per pass
+      static_assert(RP >= 32 && C::BM % RP == 0, "staging");
       constexpr int CH = BNO / 8;                          // 16-byte output chunks per row
 #pragma unroll
       for (int pass = 0; pass < C::BM / RP; ++pass) {
@@ -841,6 +855,7 @@ void tile_dims(int cfg, int& bm, int& bn) {
     case 26: case 27: bm = 256; bn = 256; return;
     case 28: bm = 256; bn = 128; return;
     case 29: bm = 128; bn = 128; return;
+    case 30: bm = 160; bn = 256; return;
     default: bm = 128; bn = 128; return;
   }
 }
@@ -864,10 +879,13 @@ namespace {
 // MI355X: a workgroup streams at most kWgGBps, at most two workgroups share a
 // CU, and the chip at most kHbmGBps; split-K adds its fp32 partial slices
 // (written, then read again by the reduce).
-constexpr double kWgGBps = 20.0, kHbmGBps = 6000.0;
+// (double-buffered configurations 46 and 47 keep a second chunk in flight:
+// about 24 GB/s per workgroup)
+constexpr double kWgGBps = 20.0, kWgGBpsDB = 24.0, kHbmGBps = 6000.0;
 int stream_splits(const GemmArgs& a, int cfg, int cus) {
+  const double wg_gbps = (cfg == 46 || cfg == 47) ? kWgGBpsDB : kWgGBps;
   const bool sw = a.mode == GEMM_SWIGLU;
-  const int nbw = (cfg == 42 || cfg == 43 || cfg == 45) ? 2 : 1;
+  const int nbw = (cfg == 42 || cfg == 43 || cfg == 45 || cfg == 47) ? 2 : 1;
   const int nbt = (sw ? 2 : 1) * (a.N / 32);
   const int n_wg = (nbt + 4 * nbw - 1) / (4 * nbw);
   const int nch = a.K / 16 / stream_kc(cfg);
@@ -879,7 +897,7 @@ int stream_splits(const GemmArgs& a, int cfg, int cus) {
     const int ch_per = (nch + want - 1) / want;
     const int z = (nch + ch_per - 1) / ch_per;
     const double wgs = (double)n_wg * z * a.n_groups;
-    const double bw = std::min(kHbmGBps, std::min(wgs, 2.0 * cus) * kWgGBps) * 1e9;
+    const double bw = std::min(kHbmGBps, std::min(wgs, 2.0 * cus) * wg_gbps) * 1e9;
     const double t = (wbytes + (z > 1 ? 2.0 * z * a.M * pld * 4 : 0.0)) / bw;
     if (t < best_t * 0.98) {
       best_t = t;
@@ -895,10 +913,12 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   if (cus <= 0) cus = 256;
   if (a.Bp) {                   // packed weights: stream them for expert groups
     // (measured: for dense decode-sized M the pipelined LDS kernel below is
-    // faster, so configurations 40..43 are chosen only on request)
+    // faster, so configurations 40..43 are chosen only on request; the
+    // double-buffered 46 / 47 beat 44 / 45 on the 8-expert workload, and a
+    // 160 x 256 LDS-pipelined tile (configuration 30) ties with them)
     const bool sw = a.mode == GEMM_SWIGLU;
     int cfg = 0;
-    if (a.group_off && a.max_group_rows / std::max(1, a.n_groups) <= 160) cfg = sw ? 45 : 44;
+    if (a.group_off && a.max_group_rows / std::max(1, a.n_groups) <= 160) cfg = sw ? 47 : 46;
     if (cfg && a.N % 32 == 0 && a.K % (16 * stream_kc(cfg)) == 0) {
       p.cfg = cfg;
       p.k_splits = stream_splits(a, cfg, cus);
@@ -1018,6 +1038,7 @@ hipError_t gemm_bf16(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t
     case 27: return launch_pipe<P27>(a, p, ws, s, hook);
     case 28: return launch_pipe<P28>(a, p, ws, s, hook);
     case 29: return launch_pipe<P29>(a, p, ws, s, hook);
+    case 30: return launch_pipe<P30>(a, p, ws, s, hook);
     default: return launch_cfg<Cfg0>(a, p, ws, s, hook);
   }
 }

@@ -47,7 +47,9 @@ __device__ __forceinline__ int acc_row32(int lane, int r) { return 8 * (r >> 2) 
 
 // MB m-blocks of 32 rows per pass, NBW packed n-blocks per wave, KC k-steps
 // per A chunk.  MODE as in GemmMode; PARTIAL writes fp32 partial slices.
-template <int MB, int NBW, int KC, int MODE, bool PARTIAL>
+// DB double-buffers the chunks (two LDS A buffers, two register sets of B):
+// chunk c + 1's loads are in flight while chunk c's MFMAs run.
+template <int MB, int NBW, int KC, int MODE, bool PARTIAL, bool DB>
 __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SParams p) {
   constexpr int ROWS = MB * SB;
   constexpr int PR = KC * 2;                 // 16-byte pieces of one A row in a chunk
@@ -55,9 +57,9 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
   constexpr int NA = CH / 4096;              // 16-byte A loads per lane per chunk
   constexpr int NB = KC * NBW;               // B loads per wave per chunk
   static_assert(CH % 4096 == 0 && NA >= 1, "chunk");
-  static_assert(NA + NB <= 63, "vmcnt range");
+  static_assert((DB ? 2 : 1) * (NA + NB) <= 63, "vmcnt range");
   static_assert((MODE == GEMM_SWIGLU) == (NBW == 2), "SWIGLU pairs a gate and an up block per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[CH];
+  __shared__ __attribute__((aligned(1024))) char smem[(DB ? 2 : 1) * CH];
 
   const GemmArgs& a = p.a;
   const int total = p.n_wg * p.splits * a.n_groups;
@@ -74,7 +76,8 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
   if (rows <= 0) return;                                   // whole workgroup exits together
   const int ks0 = z * p.ks_per;
   const int nch = min(p.ks_per, p.kbt - ks0) / KC;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // B sources: this wave's packed n-blocks, clamped into range so that every
   // wave issues the same number of loads (the vmcnt arithmetic relies on it)
@@ -116,7 +119,82 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
     // consumed in the same iteration, so the compiler's in-order counting
     // stays exact; the other waves of the CU keep HBM busy while one wave
     // computes.
-    bf16x8 br[KC][NBW], ar[NA];
+    bf16x8 ar[NA];
+    if constexpr (DB) {
+      // Every load is unconditional (the chunk after the last one reloads
+      // the last), so the compiler's in-order wait counts stay exact across
+      // the loop; one barrier per chunk separates the A writes of chunk c + 1
+      // from the fragment reads of chunk c - 1 in the same buffer.
+      // buffer loads: a scalar base per operand (per packed n-block for B)
+      // and 32-bit lane offsets, with the chunk's offset in the scalar
+      // offset, keep the address registers few
+      const __amdgpu_buffer_rsrc_t rA = buf_rsrc(a.A);
+      uint32_t aoff[NA];
+#pragma unroll
+      for (int i = 0; i < NA; ++i) aoff[i] = (uint32_t)((asrc[i] - (const bf16*)a.A) * 2);
+      __amdgpu_buffer_rsrc_t rB[NBW];
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) rB[j] = buf_rsrc(bsrc[j] - lane);      // wave-uniform: the wave's n-block
+      bf16x8 bq[2][KC][NBW];
+      auto load = [&](int c, bf16x8 (&dst)[KC][NBW]) {
+        c = min(c, nch - 1);
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+          ar[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[i], c * KC * SK * 2, 0));
+#pragma unroll
+        for (int s = 0; s < KC; ++s)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j)      // nontemporal: each weight byte is read once
+            dst[s][j] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB[j], lane * 16, (c * KC + s) * 1024, 2));
+      };
+      auto put_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) *(bf16x8*)(smem + buf * CH + ((wave * NA + i) * 64 + lane) * 16) = ar[i];
+      };
+      auto mma = [&](int buf, const bf16x8 (&src)[KC][NBW]) {
+#pragma unroll
+        for (int s = 0; s < KC; ++s) {
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const int r = m * SB + (lane & 31);
+            const int sl = (2 * s + (lane >> 5)) ^ (r % PR);
+            const bf16x8 af = *(const bf16x8*)(smem + buf * CH + r * PR * 16 + sl * 16);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) acc[m][j] = mfma32(af, src[s][j], acc[m][j]);
+          }
+        }
+        // fragment reads run two ahead of their MFMAs (hoisting all of them
+        // would take 4 registers each)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < KC * MB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NBW, 0);
+          if (i + 2 < KC * MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      };
+      // chunks in pairs (no exit between the halves, so the accumulators
+      // keep their registers), an odd last chunk after the loop
+      load(0, bq[0]);
+      put_a(0);
+      int c = 0;
+      for (; c + 1 < nch; c += 2) {
+        load(c + 1, bq[1]);
+        barrier_lds();                // chunk c's A is in buffer 0; chunk c - 1 is done with buffer 1
+        mma(0, bq[0]);
+        put_a(1);
+        load(c + 2, bq[0]);
+        barrier_lds();
+        mma(1, bq[1]);
+        put_a(0);
+      }
+      if (c < nch) {
+        barrier_lds();
+        mma(0, bq[0]);
+      }
+      barrier_lds();                  // LDS may take the next pass
+    } else {
+    bf16x8 br[KC][NBW];
     for (int c = 0; c < nch; ++c) {
 #pragma unroll
       for (int i = 0; i < NA; ++i) ar[i] = *(const bf16x8*)(asrc[i] + (int64_t)c * KC * SK);
@@ -139,6 +217,7 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
         }
       }
       barrier_lds();                  // LDS may take the next chunk
+    }
     }
 
     // epilogue: lane holds D[acc_row32(lane, r)][lane % 32] of each block
@@ -206,7 +285,7 @@ __global__ __launch_bounds__(256) void pack_b_kernel(const bf16* __restrict__ W,
   }
 }
 
-template <int MB, int NBW, int KC>
+template <int MB, int NBW, int KC, bool DB = false>
 hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream_t s, const LaunchHook* hook) {
   if (a.N % SB || a.K % (KC * SK)) return hipErrorInvalidValue;
   SParams p;
@@ -228,21 +307,21 @@ hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStr
   if (sw != (NBW == 2)) return hipErrorInvalidValue;    // SWIGLU configurations pair gate and up blocks
   if (p.splits > 1) {
     if constexpr (NBW == 2)
-      launch(gemm_stream_kernel<MB, NBW, KC, GEMM_SWIGLU, true>, total, 256, 0, s, p);
+      launch(gemm_stream_kernel<MB, NBW, KC, GEMM_SWIGLU, true, DB>, total, 256, 0, s, p);
     else
-      launch(gemm_stream_kernel<MB, NBW, KC, GEMM_STORE, true>, total, 256, 0, s, p);
+      launch(gemm_stream_kernel<MB, NBW, KC, GEMM_STORE, true, DB>, total, 256, 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.defer_reduce) return e;
     if (hook && hook->fn) hook->fn(hook->ctx, 1);
     return splitk_reduce(a, p.part, p.part_ld, p.splits, s);
   }
   if constexpr (NBW == 2) {
-    launch(gemm_stream_kernel<MB, NBW, KC, GEMM_SWIGLU, false>, total, 256, 0, s, p);
+    launch(gemm_stream_kernel<MB, NBW, KC, GEMM_SWIGLU, false, DB>, total, 256, 0, s, p);
   } else {
     switch (a.mode) {
-      case GEMM_STORE: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_STORE, false>, total, 256, 0, s, p); break;
-      case GEMM_RESIDUAL: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_RESIDUAL, false>, total, 256, 0, s, p); break;
-      default: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_F32OUT, false>, total, 256, 0, s, p); break;
+      case GEMM_STORE: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_STORE, false, DB>, total, 256, 0, s, p); break;
+      case GEMM_RESIDUAL: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_RESIDUAL, false, DB>, total, 256, 0, s, p); break;
+      default: launch(gemm_stream_kernel<MB, NBW, KC, GEMM_F32OUT, false, DB>, total, 256, 0, s, p); break;
     }
   }
   return hipGetLastError();
@@ -255,6 +334,7 @@ hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStr
 //   42: 32 rows,  2 blocks, 16   43: 64 rows, 2 blocks, 16  (SWIGLU)
 //   44: 160 rows, 1 block, 16    45: 160 rows, 2 blocks, 16 (expert groups; one
 //   workgroup per CU, so that an expert of up to 160 rows streams its weights once)
+//   46, 47: as 44, 45 with 8 k-steps per chunk, double-buffered
 hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook) {
   switch (p.cfg) {
     case 40: return launch_stream<1, 1, 16>(a, p, ws, s, hook);
@@ -263,6 +343,8 @@ hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream
     case 43: return launch_stream<2, 2, 16>(a, p, ws, s, hook);
     case 44: return launch_stream<5, 1, 16>(a, p, ws, s, hook);
     case 45: return launch_stream<5, 2, 16>(a, p, ws, s, hook);
+    case 46: return launch_stream<5, 1, 8, true>(a, p, ws, s, hook);
+    case 47: return launch_stream<5, 2, 8, true>(a, p, ws, s, hook);
     default: return hipErrorInvalidValue;
   }
 }
@@ -270,6 +352,7 @@ hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream
 int stream_kc(int cfg) {
   switch (cfg) {
     case 40: case 41: case 42: case 43: case 44: case 45: return 16;
+    case 46: case 47: return 8;
     default: return 0;
   }
 }

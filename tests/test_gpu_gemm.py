@@ -14,7 +14,7 @@ from intra_operation_overlap_amd import binding as B
 
 pytestmark = pytest.mark.gpu
 
-CFGS = [0, 10, 13, 14, 15, 16, 21, 22, 26, 27]
+CFGS = [0, 10, 13, 14, 15, 16, 21, 22, 26, 27, 30]
 
 
 def _case(M, N, K, mode, seed):
