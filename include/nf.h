@@ -288,9 +288,12 @@ nf_status nf_probe_cu_map(int32_t* xcc, int32_t n);
  * ldc), strides in elements, fp32 accumulation, one bf16 rounding of C.
  * tile_cfg < 0 and k_splits <= 0 let the library choose for a stream that
  * may use `cus` CUs (cus <= 0: all); a given tile_cfg must be one of the
- * layer's LDS-tiled configurations (0..6, or 10..30 with K % 64 == 0).  The
- * split-K workspace is allocated and freed inside, and the call returns after
- * the GEMM finished on `stream` (NULL: the null stream).  out_cfg and
+ * layer's LDS-tiled configurations (0..6, or 10..30 with K % 64 == 0) or of
+ * its weight-streaming ones (40..47: N % 32 == 0, K a multiple of the
+ * configuration's chunk, two n-blocks per wave exactly for mode 2), for which
+ * B is first copied into operand order.  That copy and the split-K workspace
+ * are allocated and freed inside, and the call returns after the GEMM
+ * finished on `stream` (NULL: the null stream).  out_cfg and
  * out_splits (may be NULL) return what ran.  Operands must stay under 4 GiB
  * (NF_ERR_OUT_OF_RANGE); NF_ERR_INVALID_ARG for other bad arguments. */
 nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode, const void* A, int64_t lda,

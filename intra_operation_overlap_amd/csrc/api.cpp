@@ -553,8 +553,8 @@ size_t align_words(size_t w) { return (w + 63) & ~(size_t)63; }
 hipError_t pack_weights(nf_layer* L) {
   const nf_shape& s = L->s;
   const int64_t H = s.hidden, F = s.ffn, E = s.n_experts;
-  if (E == 1 || F % 32 || H % 32) return hipSuccess;
   hipError_t e;
+  if (E == 1 || F % 32 || H % 32) return hipSuccess;
   if ((e = ensure(L->wp_gu, E * 2 * F * H * 2)) != hipSuccess) return e;
   if ((e = pack_b(L->w.w_gate, H, F * H, (int)F, (int)H, (int)E, L->wp_gu.p, 2, 0, 2 * F * H, nullptr)) != hipSuccess)
     return e;
@@ -1219,8 +1219,12 @@ extern "C" nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode,
       (mode == GEMM_RESIDUAL && !R) || (mode == GEMM_SWIGLU && !B2) || lda < K || ldb < K || ldc < N ||
       (mode == GEMM_RESIDUAL && ldr < N))
     return set_err(NF_ERR_INVALID_ARG, "nf_gemm_bf16: bad argument");
-  if (tile_cfg >= 0 && !((tile_cfg <= 6) || (tile_cfg >= 10 && tile_cfg <= 30 && K % 64 == 0)))
-    return set_err(NF_ERR_INVALID_ARG, "nf_gemm_bf16: tile_cfg %d not available for K %d", tile_cfg, K);
+  const bool streaming = tile_cfg >= 40;
+  if (tile_cfg >= 0 && !((tile_cfg <= 6) || (tile_cfg >= 10 && tile_cfg <= 30 && K % 64 == 0) ||
+                         (streaming && stream_kc(tile_cfg) > 0 && N % 32 == 0 && K % (16 * stream_kc(tile_cfg)) == 0 &&
+                          stream_nbw(tile_cfg) == (mode == GEMM_SWIGLU ? 2 : 1))))
+    return set_err(NF_ERR_INVALID_ARG, "nf_gemm_bf16: tile_cfg %d not available for N %d K %d mode %d", tile_cfg, N, K,
+                   mode);
   if ((int64_t)M * lda * 2 >= (int64_t(1) << 32) || (int64_t)N * ldb * 2 >= (int64_t(1) << 32))
     return set_err(NF_ERR_OUT_OF_RANGE, "nf_gemm_bf16: an operand would exceed 4 GiB");
   GemmArgs g;
@@ -1232,12 +1236,25 @@ extern "C" nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode,
   if (tile_cfg >= 0) p.cfg = tile_cfg;
   if (k_splits > 0) p.k_splits = k_splits;
   hipStream_t s = (hipStream_t)stream;
+  void* Bp = nullptr;
+  if (streaming) {              // the weight-streaming kernels read an operand-order copy of B
+    const int nb = mode == GEMM_SWIGLU ? 2 : 1;
+    HIP_TRY(hipMalloc(&Bp, (size_t)nb * N * K * 2));
+    hipError_t pe = pack_b(Bw, ldb, 0, N, K, 1, Bp, nb, 0, 0, s);
+    if (pe == hipSuccess && nb == 2) pe = pack_b(B2, ldb, 0, N, K, 1, Bp, 2, 1, 0, s);
+    if (pe != hipSuccess) {
+      (void)hipFree(Bp);
+      return set_err(NF_ERR_HIP, "nf_gemm_bf16: packing B: %s", hipGetErrorString(pe));
+    }
+    g.Bp = Bp;
+  }
   void* ws = nullptr;
   const size_t wsb = gemm_workspace_bytes(g, p);
   if (wsb) HIP_TRY(hipMalloc(&ws, wsb));
   hipError_t e = gemm_bf16(g, p, ws, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (ws) (void)hipFree(ws);
+  if (Bp) (void)hipFree(Bp);
   if (e != hipSuccess) return set_err(NF_ERR_HIP, "nf_gemm_bf16: %s", hipGetErrorString(e));
   if (out_cfg) *out_cfg = p.cfg;
   if (out_splits) *out_splits = p.k_splits;

@@ -50,9 +50,10 @@ __device__ __forceinline__ int acc_row32(int lane, int r) { return 8 * (r >> 2) 
 // MB m-blocks of 32 rows per pass, NBW packed n-blocks per wave, KC k-steps
 // per A chunk.  MODE as in GemmMode; PARTIAL writes fp32 partial slices.
 // PIPE 1 double-buffers the chunks (two LDS A buffers, two register sets of
-// B): chunk c + 1's loads are in flight while chunk c's MFMAs run.  PIPE 2
-// keeps two chunks ahead: A goes to LDS by DMA (three buffers), B to three
-// register sets.
+// B): chunk c + 1's loads are in flight while chunk c's MFMAs run.  Only
+// register loads are used: a buffer-to-LDS fill in flight beside register
+// loads made in-order vmcnt counting unsafe (the two kinds completed out of
+// order on MI355X; wrong sums, found by the streaming-configuration tests).
 template <int MB, int NBW, int KC, int MODE, bool PARTIAL, int PIPE>
 __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SParams p) {
   constexpr int ROWS = MB * SB;
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
   constexpr int NA = CH / 4096;              // 16-byte A loads per lane per chunk
   constexpr int NB = KC * NBW;               // B loads per wave per chunk
   static_assert(CH % 4096 == 0 && NA >= 1, "chunk");
-  static_assert((PIPE == 2 ? 2 * NB + NA : (PIPE == 1 ? 2 : 1) * (NA + NB)) <= 63, "vmcnt range");
+  static_assert((PIPE == 1 ? 2 : 1) * (NA + NB) <= 63, "vmcnt range");
   static_assert((MODE == GEMM_SWIGLU) == (NBW == 2), "SWIGLU pairs a gate and an up block per wave");
   __shared__ __attribute__((aligned(1024))) char smem[(PIPE + 1) * CH];
 
@@ -124,78 +125,7 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
     // stays exact; the other waves of the CU keep HBM busy while one wave
     // computes.
     bf16x8 ar[NA];
-    if constexpr (PIPE == 2) {
-      // Per chunk c: issue B(c + 2) into a free register set, wait for chunk
-      // c's A and B (everything but the 2 NB + NA loads issued after A(c)),
-      // barrier (every wave's A(c) landed, every wave is done with chunk
-      // c - 1's buffer), DMA A(c + 2) into that buffer, then chunk c's MFMAs.
-      // Loads go out in the order they are consumed, so in-order counting
-      // holds; indices past the last chunk reload the last one.
-      const __amdgpu_buffer_rsrc_t rA = buf_rsrc(a.A);
-      uint32_t aoff[NA];
-#pragma unroll
-      for (int i = 0; i < NA; ++i) aoff[i] = (uint32_t)((asrc[i] - (const bf16*)a.A) * 2);
-      __amdgpu_buffer_rsrc_t rB[NBW];
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) rB[j] = buf_rsrc(bsrc[j] - lane);      // wave-uniform: the wave's n-block
-      bf16x8 bq[3][KC][NBW];
-      auto load_b = [&](int c, bf16x8 (&dst)[KC][NBW]) {
-        c = min(c, nch - 1);
-#pragma unroll
-        for (int s = 0; s < KC; ++s)
-#pragma unroll
-          for (int j = 0; j < NBW; ++j)      // nontemporal: each weight byte is read once
-            dst[s][j] = __builtin_bit_cast(
-                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB[j], lane * 16, (c * KC + s) * 1024, 2));
-      };
-      auto dma_a = [&](int c, int buf) {
-        c = min(c, nch - 1);
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-          dma16_buf(rA, aoff[i], (uint32_t)(c * KC * SK * 2), smem + buf * CH + (wave * NA + i) * 1024);
-      };
-      auto mma = [&](int buf, const bf16x8 (&src)[KC][NBW]) {
-#pragma unroll
-        for (int s = 0; s < KC; ++s) {
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const int r = m * SB + (lane & 31);
-            const int sl = (2 * s + (lane >> 5)) ^ (r % PR);
-            const bf16x8 af = *(const bf16x8*)(smem + buf * CH + r * PR * 16 + sl * 16);
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) acc[m][j] = mfma32(af, src[s][j], acc[m][j]);
-          }
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int i = 0; i < KC * MB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, NBW, 0);
-          if (i + 2 < KC * MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      };
-      auto chunk = [&](int c, auto kk) {
-        constexpr int k = decltype(kk)::value, k2 = (k + 2) % 3;
-        load_b(c + 2, bq[k2]);
-        wait_vmcnt<2 * NB + NA>();
-        barrier_lds();
-        dma_a(c + 2, k2);
-        mma(k, bq[k]);
-      };
-      load_b(0, bq[0]);
-      dma_a(0, 0);
-      load_b(1, bq[1]);
-      dma_a(1, 1);
-      int c = 0;
-      for (; c + 2 < nch; c += 3) {
-        chunk(c, std::integral_constant<int, 0>{});
-        chunk(c + 1, std::integral_constant<int, 1>{});
-        chunk(c + 2, std::integral_constant<int, 2>{});
-      }
-      if (c < nch) chunk(c, std::integral_constant<int, 0>{});
-      if (c + 1 < nch) chunk(c + 1, std::integral_constant<int, 1>{});
-      wait_vmcnt<0>();                // no fill still writing LDS
-      barrier_lds();                  // LDS may take the next pass
-    } else if constexpr (PIPE == 1) {
+    if constexpr (PIPE == 1) {
       // Every load is unconditional (the chunk after the last one reloads
       // the last), so the compiler's in-order wait counts stay exact across
       // the loop; one barrier per chunk separates the A writes of chunk c + 1
@@ -410,7 +340,6 @@ hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStr
 //   44: 160 rows, 1 block, 16    45: 160 rows, 2 blocks, 16 (expert groups; one
 //   workgroup per CU, so that an expert of up to 160 rows streams its weights once)
 //   46, 47: as 44, 45 with 8 k-steps per chunk, double-buffered
-//   48, 49: as 46, 47 with A filled by DMA and both operands two chunks ahead
 hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook) {
   switch (p.cfg) {
     case 40: return launch_stream<1, 1, 16>(a, p, ws, s, hook);
@@ -421,16 +350,22 @@ hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream
     case 45: return launch_stream<5, 2, 16>(a, p, ws, s, hook);
     case 46: return launch_stream<5, 1, 8, 1>(a, p, ws, s, hook);
     case 47: return launch_stream<5, 2, 8, 1>(a, p, ws, s, hook);
-    case 48: return launch_stream<5, 1, 8, 2>(a, p, ws, s, hook);
-    case 49: return launch_stream<5, 2, 8, 2>(a, p, ws, s, hook);
     default: return hipErrorInvalidValue;
+  }
+}
+
+int stream_nbw(int cfg) {
+  switch (cfg) {
+    case 42: case 43: case 45: case 47: return 2;
+    case 40: case 41: case 44: case 46: return 1;
+    default: return 0;
   }
 }
 
 int stream_kc(int cfg) {
   switch (cfg) {
     case 40: case 41: case 42: case 43: case 44: case 45: return 16;
-    case 46: case 47: case 48: case 49: return 8;
+    case 46: case 47: return 8;
     default: return 0;
   }
 }

@@ -83,9 +83,10 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
 // Sum of `splits` fp32 partial slices (M x part_ld each) plus the mode's
 // epilogue, written to C.
 hipError_t splitk_reduce(const GemmArgs& a, const float* part, int64_t part_ld, int splits, hipStream_t s);
-// Weight-streaming kernels (tile configurations 40..45; need a.Bp).
+// Weight-streaming kernels (tile configurations 40..47; need a.Bp).
 hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook);
 int stream_kc(int cfg);   // k-steps (of 16) per A chunk of a streaming configuration, 0 if none
+int stream_nbw(int cfg);  // packed n-blocks per wave (2: SwiGLU gate + up), 0 if none
 // Packs W [groups][N][K] (row stride ldw, group stride group_stride; N % 32 ==
 // 0, K % 16 == 0) into 1 KB operand blocks (32 rows x 16 k); source n-block b
 // becomes packed n-block b * nb_stride + nb_offset (gate/up interleave: 2, 0/1).

@@ -82,3 +82,28 @@ def test_gemm_library_choice_on_a_large_ragged_problem(mode):
     err = ((got.float() - want).norm() / want.norm()).item()
     assert err < 5e-3, f"choice {ran}: normwise relative error {err:.2e}"
 
+
+
+# weight-streaming configurations: (cfg, rows per pass) for one n-block per
+# wave (modes 0, 1) and two (SwiGLU)
+STREAM_1 = [40, 41, 44, 46]
+STREAM_2 = [42, 43, 45, 47]
+
+
+@pytest.mark.parametrize("cfg", STREAM_1 + STREAM_2)
+def test_streaming_config_matches_fp32_reference(cfg):
+    """The weight-streaming kernels (B copied into MFMA operand order first),
+    with M ragged against their 32-row blocks, one pass or several, and
+    split-K with ragged chunk counts per piece."""
+    modes = [2] if cfg in STREAM_2 else [0, 1]
+    N, K = 192, 1024
+    for mode in modes:
+        for M in (20, 64, 170):
+            case = _case(M, N, K, mode, seed=1000 + 7 * cfg + M + mode)
+            want = _reference(mode, *case)
+            for ks in (1, 3):
+                got, ran = _run(M, N, K, mode, cfg, ks, 0, case)
+                assert ran[0] == cfg
+                assert not torch.isnan(got.float()).any(), f"cfg {cfg} M {M} split {ks}: unwritten outputs"
+                err = ((got.float() - want).norm() / want.norm()).item()
+                assert err < 5e-3, f"cfg {cfg} mode {mode} M {M} split {ks}: normwise relative error {err:.2e}"
