@@ -8,7 +8,8 @@ of seeded synthetic inputs that are resident in HBM before timing starts.
 Prints one JSON line: throughput (tokens/s), the fraction of the
 compute-bound optimum (peaks measured in this run), the roofline of the
 dominant kernel (its duration measured with HIP events on its own stream
-during the timed steps) and the CPU oracle timed on a bounded sample.
+during the timed steps), the step time with cold caches (a 512 MiB scratch
+read before each step) and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -146,6 +147,29 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    def time_cold(n):
+        """Median step time with cold caches: before each step a 512 MiB read
+        of a scratch buffer evicts the weights and the KV pool from L2 and the
+        Infinity Cache, so the step reads them from HBM.  (A read rather than
+        a write: a write would also leave dirty lines for the step to write
+        back.)  Each step is bracketed by its own events; the flush is
+        outside them."""
+        scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(n):
+            torch.sum(scratch)
+            e0.record(stream)
+            layer.step(pool, hb, sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        times.sort()
+        return {"ms_per_step": round(times[len(times) // 2], 5), "steps": n,
+                "tokens_per_s": round(T / (times[len(times) // 2] * 1e-3), 1),
+                "flush": "512 MiB read of a scratch buffer before each step"}
+
     comparisons = {}
     if args.plan.startswith("overlap2"):
         parts = args.plan.split(":")
@@ -205,6 +229,8 @@ def main():
     launches, dom_ms = dprof[dominant]
     dom_avg_ms = dom_ms / launches
     value = T / (ms * 1e-3)
+    cold = time_cold(min(args.steps, 20))
+    log(f"cold caches: {cold['ms_per_step'] * 1e3:.1f} us per step (median of {cold['steps']})")
     if comparisons:
         comparisons["searched_plan_ms"] = ms
 
@@ -263,6 +289,7 @@ def main():
         "flops_per_token": fpt,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cold_cache": cold,
     }
     if comparisons:
         line["comparisons"] = {k: round(v, 5) for k, v in comparisons.items()}
