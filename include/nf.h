@@ -169,7 +169,14 @@ typedef struct nf_kv_pool nf_kv_pool;
  * layer), so weights must not change while the layer exists.  The default plan is
  * one nano-batch on the caller's stream.  Errors: NF_ERR_INVALID_ARG (null
  * pointers, inconsistent shape), NF_ERR_UNSUPPORTED (head_dim or dtype
- * outside the list above), NF_ERR_HIP (allocation failure). */
+ * outside the list above), NF_ERR_HIP (allocation failure).
+ * Diagnostics read from the environment (for measurements; not needed for
+ * normal use): NF_ATTN_VARIANT=0|1 fixes the bf16 attention kernel of layers
+ * created afterwards to one-wave work items (0, split page ranges plus a
+ * merge) or four-wave workgroups (1); by default four-wave workgroups run
+ * unless the plan bounds the attention waves per CU.  NF_SEARCH_VERBOSE
+ * prints each plan the search re-times; NF_PROBE_VERBOSE prints the MFMA
+ * probe's rate per shape (both to stderr). */
 nf_status nf_layer_create(const nf_shape* shape, const nf_weights* w, nf_layer** out);
 void nf_layer_destroy(nf_layer* layer);   /* waits for the layer's streams */
 
