@@ -279,11 +279,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, const fl
   const int c = (int)(idx % cols4) * 4;
   const int64_t zstride = (int64_t)a.M * part_ld;
   const float* P = part + (int64_t)row * part_ld + c;
-  f32x4 v = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    v += *(const f32x4*)(P + s * zstride);
-    if (MODE == GEMM_SWIGLU) u += *(const f32x4*)(P + s * zstride + a.N);
-  }
+  const f32x4 v = sum_slices<f32x4>(P, zstride, splits);
+  f32x4 u = {0.f, 0.f, 0.f, 0.f};
+  if (MODE == GEMM_SWIGLU) u = sum_slices<f32x4>(P + a.N, zstride, splits);
   const int64_t o = (int64_t)row * a.ldc + c;
   if (MODE == GEMM_F32OUT) {
     *(f32x4*)((float*)a.C + o) = v;

@@ -48,6 +48,25 @@ __device__ __forceinline__ int kv_v_off(int s, int d) {
   return (d >> 5) * 512 + ((d & 15) + ((s >> 2) << 4)) * 8 + ((d >> 4) & 1) * 4 + (s & 3);
 }
 
+// Sum of `splits` fp32 partial slices p[0], p[zstride], p[2 zstride], ...
+// (V: float or an fp32 vector) added in slice order from zero, so the result
+// is bit-identical to a sequential loop; the loads of up to 8 slices are
+// issued together instead of one memory latency per slice.
+template <typename V>
+__device__ __forceinline__ V sum_slices(const float* p, int64_t zstride, int splits) {
+  V acc = V{};
+  for (int z0 = 0; z0 < splits; z0 += 8) {
+    V buf[8];
+#pragma unroll
+    for (int z = 0; z < 8; ++z)
+      if (z0 + z < splits) buf[z] = *(const V*)(p + (int64_t)(z0 + z) * zstride);
+#pragma unroll
+    for (int z = 0; z < 8; ++z)
+      if (z0 + z < splits) acc += buf[z];
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------- launch and memory helpers
 
 // The dispatcher deals workgroups round-robin over the 8 XCDs; this maps the

@@ -87,11 +87,8 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_partials_kernel(
   bf16x8* x1r = (bf16x8*)(x1 + row * ldx1);
   float ss = 0.f;
   for (int i = threadIdx.x; i < n8; i += 256) {
-    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-    for (int z = 0; z < splits; ++z) {
-      lo += *(const f32x4*)(P + (int64_t)z * zstride + 8 * i);
-      hi += *(const f32x4*)(P + (int64_t)z * zstride + 8 * i + 4);
-    }
+    const f32x4 lo = sum_slices<f32x4>(P + 8 * i, zstride, splits);
+    const f32x4 hi = sum_slices<f32x4>(P + 8 * i + 4, zstride, splits);
     const bf16x8 r = xr[i];
     bf16x8 o;
 #pragma unroll
@@ -142,11 +139,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   T v0, v1;
   if (a.splits > 1) {           // reduce the QKV GEMM's split-K partials here
     const float* P = a.part + (int64_t)t * a.part_ld + (int64_t)head * d + j;
-    float s0 = 0.f, s1 = 0.f;
-    for (int z = 0; z < a.splits; ++z) {
-      s0 += P[(int64_t)z * a.zstride];
-      s1 += P[(int64_t)z * a.zstride + half];
-    }
+    const float s0 = sum_slices<float>(P, a.zstride, a.splits);
+    const float s1 = sum_slices<float>(P + half, a.zstride, a.splits);
     v0 = from_f32<T>(s0);
     v1 = from_f32<T>(s1);
     T* out = (T*)a.qkv + (int64_t)t * ncols + (int64_t)head * d;
