@@ -881,9 +881,9 @@ namespace {
 // flight: about 24 GB/s per workgroup)
 constexpr double kWgGBps = 20.0, kWgGBpsDB = 24.0, kHbmGBps = 6000.0;
 int stream_splits(const GemmArgs& a, int cfg, int cus) {
-  const double wg_gbps = (cfg == 46 || cfg == 47) ? kWgGBpsDB : kWgGBps;
+  const double wg_gbps = (cfg >= 46 && cfg <= 49) ? kWgGBpsDB : kWgGBps;
   const bool sw = a.mode == GEMM_SWIGLU;
-  const int nbw = (cfg == 42 || cfg == 43 || cfg == 45 || cfg == 47) ? 2 : 1;
+  const int nbw = (cfg == 42 || cfg == 43 || cfg == 45 || cfg == 47 || cfg == 49) ? 2 : 1;
   const int nbt = (sw ? 2 : 1) * (a.N / 32);
   const int n_wg = (nbt + 4 * nbw - 1) / (4 * nbw);
   const int nch = a.K / 16 / stream_kc(cfg);
@@ -912,11 +912,14 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   if (a.Bp) {                   // packed weights: stream them for expert groups
     // (measured: for dense decode-sized M the pipelined LDS kernel below is
     // faster, so configurations 40..43 are chosen only on request; on the
-    // 8-expert workload the double-buffered 46 / 47 beat 44 / 45, and a
-    // 160 x 256 LDS-pipelined tile (configuration 30) ties with them)
+    // 8-expert workload the double-buffered 46 / 47 beat 44 / 45, and for
+    // the down projection (112 chunks per workgroup) 48, which loads A two
+    // chunks ahead, beats 46 by a fifth; for gate/up (32 chunks per
+    // workgroup, 3.5 rounds) 49 did not beat 47; a 160 x 256 LDS-pipelined
+    // tile (configuration 30) ties with 46 / 47)
     const bool sw = a.mode == GEMM_SWIGLU;
     int cfg = 0;
-    if (a.group_off && a.max_group_rows / std::max(1, a.n_groups) <= 160) cfg = sw ? 47 : 46;
+    if (a.group_off && a.max_group_rows / std::max(1, a.n_groups) <= 160) cfg = sw ? 47 : 48;
     if (cfg && a.N % 32 == 0 && a.K % (16 * stream_kc(cfg)) == 0) {
       p.cfg = cfg;
       p.k_splits = stream_splits(a, cfg, cus);

@@ -62,9 +62,9 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
   constexpr int NA = CH / 4096;              // 16-byte A loads per lane per chunk
   constexpr int NB = KC * NBW;               // B loads per wave per chunk
   static_assert(CH % 4096 == 0 && NA >= 1, "chunk");
-  static_assert((PIPE == 1 ? 2 : 1) * (NA + NB) <= 63, "vmcnt range");
+  static_assert((PIPE >= 1 ? 2 : 1) * (NA + NB) + (PIPE == 3 ? NA : 0) <= 63, "vmcnt range");
   static_assert((MODE == GEMM_SWIGLU) == (NBW == 2), "SWIGLU pairs a gate and an up block per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[(PIPE + 1) * CH];
+  __shared__ __attribute__((aligned(1024))) char smem[(PIPE >= 1 ? 2 : 1) * CH];
 
   const GemmArgs& a = p.a;
   const int total = p.n_wg * p.splits * a.n_groups;
@@ -125,7 +125,11 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
     // stays exact; the other waves of the CU keep HBM busy while one wave
     // computes.
     bf16x8 ar[NA];
-    if constexpr (PIPE == 1) {
+    if constexpr (PIPE == 1 || PIPE == 3) {
+      // PIPE 3 loads A two chunks ahead (a second register set), so the A
+      // written to LDS after chunk c's MFMAs has been in flight for a chunk
+      // and a half instead of for the MFMAs alone.
+      constexpr bool A2 = PIPE == 3;
       // Every load is unconditional (the chunk after the last one reloads
       // the last), so the compiler's in-order wait counts stay exact across
       // the loop; one barrier per chunk separates the A writes of chunk c + 1
@@ -141,11 +145,15 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
 #pragma unroll
       for (int j = 0; j < NBW; ++j) rB[j] = buf_rsrc(bsrc[j] - lane);      // wave-uniform: the wave's n-block
       bf16x8 bq[2][KC][NBW];
-      auto load = [&](int c, bf16x8 (&dst)[KC][NBW]) {
+      bf16x8 aq[A2 ? 2 : 1][NA];
+      auto load_a = [&](int c, bf16x8 (&dst)[NA]) {
         c = min(c, nch - 1);
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-          ar[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[i], c * KC * SK * 2, 0));
+          dst[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[i], c * KC * SK * 2, 0));
+      };
+      auto load_b = [&](int c, bf16x8 (&dst)[KC][NBW]) {
+        c = min(c, nch - 1);
 #pragma unroll
         for (int s = 0; s < KC; ++s)
 #pragma unroll
@@ -153,9 +161,9 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
             dst[s][j] = __builtin_bit_cast(
                 bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB[j], lane * 16, (c * KC + s) * 1024, 2));
       };
-      auto put_a = [&](int buf) {
+      auto put_a = [&](int buf, const bf16x8 (&src)[NA]) {
 #pragma unroll
-        for (int i = 0; i < NA; ++i) *(bf16x8*)(smem + buf * CH + ((wave * NA + i) * 64 + lane) * 16) = ar[i];
+        for (int i = 0; i < NA; ++i) *(bf16x8*)(smem + buf * CH + ((wave * NA + i) * 64 + lane) * 16) = src[i];
       };
       auto mma = [&](int buf, const bf16x8 (&src)[KC][NBW]) {
 #pragma unroll
@@ -180,18 +188,40 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
       };
       // chunks in pairs (no exit between the halves, so the accumulators
       // keep their registers), an odd last chunk after the loop
-      load(0, bq[0]);
-      put_a(0);
       int c = 0;
-      for (; c + 1 < nch; c += 2) {
-        load(c + 1, bq[1]);
-        barrier_lds();                // chunk c's A is in buffer 0; chunk c - 1 is done with buffer 1
-        mma(0, bq[0]);
-        put_a(1);
-        load(c + 2, bq[0]);
-        barrier_lds();
-        mma(1, bq[1]);
-        put_a(0);
+      if constexpr (!A2) {
+        load_a(0, aq[0]);
+        load_b(0, bq[0]);
+        put_a(0, aq[0]);
+        for (; c + 1 < nch; c += 2) {
+          load_a(c + 1, aq[0]);
+          load_b(c + 1, bq[1]);
+          barrier_lds();              // chunk c's A is in buffer 0; chunk c - 1 is done with buffer 1
+          mma(0, bq[0]);
+          put_a(1, aq[0]);
+          load_a(c + 2, aq[0]);
+          load_b(c + 2, bq[0]);
+          barrier_lds();
+          mma(1, bq[1]);
+          put_a(0, aq[0]);
+        }
+      } else {
+        load_a(0, aq[0]);
+        load_b(0, bq[0]);
+        load_a(1, aq[1]);
+        put_a(0, aq[0]);
+        for (; c + 1 < nch; c += 2) {
+          load_a(c + 2, aq[0]);       // aq[0] went to LDS as chunk c's A
+          load_b(c + 1, bq[1]);
+          barrier_lds();              // chunk c's A is in buffer 0; chunk c - 1 is done with buffer 1
+          mma(0, bq[0]);
+          put_a(1, aq[1]);            // chunk c + 1's A, loaded a chunk earlier
+          load_a(c + 3, aq[1]);
+          load_b(c + 2, bq[0]);
+          barrier_lds();
+          mma(1, bq[1]);
+          put_a(0, aq[0]);
+        }
       }
       if (c < nch) {
         barrier_lds();
@@ -340,6 +370,7 @@ hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStr
 //   44: 160 rows, 1 block, 16    45: 160 rows, 2 blocks, 16 (expert groups; one
 //   workgroup per CU, so that an expert of up to 160 rows streams its weights once)
 //   46, 47: as 44, 45 with 8 k-steps per chunk, double-buffered
+//   48, 49: as 46, 47 with A loaded two chunks ahead
 hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook) {
   switch (p.cfg) {
     case 40: return launch_stream<1, 1, 16>(a, p, ws, s, hook);
@@ -350,14 +381,16 @@ hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream
     case 45: return launch_stream<5, 2, 16>(a, p, ws, s, hook);
     case 46: return launch_stream<5, 1, 8, 1>(a, p, ws, s, hook);
     case 47: return launch_stream<5, 2, 8, 1>(a, p, ws, s, hook);
+    case 48: return launch_stream<5, 1, 8, 3>(a, p, ws, s, hook);
+    case 49: return launch_stream<5, 2, 8, 3>(a, p, ws, s, hook);
     default: return hipErrorInvalidValue;
   }
 }
 
 int stream_nbw(int cfg) {
   switch (cfg) {
-    case 42: case 43: case 45: case 47: return 2;
-    case 40: case 41: case 44: case 46: return 1;
+    case 42: case 43: case 45: case 47: case 49: return 2;
+    case 40: case 41: case 44: case 46: case 48: return 1;
     default: return 0;
   }
 }
@@ -365,7 +398,7 @@ int stream_nbw(int cfg) {
 int stream_kc(int cfg) {
   switch (cfg) {
     case 40: case 41: case 42: case 43: case 44: case 45: return 16;
-    case 46: case 47: return 8;
+    case 46: case 47: case 48: case 49: return 8;
     default: return 0;
   }
 }
