@@ -438,7 +438,7 @@ struct PCfg {
   static constexpr int SLAB = (BM + BN) * ROWB;          // LDS bytes per stage
   static_assert(BK == 64 || BK == 32, "slab K");
   static_assert(WM * WN == 4 && FM >= 1 && FN >= 2 && FN % 2 == 0 && A_IN >= 1 && B_IN >= 1 && KS >= 1, "cfg");
-  static_assert(STAGES >= 2 && STAGES <= 10 && (STAGES - 2) * X <= 63, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 10 && (STAGES - 1) * X <= 63, "vmcnt range");
   static_assert(STAGES * SLAB <= 160 * 1024, "LDS");
 };
 
@@ -604,60 +604,90 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
   // row fragments of this wave that hold at least one live row (wave-uniform);
   // the rest skip their fragment loads and MFMAs (ragged groups, M % BM)
   const int live = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (rows - m0 - wm * C::WTM + C::MS - 1) / C::MS)));
+  // prologue: every stage's buffer receives a slab
 #pragma unroll
-  for (int t = 0; t < C::STAGES - 1; ++t)
+  for (int t = 0; t < C::STAGES; ++t)
     if (t < nk) issue(t, t);
   const int fr = lane % C::MS, fq = lane / C::MS;
-  // The k loop is instantiated twice: without the live-row checks when every
-  // row fragment of the wave is live (straight-line code, so the LDS reads of
-  // k-step s+1 are waited on only where the MFMAs of s+1 need them), and with
-  // them for the ragged tiles.
+  // Fragment reads run L k-steps ahead of the MFMAs.  A slab's barrier sits
+  // where its last reads have been issued: after it the slab's buffer takes
+  // slab kt + STAGES, and the next slab's first L k-steps are read while the
+  // MFMAs of this slab's last L k-steps run, so no LDS round trip is exposed
+  // at a slab boundary.  The k loop is instantiated twice: without the
+  // live-row checks when every row fragment of the wave is live
+  // (straight-line code), and with them for the ragged tiles.
+  constexpr int KS = C::KS;
+  constexpr int L = KS > 2 ? 2 : 1;
   auto k_loop = [&](auto checked) {
     constexpr bool CHECK = decltype(checked)::value;
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_slab<C>(min(C::STAGES - 2, nk - 1 - kt));
-      barrier_lds();
-      if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
-      const char* sA = smem + (kt % C::STAGES) * C::SLAB;
+    bf16x8 af[KS][C::FM], bfr[KS][C::FN];
+    auto load_frags = [&](const char* sA, int s) {
       const char* sB = sA + C::BM * C::ROWB;
-      // fragments of k-step s+1 are read while the MFMAs of k-step s run
-      constexpr int KS = C::KS;
-      bf16x8 af[2][C::FM], bfr[2][C::FN];
-      auto load_frags = [&](int s, int set) {
-        const int c = s * (C::KSTEP / 8) + fq;
+      const int c = s * (C::KSTEP / 8) + fq;
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          if (CHECK && i >= live) break;
-          const int r = wm * C::WTM + i * C::MS + fr;
-          af[set][i] = *(const bf16x8*)(sA + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int r = b_row(j) + fr;
-          bfr[set][j] = *(const bf16x8*)(sB + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
-        }
-      };
-      load_frags(0, 0);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) load_frags(s + 1, (s + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          if (CHECK && i >= live) break;
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma<C::MS>(af[s & 1][i], bfr[s & 1][j], acc[i][j]);
-        }
+      for (int i = 0; i < C::FM; ++i) {
+        if (CHECK && i >= live) break;
+        const int r = wm * C::WTM + i * C::MS + fr;
+        af[s][i] = *(const bf16x8*)(sA + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
       }
-      if constexpr (!CHECK) {
-        // issue order in the slab: reads of k-steps 0 and 1, then for each
-        // k-step s its MFMAs followed by the reads of step s + 2
-        constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
-        __builtin_amdgcn_sched_group_barrier(0x100, KS > 1 ? 2 * NR : NR, 0);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-          if (s + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+      for (int j = 0; j < C::FN; ++j) {
+        const int r = b_row(j) + fr;
+        bfr[s][j] = *(const bf16x8*)(sB + r * C::ROWB + ((c ^ swz<C>(r)) << 4));
+      }
+    };
+    auto mma_step = [&](int s) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        if (CHECK && i >= live) break;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma<C::MS>(af[s][i], bfr[s][j], acc[i][j]);
+      }
+    };
+    // issue order of a k-step: the NR fragment reads of step s + L go out
+    // RPM at a time after each of its first MFMAs, all within the first half
+    // of them, so the last read has half the step's MFMAs to land
+    constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
+    constexpr int HALF = NM / 2 > 0 ? NM / 2 : 1;
+    constexpr int RPM = (NR + HALF - 1) / HALF;
+    auto order = [&]() {
+      if constexpr (!CHECK) {
+        constexpr int NI = (NR + RPM - 1) / RPM;       // MFMAs with reads after them
+        constexpr int LAST = NR - (NI - 1) * RPM;
+#pragma unroll
+        for (int q = 0; q < NI - 1; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, LAST, 0);
+        if constexpr (NM > NI) __builtin_amdgcn_sched_group_barrier(0x008, NM - NI, 0);
+      }
+    };
+    wait_slab<C, C::STAGES - 1>(min(C::STAGES, nk) - 1);
+    barrier_lds();
+#pragma unroll
+    for (int s = 0; s < L; ++s) load_frags(smem, s);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = smem + (kt % C::STAGES) * C::SLAB;
+      const char* nxt = smem + ((kt + 1) % C::STAGES) * C::SLAB;
+#pragma unroll
+      for (int s = 0; s < KS - L; ++s) {
+        mma_step(s);
+        load_frags(cur, s + L);
+        order();
+      }
+      // every wave holds this slab's last fragments and slab kt + 1 has landed
+      // (nothing of the k-steps above moves below the wait)
+      __builtin_amdgcn_sched_barrier(0);
+      wait_slab<C>(max(0, min(C::STAGES - 2, nk - kt - 2)));
+      barrier_lds();
+      if (kt + C::STAGES < nk) issue(kt + C::STAGES, kt % C::STAGES);
+#pragma unroll
+      for (int s = KS - L; s < KS; ++s) {
+        mma_step(s);
+        load_frags(nxt, s + L - KS);     // after the last slab these reads go unused
+        order();
       }
     }
   };
