@@ -440,6 +440,12 @@ struct PCfg {
   static_assert(WM * WN == 4 && FM >= 1 && FN >= 2 && FN % 2 == 0 && A_IN >= 1 && B_IN >= 1 && KS >= 1, "cfg");
   static_assert(STAGES >= 2 && STAGES <= 10 && (STAGES - 1) * X <= 63, "vmcnt range");
   static_assert(STAGES * SLAB <= 160 * 1024, "LDS");
+  // Slab refills spread over the MFMAs (else issued in one burst): for tiles
+  // that run one workgroup per CU, whose single wave per SIMD would leave the
+  // matrix unit idle while it waits to issue a burst.  With two workgroups
+  // per CU the other one's MFMAs fill that time, and decode-sized tiles gain
+  // more from the earlier issue.
+  static constexpr bool SPREAD = (160 * 1024) / (STAGES * SLAB) == 1 && BM >= 128;
 };
 
 using P10 = PCfg<256, 256, 2, 2, 32, 2>;
@@ -546,6 +552,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
   const __amdgpu_buffer_rsrc_t rA = buf_rsrc(a.A);
   const __amdgpu_buffer_rsrc_t rB = buf_rsrc(Bbase);
   const __amdgpu_buffer_rsrc_t rB2 = buf_rsrc(MODE == GEMM_SWIGLU ? B2base : Bbase);
+  const __amdgpu_buffer_rsrc_t rNone = buf_rsrc_empty(a.A);
   uint32_t offA[C::A_IN], offB[C::B_IN];
   const int lrow = lane / C::CPR, pch = lane % C::CPR;
 #pragma unroll
@@ -570,16 +577,19 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
     n = min(n, a.N - 1);
     offB[i] = (uint32_t)(((int64_t)n * a.ldb + k_lo + 8 * (pch ^ swz<C>(row))) * 2);
   }
-  auto issue = [&](int t, int buf) {
+  // Load d (of X) of slab t into stage buffer buf.  Slabs past the end
+  // (real == false) go through the empty resource: no memory moves, but every
+  // wave issues the same X loads per slab, so the slab waits are constant
+  // vmcnt counts.
+  auto dma1 = [&](int t, int buf, bool real, int d) {
     const uint32_t koff = (uint32_t)(t * C::BK * 2);
     char* sA = smem + buf * C::SLAB;
-    char* sB = sA + C::BM * C::ROWB;
-#pragma unroll
-    for (int i = 0; i < C::A_IN; ++i) dma16_buf(rA, offA[i], koff, sA + (4 * i + wave) * 1024);
-#pragma unroll
-    for (int i = 0; i < C::B_IN; ++i) {
+    if (d < C::A_IN) {
+      dma16_buf(real ? rA : rNone, offA[d], koff, sA + (4 * d + wave) * 1024);
+    } else {
+      const int i = d - C::A_IN;
       const bool up = MODE == GEMM_SWIGLU && (4 * i + wave) * C::RPI >= C::BN / 2;   // wave-uniform
-      dma16_buf(up ? rB2 : rB, offB[i], koff, sB + (4 * i + wave) * 1024);
+      dma16_buf(real ? (up ? rB2 : rB) : rNone, offB[i], koff, sA + C::BM * C::ROWB + (4 * i + wave) * 1024);
     }
   };
 
@@ -604,21 +614,98 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
   // row fragments of this wave that hold at least one live row (wave-uniform);
   // the rest skip their fragment loads and MFMAs (ragged groups, M % BM)
   const int live = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (rows - m0 - wm * C::WTM + C::MS - 1) / C::MS)));
-  // prologue: every stage's buffer receives a slab
+  // prologue: every stage's buffer receives a slab (with SPREAD, slabs past
+  // the end as empty loads)
 #pragma unroll
   for (int t = 0; t < C::STAGES; ++t)
-    if (t < nk) issue(t, t);
+    if (C::SPREAD || t < nk)
+#pragma unroll
+      for (int d = 0; d < C::X; ++d) dma1(t, t, t < nk, d);
   const int fr = lane % C::MS, fq = lane / C::MS;
   // Fragment reads run L k-steps ahead of the MFMAs.  A slab's barrier sits
   // where its last reads have been issued: after it the slab's buffer takes
   // slab kt + STAGES, and the next slab's first L k-steps are read while the
   // MFMAs of this slab's last L k-steps run, so no LDS round trip is exposed
-  // at a slab boundary.  The k loop is instantiated twice: without the
-  // live-row checks when every row fragment of the wave is live
+  // at a slab boundary.  With SPREAD the refill loads are spread evenly over
+  // those MFMAs: the CU's path from L2 takes about as long to accept a slab
+  // as the MFMAs of half a slab take, and a wave waiting to issue a load
+  // issues no MFMA, so a burst of loads would leave the matrix unit idle.
+  // The instruction order is fixed by scheduling barriers (the compiler's own
+  // interleaving bunched the loads).  The k loop is instantiated twice:
+  // without the live-row checks when every row fragment of the wave is live
   // (straight-line code), and with them for the ragged tiles.
   constexpr int KS = C::KS;
   constexpr int L = KS > 2 ? 2 : 1;
-  auto k_loop = [&](auto checked) {
+  auto k_loop_spread = [&](auto checked) {
+    constexpr bool CHECK = decltype(checked)::value;
+    bf16x8 af[KS][C::FM], bfr[KS][C::FN];
+    // fragment read r of k-step s: A row fragments first, then B
+    auto read1 = [&](const char* sA, int s, int r) {
+      const int c = s * (C::KSTEP / 8) + fq;
+      if (r < C::FM) {
+        if (CHECK && r >= live) return;
+        const int row = wm * C::WTM + r * C::MS + fr;
+        af[s][r] = *(const bf16x8*)(sA + row * C::ROWB + ((c ^ swz<C>(row)) << 4));
+      } else {
+        const int row = b_row(r - C::FM) + fr;
+        bfr[s][r - C::FM] = *(const bf16x8*)(sA + C::BM * C::ROWB + row * C::ROWB + ((c ^ swz<C>(row)) << 4));
+      }
+    };
+    auto mma1 = [&](int s, int q) {
+      const int i = q / C::FN, j = q % C::FN;
+      if (CHECK && i >= live) return;
+      acc[i][j] = mfma<C::MS>(af[s][i], bfr[s][j], acc[i][j]);
+    };
+    // One k-step: after MFMA q come the fragment reads of step `rs` from
+    // `src` assigned to it (RPM each for the first MFMAs, so the last read has
+    // half the step's MFMAs to land) and the refill loads d0 .. d0 + D - 1
+    // whose even spacing over the NM MFMAs falls on q.
+    constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
+    constexpr int HALF = NM / 2 > 0 ? NM / 2 : 1;
+    constexpr int RPM = (NR + HALF - 1) / HALF;
+    auto step = [&](int s, const char* src, int rs, int D, int d0, int t, int buf, bool real) {
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        mma1(s, q);
+#pragma unroll
+        for (int r = min(q * RPM, NR); r < min((q + 1) * RPM, NR); ++r) read1(src, rs, r);
+#pragma unroll
+        for (int d = (q * D + NM - 1) / NM; d < ((q + 1) * D + NM - 1) / NM; ++d) dma1(t, buf, real, d0 + d);
+        if constexpr (!CHECK) __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    constexpr int D_FIRST = (C::X + L - 1) / L, D_REST = (C::X - D_FIRST) / (L > 1 ? L - 1 : 1);
+    static_assert(D_FIRST + (L - 1) * D_REST == C::X, "refill loads per k-step");
+    wait_vmcnt<(C::STAGES - 1) * C::X>();
+    barrier_lds();
+#pragma unroll
+    for (int s = 0; s < L; ++s)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read1(smem, s, r);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = smem + (kt % C::STAGES) * C::SLAB;
+      const char* nxt = smem + ((kt + 1) % C::STAGES) * C::SLAB;
+#pragma unroll
+      for (int s = 0; s < KS - L; ++s) step(s, cur, s + L, 0, 0, 0, 0, false);
+      // every wave holds this slab's last fragments and slab kt + 1 has landed
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<(C::STAGES - 2) * C::X>();
+      barrier_lds();
+      const int t = kt + C::STAGES, buf = kt % C::STAGES;
+      const bool real = t < nk;
+#pragma unroll
+      for (int s = KS - L; s < KS; ++s) {
+        // the next slab's first k-steps (after the last slab these reads go unused)
+        const int first = s == KS - L;
+        step(s, nxt, s + L - KS, first ? D_FIRST : D_REST, first ? 0 : D_FIRST + (s - KS + L - 1) * D_REST, t, buf, real);
+      }
+    }
+    wait_vmcnt<0>();                     // the empty loads too: none may land during the epilogue
+  };
+  // Burst refills: the slab's loads are issued together right after the
+  // barrier, only for slabs that exist, and the compiler interleaves the
+  // fragment reads with the MFMAs.
+  auto k_loop_burst = [&](auto checked) {
     constexpr bool CHECK = decltype(checked)::value;
     bf16x8 af[KS][C::FM], bfr[KS][C::FN];
     auto load_frags = [&](const char* sA, int s) {
@@ -682,7 +769,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
       __builtin_amdgcn_sched_barrier(0);
       wait_slab<C>(max(0, min(C::STAGES - 2, nk - kt - 2)));
       barrier_lds();
-      if (kt + C::STAGES < nk) issue(kt + C::STAGES, kt % C::STAGES);
+      if (kt + C::STAGES < nk)
+#pragma unroll
+        for (int d = 0; d < C::X; ++d) dma1(kt + C::STAGES, kt % C::STAGES, true, d);
 #pragma unroll
       for (int s = KS - L; s < KS; ++s) {
         mma_step(s);
@@ -690,6 +779,12 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
         order();
       }
     }
+  };
+  auto k_loop = [&](auto checked) {
+    if constexpr (C::SPREAD)
+      k_loop_spread(checked);
+    else
+      k_loop_burst(checked);
   };
   // grouped GEMMs stream weights: their MFMAs on clamped rows past a
   // group's end cost nothing, the checked loop's waits would

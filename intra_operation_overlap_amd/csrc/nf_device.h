@@ -85,6 +85,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)0xffffffff, 0x00020000);
 }
 
+// Buffer resource with no records: every load through it is out of range, so
+// it moves no memory (a load with it stands in for a load that must not run,
+// keeping loop bodies branch-free and per-wave load counts constant).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_empty(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0, 0x00020000);
+}
+
 // 16 bytes per lane from base + soff + voff straight into LDS through the
 // buffer unit (buffer_load_dwordx4 ... lds): lane l writes lds + 16 l, so one
 // instruction fills 1 KB.  The global form (global_load_lds) would do the
