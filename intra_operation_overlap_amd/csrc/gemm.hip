@@ -812,8 +812,25 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
       constexpr int RP = stage_rows(C::BM, FIT);          // rows per pass
       static_assert(RP >= 32 && C::BM % RP == 0, "staging");
       constexpr int CH = BNO / 8;                          // 16-byte output chunks per row
+      // Residual chunks of a pass are loaded one pass ahead (the first right
+      // after the k loop), so their latency hides behind the previous pass.
+      constexpr int NPASS = C::BM / RP, PER = RP * CH / 256;
+      static_assert(RP * CH % 256 == 0, "chunks per thread");
+      bf16x8 res[F32S ? NPASS : 1][F32S ? PER : 1];
+      auto load_res = [&](int pass) {
+        if constexpr (F32S) {
 #pragma unroll
-      for (int pass = 0; pass < C::BM / RP; ++pass) {
+          for (int e = 0; e < PER; ++e) {
+            const int idx = threadIdx.x + e * 256;
+            const int local = m0 + pass * RP + idx / CH, col = n0 + (idx % CH) * 8;
+            if (local < rows && col < a.N)
+              res[pass][e] = *(const bf16x8*)((const bf16*)a.R + (m_begin + local) * a.ldr + col);
+          }
+        }
+      };
+      load_res(0);
+#pragma unroll
+      for (int pass = 0; pass < NPASS; ++pass) {
         __syncthreads();                                   // LDS free (slabs, or the previous pass)
         const int r_lo = pass * RP;
 #pragma unroll
@@ -840,7 +857,10 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
           }
         }
         __syncthreads();
-        for (int idx = threadIdx.x; idx < RP * CH; idx += 256) {
+        if (pass + 1 < NPASS) load_res(pass + 1);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int idx = threadIdx.x + e * 256;
           const int rr = idx / CH, ch = idx % CH;
           const int local = m0 + r_lo + rr;
           const int col = n0 + ch * 8;
@@ -850,11 +870,11 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
           if constexpr (F32S) {
             const f32x4 v0 = *(const f32x4*)(smem + rr * ROWB_O + ch * 32);
             const f32x4 v1 = *(const f32x4*)(smem + rr * ROWB_O + ch * 32 + 16);
-            const bf16x8 res = *(const bf16x8*)((const bf16*)a.R + orow * a.ldr + col);
+            const bf16x8 rv = res[pass][e];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              out[e] = (bf16)(v0[e] + (float)res[e]);
-              out[e + 4] = (bf16)(v1[e] + (float)res[e + 4]);
+            for (int q = 0; q < 4; ++q) {
+              out[q] = (bf16)(v0[q] + (float)rv[q]);
+              out[q + 4] = (bf16)(v1[q] + (float)rv[q + 4]);
             }
           } else {
             out = *(const bf16x8*)(smem + rr * ROWB_O + ch * 16);

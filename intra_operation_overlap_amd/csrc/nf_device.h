@@ -30,7 +30,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU z * sigmoid(z), the reciprocal by v_rcp_f32 (1 ulp; the result is
+// rounded to bf16).  Large negative z gives -0, as the quotient does.
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Element offsets inside one (page, KV head) block of 16 key slots x D dims
 // (D % 32 == 0): the KV pool stores each block in the operand order of the
