@@ -159,6 +159,7 @@ typedef struct nf_search_opts {
 
 typedef struct nf_layer nf_layer;
 typedef struct nf_kv_pool nf_kv_pool;
+typedef struct nf_graph nf_graph;
 
 /* ---- layer ---------------------------------------------------------------
  * nf_layer_create: validates the shape, binds the caller's weights (pointers
@@ -220,6 +221,54 @@ nf_status nf_batch_validate(const nf_shape* shape, int32_t n_pages, int32_t page
  * slots of the batch's new positions and the layer's workspace.  Calls on
  * one layer must not overlap on different host threads. */
 nf_status nf_layer_step(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch, void* stream);
+
+/* ---- multi-layer step -------------------------------------------------------
+ * Runs layers[0..n_layers-1] in order on one batch, each with its own KV pool
+ * (pools[l] created for layers[l]): batch->x is layer 0's input, each layer
+ * reads the previous one's output (a buffer of the producing layer, grown to
+ * [T][H] on first use), and the last layer writes batch->out.  The layers
+ * must be distinct objects with the same hidden size, dtype, max_tokens,
+ * expert count and device; mixture-of-experts layers all route with
+ * batch->router_logits.  Every layer runs layer 0's plan.
+ * With two streams, two or more nano-batches and the pipelined order, the
+ * nano-batches are pipelined across layers.  The hysenlabs Nanoflow page
+ * (section "Nano-batching and the device-level pipeline") has nano-batching
+ * break the dependency between sequential operations so a device-level
+ * pipeline can co-schedule them; a nano-batch's rows depend only on its own
+ * rows of the previous layer, so here the pipeline continues across layer
+ * boundaries: nano-batch j's norm, QKV and RoPE/append of layer l + 1 are
+ * issued right after its O-projection and FFN of layer l, before nano-batch
+ * j + 1's of layer l, so j's attention in layer l + 1 runs beside j + 1's
+ * GEMMs and no layer boundary drains the pipeline.  Otherwise each layer
+ * runs as nf_layer_step would run it.  The
+ * result equals that of nf_layer_step applied layer by layer (bit for bit:
+ * the same kernels on the same rows).  Asynchronous like nf_layer_step; calls
+ * on the same layers must not overlap.  Errors: NF_ERR_INVALID_ARG (null
+ * argument, n_layers < 1, a pool of another layer, a repeated layer, layers
+ * that differ), then any error of nf_layer_step. */
+nf_status nf_stack_step(nf_layer* const* layers, nf_kv_pool* const* pools, int32_t n_layers, const nf_batch* batch,
+                        void* stream);
+
+/* Records nf_stack_step(layers, pools, n_layers, batch) as a HIP graph, whose
+ * replays (nf_graph_launch) redo exactly that step, launch for launch, with no
+ * host work per kernel.  It first runs the step once on `stream` (writing
+ * batch->out and the batch's pool slots), synchronises, copies each layer's
+ * step metadata (positions, page tables, attention work items) into device
+ * buffers the graph owns, then captures the launches on `stream`.  The graph
+ * reads batch->x, writes batch->out, the batch's pool slots and the layers'
+ * buffers at every replay, so those must stay allocated, and replays must
+ * not overlap each other or steps on the same layers; a layer's buffers are
+ * never freed before nf_layer_destroy, so a later larger step does not
+ * invalidate the graph.  The host arrays of `batch` may be reused on return.
+ * Errors: as nf_stack_step; NF_ERR_INVALID_ARG for an empty batch;
+ * NF_ERR_UNSUPPORTED for a plan with a CU split (a graph keeps no stream's CU
+ * mask) or with per-kernel timing on; NF_ERR_HIP if the capture fails. */
+nf_status nf_stack_graph_create(nf_layer* const* layers, nf_kv_pool* const* pools, int32_t n_layers,
+                                const nf_batch* batch, void* stream, nf_graph** out);
+/* Enqueues one replay on `stream`.  Errors: NF_ERR_INVALID_ARG, NF_ERR_HIP. */
+nf_status nf_graph_launch(nf_graph* graph, void* stream);
+/* Waits for the device, then frees the graph and its metadata buffers. */
+void nf_graph_destroy(nf_graph* graph);
 
 /* ---- plan search -----------------------------------------------------------
  * Profile-driven choice of the plan for this batch.  It stands in for the

@@ -67,6 +67,11 @@ _SIGS = {
     "nf_batch_validate": (i32, [ctypes.POINTER(nf_shape), i32, i32, ctypes.POINTER(nf_batch),
                                 ctypes.POINTER(nf_plan)]),
     "nf_layer_step": (i32, [vp, vp, ctypes.POINTER(nf_batch), vp]),
+    "nf_stack_step": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(nf_batch), vp]),
+    "nf_stack_graph_create": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(nf_batch), vp,
+                                    ctypes.POINTER(vp)]),
+    "nf_graph_launch": (i32, [vp, vp]),
+    "nf_graph_destroy": (None, [vp]),
     "nf_plan_search": (i32, [vp, vp, ctypes.POINTER(nf_batch), ctypes.POINTER(nf_search_opts),
                              ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double), vp]),
     "nf_layer_intermediate": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64)]),
@@ -235,6 +240,41 @@ class KVPool:
     def close(self):
         if self.h:
             lib().nf_kv_pool_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _handles(objs) -> "ctypes.Array":
+    return (vp * len(objs))(*(o.h for o in objs))
+
+
+def stack_step(layers: List[Layer], pools: List[KVPool], hb: HostBatch, stream: int = 0) -> None:
+    """nf_stack_step: the layers in order on one batch (hb.x in, hb.out out)."""
+    check(lib().nf_stack_step(_handles(layers), _handles(pools), len(layers), ctypes.byref(hb.c), stream),
+          "nf_stack_step")
+
+
+class StackGraph:
+    """nf_stack_graph_create / nf_graph_launch / nf_graph_destroy."""
+
+    def __init__(self, layers: List[Layer], pools: List[KVPool], hb: HostBatch, stream: int = 0):
+        self._keep = (layers, pools, hb)
+        h = vp()
+        check(lib().nf_stack_graph_create(_handles(layers), _handles(pools), len(layers), ctypes.byref(hb.c), stream,
+                                          ctypes.byref(h)), "nf_stack_graph_create")
+        self.h = h
+
+    def launch(self, stream: int = 0) -> None:
+        check(lib().nf_graph_launch(self.h, stream), "nf_graph_launch")
+
+    def close(self):
+        if self.h:
+            lib().nf_graph_destroy(self.h)
             self.h = None
 
     def __del__(self):

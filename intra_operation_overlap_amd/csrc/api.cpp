@@ -64,6 +64,9 @@ constexpr int PAGE_SIZE = 16;
 struct DevBuf {
   void* p = nullptr;
   size_t bytes = 0;
+  // buffers this one outgrew: kept until the layer is destroyed, so device
+  // pointers captured in a graph stay valid (and growing needs no sync)
+  std::vector<void*> old;
 };
 
 // Kinds of kernel launches, for the per-kernel timing facility.
@@ -105,6 +108,7 @@ struct nf_layer {
   DevBuf h, qkv, q_rot, attn, x1, h2, act, y;
   DevBuf r_idx, r_w, r_perm, r_inv, r_off;
   DevBuf splitk, part_o, part_ml, meta, cos_sin;
+  DevBuf stack_out;                             // this layer's output inside a multi-layer step
   // expert weights in MFMA operand order for the weight-streaming kernels
   // (bf16 mixture-of-experts layers; empty otherwise)
   DevBuf wp_qkv, wp_o, wp_gu, wp_down;
@@ -136,11 +140,8 @@ namespace {
 
 hipError_t ensure(DevBuf& b, size_t bytes) {
   if (bytes <= b.bytes) return hipSuccess;
-  if (b.p) {
-    hipError_t e = hipDeviceSynchronize();     // the old buffer may still be in use
-    if (e != hipSuccess) return e;
-    e = hipFree(b.p);
-    if (e != hipSuccess) return e;
+  if (b.p) {                 // may still be in use by queued work or a graph
+    b.old.push_back(b.p);
     b.p = nullptr;
     b.bytes = 0;
   }
@@ -156,6 +157,8 @@ hipError_t ensure(DevBuf& b, size_t bytes) {
 
 void release(DevBuf& b) {
   if (b.p) (void)hipFree(b.p);
+  for (void* q : b.old) (void)hipFree(q);
+  b.old.clear();
   b.p = nullptr;
   b.bytes = 0;
 }
@@ -566,7 +569,23 @@ hipError_t pack_weights(nf_layer* L) {
   return hipDeviceSynchronize();
 }
 
-nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t caller, const nf_plan& plan) {
+// One layer's step as prepared for launch: its batch (the caller's, with this
+// layer's input and output rows), its context and nano-batch count.
+struct LayerRun {
+  nf_layer* L = nullptr;
+  nf_batch b{};
+  StepCtx c{};
+  int count = 0;
+};
+
+// Everything of one layer's step before its launches: the checks, the
+// attention work items, the workspace and the metadata image.  With
+// fixed_meta == nullptr the metadata goes through the layer's pinned staging
+// buffer and the first front's RMSNorm copies it on the device; otherwise it
+// is copied now, synchronously, into *fixed_meta (a buffer the caller owns,
+// grown here), so that launches captured in a graph read it there.
+nf_status prepare_layer(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_plan& plan, DevBuf* fixed_meta,
+                        LayerRun& r) {
   std::string err;
   nf_status st = check_batch(L->s, P->n_pages, P->page_size, *b, err);
   if (st != NF_OK) return set_err(st, "%s", err.c_str());
@@ -574,16 +593,20 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
   if (st != NF_OK) return set_err(st, "%s", err.c_str());
   const int T = b->n_tokens, R = b->n_requests;
   L->last_T = T;
+  r.L = L;
+  r.b = *b;
+  r.count = 0;
   if (T == 0) return NF_OK;
   HIP_TRY(hipSetDevice(L->device));
 
   const bool two = plan.n_streams == 2;
   const int gsplit = two ? plan.gemm_cus_per_xcd : 0;
   const int asplit = two ? attn_budget(plan.gemm_cus_per_xcd, plan.attn_cus_per_xcd, L->cus_per_xcd) : 0;
-  StepCtx c{};
+  StepCtx& c = r.c;
+  c = StepCtx{};
   c.L = L;
   c.P = P;
-  c.b = b;
+  c.b = &r.b;
   c.gemm_cus = gsplit ? gsplit * L->n_xcd : L->n_cus;
   c.attn_cus = asplit ? asplit * L->n_xcd : L->n_cus;
   c.attn_waves_per_cu = two ? plan.attn_waves_per_cu : 0;
@@ -596,11 +619,11 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
   build_work(L->s, *b, plan, P->page_size, wave_items ? 8 * c.attn_cus : 2 * c.attn_cus, 8,
              wave_items ? 32 : 0, L->work);
   const StepWork& w = L->work;
-  const int count = (int)w.nanos.size();
+  r.count = (int)w.nanos.size();
 
   // workspace the GEMMs and the split attention items need (before any launch)
   size_t ws = 0;
-  for (int j = 0; j < count; ++j) {
+  for (int j = 0; j < r.count; ++j) {
     NanoGemms g = nano_gemms(c, j, w.nanos[j].t0, w.nanos[j].t1);
     if (L->s.n_experts == 1)
       for (const GemmArgs* a : {&g.qkv, &g.o, &g.gu, &g.down}) ws = std::max(ws, gemm_ws_need(c, *a));
@@ -618,93 +641,211 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
                o_it = o_ix + align_words(nnz), o_mg = o_it + align_words(w.items.size() * 8),
                words = o_mg + align_words(w.merges.size() * 4);
   const size_t bytes = words * 4;
-  const int si = L->stage_i;
-  L->stage_i ^= 1;
-  if (L->stage_used[si]) HIP_TRY(hipEventSynchronize(L->stage_ev[si]));  // previous copy from it done
-  if (L->stage_bytes[si] < bytes) {
-    if (L->stage[si]) HIP_TRY(hipHostFree(L->stage[si]));
-    L->stage[si] = nullptr;
-    L->stage_bytes[si] = 0;
-    HIP_TRY(hipHostMalloc(&L->stage[si], bytes * 2, hipHostMallocMapped | hipHostMallocCoherent));
-    HIP_TRY(hipHostGetDevicePointer(&L->stage_dev[si], L->stage[si], 0));
-    L->stage_bytes[si] = bytes * 2;
+  auto fill = [&](int32_t* hs) {
+    std::memcpy(hs + o_tok, w.tok_req.data(), (size_t)T * 4);
+    std::memcpy(hs + o_pos, b->pos, (size_t)T * 4);
+    std::memcpy(hs + o_ip, b->page_indptr, (size_t)(R + 1) * 4);
+    std::memcpy(hs + o_ix, b->page_indices, (size_t)nnz * 4);
+    if (!w.items.empty()) std::memcpy(hs + o_it, w.items.data(), w.items.size() * sizeof(AttnItem));
+    if (!w.merges.empty()) std::memcpy(hs + o_mg, w.merges.data(), w.merges.size() * sizeof(MergeItem));
+  };
+  const int32_t* dm = nullptr;
+  if (fixed_meta) {
+    HIP_TRY(ensure(*fixed_meta, bytes));
+    std::vector<int32_t> img(words, 0);
+    fill(img.data());
+    HIP_TRY(hipMemcpy(fixed_meta->p, img.data(), bytes, hipMemcpyHostToDevice));
+    c.mc_pending = false;
+    dm = (const int32_t*)fixed_meta->p;
+  } else {
+    const int si = L->stage_i;
+    L->stage_i ^= 1;
+    if (L->stage_used[si]) HIP_TRY(hipEventSynchronize(L->stage_ev[si]));  // previous copy from it done
+    if (L->stage_bytes[si] < bytes) {
+      if (L->stage[si]) HIP_TRY(hipHostFree(L->stage[si]));
+      L->stage[si] = nullptr;
+      L->stage_bytes[si] = 0;
+      HIP_TRY(hipHostMalloc(&L->stage[si], bytes * 2, hipHostMallocMapped | hipHostMallocCoherent));
+      HIP_TRY(hipHostGetDevicePointer(&L->stage_dev[si], L->stage[si], 0));
+      L->stage_bytes[si] = bytes * 2;
+    }
+    if (L->meta.bytes < bytes) HIP_TRY(ensure(L->meta, bytes * 2));
+    fill((int32_t*)L->stage[si]);
+    // copied on the device by extra blocks of the first front's RMSNorm, which
+    // precedes every reader of the metadata on its stream
+    c.mc.src = L->stage_dev[si];
+    c.mc.dst = L->meta.p;
+    c.mc.n16 = (int64_t)(bytes / 16);
+    c.mc_pending = true;
+    c.mc_event = L->stage_ev[si];
+    L->stage_used[si] = true;
+    dm = (const int32_t*)L->meta.p;
   }
-  if (L->meta.bytes < bytes) HIP_TRY(ensure(L->meta, bytes * 2));
-  int32_t* hs = (int32_t*)L->stage[si];
-  std::memcpy(hs + o_tok, w.tok_req.data(), (size_t)T * 4);
-  std::memcpy(hs + o_pos, b->pos, (size_t)T * 4);
-  std::memcpy(hs + o_ip, b->page_indptr, (size_t)(R + 1) * 4);
-  std::memcpy(hs + o_ix, b->page_indices, (size_t)nnz * 4);
-  if (!w.items.empty()) std::memcpy(hs + o_it, w.items.data(), w.items.size() * sizeof(AttnItem));
-  if (!w.merges.empty()) std::memcpy(hs + o_mg, w.merges.data(), w.merges.size() * sizeof(MergeItem));
-  // copied on the device by extra blocks of the first front's RMSNorm, which
-  // precedes every reader of the metadata on its stream
-  c.mc.src = L->stage_dev[si];
-  c.mc.dst = L->meta.p;
-  c.mc.n16 = (int64_t)(bytes / 16);
-  c.mc_pending = true;
-  c.mc_event = L->stage_ev[si];
-  L->stage_used[si] = true;
-  const int32_t* dm = (const int32_t*)L->meta.p;
   c.tok_req = dm + o_tok;
   c.pos = dm + o_pos;
   c.indptr = dm + o_ip;
   c.indices = dm + o_ix;
   c.items = (const AttnItem*)(dm + o_it);
   c.merges = (const MergeItem*)(dm + o_mg);
+  return NF_OK;
+}
 
-  // Streams: the GEMM side runs on the caller's stream unless it is CU-masked;
-  // attention runs on the pair's attention stream.  Cross-stream waits cost
-  // ~20 us each on this runtime, so only the necessary ones are issued:
-  // attention(j) waits for RoPE/append(j), the O-projection of j waits for
-  // attention(j).  The last of those also orders every attention kernel
-  // before the end of the step on the GEMM stream.
-  hipStream_t sg = caller, sa = caller;
-  if (two) {
-    StreamPair pr;
-    st = get_pair(L, gsplit, plan.attn_cus_per_xcd, pr);
-    if (st != NF_OK) return st;
-    sa = pr.a;
-    if (gsplit) {
-      sg = pr.g;
-      HIP_TRY(hipEventRecord(L->ev_start, caller));
-      HIP_TRY(hipStreamWaitEvent(sg, L->ev_start, 0));
-    }
-  }
-  auto front_and_attn = [&](int j) -> nf_status {
-    nf_status s1 = issue_front(c, j, sg);
-    if (s1 != NF_OK) return s1;
-    if (two) {
-      HIP_TRY(hipEventRecord(L->ev_app[j], sg));
-      HIP_TRY(hipStreamWaitEvent(sa, L->ev_app[j], 0));
-    }
-    s1 = issue_attention(c, j, sa);
-    if (s1 != NF_OK) return s1;
-    if (two) HIP_TRY(hipEventRecord(L->ev_att[j], sa));
-    return NF_OK;
-  };
-  auto back = [&](int j) -> nf_status {
-    if (two) HIP_TRY(hipStreamWaitEvent(sg, L->ev_att[j], 0));
-    return issue_back(c, j, sg);
-  };
-  if (plan.order == NF_ORDER_PIPELINED) {
-    st = front_and_attn(0);
-    if (st != NF_OK) return st;
-    for (int j = 0; j < count; ++j) {
-      if (j + 1 < count && (st = front_and_attn(j + 1)) != NF_OK) return st;
-      if ((st = back(j)) != NF_OK) return st;
-    }
-  } else {
-    for (int j = 0; j < count; ++j) {
-      if ((st = front_and_attn(j)) != NF_OK) return st;
-      if ((st = back(j)) != NF_OK) return st;
-    }
-  }
-  if (two && sg != caller) {
-    HIP_TRY(hipEventRecord(L->ev_g, sg));
-    HIP_TRY(hipStreamWaitEvent(caller, L->ev_g, 0));
+// Streams of a step (or of every layer of a multi-layer step): the GEMM side
+// runs on the caller's stream unless it is CU-masked; attention runs on the
+// pair's attention stream.  Cross-stream waits cost ~20 us each on this
+// runtime, so only the necessary ones are issued: attention(j) waits for
+// RoPE/append(j), the O-projection of j waits for attention(j).  The last of
+// those also orders every attention kernel before the end of the step on the
+// GEMM stream.
+struct Streams {
+  bool two = false;
+  hipStream_t caller = nullptr, sg = nullptr, sa = nullptr;
+};
+
+nf_status open_streams(nf_layer* L, const nf_plan& plan, hipStream_t caller, Streams& S) {
+  S.two = plan.n_streams == 2;
+  S.caller = S.sg = S.sa = caller;
+  if (!S.two) return NF_OK;
+  StreamPair pr;
+  nf_status st = get_pair(L, plan.gemm_cus_per_xcd, plan.attn_cus_per_xcd, pr);
+  if (st != NF_OK) return st;
+  S.sa = pr.a;
+  if (plan.gemm_cus_per_xcd) {
+    S.sg = pr.g;
+    HIP_TRY(hipEventRecord(L->ev_start, caller));
+    HIP_TRY(hipStreamWaitEvent(S.sg, L->ev_start, 0));
   }
   return NF_OK;
+}
+
+nf_status close_streams(nf_layer* L, const Streams& S) {
+  if (S.two && S.sg != S.caller) {
+    HIP_TRY(hipEventRecord(L->ev_g, S.sg));
+    HIP_TRY(hipStreamWaitEvent(S.caller, L->ev_g, 0));
+  }
+  return NF_OK;
+}
+
+// front (norm, QKV, RoPE/append) of nano-batch j and its attention
+nf_status issue_front_attn(LayerRun& r, const Streams& S, int j) {
+  nf_layer* L = r.L;
+  nf_status st = issue_front(r.c, j, S.sg);
+  if (st != NF_OK) return st;
+  if (S.two) {
+    HIP_TRY(hipEventRecord(L->ev_app[j], S.sg));
+    HIP_TRY(hipStreamWaitEvent(S.sa, L->ev_app[j], 0));
+  }
+  st = issue_attention(r.c, j, S.sa);
+  if (st != NF_OK) return st;
+  if (S.two) HIP_TRY(hipEventRecord(L->ev_att[j], S.sa));
+  return NF_OK;
+}
+
+// back (O-projection, norm, FFN or experts) of nano-batch j
+nf_status issue_back_after_attn(LayerRun& r, const Streams& S, int j) {
+  if (S.two) HIP_TRY(hipStreamWaitEvent(S.sg, r.L->ev_att[j], 0));
+  return issue_back(r.c, j, S.sg);
+}
+
+// one layer's launches in the plan's order
+nf_status issue_layer(LayerRun& r, const Streams& S, int order) {
+  nf_status st;
+  if (order == NF_ORDER_PIPELINED) {
+    if ((st = issue_front_attn(r, S, 0)) != NF_OK) return st;
+    for (int j = 0; j < r.count; ++j) {
+      if (j + 1 < r.count && (st = issue_front_attn(r, S, j + 1)) != NF_OK) return st;
+      if ((st = issue_back_after_attn(r, S, j)) != NF_OK) return st;
+    }
+  } else {
+    for (int j = 0; j < r.count; ++j) {
+      if ((st = issue_front_attn(r, S, j)) != NF_OK) return st;
+      if ((st = issue_back_after_attn(r, S, j)) != NF_OK) return st;
+    }
+  }
+  return NF_OK;
+}
+
+// The launches of a prepared multi-layer step.  With two streams, several
+// nano-batches and the pipelined order, nano-batches are pipelined across
+// layers: nano-batch j's front of layer l + 1 is issued right after its back
+// of layer l, before nano-batch j + 1's back of layer l, so j's next
+// attention overlaps j + 1's remaining GEMMs and no layer boundary drains the
+// pipeline.  Otherwise the layers run one after another in the plan's order.
+nf_status issue_stack(std::vector<LayerRun>& runs, const Streams& S, int order) {
+  nf_status st;
+  const int n = (int)runs.size(), count = runs[0].count;
+  if (!S.two || count < 2 || order != NF_ORDER_PIPELINED) {
+    for (LayerRun& r : runs)
+      if ((st = issue_layer(r, S, order)) != NF_OK) return st;
+    return NF_OK;
+  }
+  if ((st = issue_front_attn(runs[0], S, 0)) != NF_OK) return st;
+  for (int l = 0; l < n; ++l)
+    for (int j = 0; j < count; ++j) {
+      if (l == 0 && j + 1 < count && (st = issue_front_attn(runs[0], S, j + 1)) != NF_OK) return st;
+      if ((st = issue_back_after_attn(runs[l], S, j)) != NF_OK) return st;
+      if (l + 1 < n && (st = issue_front_attn(runs[l + 1], S, j)) != NF_OK) return st;
+    }
+  return NF_OK;
+}
+
+nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t caller, const nf_plan& plan) {
+  LayerRun r;
+  nf_status st = prepare_layer(L, P, b, plan, nullptr, r);
+  if (st != NF_OK || r.count == 0) return st;
+  Streams S;
+  if ((st = open_streams(L, plan, caller, S)) != NF_OK) return st;
+  if ((st = issue_layer(r, S, plan.order)) != NF_OK) return st;
+  return close_streams(L, S);
+}
+
+// Checks of a multi-layer step's arguments (no HIP call).
+nf_status check_stack(nf_layer* const* layers, nf_kv_pool* const* pools, int n, const nf_batch* b) {
+  if (!layers || !pools || !b) return set_err(NF_ERR_INVALID_ARG, "stack: null argument");
+  if (n < 1) return set_err(NF_ERR_INVALID_ARG, "stack: n_layers %d must be positive", n);
+  for (int l = 0; l < n; ++l) {
+    if (!layers[l] || !pools[l]) return set_err(NF_ERR_INVALID_ARG, "stack: layer or pool %d is null", l);
+    if (pools[l]->layer != layers[l]) return set_err(NF_ERR_INVALID_ARG, "stack: pool %d belongs to another layer", l);
+    for (int m = 0; m < l; ++m)
+      if (layers[m] == layers[l]) return set_err(NF_ERR_INVALID_ARG, "stack: layer %d appears twice", l);
+    const nf_shape &s0 = layers[0]->s, &sl = layers[l]->s;
+    if (sl.hidden != s0.hidden || sl.dtype != s0.dtype || sl.max_tokens != s0.max_tokens ||
+        sl.n_experts != s0.n_experts || layers[l]->device != layers[0]->device)
+      return set_err(NF_ERR_INVALID_ARG, "stack: layer %d differs from layer 0 in hidden size, dtype, "
+                     "max_tokens, experts or device", l);
+  }
+  return NF_OK;
+}
+
+// Prepares every layer of a multi-layer step (layer 0's plan for all); layer
+// l writes its own stack_out buffer, which layer l + 1 reads.
+nf_status prepare_stack(nf_layer* const* layers, nf_kv_pool* const* pools, int n, const nf_batch* b,
+                        std::vector<DevBuf>* fixed_meta, std::vector<LayerRun>& runs) {
+  const nf_plan& plan = layers[0]->plan;
+  const nf_shape& s = layers[0]->s;
+  runs.assign(n, LayerRun{});
+  HIP_TRY(hipSetDevice(layers[0]->device));
+  const size_t io = (size_t)std::max(0, b->n_tokens) * s.hidden * dtype_bytes(s.dtype);
+  for (int l = 0; l + 1 < n; ++l) HIP_TRY(ensure(layers[l]->stack_out, io));
+  for (int l = 0; l < n; ++l) {
+    nf_batch bl = *b;
+    if (l > 0) bl.x = layers[l - 1]->stack_out.p;
+    if (l + 1 < n) bl.out = layers[l]->stack_out.p;
+    nf_status st = prepare_layer(layers[l], pools[l], &bl, plan, fixed_meta ? &(*fixed_meta)[l] : nullptr, runs[l]);
+    if (st != NF_OK) return st;
+  }
+  return NF_OK;
+}
+
+nf_status stack_impl(nf_layer* const* layers, nf_kv_pool* const* pools, int n, const nf_batch* b,
+                     hipStream_t caller) {
+  std::vector<LayerRun> runs;
+  nf_status st = prepare_stack(layers, pools, n, b, nullptr, runs);
+  if (st != NF_OK || runs[0].count == 0) return st;
+  Streams S;
+  if ((st = open_streams(layers[0], layers[0]->plan, caller, S)) != NF_OK) return st;
+  if ((st = issue_stack(runs, S, layers[0]->plan.order)) != NF_OK) return st;
+  return close_streams(layers[0], S);
 }
 
 }  // namespace
@@ -843,7 +984,7 @@ void nf_layer_destroy(nf_layer* L) {
   }
   for (DevBuf* b : {&L->h, &L->qkv, &L->q_rot, &L->attn, &L->x1, &L->h2, &L->act, &L->y, &L->r_idx, &L->r_w,
                     &L->r_perm, &L->r_inv, &L->r_off, &L->splitk, &L->part_o, &L->part_ml, &L->meta, &L->cos_sin,
-                    &L->wp_qkv, &L->wp_o, &L->wp_gu, &L->wp_down})
+                    &L->wp_qkv, &L->wp_o, &L->wp_gu, &L->wp_down, &L->stack_out})
     release(*b);
   for (int i = 0; i < 2; ++i) {
     if (L->stage[i]) (void)hipHostFree(L->stage[i]);
@@ -906,6 +1047,97 @@ nf_status nf_layer_step(nf_layer* L, nf_kv_pool* P, const nf_batch* b, void* str
   if (!L || !P || !b) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: null argument");
   if (P->layer != L) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: pool belongs to another layer");
   return step_impl(L, P, b, (hipStream_t)stream, L->plan);
+}
+
+nf_status nf_stack_step(nf_layer* const* layers, nf_kv_pool* const* pools, int32_t n_layers, const nf_batch* batch,
+                        void* stream) {
+  nf_status st = check_stack(layers, pools, n_layers, batch);
+  if (st != NF_OK) return st;
+  return stack_impl(layers, pools, n_layers, batch, (hipStream_t)stream);
+}
+
+struct nf_graph {
+  int device = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  std::vector<DevBuf> meta;      // each layer's step metadata, read by the captured launches
+};
+
+void nf_graph_destroy(nf_graph* g) {
+  if (!g) return;
+  (void)hipSetDevice(g->device);
+  (void)hipDeviceSynchronize();
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  for (DevBuf& b : g->meta) release(b);
+  delete g;
+}
+
+nf_status nf_stack_graph_create(nf_layer* const* layers, nf_kv_pool* const* pools, int32_t n_layers,
+                                const nf_batch* batch, void* stream, nf_graph** out) {
+  if (!out) return set_err(NF_ERR_INVALID_ARG, "nf_stack_graph_create: null argument");
+  *out = nullptr;
+  nf_status st = check_stack(layers, pools, n_layers, batch);
+  if (st != NF_OK) return st;
+  const nf_plan& plan = layers[0]->plan;
+  if (plan.n_streams == 2 && (plan.gemm_cus_per_xcd || plan.attn_cus_per_xcd))
+    return set_err(NF_ERR_UNSUPPORTED, "nf_stack_graph_create: a graph does not keep a stream's CU mask; "
+                   "use a plan without a CU split");
+  for (int l = 0; l < n_layers; ++l)
+    if (layers[l]->prof) return set_err(NF_ERR_UNSUPPORTED, "nf_stack_graph_create: per-kernel timing is on");
+  if (batch->n_tokens == 0) return set_err(NF_ERR_INVALID_ARG, "nf_stack_graph_create: empty batch");
+  hipStream_t s = (hipStream_t)stream;
+  // one eager step first: every buffer, stream and event the step needs
+  // exists before the capture, which must not allocate
+  if ((st = stack_impl(layers, pools, n_layers, batch, s)) != NF_OK) return st;
+  HIP_TRY(hipStreamSynchronize(s));
+  nf_graph* g = new nf_graph();
+  g->device = layers[0]->device;
+  g->meta.resize(n_layers);
+  std::vector<LayerRun> runs;
+  st = prepare_stack(layers, pools, n_layers, batch, &g->meta, runs);
+  if (st != NF_OK) {
+    nf_graph_destroy(g);
+    return st;
+  }
+  // captured on a stream of its own (the caller's may be the null stream,
+  // which cannot be captured); the caller's stream is idle after the warm-up
+  hipStream_t cap = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamBeginCapture(cap, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) {
+    if (cap) (void)hipStreamDestroy(cap);
+    nf_graph_destroy(g);
+    return set_err(NF_ERR_HIP, "stream capture could not start: %s", hipGetErrorString(e));
+  }
+  Streams S;
+  st = open_streams(layers[0], plan, cap, S);
+  if (st == NF_OK) st = issue_stack(runs, S, plan.order);
+  if (st == NF_OK) st = close_streams(layers[0], S);
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(cap, &graph);
+  (void)hipStreamDestroy(cap);
+  if (st != NF_OK || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    nf_graph_destroy(g);
+    return st != NF_OK ? st : set_err(NF_ERR_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+  }
+  g->graph = graph;
+  e = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    g->exec = nullptr;
+    nf_graph_destroy(g);
+    return set_err(NF_ERR_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+  }
+  *out = g;
+  return NF_OK;
+}
+
+nf_status nf_graph_launch(nf_graph* g, void* stream) {
+  if (!g) return set_err(NF_ERR_INVALID_ARG, "nf_graph_launch: null argument");
+  HIP_TRY(hipSetDevice(g->device));
+  HIP_TRY(hipGraphLaunch(g->exec, (hipStream_t)stream));
+  return NF_OK;
 }
 
 nf_status nf_layer_intermediate(const nf_layer* L, int32_t which, const void** dev, int64_t* stride) {

@@ -157,3 +157,21 @@ def test_kv_pool_bytes():
     with pytest.raises(B.NfError) as e:
         B.kv_pool_bytes(shape, 10, 32)
     assert e.value.status == B.NF_ERR_UNSUPPORTED
+
+
+def test_stack_and_graph_reject_bad_arguments_before_launching():
+    L = B.lib()
+    _, batch, _ = _small()
+    hb = B.HostBatch(batch, 0x1000, 0x2000)
+    one = (ctypes.c_void_p * 1)(None)
+    # null arrays, no layers, null handles: rejected before any HIP call
+    assert L.nf_stack_step(None, None, 1, ctypes.byref(hb.c), None) == B.NF_ERR_INVALID_ARG
+    assert L.nf_stack_step(one, one, 0, ctypes.byref(hb.c), None) == B.NF_ERR_INVALID_ARG
+    assert L.nf_stack_step(one, one, 1, ctypes.byref(hb.c), None) == B.NF_ERR_INVALID_ARG
+    assert L.nf_stack_step(one, one, 1, None, None) == B.NF_ERR_INVALID_ARG
+    out = ctypes.c_void_p()
+    assert L.nf_stack_graph_create(one, one, 1, ctypes.byref(hb.c), None, None) == B.NF_ERR_INVALID_ARG
+    assert L.nf_stack_graph_create(one, one, 0, ctypes.byref(hb.c), None, ctypes.byref(out)) == B.NF_ERR_INVALID_ARG
+    assert out.value is None
+    assert L.nf_graph_launch(None, None) == B.NF_ERR_INVALID_ARG
+    L.nf_graph_destroy(None)                      # a no-op
