@@ -9,7 +9,10 @@ Prints one JSON line: throughput (tokens/s), the fraction of the
 compute-bound optimum (peaks measured in this run), the roofline of the
 dominant kernel (its duration measured with HIP events on its own stream
 during the timed steps), the step time with cold caches (a 512 MiB scratch
-read before each step) and the CPU oracle timed on a bounded sample.
+read before each step), a stack of --stack layers of the same shape
+(nf_stack_step eager and as a HIP graph: unsplit, two nano-batches one
+after the other, and two nano-batches on two streams pipelined across
+layers; time per layer) and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -92,6 +95,9 @@ def main():
                     help="auto (workload default / search), k1 (unsplit), overlap2 (two nano-batches on two "
                          "streams), or overlap2:G:A (the same with G GEMM and A attention CUs per XCD)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stack", type=int, default=4,
+                    help="also time a stack of this many layers of the workload's shape (nf_stack_step, eager "
+                         "and as a HIP graph; unsplit and two nano-batches pipelined across layers); 0: skip")
     ap.add_argument("--traffic", default=None, help="text file with the rocprofv3 FETCH/WRITE bytes per launch")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 5 times (counter calibration) and exit")
@@ -263,6 +269,11 @@ def main():
     optimum = peak_tflops * 1e12 / fpt
     frac_opt = value / optimum
 
+    stack = None
+    if args.stack > 0:
+        stack = stack_measure(args.stack, wl, batch, layer, pool, acts, plan, sp)
+        layer.set_plan(plan)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, batch, weights, acts, k_pool, v_pool)
@@ -293,7 +304,70 @@ def main():
     }
     if comparisons:
         line["comparisons"] = {k: round(v, 5) for k, v in comparisons.items()}
+    if stack is not None:
+        line["stack"] = stack
     print(json.dumps(line), flush=True)
+
+
+def stack_measure(n, wl, batch, layer0, pool0, acts, main_plan, sp, steps=10):
+    """A stack of n layers of the workload's shape: layer 0 is the bench's
+    layer, layers 1.. have their own seeded weights and KV pools.  Times
+    nf_stack_step eagerly and as a replayed HIP graph, with the unsplit plan
+    and with two nano-batches on two streams pipelined across layers; returns
+    milliseconds per layer (events around `steps` stack steps).  The same
+    two nano-batches run one after the other on one stream are the baseline
+    the pipelined overlap is compared with."""
+    import torch
+    from intra_operation_overlap_amd import binding as B
+    from intra_operation_overlap_amd import workload as W
+    s = wl.shape
+    T = batch.n_tokens
+    log(f"stack of {n} layers")
+    layers, pools, keep = [layer0], [pool0], []
+    for l in range(1, n):
+        seed = wl.seed + 1000 * l
+        w = W.make_weights(wl, "cuda", seed=seed)
+        k, v = W.make_pool(wl, batch.n_pages, "cuda", seed=seed)
+        L = B.Layer(s, w, T, int(batch.pos.max()) + 1)
+        layers.append(L)
+        pools.append(B.KVPool(L, batch.n_pages, s.page_size, k, v))
+        keep.append((w, k, v))
+    out = torch.empty_like(acts["x"])
+    hb = B.HostBatch(batch, acts["x"].data_ptr(), out.data_ptr(),
+                     acts["router_logits"].data_ptr() if "router_logits" in acts else None)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps / n
+
+    res = {}
+    half = [T - T // 2, T // 2]
+    for name, plan in (("unsplit", B.make_plan(1, [T])),
+                       ("split2_sequential", B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL)),
+                       ("overlap2_pipelined", B.make_plan(2, half, n_streams=2))):
+        for L in layers:
+            L.set_plan(plan)
+        res[f"{name}_eager"] = timed(lambda: B.stack_step(layers, pools, hb, sp))
+        g = B.StackGraph(layers, pools, hb, sp)
+        res[f"{name}_graph"] = timed(lambda: g.launch(sp))
+        g.close()
+        log(f"  {name}: eager {res[name + '_eager'] * 1e3:.1f} us/layer, graph {res[name + '_graph'] * 1e3:.1f} us/layer")
+    for L in layers:
+        L.set_plan(main_plan)
+    for L in layers[1:]:
+        L.close()
+    return {"layers": n, "ms_per_layer": {k: round(v, 5) for k, v in res.items()},
+            "tokens_per_s_per_layer": {k: round(T / (v * 1e-3), 1) for k, v in res.items()},
+            "steps": steps}
 
 
 # Sources that decide the HBM traffic of each kernel kind; a counter summary
