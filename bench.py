@@ -12,7 +12,9 @@ during the timed steps), the step time with cold caches (a 512 MiB scratch
 read before each step), a stack of --stack layers of the same shape
 (nf_stack_step eager and as a HIP graph: unsplit, two nano-batches one
 after the other, and two nano-batches on two streams pipelined across
-layers; time per layer) and the CPU oracle timed on a bounded sample.
+layers; time per layer), the KV offload of an eighth of the requests to
+pinned host memory alone and beside steps (nf_kv_offload), and the CPU
+oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -95,6 +97,8 @@ def main():
                     help="auto (workload default / search), k1 (unsplit), overlap2 (two nano-batches on two "
                          "streams), or overlap2:G:A (the same with G GEMM and A attention CUs per XCD)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the KV-offload measurement (nf_kv_offload alone and beside steps)")
     ap.add_argument("--stack", type=int, default=4,
                     help="also time a stack of this many layers of the workload's shape (nf_stack_step, eager "
                          "and as a HIP graph; unsplit and two nano-batches pipelined across layers); 0: skip")
@@ -269,6 +273,10 @@ def main():
     optimum = peak_tflops * 1e12 / fpt
     frac_opt = value / optimum
 
+    offload = None
+    if not args.no_offload:
+        offload = offload_measure(batch, layer, pool, k_pool, hb, sp, ms)
+
     stack = None
     if args.stack > 0:
         stack = stack_measure(args.stack, wl, batch, layer, pool, acts, plan, sp)
@@ -304,9 +312,77 @@ def main():
     }
     if comparisons:
         line["comparisons"] = {k: round(v, 5) for k, v in comparisons.items()}
+    if offload is not None:
+        line["kv_offload"] = offload
     if stack is not None:
         line["stack"] = stack
     print(json.dumps(line), flush=True)
+
+
+def offload_measure(batch, layer, pool, k_pool, hb, sp, step_ms, reps=10):
+    """nf_kv_offload of the KV pages of the batch's first eighth of requests
+    (the pages the step only reads), to pinned host memory on a stream of its
+    own: alone, and beside as many back-to-back steps on the main stream as
+    span it (medians)."""
+    import torch
+    from intra_operation_overlap_amd import binding as B
+    R = batch.n_requests
+    written = set()
+    for r in range(R):
+        p0, ql, st = int(batch.req_pos0[r]), int(batch.req_q_len[r]), int(batch.page_indptr[r])
+        for p in range(p0, p0 + ql):
+            written.add(int(batch.page_indices[st + p // 16]))
+    pages = [int(p) for r in range(max(1, R // 8))
+             for p in batch.page_indices[batch.page_indptr[r]:batch.page_indptr[r + 1]] if int(p) not in written]
+    if not pages:
+        return None
+    pages = np.array(pages, np.int32)
+    n = len(pages)
+    hk = torch.empty((n,) + tuple(k_pool.shape[1:]), dtype=k_pool.dtype, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    nbytes = 2 * hk.numel() * hk.element_size()
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    log(f"KV offload: {n} pages, {nbytes / 2**20:.0f} MiB")
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+    alone = []
+    for _ in range(reps):
+        a0, a1 = ev(), ev()
+        a0.record(side)
+        B.kv_offload(pool, pages, hk, hv, side.cuda_stream)
+        a1.record(side)
+        torch.cuda.synchronize()
+        alone.append(a0.elapsed_time(a1))
+    med = lambda v: sorted(v)[len(v) // 2]
+    # beside steps: enough back-to-back steps on the main stream to span the
+    # whole offload, so their mean is the offload's amortised cost per step
+    m = int(med(alone) / step_ms) + 2
+    beside, steps = [], []
+    for _ in range(max(3, reps // 2)):
+        torch.cuda.synchronize()
+        a0, a1, s0, s1 = ev(), ev(), ev(), ev()
+        a0.record(side)
+        s0.record(main)
+        B.kv_offload(pool, pages, hk, hv, side.cuda_stream)
+        for _ in range(m):
+            layer.step(pool, hb, sp)
+        a1.record(side)
+        s1.record(main)
+        torch.cuda.synchronize()
+        beside.append(a0.elapsed_time(a1))
+        steps.append(s0.elapsed_time(s1) / m)
+    res = {"pages": n, "bytes": int(nbytes), "alone_ms": round(med(alone), 4),
+           "alone_gbps": round(nbytes / (med(alone) * 1e-3) / 1e9, 1),
+           "beside_steps_ms": round(med(beside), 4),
+           "beside_steps_gbps": round(nbytes / (med(beside) * 1e-3) / 1e9, 1),
+           "steps_beside": m, "step_ms_alone": round(step_ms, 5),
+           "step_ms_beside_offload": round(med(steps), 5),
+           "requests": max(1, R // 8), "host_memory": "pinned"}
+    log(f"  alone {res['alone_gbps']} GB/s; beside {m} steps {res['beside_steps_gbps']} GB/s, step "
+        f"{res['step_ms_beside_offload'] * 1e3:.1f} us (alone {step_ms * 1e3:.1f})")
+    return res
 
 
 def stack_measure(n, wl, batch, layer0, pool0, acts, main_plan, sp, steps=10):

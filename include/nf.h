@@ -200,6 +200,27 @@ nf_status nf_kv_pool_create(const nf_layer* layer, int32_t n_pages, int32_t page
                             void* k_dev, void* v_dev, nf_kv_pool** out);
 void nf_kv_pool_destroy(nf_kv_pool* pool);
 
+/* Offloads whole pool pages to host memory, the KV offload of retired
+ * requests that the hysenlabs Nanoflow page (section "KV-cache offload to
+ * SSD, and the bandwidth arithmetic behind it") and the ossradar page
+ * ("Introduction") describe as running beside the inference operations (the
+ * SSD leg is not part of this library).  For i < n, page pages[i]'s K block
+ * (n_kv_heads x page_size x head_dim elements, in the pool's layout) is
+ * written to host_k + i * block and its V block to host_v + i * block, block
+ * = n_kv_heads * page_size * head_dim * element size.  The pages are gathered
+ * on `stream` into a staging buffer the pool owns, then copied to the host
+ * with two DMA transfers (the copy engines, not the compute units), so an
+ * offload on its own stream can run beside a step.  host_k / host_v:
+ * caller-owned host memory of n * block bytes each; pinned memory
+ * (hipHostMalloc, torch pin_memory) keeps the call asynchronous.  `pages`
+ * may be reused on return; a page may appear more than once.  Offloads on
+ * one pool must not overlap each other; the pages must not be written while
+ * the offload reads them.  Errors: NF_ERR_INVALID_ARG (null pool, negative
+ * n, null arrays with n > 0), NF_ERR_OUT_OF_RANGE (a page outside the pool),
+ * NF_ERR_HIP. */
+nf_status nf_kv_offload(nf_kv_pool* pool, const int32_t* pages, int32_t n, void* host_k, void* host_v,
+                        void* stream);
+
 /* ---- plan -----------------------------------------------------------------
  * nf_plan_set validates count, order, streams and CU split against the device
  * (sizes are checked against each batch at step time) and (re)creates the

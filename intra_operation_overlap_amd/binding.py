@@ -71,6 +71,7 @@ _SIGS = {
     "nf_stack_graph_create": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(nf_batch), vp,
                                     ctypes.POINTER(vp)]),
     "nf_graph_launch": (i32, [vp, vp]),
+    "nf_kv_offload": (i32, [vp, P_i32, i32, vp, vp, vp]),
     "nf_graph_destroy": (None, [vp]),
     "nf_plan_search": (i32, [vp, vp, ctypes.POINTER(nf_batch), ctypes.POINTER(nf_search_opts),
                              ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double), vp]),
@@ -282,6 +283,13 @@ class StackGraph:
             self.close()
         except Exception:
             pass
+
+
+def kv_offload(pool: KVPool, pages, host_k, host_v, stream: int = 0) -> None:
+    """nf_kv_offload: pool pages `pages` (int32) to host tensors host_k / host_v."""
+    a = np.ascontiguousarray(np.asarray(pages, np.int32))
+    check(lib().nf_kv_offload(pool.h, _i32p(a), len(a), host_k.data_ptr(), host_v.data_ptr(), stream),
+          "nf_kv_offload")
 
 
 def kv_pool_bytes(shape: nf_shape, n_pages: int, page_size: int):

@@ -134,6 +134,7 @@ struct nf_kv_pool {
   int32_t n_pages = 0, page_size = 0;
   void* k = nullptr;
   void* v = nullptr;
+  DevBuf offload;      // page list and gathered K / V blocks of nf_kv_offload
 };
 
 namespace {
@@ -1020,7 +1021,41 @@ nf_status nf_kv_pool_create(const nf_layer* L, int32_t n_pages, int32_t page_siz
   return NF_OK;
 }
 
-void nf_kv_pool_destroy(nf_kv_pool* p) { delete p; }
+void nf_kv_pool_destroy(nf_kv_pool* p) {
+  if (!p) return;
+  if (p->offload.p || !p->offload.old.empty()) {
+    (void)hipSetDevice(p->layer->device);
+    (void)hipDeviceSynchronize();
+    release(p->offload);
+  }
+  delete p;
+}
+
+nf_status nf_kv_offload(nf_kv_pool* P, const int32_t* pages, int32_t n, void* host_k, void* host_v,
+                        void* stream) {
+  if (!P || n < 0 || (n > 0 && (!pages || !host_k || !host_v)))
+    return set_err(NF_ERR_INVALID_ARG, "nf_kv_offload: null argument or negative count");
+  for (int i = 0; i < n; ++i)
+    if (pages[i] < 0 || pages[i] >= P->n_pages)
+      return set_err(NF_ERR_OUT_OF_RANGE, "nf_kv_offload: page %d at %d is outside the pool's %d pages", pages[i],
+                     i, P->n_pages);
+  if (n == 0) return NF_OK;
+  const nf_shape& s = P->layer->s;
+  const int64_t blk = (int64_t)s.n_kv_heads * P->page_size * s.head_dim * (int64_t)dtype_bytes(s.dtype);
+  const size_t idx_bytes = ((size_t)n * 4 + 255) & ~(size_t)255;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(P->layer->device));
+  HIP_TRY(ensure(P->offload, idx_bytes + 2 * (size_t)n * blk));
+  char* base = (char*)P->offload.p;
+  int32_t* d_pages = (int32_t*)base;
+  char* gk = base + idx_bytes;
+  char* gv = gk + (size_t)n * blk;
+  HIP_TRY(hipMemcpyAsync(d_pages, pages, (size_t)n * 4, hipMemcpyHostToDevice, st));
+  HIP_TRY(kv_gather(P->k, P->v, d_pages, n, blk, gk, gv, st));
+  HIP_TRY(hipMemcpyAsync(host_k, gk, (size_t)n * blk, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipMemcpyAsync(host_v, gv, (size_t)n * blk, hipMemcpyDeviceToHost, st));
+  return NF_OK;
+}
 
 nf_status nf_plan_set(nf_layer* L, const nf_plan* p) {
   if (!L || !p) return set_err(NF_ERR_INVALID_ARG, "nf_plan_set: null argument");

@@ -164,6 +164,10 @@ hipError_t moe_route(const RouteArgs& a, hipStream_t s);
 hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w,
                        const int32_t* inv, void* out, int T, int H, int k, hipStream_t s);
 
+// copies pool pages pages[0..n) (K and V, block_bytes each) to dst_k / dst_v in list order
+hipError_t kv_gather(const void* k_pool, const void* v_pool, const int32_t* pages, int n, int64_t block_bytes,
+                     void* dst_k, void* dst_v, hipStream_t s);
+
 // ---------------------------------------------------------------- probes
 // shape 0: v_mfma_f32_16x16x32_bf16 (8 chains), 1: v_mfma_f32_32x32x16_bf16 (4 chains)
 hipError_t probe_mfma(int shape, int n_blocks, int iters, float* sink, hipStream_t s);

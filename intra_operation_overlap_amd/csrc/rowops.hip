@@ -263,7 +263,29 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const T* __restrict__ 
   }
 }
 
+// Gathers whole pool pages: block b < n copies page pages[b] of K into
+// dst_k + b * blk16 (16-byte units); blocks n .. 2n - 1 do V.
+__global__ __launch_bounds__(256) void kv_gather_kernel(const u32x4* __restrict__ k_pool,
+                                                        const u32x4* __restrict__ v_pool,
+                                                        const int32_t* __restrict__ pages, int n, int64_t blk16,
+                                                        u32x4* __restrict__ dst_k, u32x4* __restrict__ dst_v) {
+  const bool is_v = blockIdx.x >= (unsigned)n;
+  const int b = is_v ? blockIdx.x - n : blockIdx.x;
+  const u32x4* src = (is_v ? v_pool : k_pool) + (int64_t)pages[b] * blk16;
+  u32x4* dst = (is_v ? dst_v : dst_k) + (int64_t)b * blk16;
+  for (int64_t i = threadIdx.x; i < blk16; i += 256) dst[i] = __builtin_nontemporal_load(src + i);
+}
+
 }  // namespace
+
+hipError_t kv_gather(const void* k_pool, const void* v_pool, const int32_t* pages, int n, int64_t block_bytes,
+                     void* dst_k, void* dst_v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (block_bytes % 16) return hipErrorInvalidValue;
+  launch(kv_gather_kernel, 2 * n, 256, 0, s, (const u32x4*)k_pool, (const u32x4*)v_pool, pages, n,
+         block_bytes / 16, (u32x4*)dst_k, (u32x4*)dst_v);
+  return hipGetLastError();
+}
 
 hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps, hipStream_t s,
                    const MetaCopy* mc) {

@@ -175,3 +175,12 @@ def test_stack_and_graph_reject_bad_arguments_before_launching():
     assert out.value is None
     assert L.nf_graph_launch(None, None) == B.NF_ERR_INVALID_ARG
     L.nf_graph_destroy(None)                      # a no-op
+
+
+def test_kv_offload_rejects_bad_arguments_before_launching():
+    L = B.lib()
+    pages = (ctypes.c_int32 * 2)(0, 1)
+    assert L.nf_kv_offload(None, pages, 2, 1, 1, None) == B.NF_ERR_INVALID_ARG
+    assert L.nf_kv_offload(ctypes.c_void_p(8), pages, -1, 1, 1, None) == B.NF_ERR_INVALID_ARG
+    assert L.nf_kv_offload(ctypes.c_void_p(8), None, 2, 1, 1, None) == B.NF_ERR_INVALID_ARG
+    assert L.nf_kv_offload(ctypes.c_void_p(8), pages, 2, None, 1, None) == B.NF_ERR_INVALID_ARG
