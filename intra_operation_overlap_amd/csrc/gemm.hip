@@ -1110,6 +1110,20 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
       return p;
     }
   }
+  // 128 x 128 tiles that fill one round on the CUs (at least three quarters
+  // of them) run unsplit, one workgroup per CU with three stages and the
+  // refill spread over the MFMAs (configuration 13).  Inside the step: the
+  // 1024 x 4096 x 4096 O projection and its FFN norm 56 -> 45 us (no split-K
+  // partials to reduce), the 512 x 6144 x 4096 QKV with RoPE 45 -> 41 us; with
+  // fewer tiles (160 or 128 for 256 CUs) the split 128 x 128 tiles were faster
+  if (p.cfg == 14 && a.K >= 1024) {
+    const int64_t t128 = (int64_t)((M + 127) / 128) * n_tiles_of(a, 128);
+    if (4 * t128 >= 3 * (int64_t)cus && t128 <= cus) {
+      p.cfg = 13;
+      p.k_splits = 1;
+      return p;
+    }
+  }
   int bm, bn;
   tile_dims(p.cfg, bm, bn);
   const int tiles = ((M + bm - 1) / bm) * n_tiles_of(a, bn);
