@@ -217,8 +217,11 @@ __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(AttnArgs a) {
   __shared__ float m_s[4 * ROWS], l_s[4 * ROWS];
   __shared__ float O_s[4 * ROWS * DH];
 
-  const AttnItem it = a.items[blockIdx.x];
-  const int kh = blockIdx.y;
+  // workgroup w takes KV head w % nkv of item w / nkv: the heads of one item
+  // (the same pages, adjacent blocks in the pool) are dispatched together,
+  // and the longest items' heads all go first
+  const AttnItem it = a.items[blockIdx.x / a.nkv];
+  const int kh = blockIdx.x % a.nkv;
   const int G = a.nq / a.nkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15;        // row index of the S^T / O^T column this lane holds
@@ -431,7 +434,7 @@ hipError_t attention(int dtype, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_items, a.nkv);
   if (dtype == 1 && a.d == 128 && a.page_size == 16) {
     if (a.variant == 1) {
-      launch(attn_bf16_d128_kernel, grid, 256, 0, s, a);
+      launch(attn_bf16_d128_kernel, a.n_items * a.nkv, 256, 0, s, a);
     } else {
       int blocks = a.n_items * a.nkv;
       if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
