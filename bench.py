@@ -13,8 +13,8 @@ read before each step), a stack of --stack layers of the same shape
 (nf_stack_step eager and as a HIP graph: unsplit, two nano-batches one
 after the other, and two nano-batches on two streams pipelined across
 layers; time per layer), the KV offload of an eighth of the requests to
-pinned host memory alone and beside steps (nf_kv_offload), and the CPU
-oracle timed on a bounded sample.
+pinned host memory alone and beside steps (nf_kv_offload), the host time to
+enqueue one step, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -273,6 +273,21 @@ def main():
     optimum = peak_tflops * 1e12 / fpt
     frac_opt = value / optimum
 
+    # host cost of one step: the enqueue of a single nf_layer_step with the
+    # device idle (in the timed loop the host also waits for the staging
+    # buffer of the step two back, so that figure includes device time)
+    host_idle = []
+    for _ in range(10):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        layer.step(pool, hb, sp)
+        host_idle.append((time.perf_counter() - h0) * 1e6)
+    torch.cuda.synchronize()
+    host = {"step_enqueue_us": round(sorted(host_idle)[5], 1),
+            "step_enqueue_frac_of_step": round(sorted(host_idle)[5] / (ms * 1e3), 4)}
+    log(f"host enqueue of one step with the device idle: {host['step_enqueue_us']} us "
+        f"({100 * host['step_enqueue_frac_of_step']:.1f}% of the step)")
+
     offload = None
     if not args.no_offload:
         offload = offload_measure(batch, layer, pool, k_pool, hb, sp, ms)
@@ -312,6 +327,7 @@ def main():
     }
     if comparisons:
         line["comparisons"] = {k: round(v, 5) for k, v in comparisons.items()}
+    line["host"] = host
     if offload is not None:
         line["kv_offload"] = offload
     if stack is not None:
@@ -435,6 +451,15 @@ def stack_measure(n, wl, batch, layer0, pool0, acts, main_plan, sp, steps=10):
         res[f"{name}_eager"] = timed(lambda: B.stack_step(layers, pools, hb, sp))
         g = B.StackGraph(layers, pools, hb, sp)
         res[f"{name}_graph"] = timed(lambda: g.launch(sp))
+        if name == "unsplit":
+            hs = []
+            for _ in range(10):
+                torch.cuda.synchronize()
+                h0 = time.perf_counter()
+                g.launch(sp)
+                hs.append((time.perf_counter() - h0) * 1e6)
+            torch.cuda.synchronize()
+            graph_launch_us = sorted(hs)[5]
         g.close()
         log(f"  {name}: eager {res[name + '_eager'] * 1e3:.1f} us/layer, graph {res[name + '_graph'] * 1e3:.1f} us/layer")
     for L in layers:
@@ -443,7 +468,7 @@ def stack_measure(n, wl, batch, layer0, pool0, acts, main_plan, sp, steps=10):
         L.close()
     return {"layers": n, "ms_per_layer": {k: round(v, 5) for k, v in res.items()},
             "tokens_per_s_per_layer": {k: round(T / (v * 1e-3), 1) for k, v in res.items()},
-            "steps": steps}
+            "graph_launch_host_us": round(graph_launch_us, 1), "steps": steps}
 
 
 # Sources that decide the HBM traffic of each kernel kind; a counter summary
