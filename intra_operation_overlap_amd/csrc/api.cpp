@@ -426,17 +426,28 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
   const NanoWork& nw = L->work.nanos[j];
   const int t0 = nw.t0, Tj = nw.t1 - nw.t0, dt = sh.dtype, H = sh.hidden;
   if (Tj == 0) return NF_OK;
+  NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
+  // The step's metadata (first reader: RoPE/append, after the QKV GEMM)
+  // crosses PCIe from the pinned staging buffer in extra blocks of a kernel.
+  // Above 64 KB (page tables of hundreds of requests: ~12 us at c4) those
+  // ride on the QKV GEMM when it takes the LDS-pipelined path, beside its
+  // tiles; otherwise on the RMSNorm before it.
+  const bool meta_in_gemm = c.mc_pending && dt == NF_BF16 && c.mc.n16 * 16 > (64 << 10) && [&] {
+    const int cfg = gemm_choose(g.qkv, c.gemm_cus).cfg;
+    return cfg >= 10 && cfg <= 30 && g.qkv.K % 64 == 0;
+  }();
   prof_begin(L, K_NORM1, s);
   HIP_STEP(rmsnorm(dt, (const char*)c.b->x + (int64_t)t0 * H * dtype_bytes(dt), L->w.attn_norm,
-                   ptr(L->h, (int64_t)t0 * H, dt), Tj, H, sh.rms_eps, s, c.mc_pending ? &c.mc : nullptr));
+                   ptr(L->h, (int64_t)t0 * H, dt), Tj, H, sh.rms_eps, s,
+                   c.mc_pending && !meta_in_gemm ? &c.mc : nullptr));
   prof_end(L, K_NORM1, s);
-  if (c.mc_pending) {
-    HIP_TRY(hipEventRecord(c.mc_event, s));
-    c.mc_pending = false;
-  }
-  NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
+  if (meta_in_gemm) g.qkv.meta = c.mc;
   int qkv_parts = 1;
   HIP_STEP(run_gemm(c, g.qkv, K_QKV, s, &qkv_parts));
+  if (c.mc_pending) {
+    HIP_TRY(hipEventRecord(c.mc_event, s));     // the copy's reads of the staging buffer are done
+    c.mc_pending = false;
+  }
   RopeAppendArgs r;
   const int Nqkv = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim;
   if (qkv_parts > 1) {          // RoPE reduces the split-K partials itself

@@ -516,6 +516,14 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[C::STAGES * C::SLAB];
   const GemmArgs& a = p.a;
   const int total = p.m_tiles * p.n_tiles * p.z_count;
+  if ((int)blockIdx.x >= total) {               // extra blocks: the step's metadata copy
+    const u32x4* src = (const u32x4*)a.meta.src;
+    u32x4* dst = (u32x4*)a.meta.dst;
+    const int64_t nb = gridDim.x - total;
+    for (int64_t i = (int64_t)(blockIdx.x - total) * 256 + threadIdx.x; i < a.meta.n16; i += nb * 256)
+      dst[i] = src[i];
+    return;
+  }
   const int logical = xcd_logical(blockIdx.x, total);
   const int m_tile = logical % p.m_tiles;
   const int rest = logical / p.m_tiles;
@@ -948,24 +956,26 @@ hipError_t launch_pipe(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStrea
   }
   const int total = p.m_tiles * p.n_tiles * p.z_count;
   if (total == 0) return hipSuccess;
+  // blocks after the tiles copy the step's metadata (a.meta), then exit
+  const int grid = total + (a.meta.n16 > 0 ? (int)std::min<int64_t>((a.meta.n16 + 255) / 256, 64) : 0);
   auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
   p.vec_epi = a.N % 8 == 0 && a.ldc % 8 == 0 && al16(a.C) &&
               (a.mode != GEMM_RESIDUAL || (a.ldr % 8 == 0 && al16(a.R)));
   if (split && p.z_count > 1) {
     if (a.mode == GEMM_SWIGLU)
-      launch(gemm_pipe_kernel<C, GEMM_SWIGLU, true>, total, 256, 0, s, p);
+      launch(gemm_pipe_kernel<C, GEMM_SWIGLU, true>, grid, 256, 0, s, p);
     else
-      launch(gemm_pipe_kernel<C, GEMM_STORE, true>, total, 256, 0, s, p);
+      launch(gemm_pipe_kernel<C, GEMM_STORE, true>, grid, 256, 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.defer_reduce) return e;
     if (hook && hook->fn) hook->fn(hook->ctx, 1);
     return splitk_reduce(a, p.part, p.part_ld, p.z_count, s);
   }
   switch (a.mode) {
-    case GEMM_STORE: launch(gemm_pipe_kernel<C, GEMM_STORE, false>, total, 256, 0, s, p); break;
-    case GEMM_RESIDUAL: launch(gemm_pipe_kernel<C, GEMM_RESIDUAL, false>, total, 256, 0, s, p); break;
-    case GEMM_SWIGLU: launch(gemm_pipe_kernel<C, GEMM_SWIGLU, false>, total, 256, 0, s, p); break;
-    default: launch(gemm_pipe_kernel<C, GEMM_F32OUT, false>, total, 256, 0, s, p); break;
+    case GEMM_STORE: launch(gemm_pipe_kernel<C, GEMM_STORE, false>, grid, 256, 0, s, p); break;
+    case GEMM_RESIDUAL: launch(gemm_pipe_kernel<C, GEMM_RESIDUAL, false>, grid, 256, 0, s, p); break;
+    case GEMM_SWIGLU: launch(gemm_pipe_kernel<C, GEMM_SWIGLU, false>, grid, 256, 0, s, p); break;
+    default: launch(gemm_pipe_kernel<C, GEMM_F32OUT, false>, grid, 256, 0, s, p); break;
   }
   return hipGetLastError();
 }

@@ -39,6 +39,14 @@ enum GemmMode : int {
   GEMM_F32OUT = 3,    // C (fp32) = acc
 };
 
+// A copy of the step's metadata (pinned host staging -> device) done by extra
+// blocks of a kernel that runs anyway: n16 16-byte units.
+struct MetaCopy {
+  const void* src = nullptr;
+  void* dst = nullptr;
+  int64_t n16 = 0;
+};
+
 struct GemmArgs {
   const void* A = nullptr; int64_t lda = 0;
   const void* B = nullptr; const void* B2 = nullptr; int64_t ldb = 0;  // B2: up rows (SWIGLU)
@@ -58,6 +66,9 @@ struct GemmArgs {
   // B (B2 interleaved for SWIGLU) packed in MFMA operand order by pack_b
   // (optional; enables the weight-streaming kernels), group stride in elements
   const void* Bp = nullptr; int64_t bp_group_stride = 0;
+  // LDS-pipelined configurations (10..31) only: extra blocks after the tiles
+  // also do this copy (meta.n16 == 0: none)
+  MetaCopy meta;
 };
 
 struct GemmPlan {
@@ -100,11 +111,6 @@ int gemm_partials(const GemmArgs& a, const GemmPlan& p);
 // ---------------------------------------------------------------- row ops
 // Copy of a step's metadata (16-byte units) from device-visible pinned host
 // memory, done by extra blocks of the first kernel of a step.
-struct MetaCopy {
-  const void* src = nullptr;
-  void* dst = nullptr;
-  int64_t n16 = 0;
-};
 hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int H, float eps, hipStream_t s,
                    const MetaCopy* mc = nullptr);
 
