@@ -198,6 +198,8 @@ nf_status nf_kv_pool_bytes(const nf_shape* shape, int32_t n_pages, int32_t page_
                            size_t* k_bytes, size_t* v_bytes);
 nf_status nf_kv_pool_create(const nf_layer* layer, int32_t n_pages, int32_t page_size,
                             void* k_dev, void* v_dev, nf_kv_pool** out);
+/* Frees the pool object and its offload staging (waiting for the device when
+ * there is any); may run before or after nf_layer_destroy of its layer. */
 void nf_kv_pool_destroy(nf_kv_pool* pool);
 
 /* Offloads whole pool pages to host memory, the KV offload of retired
@@ -215,9 +217,9 @@ void nf_kv_pool_destroy(nf_kv_pool* pool);
  * (hipHostMalloc, torch pin_memory) keeps the call asynchronous.  `pages`
  * may be reused on return; a page may appear more than once.  Offloads on
  * one pool must not overlap each other; the pages must not be written while
- * the offload reads them.  Errors: NF_ERR_INVALID_ARG (null pool, negative
- * n, null arrays with n > 0), NF_ERR_OUT_OF_RANGE (a page outside the pool),
- * NF_ERR_HIP. */
+ * the offload reads them; the pool's layer must still exist.  Errors:
+ * NF_ERR_INVALID_ARG (null pool, negative n, null arrays with n > 0),
+ * NF_ERR_OUT_OF_RANGE (a page outside the pool), NF_ERR_HIP. */
 nf_status nf_kv_offload(nf_kv_pool* pool, const int32_t* pages, int32_t n, void* host_k, void* host_v,
                         void* stream);
 

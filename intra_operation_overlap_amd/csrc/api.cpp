@@ -131,6 +131,7 @@ struct nf_layer {
 
 struct nf_kv_pool {
   const nf_layer* layer = nullptr;
+  int device = 0;
   int32_t n_pages = 0, page_size = 0;
   void* k = nullptr;
   void* v = nullptr;
@@ -141,12 +142,13 @@ namespace {
 
 hipError_t ensure(DevBuf& b, size_t bytes) {
   if (bytes <= b.bytes) return hipSuccess;
+  // at least doubling, so the buffers kept below stay under the final size
+  const size_t want = std::max({bytes, 2 * b.bytes, (size_t)256});
   if (b.p) {                 // may still be in use by queued work or a graph
     b.old.push_back(b.p);
     b.p = nullptr;
     b.bytes = 0;
   }
-  const size_t want = std::max(bytes, (size_t)256);
   hipError_t e = hipMalloc(&b.p, want);
   if (e != hipSuccess) {
     b.p = nullptr;
@@ -1024,6 +1026,7 @@ nf_status nf_kv_pool_create(const nf_layer* L, int32_t n_pages, int32_t page_siz
   if (n_pages <= 0) return set_err(NF_ERR_INVALID_ARG, "n_pages must be positive");
   nf_kv_pool* p = new nf_kv_pool();
   p->layer = L;
+  p->device = L->device;
   p->n_pages = n_pages;
   p->page_size = page_size;
   p->k = k_dev;
@@ -1034,8 +1037,8 @@ nf_status nf_kv_pool_create(const nf_layer* L, int32_t n_pages, int32_t page_siz
 
 void nf_kv_pool_destroy(nf_kv_pool* p) {
   if (!p) return;
-  if (p->offload.p || !p->offload.old.empty()) {
-    (void)hipSetDevice(p->layer->device);
+  if (p->offload.p || !p->offload.old.empty()) {   // the layer may be gone already
+    (void)hipSetDevice(p->device);
     (void)hipDeviceSynchronize();
     release(p->offload);
   }
@@ -1055,7 +1058,7 @@ nf_status nf_kv_offload(nf_kv_pool* P, const int32_t* pages, int32_t n, void* ho
   const int64_t blk = (int64_t)s.n_kv_heads * P->page_size * s.head_dim * (int64_t)dtype_bytes(s.dtype);
   const size_t idx_bytes = ((size_t)n * 4 + 255) & ~(size_t)255;
   hipStream_t st = (hipStream_t)stream;
-  HIP_TRY(hipSetDevice(P->layer->device));
+  HIP_TRY(hipSetDevice(P->device));
   HIP_TRY(ensure(P->offload, idx_bytes + 2 * (size_t)n * blk));
   char* base = (char*)P->offload.p;
   int32_t* d_pages = (int32_t*)base;
