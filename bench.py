@@ -481,8 +481,9 @@ KERNEL_SOURCES = {
     "gemm_o_residual": ["gemm.hip"] + _COMMON,
     "gemm_gate_up_swiglu": ["gemm.hip"] + _COMMON,
     "gemm_down_residual": ["gemm.hip"] + _COMMON,
-    "moe_gemm_gate_up_swiglu": ["gemm_stream.hip"] + _COMMON,
-    "moe_gemm_down": ["gemm_stream.hip"] + _COMMON,
+    # the streaming kernel's configuration is chosen in gemm.hip
+    "moe_gemm_gate_up_swiglu": ["gemm_stream.hip", "gemm.hip"] + _COMMON,
+    "moe_gemm_down": ["gemm_stream.hip", "gemm.hip"] + _COMMON,
 }
 
 

@@ -368,7 +368,7 @@ nf_status nf_probe_cu_map(int32_t* xcc, int32_t n);
  * tile_cfg < 0 and k_splits <= 0 let the library choose for a stream that
  * may use `cus` CUs (cus <= 0: all); a given tile_cfg must be one of the
  * layer's LDS-tiled configurations (0..6, or 10..30 with K % 64 == 0) or of
- * its weight-streaming ones (40..49: N % 32 == 0, K a multiple of the
+ * its weight-streaming ones (40..51: N % 32 == 0, K a multiple of the
  * configuration's chunk, two n-blocks per wave exactly for mode 2), for which
  * B is first copied into operand order.  That copy and the split-K workspace
  * are allocated and freed inside, and the call returns after the GEMM

@@ -1032,13 +1032,13 @@ namespace {
 // MI355X: a workgroup streams at most kWgGBps, at most two workgroups share a
 // CU, and the chip at most kHbmGBps; split-K adds its fp32 partial slices
 // (written, then read again by the reduce).
-// (the double-buffered configurations 46 and 47 keep a second chunk in
+// (the double-buffered configurations 46..51 keep a second chunk in
 // flight: about 24 GB/s per workgroup)
 constexpr double kWgGBps = 20.0, kWgGBpsDB = 24.0, kHbmGBps = 6000.0;
 int stream_splits(const GemmArgs& a, int cfg, int cus) {
-  const double wg_gbps = (cfg >= 46 && cfg <= 49) ? kWgGBpsDB : kWgGBps;
+  const double wg_gbps = (cfg >= 46 && cfg <= 51) ? kWgGBpsDB : kWgGBps;
   const bool sw = a.mode == GEMM_SWIGLU;
-  const int nbw = (cfg == 42 || cfg == 43 || cfg == 45 || cfg == 47 || cfg == 49) ? 2 : 1;
+  const int nbw = stream_nbw(cfg);
   const int nbt = (sw ? 2 : 1) * (a.N / 32);
   const int n_wg = (nbt + 4 * nbw - 1) / (4 * nbw);
   const int nch = a.K / 16 / stream_kc(cfg);
@@ -1071,10 +1071,12 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
     // the down projection (112 chunks per workgroup) 48, which loads A two
     // chunks ahead, beats 46 by a fifth; for gate/up (32 chunks per
     // workgroup, 3.5 rounds) 49 did not beat 47; a 160 x 256 LDS-pipelined
-    // tile (configuration 30) ties with 46 / 47)
+    // tile (configuration 30) ties with 46 / 47; 50 / 51, which issue the
+    // next chunk's loads spread among this chunk's MFMAs, beat 48 / 47 by
+    // an eighth and a tenth)
     const bool sw = a.mode == GEMM_SWIGLU;
     int cfg = 0;
-    if (a.group_off && a.max_group_rows / std::max(1, a.n_groups) <= 160) cfg = sw ? 47 : 48;
+    if (a.group_off && a.max_group_rows / std::max(1, a.n_groups) <= 160) cfg = sw ? 51 : 50;
     if (cfg && a.N % 32 == 0 && a.K % (16 * stream_kc(cfg)) == 0) {
       p.cfg = cfg;
       p.k_splits = stream_splits(a, cfg, cus);

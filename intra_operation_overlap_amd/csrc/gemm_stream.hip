@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
   constexpr int NB = KC * NBW;               // B loads per wave per chunk
   static_assert(CH % 4096 == 0 && NA >= 1, "chunk");
   static_assert((PIPE >= 1 ? 2 : 1) * (NA + NB) + (PIPE == 3 ? NA : 0) <= 63, "vmcnt range");
+  static_assert(PIPE != 5 || NA + NB <= KC * MB * 4, "loads per MFMA slot");
   static_assert((MODE == GEMM_SWIGLU) == (NBW == 2), "SWIGLU pairs a gate and an up block per wave");
   __shared__ __attribute__((aligned(1024))) char smem[(PIPE >= 1 ? 2 : 1) * CH];
 
@@ -125,7 +126,82 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void gemm_stream_kernel(SPara
     // stays exact; the other waves of the CU keep HBM busy while one wave
     // computes.
     bf16x8 ar[NA];
-    if constexpr (PIPE == 1 || PIPE == 3) {
+    if constexpr (PIPE == 5) {
+      // PIPE 5: as PIPE 1 (chunk c + 1's loads in flight while chunk c's
+      // MFMAs run), but the NA + NB loads of chunk c + 1 are issued spread
+      // over chunk c's MFMAs in a fixed order, not in a block before them:
+      // the CU's path from L2 accepts about one 1 KB load per 16 cycles, and
+      // a wave waiting to issue a load issues no MFMA (per-wave timing: the
+      // block of 26 loads took ~2500 cycles per chunk beside ~3200 of MFMAs).
+      const __amdgpu_buffer_rsrc_t rA = buf_rsrc(a.A);
+      uint32_t aoff[NA];
+#pragma unroll
+      for (int i = 0; i < NA; ++i) aoff[i] = (uint32_t)((asrc[i] - (const bf16*)a.A) * 2);
+      __amdgpu_buffer_rsrc_t rB[NBW];
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) rB[j] = buf_rsrc(bsrc[j] - lane);
+      bf16x8 bq[2][KC][NBW];
+      bf16x8 aq[NA];
+      // load d of chunk c: A pieces first (they go to LDS right after the
+      // MFMAs), then the weights (the chunk after the last reloads the last,
+      // so every wave issues the same loads and the in-order waits stay exact)
+      auto load1 = [&](int c, int d, bf16x8 (&bdst)[KC][NBW]) {
+        c = min(c, nch - 1);
+        if (d < NA) {
+          aq[d] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[d], c * KC * SK * 2, 0));
+        } else {
+          const int q = d - NA, st = q / NBW, j = q % NBW;
+          bdst[st][j] = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB[j], lane * 16, (c * KC + st) * 1024, 2));
+        }
+      };
+      auto put_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) *(bf16x8*)(smem + buf * CH + ((wave * NA + i) * 64 + lane) * 16) = aq[i];
+      };
+      auto frag = [&](int buf, int idx) {
+        const int st = idx / MB, m = idx % MB;
+        const int r = m * SB + (lane & 31);
+        const int sl = (2 * st + (lane >> 5)) ^ (r % PR);
+        return *(const bf16x8*)(smem + buf * CH + r * PR * 16 + sl * 16);
+      };
+      constexpr int NI = KC * MB, NL = NA + NB;
+      // chunk c's MFMAs from LDS buffer buf and registers src, with chunk
+      // c + 1's loads (into aq and bnext) spread over them
+      auto mma_load = [&](int buf, const bf16x8 (&src)[KC][NBW], int cnext, bf16x8 (&bnext)[KC][NBW]) {
+        bf16x8 af[3];
+        af[0] = frag(buf, 0);
+        if (NI > 1) af[1] = frag(buf, 1);
+#pragma unroll
+        for (int idx = 0; idx < NI; ++idx) {
+          if (idx + 2 < NI) af[(idx + 2) % 3] = frag(buf, idx + 2);
+          const int st = idx / MB, m = idx % MB;
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) acc[m][j] = mfma32(af[idx % 3], src[st][j], acc[m][j]);
+#pragma unroll
+          for (int d = (idx * NL + NI - 1) / NI; d < ((idx + 1) * NL + NI - 1) / NI; ++d) load1(cnext, d, bnext);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // prologue: chunk 0 to LDS and registers
+#pragma unroll
+      for (int d = 0; d < NL; ++d) load1(0, d, bq[0]);
+      put_a(0);
+      int c = 0;
+      for (; c + 1 < nch; c += 2) {
+        barrier_lds();                // chunk c's A is in buffer 0; chunk c - 1 is done with buffer 1
+        mma_load(0, bq[0], c + 1, bq[1]);
+        put_a(1);
+        barrier_lds();
+        mma_load(1, bq[1], c + 2, bq[0]);
+        put_a(0);
+      }
+      if (c < nch) {
+        barrier_lds();
+        mma_load(0, bq[0], c + 1, bq[1]);
+      }
+      barrier_lds();                  // LDS may take the next pass
+    } else if constexpr (PIPE == 1 || PIPE == 3) {
       // PIPE 3 loads A two chunks ahead (a second register set), so the A
       // written to LDS after chunk c's MFMAs has been in flight for a chunk
       // and a half instead of for the MFMAs alone.
@@ -371,6 +447,7 @@ hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStr
 //   workgroup per CU, so that an expert of up to 160 rows streams its weights once)
 //   46, 47: as 44, 45 with 8 k-steps per chunk, double-buffered
 //   48, 49: as 46, 47 with A loaded two chunks ahead
+//   50, 51: as 46, 47 with the next chunk's loads spread over the MFMAs
 hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook) {
   switch (p.cfg) {
     case 40: return launch_stream<1, 1, 16>(a, p, ws, s, hook);
@@ -383,14 +460,16 @@ hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream
     case 47: return launch_stream<5, 2, 8, 1>(a, p, ws, s, hook);
     case 48: return launch_stream<5, 1, 8, 3>(a, p, ws, s, hook);
     case 49: return launch_stream<5, 2, 8, 3>(a, p, ws, s, hook);
+    case 50: return launch_stream<5, 1, 8, 5>(a, p, ws, s, hook);
+    case 51: return launch_stream<5, 2, 8, 5>(a, p, ws, s, hook);
     default: return hipErrorInvalidValue;
   }
 }
 
 int stream_nbw(int cfg) {
   switch (cfg) {
-    case 42: case 43: case 45: case 47: case 49: return 2;
-    case 40: case 41: case 44: case 46: case 48: return 1;
+    case 42: case 43: case 45: case 47: case 49: case 51: return 2;
+    case 40: case 41: case 44: case 46: case 48: case 50: return 1;
     default: return 0;
   }
 }
@@ -398,7 +477,7 @@ int stream_nbw(int cfg) {
 int stream_kc(int cfg) {
   switch (cfg) {
     case 40: case 41: case 42: case 43: case 44: case 45: return 16;
-    case 46: case 47: case 48: case 49: return 8;
+    case 46: case 47: case 48: case 49: case 50: case 51: return 8;
     default: return 0;
   }
 }

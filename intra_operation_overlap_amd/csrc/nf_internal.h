@@ -94,7 +94,7 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
 // Sum of `splits` fp32 partial slices (M x part_ld each) plus the mode's
 // epilogue, written to C.
 hipError_t splitk_reduce(const GemmArgs& a, const float* part, int64_t part_ld, int splits, hipStream_t s);
-// Weight-streaming kernels (tile configurations 40..49; need a.Bp).
+// Weight-streaming kernels (tile configurations 40..51; need a.Bp).
 hipError_t gemm_stream(const GemmArgs& a, const GemmPlan& p, void* ws, hipStream_t s, const LaunchHook* hook);
 int stream_kc(int cfg);   // k-steps (of 16) per A chunk of a streaming configuration, 0 if none
 int stream_nbw(int cfg);  // packed n-blocks per wave (2: SwiGLU gate + up), 0 if none

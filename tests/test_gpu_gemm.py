@@ -86,8 +86,8 @@ def test_gemm_library_choice_on_a_large_ragged_problem(mode):
 
 # weight-streaming configurations: (cfg, rows per pass) for one n-block per
 # wave (modes 0, 1) and two (SwiGLU)
-STREAM_1 = [40, 41, 44, 46, 48]
-STREAM_2 = [42, 43, 45, 47, 49]
+STREAM_1 = [40, 41, 44, 46, 48, 50]
+STREAM_2 = [42, 43, 45, 47, 49, 51]
 
 
 @pytest.mark.parametrize("cfg", STREAM_1 + STREAM_2)
