@@ -217,7 +217,7 @@ void nf_kv_pool_destroy(nf_kv_pool* pool);
  * (hipHostMalloc, torch pin_memory) keeps the call asynchronous.  `pages`
  * may be reused on return; a page may appear more than once.  Offloads on
  * one pool must not overlap each other; the pages must not be written while
- * the offload reads them; the pool's layer must still exist.  Errors:
+ * the offload reads them (the pool's layer need not exist any more).  Errors:
  * NF_ERR_INVALID_ARG (null pool, negative n, null arrays with n > 0),
  * NF_ERR_OUT_OF_RANGE (a page outside the pool), NF_ERR_HIP. */
 nf_status nf_kv_offload(nf_kv_pool* pool, const int32_t* pages, int32_t n, void* host_k, void* host_v,
@@ -277,7 +277,8 @@ nf_status nf_stack_step(nf_layer* const* layers, nf_kv_pool* const* pools, int32
  * host work per kernel.  It first runs the step once on `stream` (writing
  * batch->out and the batch's pool slots), synchronises, copies each layer's
  * step metadata (positions, page tables, attention work items) into device
- * buffers the graph owns, then captures the launches on `stream`.  The graph
+ * buffers the graph owns, then captures the launches on a stream of its own
+ * (`stream` may be the null stream, which cannot be captured).  The graph
  * reads batch->x, writes batch->out, the batch's pool slots and the layers'
  * buffers at every replay, so those must stay allocated, and replays must
  * not overlap each other or steps on the same layers; a layer's buffers are

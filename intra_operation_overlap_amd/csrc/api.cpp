@@ -133,6 +133,7 @@ struct nf_kv_pool {
   const nf_layer* layer = nullptr;
   int device = 0;
   int32_t n_pages = 0, page_size = 0;
+  int64_t block_bytes = 0;   // one page's K (or V) block: n_kv_heads x page_size x head_dim elements
   void* k = nullptr;
   void* v = nullptr;
   DevBuf offload;      // page list and gathered K / V blocks of nf_kv_offload
@@ -1031,6 +1032,7 @@ nf_status nf_kv_pool_create(const nf_layer* L, int32_t n_pages, int32_t page_siz
   p->page_size = page_size;
   p->k = k_dev;
   p->v = v_dev;
+  p->block_bytes = (int64_t)L->s.n_kv_heads * page_size * L->s.head_dim * (int64_t)dtype_bytes(L->s.dtype);
   *out = p;
   return NF_OK;
 }
@@ -1054,8 +1056,7 @@ nf_status nf_kv_offload(nf_kv_pool* P, const int32_t* pages, int32_t n, void* ho
       return set_err(NF_ERR_OUT_OF_RANGE, "nf_kv_offload: page %d at %d is outside the pool's %d pages", pages[i],
                      i, P->n_pages);
   if (n == 0) return NF_OK;
-  const nf_shape& s = P->layer->s;
-  const int64_t blk = (int64_t)s.n_kv_heads * P->page_size * s.head_dim * (int64_t)dtype_bytes(s.dtype);
+  const int64_t blk = P->block_bytes;
   const size_t idx_bytes = ((size_t)n * 4 + 255) & ~(size_t)255;
   hipStream_t st = (hipStream_t)stream;
   HIP_TRY(hipSetDevice(P->device));
@@ -1270,28 +1271,40 @@ nf_status nf_probe_cu_map(int32_t* xcc, int32_t n) {
   return NF_OK;
 }
 
+// Device buffers and events of a probe, released on every return path.
+struct ProbeRes {
+  void* buf = nullptr;
+  float* sink = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  ~ProbeRes() {
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (buf) (void)hipFree(buf);
+    if (sink) (void)hipFree(sink);
+  }
+};
+
 nf_status nf_probe_mfma_bf16_tflops(double* tflops) {
   if (!tflops) return set_err(NF_ERR_INVALID_ARG, "nf_probe_mfma_bf16_tflops: null argument");
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   hipDeviceProp_t prop;
   HIP_TRY(hipGetDeviceProperties(&prop, dev));
-  float* sink = nullptr;
-  HIP_TRY(hipMalloc(&sink, 1024 * sizeof(float)));
-  hipEvent_t e0, e1;
-  HIP_TRY(hipEventCreate(&e0));
-  HIP_TRY(hipEventCreate(&e1));
+  ProbeRes r;
+  HIP_TRY(hipMalloc(&r.sink, 1024 * sizeof(float)));
+  HIP_TRY(hipEventCreate(&r.e0));
+  HIP_TRY(hipEventCreate(&r.e1));
   const int blocks = prop.multiProcessorCount * 4, iters = 4096;
   double best = 0;
   for (int shape = 0; shape < 2; ++shape) {
     double best_shape = 0;
     for (int rep = 0; rep < 4; ++rep) {
-      HIP_TRY(hipEventRecord(e0, nullptr));
-      HIP_TRY(probe_mfma(shape, blocks, iters, sink, nullptr));
-      HIP_TRY(hipEventRecord(e1, nullptr));
-      HIP_TRY(hipEventSynchronize(e1));
+      HIP_TRY(hipEventRecord(r.e0, nullptr));
+      HIP_TRY(probe_mfma(shape, blocks, iters, r.sink, nullptr));
+      HIP_TRY(hipEventRecord(r.e1, nullptr));
+      HIP_TRY(hipEventSynchronize(r.e1));
       float ms = 0;
-      HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+      HIP_TRY(hipEventElapsedTime(&ms, r.e0, r.e1));
       // per wave and iteration: 8 x 16x16x32 or 4 x 32x32x16, both 131072 FLOP
       const double flops = (double)blocks * 4 /*waves*/ * iters * 131072.0;
       if (rep > 0) best_shape = std::max(best_shape, flops / (ms * 1e-3) / 1e12);
@@ -1300,9 +1313,6 @@ nf_status nf_probe_mfma_bf16_tflops(double* tflops) {
       std::fprintf(stderr, "nf probe: mfma %s %.1f TFLOP/s\n", shape ? "32x32x16" : "16x16x32", best_shape);
     best = std::max(best, best_shape);
   }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
-  (void)hipFree(sink);
   *tflops = best;
   return NF_OK;
 }
@@ -1314,31 +1324,25 @@ nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps) {
   HIP_TRY(hipGetDevice(&dev));
   hipDeviceProp_t prop;
   HIP_TRY(hipGetDeviceProperties(&prop, dev));
-  void* buf = nullptr;
-  float* sink = nullptr;
-  HIP_TRY(hipMalloc(&buf, bytes));
-  HIP_TRY(hipMalloc(&sink, 1024 * sizeof(float)));
-  HIP_TRY(hipMemset(buf, 1, bytes));
-  hipEvent_t e0, e1;
-  HIP_TRY(hipEventCreate(&e0));
-  HIP_TRY(hipEventCreate(&e1));
+  ProbeRes r;
+  HIP_TRY(hipMalloc(&r.buf, bytes));
+  HIP_TRY(hipMalloc(&r.sink, 1024 * sizeof(float)));
+  HIP_TRY(hipMemset(r.buf, 1, bytes));
+  HIP_TRY(hipEventCreate(&r.e0));
+  HIP_TRY(hipEventCreate(&r.e1));
   // best of a few occupancies (workgroups per CU) of a streaming read
   double best = 0;
   for (int per_cu : {2, 4, 8}) {
     for (int rep = 0; rep < 4; ++rep) {
-      HIP_TRY(hipEventRecord(e0, nullptr));
-      HIP_TRY(probe_read(buf, bytes, sink, prop.multiProcessorCount * per_cu, nullptr));
-      HIP_TRY(hipEventRecord(e1, nullptr));
-      HIP_TRY(hipEventSynchronize(e1));
+      HIP_TRY(hipEventRecord(r.e0, nullptr));
+      HIP_TRY(probe_read(r.buf, bytes, r.sink, prop.multiProcessorCount * per_cu, nullptr));
+      HIP_TRY(hipEventRecord(r.e1, nullptr));
+      HIP_TRY(hipEventSynchronize(r.e1));
       float ms = 0;
-      HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+      HIP_TRY(hipEventElapsedTime(&ms, r.e0, r.e1));
       if (rep > 0) best = std::max(best, (double)bytes / (ms * 1e-3) / 1e9);
     }
   }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
-  (void)hipFree(buf);
-  (void)hipFree(sink);
   *gbps = best;
   return NF_OK;
 }
@@ -1531,8 +1535,8 @@ extern "C" nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode,
   }
   void* ws = nullptr;
   const size_t wsb = gemm_workspace_bytes(g, p);
-  if (wsb) HIP_TRY(hipMalloc(&ws, wsb));
-  hipError_t e = gemm_bf16(g, p, ws, s);
+  hipError_t e = wsb ? hipMalloc(&ws, wsb) : hipSuccess;
+  if (e == hipSuccess) e = gemm_bf16(g, p, ws, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (ws) (void)hipFree(ws);
   if (Bp) (void)hipFree(Bp);
@@ -1545,54 +1549,62 @@ extern "C" nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode,
 extern "C" nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int32_t mode, int32_t tile_cfg,
                                            int32_t k_splits, int32_t cus, int32_t reps, double* ms,
                                            int32_t* out_cfg, int32_t* out_splits) {
-  if (!ms || M <= 0 || N <= 0 || K <= 0 || K % 8 || mode < 0 || mode > 2 || reps <= 0)
+  if (!ms || M <= 0 || N <= 0 || K <= 0 || K % 8 || N % 8 || mode < 0 || mode > 2 || reps <= 0)
     return set_err(NF_ERR_INVALID_ARG, "nf_probe_gemm_bf16_ms: bad argument");
+  if (tile_cfg >= 0 && !((tile_cfg <= 6) || (tile_cfg >= 10 && tile_cfg <= 30 && K % 64 == 0) ||
+                         (tile_cfg >= 40 && stream_kc(tile_cfg) > 0 && N % 32 == 0 &&
+                          K % (16 * stream_kc(tile_cfg)) == 0 && stream_nbw(tile_cfg) == (mode == GEMM_SWIGLU ? 2 : 1))))
+    return set_err(NF_ERR_INVALID_ARG, "nf_probe_gemm_bf16_ms: tile_cfg %d not available for N %d K %d mode %d",
+                   tile_cfg, N, K, mode);
   if ((int64_t)std::max(M, N) * K * 2 >= (int64_t(1) << 32))
     return set_err(NF_ERR_OUT_OF_RANGE, "nf_probe_gemm_bf16_ms: an operand would exceed 4 GiB");
   const int64_t nb = mode == GEMM_SWIGLU ? 2 : 1;
-  void *A = nullptr, *Bm = nullptr, *C = nullptr, *R = nullptr;
-  HIP_TRY(hipMalloc(&A, (size_t)M * K * 2));
-  HIP_TRY(hipMalloc(&Bm, (size_t)nb * N * K * 2));
-  HIP_TRY(hipMalloc(&C, (size_t)M * N * 2));
-  HIP_TRY(hipMalloc(&R, (size_t)M * N * 2));
+  // device buffers and events, released on every return path
+  struct Res {
+    void *A = nullptr, *Bm = nullptr, *C = nullptr, *R = nullptr, *Bp = nullptr, *ws = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    ~Res() {
+      if (e0) (void)hipEventDestroy(e0);
+      if (e1) (void)hipEventDestroy(e1);
+      for (void* q : {A, Bm, C, R, ws, Bp})
+        if (q) (void)hipFree(q);
+    }
+  } r;
+  HIP_TRY(hipMalloc(&r.A, (size_t)M * K * 2));
+  HIP_TRY(hipMalloc(&r.Bm, (size_t)nb * N * K * 2));
+  HIP_TRY(hipMalloc(&r.C, (size_t)M * N * 2));
+  HIP_TRY(hipMalloc(&r.R, (size_t)M * N * 2));
   // activations ~ unit scale, weights uniform with standard deviation 0.02
-  HIP_TRY(probe_fill_bf16(A, (int64_t)M * K, 1u, 1.0f, nullptr));
-  HIP_TRY(probe_fill_bf16(Bm, nb * N * K, 2u, 0.0346f, nullptr));
-  HIP_TRY(hipMemset(R, 0, (size_t)M * N * 2));
+  HIP_TRY(probe_fill_bf16(r.A, (int64_t)M * K, 1u, 1.0f, nullptr));
+  HIP_TRY(probe_fill_bf16(r.Bm, nb * N * K, 2u, 0.0346f, nullptr));
+  HIP_TRY(hipMemset(r.R, 0, (size_t)M * N * 2));
   GemmArgs g;
-  g.A = A; g.lda = K;
-  g.B = Bm; g.B2 = (char*)Bm + (size_t)N * K * 2; g.ldb = K;
-  g.C = C; g.ldc = N; g.R = R; g.ldr = N;
+  g.A = r.A; g.lda = K;
+  g.B = r.Bm; g.B2 = (char*)r.Bm + (size_t)N * K * 2; g.ldb = K;
+  g.C = r.C; g.ldc = N; g.R = r.R; g.ldr = N;
   g.M = M; g.N = N; g.K = K; g.mode = mode;
-  void* Bp = nullptr;
   if (N % 32 == 0 && K % 16 == 0) {             // operand-order copy for the streaming kernels
-    HIP_TRY(hipMalloc(&Bp, (size_t)nb * N * K * 2));
-    HIP_TRY(pack_b(g.B, K, 0, N, K, 1, Bp, (int)nb, 0, 0, nullptr));
-    if (nb == 2) HIP_TRY(pack_b(g.B2, K, 0, N, K, 1, Bp, 2, 1, 0, nullptr));
-    g.Bp = Bp;
+    HIP_TRY(hipMalloc(&r.Bp, (size_t)nb * N * K * 2));
+    HIP_TRY(pack_b(g.B, K, 0, N, K, 1, r.Bp, (int)nb, 0, 0, nullptr));
+    if (nb == 2) HIP_TRY(pack_b(g.B2, K, 0, N, K, 1, r.Bp, 2, 1, 0, nullptr));
+    g.Bp = r.Bp;
   }
   GemmPlan p = gemm_choose(g, cus);
   if (tile_cfg >= 0) p.cfg = tile_cfg;
   if (k_splits > 0) p.k_splits = k_splits;
-  void* ws = nullptr;
   const size_t wsb = gemm_workspace_bytes(g, p);
-  if (wsb) HIP_TRY(hipMalloc(&ws, wsb));
-  hipEvent_t e0, e1;
-  HIP_TRY(hipEventCreate(&e0));
-  HIP_TRY(hipEventCreate(&e1));
-  for (int i = 0; i < 3; ++i) HIP_TRY(gemm_bf16(g, p, ws, nullptr));
-  HIP_TRY(hipEventRecord(e0, nullptr));
-  for (int i = 0; i < reps; ++i) HIP_TRY(gemm_bf16(g, p, ws, nullptr));
-  HIP_TRY(hipEventRecord(e1, nullptr));
-  HIP_TRY(hipEventSynchronize(e1));
+  if (wsb) HIP_TRY(hipMalloc(&r.ws, wsb));
+  HIP_TRY(hipEventCreate(&r.e0));
+  HIP_TRY(hipEventCreate(&r.e1));
+  for (int i = 0; i < 3; ++i) HIP_TRY(gemm_bf16(g, p, r.ws, nullptr));
+  HIP_TRY(hipEventRecord(r.e0, nullptr));
+  for (int i = 0; i < reps; ++i) HIP_TRY(gemm_bf16(g, p, r.ws, nullptr));
+  HIP_TRY(hipEventRecord(r.e1, nullptr));
+  HIP_TRY(hipEventSynchronize(r.e1));
   float t = 0;
-  HIP_TRY(hipEventElapsedTime(&t, e0, e1));
+  HIP_TRY(hipEventElapsedTime(&t, r.e0, r.e1));
   *ms = t / reps;
   if (out_cfg) *out_cfg = p.cfg;
   if (out_splits) *out_splits = p.k_splits;
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
-  for (void* q : {A, Bm, C, R, ws, Bp})
-    if (q) (void)hipFree(q);
   return NF_OK;
 }
