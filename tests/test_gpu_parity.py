@@ -91,6 +91,34 @@ def test_small_bf16_prefill_from_zero_and_g8():
     _full_check(S, "k2_split_prefill", B.make_plan(2, [40, S.batch.n_tokens - 40], n_streams=2, gemm_cus_per_xcd=16))
 
 
+# Seeded shape sweep: GQA groups 1, 2 and 8, hidden not a multiple of 64 (the
+# GEMMs' non-pipelined configurations), ragged FFN widths, prefill chunks from
+# position 0 and mid-context, a decode-only batch with long contexts, and an
+# fp32 layer with head_dim 64 (the generic attention kernel).
+SWEEP = {
+    "g1_prefill_from_0": W.Workload("sw_g1", W.Shape(hidden=256, n_q_heads=8, n_kv_heads=8, head_dim=128, ffn=344,
+                                                     dtype="bf16", rope_theta=1e4),
+                                    n_decode=17, ctx_range=(1, 64), prefill=(0, 33), seed=101),
+    "g2_hidden520": W.Workload("sw_g2", W.Shape(hidden=520, n_q_heads=8, n_kv_heads=4, head_dim=128, ffn=720,
+                                                dtype="bf16", rope_theta=5e5),
+                               n_decode=33, ctx_range=(20, 400), prefill=(50, 20), seed=102),
+    "g8_long_decode": W.Workload("sw_g8", W.Shape(hidden=1024, n_q_heads=16, n_kv_heads=2, head_dim=128, ffn=1000,
+                                                  dtype="bf16", rope_theta=1e6),
+                                 n_decode=50, ctx_range=(1, 700), prefill=None, seed=103),
+    "fp32_d64": W.Workload("sw_f32", W.Shape(hidden=384, n_q_heads=6, n_kv_heads=2, head_dim=64, ffn=520,
+                                             dtype="f32", rope_theta=1e4),
+                           n_decode=12, ctx_range=(1, 150), prefill=(10, 27), seed=104),
+}
+
+
+@pytest.mark.parametrize("case", list(SWEEP))
+def test_shape_sweep_parity(case):
+    S = GH.setup(SWEEP[case])
+    T = S.batch.n_tokens
+    _full_check(S, f"{case} k1", B.make_plan(1, [T]))
+    _full_check(S, f"{case} k2", B.make_plan(2, [T // 2, T - T // 2], n_streams=2))
+
+
 def test_split_k_small_batch_parity():
     """Decode-sized nano-batches take the split-K GEMM path (fused reduction)."""
     wl = W.Workload("splitk", W.Shape(hidden=2048, n_q_heads=8, n_kv_heads=4, head_dim=128, ffn=1536,
