@@ -76,7 +76,13 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16x8_kernel(const bf16* __restr
 // RMSNorm: x1 = round(sum_z partial_z + x) is stored, then y = RMSNorm(x1) * g.
 // Same thread-to-chunk mapping and summation order as splitk_reduce_kernel
 // followed by rmsnorm_bf16x8_kernel, so the result is bit-identical.
-__global__ __launch_bounds__(256) void residual_rmsnorm_partials_kernel(
+// One row per block of RRN_THREADS threads: a row of a decode batch reads all
+// its split-K slices, and with few rows per step (one block per row) twice the
+// usual threads keep twice the slice loads in flight per CU.  The block size
+// does not depend on the batch, so every plan rounds the norm alike.
+constexpr int RRN_THREADS = 512;
+
+__global__ __launch_bounds__(RRN_THREADS) void residual_rmsnorm_partials_kernel(
     const float* __restrict__ part, int64_t part_ld, int64_t zstride, int splits, const bf16* __restrict__ x,
     int64_t ldx, bf16* __restrict__ x1, int64_t ldx1, const bf16* __restrict__ g, bf16* __restrict__ y, int H,
     float eps) {
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_partials_kernel(
   const bf16x8* xr = (const bf16x8*)(x + row * ldx);
   bf16x8* x1r = (bf16x8*)(x1 + row * ldx1);
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n8; i += 256) {
+  for (int i = threadIdx.x; i < n8; i += RRN_THREADS) {
     const f32x4 lo = sum_slices<f32x4>(P + 8 * i, zstride, splits);
     const f32x4 hi = sum_slices<f32x4>(P + 8 * i + 4, zstride, splits);
     const bf16x8 r = xr[i];
@@ -103,14 +109,18 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_partials_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += (float)o[e] * (float)o[e];
   }
-  __shared__ float red[4];
+  constexpr int NW = RRN_THREADS / 64;
+  __shared__ float red[NW];
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += red[w];
+  const float inv = rsqrtf(tot / (float)H + eps);
   const bf16x8* gr = (const bf16x8*)g;
   bf16x8* yr = (bf16x8*)(y + row * H);
-  for (int i = threadIdx.x; i < n8; i += 256) {
+  for (int i = threadIdx.x; i < n8; i += RRN_THREADS) {
     const bf16x8 v = x1r[i], w = gr[i];
     bf16x8 o;
 #pragma unroll
@@ -308,7 +318,7 @@ hipError_t residual_rmsnorm_partials(const float* part, int64_t part_ld, int64_t
                                      int T, int H, float eps, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (H % 8 != 0) return hipErrorInvalidValue;
-  launch(residual_rmsnorm_partials_kernel, T, 256, 0, s, part, part_ld, zstride, splits, (const bf16*)x, ldx,
+  launch(residual_rmsnorm_partials_kernel, T, RRN_THREADS, 0, s, part, part_ld, zstride, splits, (const bf16*)x, ldx,
          (bf16*)x1, ldx1, (const bf16*)g, (bf16*)y, H, eps);
   return hipGetLastError();
 }
