@@ -15,7 +15,8 @@ __device__ __forceinline__ bool meta_copy_block(const MetaCopy& mc, int rows) {
   const u32x4* src = (const u32x4*)mc.src;
   u32x4* dst = (u32x4*)mc.dst;
   const int64_t nb = gridDim.x - rows;
-  for (int64_t i = (int64_t)(blockIdx.x - rows) * 256 + threadIdx.x; i < mc.n16; i += nb * 256) dst[i] = src[i];
+  for (int64_t i = (int64_t)(blockIdx.x - rows) * blockDim.x + threadIdx.x; i < mc.n16; i += nb * blockDim.x)
+    dst[i] = src[i];
   return true;
 }
 
@@ -42,7 +43,28 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
 }
 
 // bf16 rows, 8 elements (16 bytes) per access; requires H % 8 == 0.
-__global__ __launch_bounds__(256) void rmsnorm_bf16x8_kernel(const bf16* __restrict__ x,
+// bf16 RMSNorms run one row per block of RN_THREADS threads.  A decode batch
+// has few rows (one block each) and the fused norm below reads all of a row's
+// split-K slices, so twice the usual threads keep twice the loads in flight per
+// CU.  Both kernels share the size, the thread-to-chunk mapping and the order
+// of the sum of squares, and the size does not depend on the batch, so every
+// plan rounds the norm alike.
+constexpr int RN_THREADS = 512;
+
+// Sum of squares of a block's threads, added wave by wave in a fixed order.
+__device__ __forceinline__ float block_sum_sq(float ss) {
+  constexpr int NW = RN_THREADS / 64;
+  __shared__ float red[NW];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += red[w];
+  return tot;
+}
+
+__global__ __launch_bounds__(RN_THREADS) void rmsnorm_bf16x8_kernel(const bf16* __restrict__ x,
                                                              const bf16* __restrict__ g,
                                                              bf16* __restrict__ y, int H, float eps, MetaCopy mc,
                                                              int rows) {
@@ -53,17 +75,13 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16x8_kernel(const bf16* __restr
   bf16x8* yr = (bf16x8*)(y + row * H);
   const int n8 = H / 8;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n8; i += 256) {
+  for (int i = threadIdx.x; i < n8; i += RN_THREADS) {
     const bf16x8 v = xr[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += (float)v[e] * (float)v[e];
   }
-  __shared__ float red[4];
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
-  for (int i = threadIdx.x; i < n8; i += 256) {
+  const float inv = rsqrtf(block_sum_sq(ss) / (float)H + eps);
+  for (int i = threadIdx.x; i < n8; i += RN_THREADS) {
     const bf16x8 v = xr[i], w = gr[i];
     bf16x8 o;
 #pragma unroll
@@ -76,13 +94,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16x8_kernel(const bf16* __restr
 // RMSNorm: x1 = round(sum_z partial_z + x) is stored, then y = RMSNorm(x1) * g.
 // Same thread-to-chunk mapping and summation order as splitk_reduce_kernel
 // followed by rmsnorm_bf16x8_kernel, so the result is bit-identical.
-// One row per block of RRN_THREADS threads: a row of a decode batch reads all
-// its split-K slices, and with few rows per step (one block per row) twice the
-// usual threads keep twice the slice loads in flight per CU.  The block size
-// does not depend on the batch, so every plan rounds the norm alike.
-constexpr int RRN_THREADS = 512;
-
-__global__ __launch_bounds__(RRN_THREADS) void residual_rmsnorm_partials_kernel(
+__global__ __launch_bounds__(RN_THREADS) void residual_rmsnorm_partials_kernel(
     const float* __restrict__ part, int64_t part_ld, int64_t zstride, int splits, const bf16* __restrict__ x,
     int64_t ldx, bf16* __restrict__ x1, int64_t ldx1, const bf16* __restrict__ g, bf16* __restrict__ y, int H,
     float eps) {
@@ -92,7 +104,7 @@ __global__ __launch_bounds__(RRN_THREADS) void residual_rmsnorm_partials_kernel(
   const bf16x8* xr = (const bf16x8*)(x + row * ldx);
   bf16x8* x1r = (bf16x8*)(x1 + row * ldx1);
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n8; i += RRN_THREADS) {
+  for (int i = threadIdx.x; i < n8; i += RN_THREADS) {
     const f32x4 lo = sum_slices<f32x4>(P + 8 * i, zstride, splits);
     const f32x4 hi = sum_slices<f32x4>(P + 8 * i + 4, zstride, splits);
     const bf16x8 r = xr[i];
@@ -109,18 +121,10 @@ __global__ __launch_bounds__(RRN_THREADS) void residual_rmsnorm_partials_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += (float)o[e] * (float)o[e];
   }
-  constexpr int NW = RRN_THREADS / 64;
-  __shared__ float red[NW];
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) tot += red[w];
-  const float inv = rsqrtf(tot / (float)H + eps);
+  const float inv = rsqrtf(block_sum_sq(ss) / (float)H + eps);
   const bf16x8* gr = (const bf16x8*)g;
   bf16x8* yr = (bf16x8*)(y + row * H);
-  for (int i = threadIdx.x; i < n8; i += RRN_THREADS) {
+  for (int i = threadIdx.x; i < n8; i += RN_THREADS) {
     const bf16x8 v = x1r[i], w = gr[i];
     bf16x8 o;
 #pragma unroll
@@ -305,7 +309,7 @@ hipError_t rmsnorm(int dtype, const void* x, const void* g, void* y, int T, int 
   const int extra = m.n16 > 0 ? (int)std::min<int64_t>((m.n16 + 255) / 256, 64) : 0;
   const int grid = T + extra;
   if (dtype == 1 && H % 8 == 0)
-    launch(rmsnorm_bf16x8_kernel, grid, 256, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps, m, T);
+    launch(rmsnorm_bf16x8_kernel, grid, RN_THREADS, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps, m, T);
   else if (dtype == 1)
     launch(rmsnorm_kernel<bf16>, grid, 256, 0, s, (const bf16*)x, (const bf16*)g, (bf16*)y, H, eps, m, T);
   else
@@ -318,7 +322,7 @@ hipError_t residual_rmsnorm_partials(const float* part, int64_t part_ld, int64_t
                                      int T, int H, float eps, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (H % 8 != 0) return hipErrorInvalidValue;
-  launch(residual_rmsnorm_partials_kernel, T, RRN_THREADS, 0, s, part, part_ld, zstride, splits, (const bf16*)x, ldx,
+  launch(residual_rmsnorm_partials_kernel, T, RN_THREADS, 0, s, part, part_ld, zstride, splits, (const bf16*)x, ldx,
          (bf16*)x1, ldx1, (const bf16*)g, (bf16*)y, H, eps);
   return hipGetLastError();
 }
