@@ -353,8 +353,11 @@ nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps);
  * library-allocated buffers filled with pseudo-random values (A uniform in
  * [-1, 1), B with standard deviation 0.02).  tile_cfg < 0 and k_splits <= 0
  * let the library choose for a stream that may use `cus` CUs; out_cfg and
- * out_splits (may be NULL) return what ran.  max(M, N) * K * 2 bytes must stay
- * under 4 GiB (NF_ERR_OUT_OF_RANGE). */
+ * out_splits (may be NULL) return what ran.  A given tile_cfg must be one that
+ * nf_gemm_bf16 accepts for this shape and mode, else NF_ERR_INVALID_ARG, as
+ * for N or K not multiples of 8 or reps <= 0.  max(M, N) * K * 2 bytes must
+ * stay under 4 GiB (NF_ERR_OUT_OF_RANGE).  Buffers and events are freed on
+ * every return path. */
 nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int32_t mode, int32_t tile_cfg,
                                 int32_t k_splits, int32_t cus, int32_t reps, double* ms,
                                 int32_t* out_cfg, int32_t* out_splits);

@@ -131,6 +131,20 @@ def test_gemm_rejects_bad_arguments_before_launching():
     assert e.value.status == B.NF_ERR_INVALID_ARG
 
 
+def test_gemm_probe_rejects_bad_arguments_before_allocating():
+    """The probe checks its configuration like nf_gemm_bf16 before any HIP call."""
+    bad = [(64, 64, 64, 0, 45, 1, 5),      # a two-n-block streaming configuration for a plain GEMM
+           (64, 64, 64, 2, 46, 1, 5),      # a one-n-block streaming configuration for SwiGLU
+           (64, 64, 96, 0, 14, 1, 5),      # a pipelined configuration with K % 64 != 0
+           (64, 60, 64, 0, -1, 0, 5),      # N % 8
+           (64, 64, 64, 0, 7, 1, 5),       # no configuration 7
+           (64, 64, 64, 0, -1, 0, 0)]      # reps <= 0
+    for M, N, K, mode, cfg, ks, reps in bad:
+        with pytest.raises(B.NfError) as e:
+            B.probe_gemm_bf16_ms(M, N, K, mode, cfg, ks, 256, reps)
+        assert e.value.status == B.NF_ERR_INVALID_ARG, (M, N, K, mode, cfg, reps)
+
+
 def test_validate_moe_needs_logits_and_shape_rules():
     wl = W.WORKLOADS["c5"]
     batch = W.make_batch(wl, n_decode=4)
