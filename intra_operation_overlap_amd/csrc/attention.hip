@@ -213,7 +213,10 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int64_t qoff, int grp,
 // ---------------------------------------------------------------- four waves per item
 // A 256-thread workgroup takes the item's pages round-robin across its four
 // waves and merges the four online-softmax states through LDS.
-__global__ __launch_bounds__(256) void attn_bf16_d128_kernel(AttnArgs a) {
+// Held to three waves per SIMD (160 registers, no spills; uncapped it takes
+// 192 and fits two): long-context grids of thousands of items keep a third
+// wave's page loads in flight per SIMD.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_bf16_d128_kernel(AttnArgs a) {
   __shared__ float m_s[4 * ROWS], l_s[4 * ROWS];
   __shared__ float O_s[4 * ROWS * DH];
 
