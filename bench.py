@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 PEAK_BF16_TFLOPS = 2500.0       # MI355X published dense bf16 MFMA
-DEFAULT_WORKLOAD = "c2"         # the Llama-3-8B-shaped decode batch (64 requests, context 512)
+DEFAULT_WORKLOAD = "c4"         # the Llama-2-70B 1/8 shard, 2048 tokens: the largest batch
 
 
 def log(msg):
@@ -128,15 +128,15 @@ def main():
     batch = W.make_batch(wl)
     weights = W.make_weights(wl, "cuda")
     acts = W.make_activations(wl, batch, "cuda")
-    k_pool, v_pool = W.make_pool(wl, batch.n_pages, "cuda")
+    k_plain, v_plain = W.make_pool(wl, batch.n_pages, "cuda")
     out = torch.empty_like(acts["x"])
     T = batch.n_tokens
     layer = B.Layer(s, weights, T, int(batch.pos.max()) + 1)
-    pool = B.KVPool(layer, batch.n_pages, s.page_size, k_pool, v_pool)
-    hb = B.HostBatch(batch, acts["x"].data_ptr(), out.data_ptr(),
-                     acts["router_logits"].data_ptr() if "router_logits" in acts else None)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    pool = B.KVPool.from_plain(layer, k_plain, v_plain, sp)
+    hb = B.HostBatch(batch, acts["x"].data_ptr(), out.data_ptr(),
+                     acts["router_logits"].data_ptr() if "router_logits" in acts else None)
 
     log("probing peaks")
     peak_tflops = B.probe_mfma_bf16_tflops()
@@ -144,8 +144,10 @@ def main():
     log(f"measured peaks: bf16 MFMA {peak_tflops:.0f} TFLOP/s, HBM read {peak_gbps:.0f} GB/s")
 
     host_us = []
+    flush_buf = torch.ones(128 << 20, dtype=torch.int32, device="cuda")     # 512 MiB
 
     def time_steps(n):
+        """Warm caches: K back-to-back steps bracketed by two events."""
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -158,33 +160,32 @@ def main():
         return e0.elapsed_time(e1) / n
 
     def time_cold(n):
-        """Median step time with cold caches: before each step a 512 MiB read
-        of a scratch buffer evicts the weights and the KV pool from L2 and the
-        Infinity Cache, so the step reads them from HBM.  (A read rather than
-        a write: a write would also leave dirty lines for the step to write
-        back.)  Each step is bracketed by its own events; the flush is
-        outside them."""
-        scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        times = []
-        for _ in range(n):
-            torch.sum(scratch)
-            e0.record(stream)
+        """Cold caches: before each step a 512 MiB read of a scratch buffer
+        evicts the weights and the KV pool from L2 and the Infinity Cache, so
+        the step reads them from HBM (a read rather than a write: a write
+        would leave dirty lines for the step to write back).  Each step is
+        bracketed by its own events, the flush outside them.  Returns the
+        mean and the median ms per step."""
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            torch.sum(flush_buf)
+            a.record(stream)
             layer.step(pool, hb, sp)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        del scratch
-        times.sort()
-        return {"ms_per_step": round(times[len(times) // 2], 5), "steps": n,
-                "tokens_per_s": round(T / (times[len(times) // 2] * 1e-3), 1),
-                "flush": "512 MiB read of a scratch buffer before each step"}
+            b.record(stream)
+        torch.cuda.synchronize()
+        times = sorted(a.elapsed_time(b) for a, b in evs)
+        return sum(times) / n, times[n // 2]
 
-    comparisons = {}
+    comparisons, comparisons_warm = {}, {}
+    half = [T - T // 2, T // 2]
+    baselines = (("sequential_unsplit_ms", B.make_plan(1, [T])),
+                 ("sequential_split2_ms", B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL)),
+                 ("overlapped_split2_two_streams_ms", B.make_plan(2, half, n_streams=2)))
     if args.plan.startswith("overlap2"):
         parts = args.plan.split(":")
         g, a = (int(parts[1]), int(parts[2])) if len(parts) == 3 else (0, 0)
-        plan = B.make_plan(2, [T - T // 2, T // 2], n_streams=2, gemm_cus_per_xcd=g, attn_cus_per_xcd=a)
+        plan = B.make_plan(2, half, n_streams=2, gemm_cus_per_xcd=g, attn_cus_per_xcd=a)
         layer.set_plan(plan)
     elif args.plan == "k1" or wl.plan_sizes == (T,):
         plan = B.make_plan(1, [T])
@@ -198,15 +199,15 @@ def main():
         log(f"searched plan {B.plan_dict(plan)} ({best_ms:.3f} ms, {int(n_cands)} candidates)")
         # the baselines the searched plan is compared with: the unsplit step,
         # two nano-batches one after the other on one stream, and the same two
-        # nano-batches overlapped on two streams without CU masks
-        half = [T - T // 2, T // 2]
-        for key, p in (("sequential_unsplit_ms", B.make_plan(1, [T])),
-                       ("sequential_split2_ms", B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL)),
-                       ("overlapped_split2_two_streams_ms", B.make_plan(2, half, n_streams=2))):
+        # nano-batches overlapped on two streams without CU masks; cold
+        # caches as for the headline, warm as well
+        for key, p in baselines:
             layer.set_plan(p)
             for _ in range(3):
                 layer.step(pool, hb, sp)
-            comparisons[key] = time_steps(20)
+            comparisons[key] = time_cold(20)[0]
+            comparisons_warm[key] = time_steps(20)
+            log(f"  {key}: cold {comparisons[key] * 1e3:.1f} us, warm {comparisons_warm[key] * 1e3:.1f} us")
         layer.set_plan(plan)
     plan_sizes = list(plan.sizes)[:plan.count]
 
@@ -224,25 +225,32 @@ def main():
     dominant = max(prof, key=lambda k: prof[k][1])
     log("per-kernel (5 steps): " + ", ".join(f"{k} {v[1] / v[0] * 1e3:.1f}us x{v[0] // 5}" for k, v in prof.items()))
 
-    # timed region: events on the caller stream bracket K steps
-    log(f"timing {args.steps} steps")
-    ms = time_steps(args.steps)
-    log(f"{ms * 1e3:.1f} us per step on the GPU, {host_us[-1]:.1f} us per step to enqueue on the host")
-    # the same K steps again, with the dominant kernel's own start/end
+    # timed region: K steps with cold caches, each bracketed by events on
+    # the caller stream (the headline); then the same K steps warm, back to
+    # back
+    log(f"timing {args.steps} steps, cold caches")
+    ms, ms_median = time_cold(args.steps)
+    log(f"{ms * 1e3:.1f} us per step on the GPU (median {ms_median * 1e3:.1f})")
+    ms_warm = time_steps(args.steps)
+    log(f"warm caches: {ms_warm * 1e3:.1f} us per step, {host_us[-1]:.1f} us per step to enqueue on the host")
+    # the same K cold steps again, with the dominant kernel's own start/end
     # timestamps recorded into HIP events on the stream it runs on (kept out
     # of the throughput pass: the event packets add a few microseconds of
     # queue time around that kernel in every step)
     layer.profile_enable(True, dominant)
-    ms_events = time_steps(args.steps)
+    ms_events = time_cold(args.steps)[0]
     dprof = layer.profile_read()
     layer.profile_enable(False)
     launches, dom_ms = dprof[dominant]
     dom_avg_ms = dom_ms / launches
     value = T / (ms * 1e-3)
-    cold = time_cold(min(args.steps, 20))
-    log(f"cold caches: {cold['ms_per_step'] * 1e3:.1f} us per step (median of {cold['steps']})")
+    cold = {"ms_per_step": round(ms, 5), "median_ms_per_step": round(ms_median, 5), "steps": args.steps,
+            "flush": "512 MiB read of a scratch buffer before each step, outside the step's events"}
+    warm = {"ms_per_step": round(ms_warm, 5), "steps": args.steps, "tokens_per_s": round(T / (ms_warm * 1e-3), 1),
+            "timing": "events around K back-to-back steps"}
     if comparisons:
         comparisons["searched_plan_ms"] = ms
+        comparisons_warm["searched_plan_ms"] = ms_warm
 
     # roofline of the dominant kernel
     logits = acts["router_logits"].float().cpu().numpy() if "router_logits" in acts else None
@@ -284,13 +292,13 @@ def main():
         host_idle.append((time.perf_counter() - h0) * 1e6)
     torch.cuda.synchronize()
     host = {"step_enqueue_us": round(sorted(host_idle)[5], 1),
-            "step_enqueue_frac_of_step": round(sorted(host_idle)[5] / (ms * 1e3), 4)}
+            "step_enqueue_frac_of_step": round(sorted(host_idle)[5] / (ms_warm * 1e3), 4)}
     log(f"host enqueue of one step with the device idle: {host['step_enqueue_us']} us "
         f"({100 * host['step_enqueue_frac_of_step']:.1f}% of the step)")
 
     offload = None
     if not args.no_offload:
-        offload = offload_measure(batch, layer, pool, k_pool, hb, sp, ms)
+        offload = offload_measure(batch, layer, pool, pool.k, hb, sp, ms_warm)
 
     stack = None
     if args.stack > 0:
@@ -299,7 +307,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, batch, weights, acts, k_pool, v_pool)
+        cpu = cpu_baseline(wl, batch, weights, acts, k_plain, v_plain)
 
     line = {
         "metric": "decoder-layer tokens/s on 1 MI355X + fraction of compute-bound optimal",
@@ -324,9 +332,12 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cold_cache": cold,
+        "warm_cache": warm,
     }
     if comparisons:
         line["comparisons"] = {k: round(v, 5) for k, v in comparisons.items()}
+        line["comparisons"]["caches"] = "cold"
+        line["comparisons_warm"] = {k: round(v, 5) for k, v in comparisons_warm.items()}
     line["host"] = host
     if offload is not None:
         line["kv_offload"] = offload
@@ -422,8 +433,10 @@ def stack_measure(n, wl, batch, layer0, pool0, acts, main_plan, sp, steps=10):
         k, v = W.make_pool(wl, batch.n_pages, "cuda", seed=seed)
         L = B.Layer(s, w, T, int(batch.pos.max()) + 1)
         layers.append(L)
-        pools.append(B.KVPool(L, batch.n_pages, s.page_size, k, v))
-        keep.append((w, k, v))
+        pools.append(B.KVPool.from_plain(L, k, v, sp))
+        torch.cuda.synchronize()
+        del k, v
+        keep.append(w)
     out = torch.empty_like(acts["x"])
     hb = B.HostBatch(batch, acts["x"].data_ptr(), out.data_ptr(),
                      acts["router_logits"].data_ptr() if "router_logits" in acts else None)
@@ -528,7 +541,8 @@ def copy_calibration(mib):
 
 def cpu_baseline(wl, batch, weights, acts, k_pool, v_pool, budget_s=20.0):
     """The CPU oracle, as it stands, on a bounded sample of this workload's
-    requests (rows are independent, so a subset is a fair per-token rate)."""
+    requests (rows are independent, so a subset is a fair per-token rate).
+    k_pool / v_pool: the generator's plain paged caches [P][nkv][16][d]."""
     import torch
     import oracle
     from intra_operation_overlap_amd import workload as W

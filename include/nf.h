@@ -162,7 +162,12 @@ typedef struct nf_kv_pool nf_kv_pool;
 typedef struct nf_graph nf_graph;
 
 /* ---- layer ---------------------------------------------------------------
- * nf_layer_create: validates the shape, binds the caller's weights (pointers
+ * nf_layer_create: one decoder layer of the Llama / Mixtral families the
+ * ossradar Nanoflow README lists ("News"; Mixtral 8x7B also in the abstract
+ * on the codewithpapers page), whose operations the device-level pipeline
+ * runs ("How it works" on the bytedragons Nanoflow page: the GEMMs
+ * compute-bound, attention and the KV cache memory-bound).  It validates the
+ * shape, binds the caller's weights (pointers
  * kept), allocates the workspace on the current HIP device and builds the
  * fp32 cos/sin table (angles in fp64).  For bf16 mixture-of-experts layers
  * it also copies the expert weights once into the MFMA operand order of the
@@ -202,6 +207,28 @@ nf_status nf_kv_pool_create(const nf_layer* layer, int32_t n_pages, int32_t page
  * there is any); may run before or after nf_layer_destroy of its layer. */
 void nf_kv_pool_destroy(nf_kv_pool* pool);
 
+/* Conversion between the pool's layout and the plain paged-cache layout
+ * [n][n_kv_heads][page_size][head_dim] (page, KV head, key slot, dimension;
+ * row-major, the layer dtype), so a caller holding a conventional PagedAttention
+ * block pool ("How it differs from vLLM and TensorRT-LLM" on the hysenlabs
+ * Nanoflow page) can hand its cache to the step and read it back.
+ * nf_kv_pool_import writes, for i < n, the K and V blocks of pool page
+ * pages[i] from entry i of k_src / v_src; nf_kv_pool_export reads them into
+ * k_dst / v_dst.  pages: host int32 [n], pool pages in range (a page listed
+ * twice on import: the later entry wins); NULL means pages 0..n-1 (n <=
+ * n_pages).  k_src / v_src / k_dst / v_dst: caller-owned device buffers of
+ * n * n_kv_heads * page_size * head_dim elements, not overlapping the pool.
+ * Enqueued on `stream` (NULL: the null stream); the page list may be reused on
+ * return.  Calls on one pool must not overlap each other, nor a step or an
+ * offload that touches the same pages.  Moves bits only (no rounding).
+ * Errors, before anything is launched: NF_ERR_INVALID_ARG (null pool,
+ * negative n, null buffers with n > 0), NF_ERR_OUT_OF_RANGE (a page outside
+ * the pool, n beyond the pool without a list); NF_ERR_HIP. */
+nf_status nf_kv_pool_import(nf_kv_pool* pool, const int32_t* pages, int32_t n, const void* k_src,
+                            const void* v_src, void* stream);
+nf_status nf_kv_pool_export(nf_kv_pool* pool, const int32_t* pages, int32_t n, void* k_dst, void* v_dst,
+                            void* stream);
+
 /* Offloads whole pool pages to host memory, the KV offload of retired
  * requests that the hysenlabs Nanoflow page (section "KV-cache offload to
  * SSD, and the bandwidth arithmetic behind it") and the ossradar page
@@ -224,9 +251,14 @@ nf_status nf_kv_offload(nf_kv_pool* pool, const int32_t* pages, int32_t n, void*
                         void* stream);
 
 /* ---- plan -----------------------------------------------------------------
- * nf_plan_set validates count, order, streams and CU split against the device
- * (sizes are checked against each batch at step time) and (re)creates the
- * CU-masked streams.  Errors: NF_ERR_INVALID_ARG, NF_ERR_OUT_OF_RANGE,
+ * nf_plan_set fixes the four choices the abstract on the codewithpapers
+ * NanoFlow page has the system make per batch -- number, size and ordering of
+ * the nano-batches and their share of the GPU's resources -- here the
+ * partition of every XCD's compute units between the GEMM and attention
+ * streams (partitioning a device's functional units: "How it works" on the
+ * bytedragons Nanoflow page).  It validates count, order, streams and CU
+ * split against the device (sizes are checked against each batch at step
+ * time) and (re)creates the CU-masked streams.  Errors: NF_ERR_INVALID_ARG, NF_ERR_OUT_OF_RANGE,
  * NF_ERR_HIP. */
 nf_status nf_plan_set(nf_layer* layer, const nf_plan* plan);
 nf_status nf_plan_get(const nf_layer* layer, nf_plan* plan);
@@ -238,7 +270,13 @@ nf_status nf_batch_validate(const nf_shape* shape, int32_t n_pages, int32_t page
                             const nf_batch* batch, const nf_plan* plan);
 
 /* ---- step -----------------------------------------------------------------
- * Enqueue one layer step after prior work on `stream`; `stream` is ordered
+ * One iteration of the layer over a batch the host formed (decode tokens and
+ * a prefill chunk together), run as the plan's nano-batches: every operation
+ * is duplicated per nano-batch so the compute-, memory-bound operations of
+ * different nano-batches overlap (abstract on the codewithpapers NanoFlow
+ * page; "Nano-batching and the device-level pipeline" on the hysenlabs
+ * Nanoflow page); the result equals the unsplit layer's up to rounding.
+ * Enqueue the step after prior work on `stream`; `stream` is ordered
  * after the step completes.  Asynchronous to the host; host arrays of the
  * batch may be reused once the call returns.  Writes batch->out, the pool
  * slots of the batch's new positions and the layer's workspace.  Calls on
@@ -306,9 +344,11 @@ void nf_graph_destroy(nf_graph* graph);
  * plan, every candidate is timed on this batch for two steps; the `top_k`
  * fastest, and the unsplit plan, are timed again with `warmup` + `reps` steps
  * and the fastest of those is kept.  Runs steps on this batch (so it writes
- * batch->out and the batch's pool slots with the values a step writes),
- * synchronises `stream`, sets the chosen plan on the layer and returns it in
- * *out.  `times_ms`, if not NULL, receives {measured ms per step of the
+ * batch->out); the pool pages holding the batch's new positions are copied
+ * aside before the first step and copied back before returning, so the pool
+ * ends bit-identical to how it was (it is not read-only while the search
+ * runs: nothing else may use it meanwhile).  Synchronises `stream`, sets the
+ * chosen plan on the layer and returns it in *out.  `times_ms`, if not NULL, receives {measured ms per step of the
  * chosen plan, number of candidates}.  An empty batch returns the unsplit
  * plan without running anything.  Errors: NF_ERR_INVALID_ARG for a null
  * argument, any error of nf_layer_step. */

@@ -72,6 +72,8 @@ _SIGS = {
                                     ctypes.POINTER(vp)]),
     "nf_graph_launch": (i32, [vp, vp]),
     "nf_kv_offload": (i32, [vp, P_i32, i32, vp, vp, vp]),
+    "nf_kv_pool_import": (i32, [vp, P_i32, i32, vp, vp, vp]),
+    "nf_kv_pool_export": (i32, [vp, P_i32, i32, vp, vp, vp]),
     "nf_graph_destroy": (None, [vp]),
     "nf_plan_search": (i32, [vp, vp, ctypes.POINTER(nf_batch), ctypes.POINTER(nf_search_opts),
                              ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double), vp]),
@@ -230,13 +232,40 @@ class Layer:
 
 
 class KVPool:
+    """nf_kv_pool over caller-owned K / V buffers in the pool's layout."""
+
     def __init__(self, layer: Layer, n_pages: int, page_size: int, k, v):
         self._keep = (k, v)
+        self.k, self.v = k, v
         h = vp()
         check(lib().nf_kv_pool_create(layer.h, n_pages, page_size, k.data_ptr(), v.data_ptr(), ctypes.byref(h)),
               "nf_kv_pool_create")
         self.h = h
         self.layer = layer
+
+    @classmethod
+    def from_plain(cls, layer: Layer, k_plain, v_plain, stream: int = 0) -> "KVPool":
+        """A pool holding the plain paged cache k_plain / v_plain
+        ([P][nkv][16][d] device tensors): buffers of the pool's size are
+        allocated with torch and filled by nf_kv_pool_import."""
+        import torch
+        P, nkv, S, d = (int(x) for x in k_plain.shape)
+        kb, _ = kv_pool_bytes(layer.shape, P, S)
+        k = torch.empty(kb // k_plain.element_size(), dtype=k_plain.dtype, device=k_plain.device).view(P, nkv, S * d)
+        v = torch.empty_like(k)
+        pool = cls(layer, P, S, k, v)
+        kv_pool_import(pool, k_plain, v_plain, None, stream)
+        return pool
+
+    def to_plain(self, stream: int = 0):
+        """(K, V) of every page as plain [P][nkv][16][d] tensors (nf_kv_pool_export)."""
+        import torch
+        P, nkv, Sd = (int(x) for x in self.k.shape)
+        d = int(self.layer.shape.head_dim)
+        k = torch.empty(P, nkv, Sd // d, d, dtype=self.k.dtype, device=self.k.device)
+        v = torch.empty_like(k)
+        kv_pool_export(self, k, v, None, stream)
+        return k, v
 
     def close(self):
         if self.h:
@@ -290,6 +319,23 @@ def kv_offload(pool: KVPool, pages, host_k, host_v, stream: int = 0) -> None:
     a = np.ascontiguousarray(np.asarray(pages, np.int32))
     check(lib().nf_kv_offload(pool.h, _i32p(a), len(a), host_k.data_ptr(), host_v.data_ptr(), stream),
           "nf_kv_offload")
+
+
+def kv_pool_import(pool: KVPool, k_src, v_src, pages=None, stream: int = 0) -> None:
+    """nf_kv_pool_import: plain [n][nkv][16][d] device tensors into the pool
+    (pages None: pool pages 0..n-1)."""
+    n = int(k_src.shape[0])
+    a = None if pages is None else np.ascontiguousarray(np.asarray(pages, np.int32))
+    check(lib().nf_kv_pool_import(pool.h, _i32p(a) if a is not None else None, n, k_src.data_ptr(),
+                                  v_src.data_ptr(), stream), "nf_kv_pool_import")
+
+
+def kv_pool_export(pool: KVPool, k_dst, v_dst, pages=None, stream: int = 0) -> None:
+    """nf_kv_pool_export: pool pages into plain [n][nkv][16][d] device tensors."""
+    n = int(k_dst.shape[0])
+    a = None if pages is None else np.ascontiguousarray(np.asarray(pages, np.int32))
+    check(lib().nf_kv_pool_export(pool.h, _i32p(a) if a is not None else None, n, k_dst.data_ptr(),
+                                  v_dst.data_ptr(), stream), "nf_kv_pool_export")
 
 
 def kv_pool_bytes(shape: nf_shape, n_pages: int, page_size: int):

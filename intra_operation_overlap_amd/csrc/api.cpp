@@ -137,6 +137,7 @@ struct nf_kv_pool {
   void* k = nullptr;
   void* v = nullptr;
   DevBuf offload;      // page list and gathered K / V blocks of nf_kv_offload
+  DevBuf xfer;         // page list of nf_kv_pool_import / nf_kv_pool_export
 };
 
 namespace {
@@ -1039,12 +1040,60 @@ nf_status nf_kv_pool_create(const nf_layer* L, int32_t n_pages, int32_t page_siz
 
 void nf_kv_pool_destroy(nf_kv_pool* p) {
   if (!p) return;
-  if (p->offload.p || !p->offload.old.empty()) {   // the layer may be gone already
+  if (p->offload.p || !p->offload.old.empty() || p->xfer.p || !p->xfer.old.empty()) {   // the layer may be gone
     (void)hipSetDevice(p->device);
     (void)hipDeviceSynchronize();
     release(p->offload);
+    release(p->xfer);
   }
   delete p;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared part of nf_kv_pool_import / nf_kv_pool_export: checks, the page list
+// on the device, the conversion kernel.
+nf_status kv_transfer(nf_kv_pool* P, const int32_t* pages, int32_t n, void* k_rm, void* v_rm, bool to_pool,
+                      void* stream, const char* who) {
+  if (!P || n < 0 || (n > 0 && (!k_rm || !v_rm)))
+    return set_err(NF_ERR_INVALID_ARG, "%s: null argument or negative count", who);
+  if (!pages && n > P->n_pages)
+    return set_err(NF_ERR_OUT_OF_RANGE, "%s: %d pages requested from a pool of %d", who, n, P->n_pages);
+  if (pages)
+    for (int i = 0; i < n; ++i)
+      if (pages[i] < 0 || pages[i] >= P->n_pages)
+        return set_err(NF_ERR_OUT_OF_RANGE, "%s: page %d at %d is outside the pool's %d pages", who, pages[i], i,
+                       P->n_pages);
+  const nf_shape& sh = P->layer->s;
+  if ((int64_t)n * sh.n_kv_heads * 2 >= (int64_t(1) << 31))
+    return set_err(NF_ERR_OUT_OF_RANGE, "%s: %d pages exceed one launch", who, n);
+  if (n == 0) return NF_OK;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(P->device));
+  const int32_t* d_pages = nullptr;
+  if (pages) {
+    HIP_TRY(ensure(P->xfer, (size_t)n * 4));
+    HIP_TRY(hipMemcpyAsync(P->xfer.p, pages, (size_t)n * 4, hipMemcpyHostToDevice, st));
+    d_pages = (const int32_t*)P->xfer.p;
+  }
+  HIP_TRY(kv_convert(sh.dtype, P->k, P->v, d_pages, n, sh.n_kv_heads, sh.head_dim, k_rm, v_rm, to_pool, st));
+  return NF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nf_status nf_kv_pool_import(nf_kv_pool* P, const int32_t* pages, int32_t n, const void* k_src, const void* v_src,
+                            void* stream) {
+  return kv_transfer(P, pages, n, const_cast<void*>(k_src), const_cast<void*>(v_src), true, stream,
+                     "nf_kv_pool_import");
+}
+
+nf_status nf_kv_pool_export(nf_kv_pool* P, const int32_t* pages, int32_t n, void* k_dst, void* v_dst, void* stream) {
+  return kv_transfer(P, pages, n, k_dst, v_dst, false, stream, "nf_kv_pool_export");
 }
 
 nf_status nf_kv_offload(nf_kv_pool* P, const int32_t* pages, int32_t n, void* host_k, void* host_v,
@@ -1430,6 +1479,44 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
     }
   }
 
+  // The candidates are timed on this batch, whose steps write K/V into the
+  // pool pages holding its new positions.  Those pages are saved first and
+  // put back before returning, so the caller's pool ends bit-identical.
+  std::string err;
+  nf_status st0 = check_batch(L->s, P->n_pages, P->page_size, *b, err);
+  if (st0 != NF_OK) return set_err(st0, "%s", err.c_str());
+  std::vector<int32_t> saved;
+  {
+    std::vector<char> mark(P->n_pages, 0);
+    for (int r = 0; r < b->n_requests; ++r)
+      for (int i = 0; i < b->req_q_len[r]; ++i) {
+        const int32_t pg = b->page_indices[b->page_indptr[r] + (b->req_pos0[r] + i) / P->page_size];
+        if (!mark[pg]) {
+          mark[pg] = 1;
+          saved.push_back(pg);
+        }
+      }
+  }
+  const size_t list_bytes = ((saved.size() * 4) + 255) & ~(size_t)255;
+  struct Backup {
+    void* p = nullptr;
+    ~Backup() {
+      if (p) (void)hipFree(p);
+    }
+  } backup;
+  HIP_TRY(hipSetDevice(L->device));
+  HIP_TRY(hipMalloc(&backup.p, list_bytes + 2 * saved.size() * (size_t)P->block_bytes));
+  int32_t* d_saved = (int32_t*)backup.p;
+  char* bk = (char*)backup.p + list_bytes;
+  char* bv = bk + saved.size() * (size_t)P->block_bytes;
+  HIP_TRY(hipMemcpyAsync(d_saved, saved.data(), saved.size() * 4, hipMemcpyHostToDevice, s));
+  HIP_TRY(kv_gather(P->k, P->v, d_saved, (int)saved.size(), P->block_bytes, bk, bv, s));
+  auto restore = [&]() -> hipError_t {
+    hipError_t e = kv_scatter(P->k, P->v, d_saved, (int)saved.size(), P->block_bytes, bk, bv, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e;
+  };
+
   hipEvent_t e0, e1;
   HIP_TRY(hipEventCreate(&e0));
   HIP_TRY(hipEventCreate(&e1));
@@ -1483,6 +1570,15 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
+  {
+    const std::string step_err = g_err;
+    const hipError_t re = restore();
+    if (re != hipSuccess) {
+      (void)hipGetLastError();
+      return set_err(NF_ERR_HIP, "nf_plan_search: restoring the pool's pages failed: %s", hipGetErrorString(re));
+    }
+    g_err = step_err;
+  }
   if (st != NF_OK) return st;
   int best = 0;
   for (size_t i = 1; i < top.size(); ++i)

@@ -170,9 +170,16 @@ hipError_t moe_route(const RouteArgs& a, hipStream_t s);
 hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w,
                        const int32_t* inv, void* out, int T, int H, int k, hipStream_t s);
 
+// pool pages pages[0..n) (pages null: 0..n-1) <-> row-major [n][nkv][16][d]
+// buffers k_rm / v_rm (to_pool: row-major -> pool); dtype 1 bf16, 0 fp32
+hipError_t kv_convert(int dtype, void* k_pool, void* v_pool, const int32_t* pages, int n, int nkv, int d, void* k_rm,
+                      void* v_rm, bool to_pool, hipStream_t s);
 // copies pool pages pages[0..n) (K and V, block_bytes each) to dst_k / dst_v in list order
 hipError_t kv_gather(const void* k_pool, const void* v_pool, const int32_t* pages, int n, int64_t block_bytes,
                      void* dst_k, void* dst_v, hipStream_t s);
+// the inverse: block i of src_k / src_v to pool page pages[i] (pages distinct)
+hipError_t kv_scatter(void* k_pool, void* v_pool, const int32_t* pages, int n, int64_t block_bytes, const void* src_k,
+                      const void* src_v, hipStream_t s);
 
 // ---------------------------------------------------------------- probes
 // shape 0: v_mfma_f32_16x16x32_bf16 (8 chains), 1: v_mfma_f32_32x32x16_bf16 (4 chains)

@@ -290,7 +290,70 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(const u32x4* __restrict_
   for (int64_t i = threadIdx.x; i < blk16; i += 256) dst[i] = __builtin_nontemporal_load(src + i);
 }
 
+// Inverse of kv_gather_kernel: block i of src_k / src_v back to pool page
+// pages[i] (pages distinct).
+__global__ __launch_bounds__(256) void kv_scatter_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
+                                                         const int32_t* __restrict__ pages, int n, int64_t blk16,
+                                                         const u32x4* __restrict__ src_k,
+                                                         const u32x4* __restrict__ src_v) {
+  const bool is_v = blockIdx.x >= (unsigned)n;
+  const int b = is_v ? blockIdx.x - n : blockIdx.x;
+  u32x4* dst = (is_v ? v_pool : k_pool) + (int64_t)pages[b] * blk16;
+  const u32x4* src = (is_v ? src_v : src_k) + (int64_t)b * blk16;
+  for (int64_t i = threadIdx.x; i < blk16; i += 256) dst[i] = src[i];
+}
+
+// Pool pages <-> the plain paged layout [n][nkv][16][d] (element type E: the
+// storage bits of one element).  Block b < n * nkv is K, the rest V; list
+// entry i = (b % (n * nkv)) / nkv names pool page pages[i] (or i when pages
+// is null).  Each thread moves single elements; this runs once per import or
+// export, not per step.
+template <typename E>
+__global__ __launch_bounds__(256) void kv_convert_kernel(E* __restrict__ k_pool, E* __restrict__ v_pool,
+                                                         const int32_t* __restrict__ pages, int n, int nkv, int d,
+                                                         E* __restrict__ k_rm, E* __restrict__ v_rm, int to_pool) {
+  const int64_t nb = (int64_t)n * nkv;
+  const bool is_v = blockIdx.x >= nb;
+  const int64_t b = is_v ? blockIdx.x - nb : blockIdx.x;
+  const int i = (int)(b / nkv), kh = (int)(b % nkv);
+  const int64_t page = pages ? pages[i] : i;
+  const int blk = 16 * d;
+  E* pool = (is_v ? v_pool : k_pool) + (page * nkv + kh) * blk;
+  E* rm = (is_v ? v_rm : k_rm) + b * blk;
+  for (int e = threadIdx.x; e < blk; e += 256) {
+    const int slot = e / d, dim = e % d;
+    const int off = is_v ? kv_v_off(slot, dim) : kv_k_off(slot, dim);
+    if (to_pool)
+      pool[off] = rm[e];
+    else
+      rm[e] = pool[off];
+  }
+}
+
 }  // namespace
+
+hipError_t kv_convert(int dtype, void* k_pool, void* v_pool, const int32_t* pages, int n, int nkv, int d, void* k_rm,
+                      void* v_rm, bool to_pool, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (d % 32 || nkv <= 0) return hipErrorInvalidValue;
+  const int64_t grid = 2 * (int64_t)n * nkv;
+  if (dtype == 1)
+    launch(kv_convert_kernel<uint16_t>, dim3((unsigned)grid), 256, 0, s, (uint16_t*)k_pool, (uint16_t*)v_pool, pages,
+           n, nkv, d, (uint16_t*)k_rm, (uint16_t*)v_rm, to_pool ? 1 : 0);
+  else
+    launch(kv_convert_kernel<uint32_t>, dim3((unsigned)grid), 256, 0, s, (uint32_t*)k_pool, (uint32_t*)v_pool, pages,
+           n, nkv, d, (uint32_t*)k_rm, (uint32_t*)v_rm, to_pool ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t kv_scatter(void* k_pool, void* v_pool, const int32_t* pages, int n, int64_t block_bytes, const void* src_k,
+                      const void* src_v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (block_bytes % 16) return hipErrorInvalidValue;
+  launch(kv_scatter_kernel, 2 * n, 256, 0, s, (u32x4*)k_pool, (u32x4*)v_pool, pages, n, block_bytes / 16,
+         (const u32x4*)src_k, (const u32x4*)src_v);
+  return hipGetLastError();
+}
 
 hipError_t kv_gather(const void* k_pool, const void* v_pool, const int32_t* pages, int n, int64_t block_bytes,
                      void* dst_k, void* dst_v, hipStream_t s) {

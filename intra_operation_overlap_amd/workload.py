@@ -243,14 +243,15 @@ def make_activations(wl: Workload, batch: Batch, device="cpu", seed: Optional[in
 
 
 def make_pool(wl: Workload, n_pages: int, device="cpu", seed: Optional[int] = None):
-    """K and V pools [P, nkv, page_size * d] (one block per page and KV head,
-    laid out as the boundary documents); every element N(0, 1), cached prefix
-    values and never-written slots alike."""
+    """The plain paged K and V caches [P, nkv, page_size, d] (page, KV head,
+    key slot, dimension); every element N(0, 1), cached prefix values and
+    never-written slots alike."""
     s = wl.shape
     seed = wl.seed if seed is None else seed
     dt = _torch_dtype(s)
-    k = _draw(seed, "k_pool", (n_pages, s.n_kv_heads, s.page_size * s.head_dim), ("normal", 1.0), dt, device)
-    v = _draw(seed, "v_pool", (n_pages, s.n_kv_heads, s.page_size * s.head_dim), ("normal", 1.0), dt, device)
+    dims = (n_pages, s.n_kv_heads, s.page_size, s.head_dim)
+    k = _draw(seed, "k_pool", dims, ("normal", 1.0), dt, device)
+    v = _draw(seed, "v_pool", dims, ("normal", 1.0), dt, device)
     return k, v
 
 

@@ -21,14 +21,15 @@ SwiGLU FFN (or a top-k mixture of SwiGLU experts) + residual.  The paged KV
 cache is the PagedAttention block-pool substrate the pages name (p1 "How it
 differs from vLLM and TensorRT-LLM"; p4 References).
 
-Layouts (identical to the boundary's, restated here independently):
-  w_qkv [(nq + 2 nkv) d, H]: output columns are Q heads, then K heads, then V
-  heads, each head's d columns contiguous; w_o [H, nq d]; w_gate, w_up
-  [E, F, H]; w_down [E, H, F].  K and V pools [P, nkv, 16 d]: one block of 16
-  key slots x d dims per (page, KV head), element (slot s, dim j) at
-  k_offset(s, j) / v_offset(s, j) below.  Request r's logical page i is pool
-  page page_indices[page_indptr[r] + i]; position p lives in logical page
-  p // 16 at slot p % 16.
+Layouts (the weights as the boundary documents them, restated here
+independently): w_qkv [(nq + 2 nkv) d, H]: output columns are Q heads, then
+K heads, then V heads, each head's d columns contiguous; w_o [H, nq d];
+w_gate, w_up [E, F, H]; w_down [E, H, F].  The K and V pools are the plain
+paged cache [P, nkv, 16, d]: pool page, KV head, key slot, dimension.
+Request r's logical page i is pool page page_indices[page_indptr[r] + i];
+position p lives in logical page p // 16 at slot p % 16.  How a device lays
+out a block inside its memory is not the oracle's concern: the tests convert
+a device pool to this layout before comparing.
 
 The one rounding the oracle applies is the write into the KV pool, which is a
 typed data structure (bf16 round-to-nearest-even or fp32); keys and values of
@@ -67,7 +68,11 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
 
 
 def round_to_f32(a: np.ndarray) -> np.ndarray:
-    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+    """Nearest fp32 value (ties to even; past the largest finite fp32 value
+    by half an ulp or more: infinity) of each fp64 element, as fp64, through
+    numpy's IEEE-754 conversion."""
+    with np.errstate(over="ignore"):
+        return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
 def store_round(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -125,21 +130,6 @@ def swiglu_ffn(h: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.n
 PAGE = 16
 
 
-def k_offset(s, j):
-    """Position of (key slot s, dim j) inside a K block: 32-dim chunks of 512
-    elements; within a chunk, slot s's 8-dim group g sits at 8 (16 g + s)."""
-    s, j = np.asarray(s), np.asarray(j)
-    return (j // 32) * 512 + (16 * ((j % 32) // 8) + s) * 8 + j % 8
-
-
-def v_offset(s, j):
-    """Position of (key slot s, dim j) inside a V block: 32-dim chunks of 512
-    elements; within a chunk, dims j and j + 16 of slot group s // 4 share an
-    8-element run at 8 (j % 16 + 16 (s // 4)), 4 slots each."""
-    s, j = np.asarray(s), np.asarray(j)
-    return (j // 32) * 512 + ((j % 16) + 16 * (s // 4)) * 8 + 4 * ((j // 16) % 2) + s % 4
-
-
 def page_slots(page_indptr, page_indices, r: int, n_keys: int, page_size: int):
     """(pool page, slot) of each of request r's first n_keys positions."""
     j = np.arange(n_keys)
@@ -150,16 +140,16 @@ def page_slots(page_indptr, page_indices, r: int, n_keys: int, page_size: int):
 def kv_append(k_pool, v_pool, k_new, v_new, tok_req, pos, page_indptr, page_indices,
               page_size: int, dtype: str) -> None:
     """Write each token's rotated key and its value into the pool slot of its
-    position, rounded to the pool's storage type.  k_new, v_new: [T, nkv, d]."""
+    position, rounded to the pool's storage type.  k_new, v_new: [T, nkv, d];
+    pools [P, nkv, page_size, d]."""
     assert page_size == PAGE
-    dims = np.arange(k_new.shape[-1])
     for t in range(k_new.shape[0]):
         r = tok_req[t]
         p = int(pos[t])
         page = page_indices[page_indptr[r] + p // page_size]
         slot = p % page_size
-        k_pool[page][:, k_offset(slot, dims)] = store_round(k_new[t], dtype)
-        v_pool[page][:, v_offset(slot, dims)] = store_round(v_new[t], dtype)
+        k_pool[page, :, slot, :] = store_round(k_new[t], dtype)
+        v_pool[page, :, slot, :] = store_round(v_new[t], dtype)
 
 
 def attention_weights(q: np.ndarray, keys: np.ndarray) -> np.ndarray:
@@ -175,11 +165,11 @@ def paged_attention(q_rot, k_pool, v_pool, req_q_start, req_q_len, pos,
     """Causal GQA attention read through the page tables.
 
     Query head h of a token at position p attends to keys 0..p of its own
-    request, held by KV head h // (nq / nkv).  Returns [T, nq, d]."""
+    request, held by KV head h // (nq / nkv).  Pools [P, nkv, page_size, d].
+    Returns [T, nq, d]."""
     T, nq, d = q_rot.shape
     G = nq // n_kv_heads
     assert page_size == PAGE
-    dims = np.arange(d)
     out = np.zeros_like(q_rot)
     for r in range(len(req_q_len)):
         t0, n = int(req_q_start[r]), int(req_q_len[r])
@@ -188,8 +178,8 @@ def paged_attention(q_rot, k_pool, v_pool, req_q_start, req_q_len, pos,
         last = int(pos[t0 + n - 1])
         pages, slots = page_slots(page_indptr, page_indices, r, last + 1, page_size)
         for kh in range(n_kv_heads):
-            K = k_pool[pages[:, None], kh, k_offset(slots[:, None], dims[None, :])]   # [L, d]
-            V = v_pool[pages[:, None], kh, v_offset(slots[:, None], dims[None, :])]   # [L, d]
+            K = k_pool[pages, kh, slots]      # [L, d]
+            V = v_pool[pages, kh, slots]      # [L, d]
             for t in range(t0, t0 + n):
                 p = int(pos[t])
                 w = attention_weights(q_rot[t, kh * G:(kh + 1) * G], K[:p + 1])

@@ -35,8 +35,8 @@ def problem():
     indptr = np.concatenate([[0], np.cumsum(n_pages)])
     indices = perm[:sum(n_pages)]
     P = len(perm)
-    kp = oracle.round_to_bf16(rng.standard_normal((P, nkv, S * d)))
-    vp = oracle.round_to_bf16(rng.standard_normal((P, nkv, S * d)))
+    kp = oracle.round_to_bf16(rng.standard_normal((P, nkv, S, d)))
+    vp = oracle.round_to_bf16(rng.standard_normal((P, nkv, S, d)))
     T = sum(qlen)
     batch = dict(x=oracle.round_to_bf16(rng.standard_normal((T, H))),
                  req_q_start=np.concatenate([[0], np.cumsum(qlen)[:-1]]), req_q_len=np.array(qlen),

@@ -198,3 +198,13 @@ def test_kv_offload_rejects_bad_arguments_before_launching():
     assert L.nf_kv_offload(ctypes.c_void_p(8), pages, -1, 1, 1, None) == B.NF_ERR_INVALID_ARG
     assert L.nf_kv_offload(ctypes.c_void_p(8), None, 2, 1, 1, None) == B.NF_ERR_INVALID_ARG
     assert L.nf_kv_offload(ctypes.c_void_p(8), pages, 2, None, 1, None) == B.NF_ERR_INVALID_ARG
+
+
+def test_kv_pool_import_export_reject_bad_arguments_before_launching():
+    L = B.lib()
+    pages = (ctypes.c_int32 * 2)(0, 1)
+    for fn in (L.nf_kv_pool_import, L.nf_kv_pool_export):
+        assert fn(None, pages, 2, 1, 1, None) == B.NF_ERR_INVALID_ARG
+        assert fn(ctypes.c_void_p(8), pages, -1, 1, 1, None) == B.NF_ERR_INVALID_ARG
+        assert fn(ctypes.c_void_p(8), pages, 2, None, 1, None) == B.NF_ERR_INVALID_ARG
+        assert fn(ctypes.c_void_p(8), None, 2, 1, None, None) == B.NF_ERR_INVALID_ARG

@@ -24,13 +24,14 @@ def small():
 
 
 def test_plan_search_returns_a_valid_plan_that_matches_the_oracle(small):
+    """The search times its candidates on scratch copies of the pages the
+    batch writes: the pool is left bit-identical."""
     T = small.batch.n_tokens
     k0, v0 = small.k.clone(), small.v.clone()
     plan, (ms, n_cands) = small.layer.search(small.pool, small.hb, max_count=3, warmup=1, reps=2, top_k=4,
                                               stream=GH.stream())
     torch.cuda.synchronize()
-    small.k.copy_(k0)
-    small.v.copy_(v0)
+    assert torch.equal(small.k, k0) and torch.equal(small.v, v0)
     GH.log(f"searched {B.plan_dict(plan)} {ms:.3f} ms over {int(n_cands)} candidates")
     assert 1 <= plan.count <= 3 and sum(list(plan.sizes)[:plan.count]) == T
     assert ms > 0 and n_cands >= 1

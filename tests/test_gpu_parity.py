@@ -13,7 +13,6 @@ import oracle
 from intra_operation_overlap_amd import binding as B
 from intra_operation_overlap_amd import workload as W
 from tests import gpu_harness as GH
-from tests import kv_layout as KV
 
 pytestmark = pytest.mark.gpu
 
@@ -30,26 +29,37 @@ def _plans_for(T):
         "k3_sequential_masked8": B.make_plan(3, [T // 3, T // 3, T - 2 * (T // 3)], order=B.NF_ORDER_SEQUENTIAL,
                                              n_streams=2, gemm_cus_per_xcd=8),
         "k4_masked24": B.make_plan(4, [T // 4] * 3 + [T - 3 * (T // 4)], n_streams=2, gemm_cus_per_xcd=24),
+        # persistent one-wave attention grids (split page ranges + merge)
+        "k1_attn_waves1": B.make_plan(1, [T], n_streams=2, attn_waves_per_cu=1),
+        "k2_attn_waves4": B.make_plan(2, [half, T - half], n_streams=2, attn_waves_per_cu=4),
+        "k2_attn_waves1_masked16": B.make_plan(2, [half, T - half], n_streams=2, gemm_cus_per_xcd=16,
+                                               attn_waves_per_cu=1),
     }
+
+
+def _check(S, where, requests=None, w_np=None):
+    """One step under the layer's plan, then every compared tensor against the
+    oracle on `requests` (all by default) and the pool sentinel; the pool's
+    own buffers are restored afterwards."""
+    k0, v0 = S.k.clone(), S.v.clone()
+    GH.run_step(S)
+    k_after, v_after = GH.pool_plain(S)
+    GH.check_sentinel(S, k_after, v_after)
+    reqs = list(range(S.batch.n_requests)) if requests is None else requests
+    GH.log(f"  oracle on {len(reqs)} requests")
+    res, rows, pages = GH.oracle_subset(S, reqs, w_np)
+    errs = GH.compare_rows(S, res, rows, pages, reqs, k_after, v_after)
+    GH.log(f"  errors {errs}")
+    GH.assert_errors(errs, GH.tolerance(S.wl), where)
+    S.k.copy_(k0)
+    S.v.copy_(v0)
+    return res, rows, errs
 
 
 def _full_check(S, plan_name, plan):
     GH.log(f"step {S.wl.name} plan={plan_name} T={S.batch.n_tokens}")
     S.layer.set_plan(plan)
-    k0, v0 = S.k.clone(), S.v.clone()
-    GH.run_step(S)
-    GH.check_sentinel(S, k0, v0)
-    reqs = list(range(S.batch.n_requests))
-    res, rows, pages = GH.oracle_subset(S, reqs, k0, v0)
-    errs = GH.compare_rows(S, res, rows, pages, reqs)
-    GH.log(f"  errors {errs}")
-    tol = GH.tolerance(S.wl)
-    for k, e in errs.items():
-        if not k.endswith("_raw"):           # raw branch deltas are diagnostics
-            assert e <= tol, (plan_name, k, e)
-    S.k.copy_(k0)
-    S.v.copy_(v0)
-    return errs
+    return _check(S, plan_name)[2]
 
 
 # ---------------------------------------------------------------- tiny fp32 layer
@@ -59,7 +69,7 @@ def c1():
     return GH.setup(W.WORKLOADS["c1"])
 
 
-@pytest.mark.parametrize("plan_name", list(_plans_for(16)))
+@pytest.mark.parametrize("plan_name", [p for p in _plans_for(16) if "attn_waves" not in p])
 def test_c1_fp32_full_parity(c1, plan_name):
     _full_check(c1, plan_name, _plans_for(c1.batch.n_tokens)[plan_name])
 
@@ -87,8 +97,11 @@ def test_small_bf16_prefill_from_zero_and_g8():
                                   rope_theta=1e4),
                     n_decode=9, ctx_range=(100, 200), prefill=(0, 70), seed=78)
     S = GH.setup(wl)
-    _full_check(S, "k1", B.make_plan(1, [S.batch.n_tokens]))
-    _full_check(S, "k2_split_prefill", B.make_plan(2, [40, S.batch.n_tokens - 40], n_streams=2, gemm_cus_per_xcd=16))
+    T = S.batch.n_tokens
+    _full_check(S, "k1", B.make_plan(1, [T]))
+    _full_check(S, "k2_split_prefill", B.make_plan(2, [40, T - 40], n_streams=2, gemm_cus_per_xcd=16))
+    _full_check(S, "k2_split_prefill_attn_waves4", B.make_plan(2, [40, T - 40], n_streams=2, attn_waves_per_cu=4))
+    _full_check(S, "k1_attn_waves1", B.make_plan(1, [T], n_streams=2, attn_waves_per_cu=1))
 
 
 # Seeded shape sweep: GQA groups 1, 2 and 8, hidden not a multiple of 64 (the
@@ -117,6 +130,10 @@ def test_shape_sweep_parity(case):
     T = S.batch.n_tokens
     _full_check(S, f"{case} k1", B.make_plan(1, [T]))
     _full_check(S, f"{case} k2", B.make_plan(2, [T // 2, T - T // 2], n_streams=2))
+    if S.wl.shape.dtype == "bf16":      # the one-wave kernel: bf16, head_dim 128
+        _full_check(S, f"{case} k2 attn_waves4", B.make_plan(2, [T // 2, T - T // 2], n_streams=2,
+                                                              attn_waves_per_cu=4))
+        _full_check(S, f"{case} k1 attn_waves1", B.make_plan(1, [T], n_streams=2, attn_waves_per_cu=1))
 
 
 def test_split_k_small_batch_parity():
@@ -186,7 +203,8 @@ def test_invalid_batch_launches_nothing(small):
 def test_one_hot_attention_selects_exact_key(wl_name):
     """Prior keys crafted so one chosen position's score beats every other by
     >= 100: attention must return that position's value bit-exactly, which
-    pins the page-table lookup and the slot arithmetic."""
+    pins the page-table lookup and the slot arithmetic.  The keys are written
+    into the plain paged cache and imported into the pool."""
     wl = W.WORKLOADS["c1"] if wl_name == "c1" else SMALL_BF16
     S = GH.setup(wl)
     b = S.batch
@@ -197,6 +215,7 @@ def test_one_hot_attention_selects_exact_key(wl_name):
     q = GH.intermediate(S, 0, b.n_tokens, s.n_q_heads * s.head_dim, dt).float().view(b.n_tokens, s.n_q_heads, s.head_dim)
     rng = np.random.Generator(np.random.PCG64(5))
     G = s.n_q_heads // s.n_kv_heads
+    kp = S.k_plain.clone()
     chosen = {}
     for r in range(b.n_requests):
         if b.req_q_len[r] != 1 or b.req_pos0[r] < 1:
@@ -204,48 +223,76 @@ def test_one_hot_attention_selects_exact_key(wl_name):
         t = b.req_q_start[r]
         p0 = int(b.req_pos0[r])
         j = int(rng.integers(0, p0))          # a cached position
-        pages = b.page_indices[b.page_indptr[r]:b.page_indptr[r + 1]]
-        kmap, vmap = KV.maps(s.head_dim)
+        pages = torch.as_tensor(b.page_indices[b.page_indptr[r]:b.page_indptr[r + 1]].astype(np.int64), device="cuda")
+        slots = torch.arange(p0, device="cuda")
         for kh in range(s.n_kv_heads):
             # zero every cached key of this request ...
-            for i in range(p0):
-                S.k[int(pages[i // 16]), kh, torch.as_tensor(kmap[i % 16], device="cuda")] = 0
+            kp[pages[slots // 16], kh, slots % 16] = 0
             # ... then point key j along the group's first query head: score 400
             qh = q[t, kh * G]
-            S.k[int(pages[j // 16]), kh, torch.as_tensor(kmap[j % 16], device="cuda")] = \
-                (qh * (400.0 * s.head_dim ** 0.5 / float(qh.norm()) ** 2)).to(dt)
+            kp[int(pages[j // 16]), kh, j % 16] = (qh * (400.0 * s.head_dim ** 0.5 / float(qh.norm()) ** 2)).to(dt)
         chosen[r] = j
+    B.kv_pool_import(S.pool, kp, S.v_plain, None, GH.stream())
     # only the group's first head is aligned with the key; the check uses it alone
     GH.run_step(S)
     attn = GH.intermediate(S, 1, b.n_tokens, s.n_q_heads * s.head_dim, dt).view(b.n_tokens, s.n_q_heads, s.head_dim)
     checked = 0
     for r, j in chosen.items():
         t = b.req_q_start[r]
-        pages = b.page_indices[b.page_indptr[r]:b.page_indptr[r + 1]]
-        kmap, vmap = KV.maps(s.head_dim)
+        page = int(b.page_indices[b.page_indptr[r] + j // 16])
         for kh in range(s.n_kv_heads):
-            v = S.v[int(pages[j // 16]), kh, torch.as_tensor(vmap[j % 16], device="cuda")]
-            assert torch.equal(attn[t, kh * G], v), (r, kh, j)
+            assert torch.equal(attn[t, kh * G], S.v_plain[page, kh, j % 16]), (r, kh, j)
             checked += 1
     assert checked > 0
+
+
+def test_pool_import_matches_documented_layout_and_round_trips():
+    """nf_kv_pool_import places plain [page][head][slot][dim] values where the
+    boundary's block layout says (an enumeration of the attention operand
+    loads, tests/kv_layout.py); export returns them bit for bit, also for a
+    page list; a step on the imported pool is checked by every parity test."""
+    from tests import kv_layout as KV
+    for wl in (SMALL_BF16, W.WORKLOADS["c1"]):
+        S = GH.setup(wl)
+        s = wl.shape
+        kmap, vmap = KV.maps(s.head_dim)
+        km = torch.as_tensor(kmap.reshape(-1), device="cuda")
+        vm = torch.as_tensor(vmap.reshape(-1), device="cuda")
+        P, nkv = S.batch.n_pages, s.n_kv_heads
+        want_k = torch.empty_like(S.k)
+        want_v = torch.empty_like(S.v)
+        want_k[:, :, km] = S.k_plain.reshape(P, nkv, -1)
+        want_v[:, :, vm] = S.v_plain.reshape(P, nkv, -1)
+        assert torch.equal(S.k, want_k) and torch.equal(S.v, want_v)
+        k_back, v_back = GH.pool_plain(S)
+        assert torch.equal(k_back, S.k_plain) and torch.equal(v_back, S.v_plain)
+        # a page list, with a repeated page, both ways
+        pages = np.array([3, 0, P - 1, 3, 7], np.int32)
+        ke = torch.empty(len(pages), nkv, 16, s.head_dim, dtype=S.k.dtype, device="cuda")
+        ve = torch.empty_like(ke)
+        B.kv_pool_export(S.pool, ke, ve, pages, GH.stream())
+        torch.cuda.synchronize()
+        idx = torch.as_tensor(pages.astype(np.int64), device="cuda")
+        assert torch.equal(ke, S.k_plain[idx]) and torch.equal(ve, S.v_plain[idx])
+        ki, vi = torch.randn_like(ke.float()).to(ke.dtype), torch.randn_like(ve.float()).to(ve.dtype)
+        B.kv_pool_import(S.pool, ki[:3], vi[:3], pages[:3], GH.stream())
+        k2, v2 = GH.pool_plain(S)
+        assert torch.equal(k2[idx[:3]], ki[:3]) and torch.equal(v2[idx[:3]], vi[:3])
+        rest = torch.ones(P, dtype=torch.bool, device="cuda")
+        rest[idx[:3]] = False
+        assert torch.equal(k2[rest], S.k_plain[rest]) and torch.equal(v2[rest], S.v_plain[rest])
+        with pytest.raises(B.NfError) as e:
+            B.kv_pool_export(S.pool, ke, ve, np.array([P], np.int32), GH.stream())
+        assert e.value.status == B.NF_ERR_OUT_OF_RANGE
+        S.pool.close()
+        S.layer.close()
 
 
 # ---------------------------------------------------------------- full-size workloads
 
 def _sampled_check(S, requests, w_np=None):
-    k0, v0 = S.k.clone(), S.v.clone()
     GH.log(f"step {S.wl.name} T={S.batch.n_tokens} plan={B.plan_dict(S.layer.get_plan())}")
-    GH.run_step(S)
-    GH.check_sentinel(S, k0, v0)
-    GH.log("oracle on sampled requests")
-    res, rows, pages = GH.oracle_subset(S, requests, k0, v0, w_np)
-    errs = GH.compare_rows(S, res, rows, pages, requests)
-    GH.log(f"  errors {errs}")
-    for k, e in errs.items():
-        if not k.endswith("_raw"):
-            assert e <= GH.tolerance(S.wl), (k, e)
-    S.k.copy_(k0)
-    S.v.copy_(v0)
+    res, rows, _ = _check(S, S.wl.name, requests, w_np)
     return res, rows
 
 
@@ -258,10 +305,10 @@ def _sample_requests(b, n, seed=3):
 
 
 @pytest.mark.slow
-def test_c2_full_size_sampled():
+def test_c2_full_size_every_request():
     S = GH.setup(W.WORKLOADS["c2"])
     S.layer.set_plan(B.make_plan(1, [S.batch.n_tokens]))
-    _sampled_check(S, _sample_requests(S.batch, 8))
+    _sampled_check(S, list(range(S.batch.n_requests)), GH.weights_np(S))
 
 
 @pytest.mark.slow
@@ -269,11 +316,13 @@ def test_c2_full_size_sampled():
 def test_mixed_full_size_sampled(wl_name):
     S = GH.setup(W.WORKLOADS[wl_name])
     T = S.batch.n_tokens
-    S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], n_streams=2, gemm_cus_per_xcd=16))
     w_np = GH.weights_np(S)
-    _sampled_check(S, _sample_requests(S.batch, 6), w_np)
+    S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], n_streams=2, gemm_cus_per_xcd=16))
+    _sampled_check(S, _sample_requests(S.batch, 16), w_np)
     S.layer.set_plan(B.make_plan(1, [T]))
-    _sampled_check(S, _sample_requests(S.batch, 4, seed=4), w_np)
+    _sampled_check(S, _sample_requests(S.batch, 16, seed=4), w_np)
+    S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], n_streams=2, attn_waves_per_cu=4))
+    _sampled_check(S, _sample_requests(S.batch, 8, seed=5), w_np)
 
 
 # ---------------------------------------------------------------- mixture of experts
@@ -350,7 +399,11 @@ def test_skewed_moe_routing_multi_pass_and_empty_expert():
 def test_c5_full_size_sampled():
     S = GH.setup(W.WORKLOADS["c5"])
     T = S.batch.n_tokens
+    w_np = GH.weights_np(S)
     S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], n_streams=2, gemm_cus_per_xcd=16))
-    _sampled_check(S, _sample_requests(S.batch, 6))
+    _sampled_check(S, _sample_requests(S.batch, 8), w_np)
     _route_check(S, 0, T // 2, 0)
     _route_check(S, T // 2, T, 1)
+    S.layer.set_plan(B.make_plan(1, [T]))
+    _sampled_check(S, _sample_requests(S.batch, 8, seed=4), w_np)
+    _route_check(S, 0, T, 0)

@@ -52,8 +52,9 @@ class Stack:
             seed = wl.seed + 1000 * l
             S = GH.setup(wl, batch=self.batch, weights=W.make_weights(wl, "cuda", seed=seed))
             k, v = W.make_pool(wl, self.batch.n_pages, "cuda", seed=seed)
-            S.k.copy_(k)
-            S.v.copy_(v)
+            B.kv_pool_import(S.pool, k, v, None, GH.stream())
+            torch.cuda.synchronize()
+            S.k_plain, S.v_plain = k, v
             self.S.append(S)
         s0 = self.S[0]
         self.x = s0.acts["x"]
@@ -92,25 +93,28 @@ def _plans(T):
     }
 
 
-def _oracle_chain(st, pools_before):
-    """The oracle layer by layer; returns the last output and each layer's
-    pools after its step (fp64)."""
+def _oracle_chain(st):
+    """The oracle layer by layer on the generator's caches (the pools before
+    the step); returns the last output and each layer's pools after its step
+    (fp64, plain layout)."""
     b = st.batch
     x = GH.f64(st.x)
     after = []
-    for S, (k0, v0) in zip(st.S, pools_before):
+    for S in st.S:
         bd = dict(x=x, req_q_start=b.req_q_start, req_q_len=b.req_q_len, req_pos0=b.req_pos0, pos=b.pos,
                   page_indptr=b.page_indptr, page_indices=np.asarray(b.page_indices, np.int64))
         if st.logits is not None:
             bd["router_logits"] = GH.f64(st.logits)
-        res = oracle.layer_step(st.wl.shape.as_dict(), GH.weights_np(S), bd, GH.f64(k0), GH.f64(v0))
+        res = oracle.layer_step(st.wl.shape.as_dict(), GH.weights_np(S), bd, GH.f64(S.k_plain),
+                                GH.f64(S.v_plain))
         after.append((res["k_pool"], res["v_pool"]))
         x = res["out"]
     return x, after
 
 
-def _written(st, k_before, k_after_ref, k_gpu):
-    """Normwise error over the pool elements the oracle step changed."""
+def _written(k_before, k_after_ref, k_gpu):
+    """Normwise error over the pool elements the oracle step changed (plain
+    layouts)."""
     ref = np.asarray(k_after_ref)
     before = GH.f64(k_before)
     changed = ref != before
@@ -124,13 +128,14 @@ def _parity(st, plan_name, plan):
     before = st.save_pools()
     B.stack_step(st.layers, st.pools, st.hb, GH.stream())
     torch.cuda.synchronize()
-    ref_out, ref_pools = _oracle_chain(st, before)
+    ref_out, ref_pools = _oracle_chain(st)
     tol = GH.tolerance(st.wl)
     e = GH.normwise(GH.f64(st.out), ref_out)
     GH.log(f"  out error {e:.3e}")
     assert e <= tol, (plan_name, e)
-    for l, (S, (kb, vb), (kr, vr)) in enumerate(zip(st.S, before, ref_pools)):
-        ek, ev = _written(st, kb, kr, S.k), _written(st, vb, vr, S.v)
+    for l, (S, (kr, vr)) in enumerate(zip(st.S, ref_pools)):
+        kg, vg = GH.pool_plain(S)
+        ek, ev = _written(S.k_plain, kr, kg), _written(S.v_plain, vr, vg)
         assert ek <= tol and ev <= tol, (plan_name, l, ek, ev)
     st.restore_pools(before)
 

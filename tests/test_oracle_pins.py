@@ -11,7 +11,6 @@ import torch
 
 import oracle
 from oracle import layer as L
-from tests import kv_layout as KV
 
 
 RNG = np.random.Generator(np.random.PCG64(7))
@@ -26,6 +25,31 @@ def test_bf16_rounding_closed_forms():
                      2.0 ** -133, 0.0, 2.0 ** -132])
     assert np.array_equal(L.round_to_bf16(vals), want)
     assert np.isinf(L.round_to_bf16(np.array([3.4e38]))).all()
+
+
+def test_f32_rounding_closed_forms():
+    """fp32 keeps 24 significant bits, normals from 2^-126, subnormals in
+    steps of 2^-149, largest finite (2 - 2^-23) 2^127."""
+    u = 2.0 ** -23                       # ulp of [1, 2)
+    big = (2 - u) * 2.0 ** 127
+    vals = np.array([1.0, 1 + u / 2, 1 + 3 * u / 2, 1 + u / 2 + 2.0 ** -40, -(1 + u / 2),
+                     2.0 ** -149, 2.0 ** -150, 3 * 2.0 ** -150, 2.0 ** -150 + 2.0 ** -170,
+                     2.0 ** -126 * (1 + u / 2), big, big + 2.0 ** 103 * 0.999, big + 2.0 ** 103, 0.0, -0.0])
+    want = np.array([1.0, 1.0, 1 + 2 * u, 1 + u, -1.0,
+                     2.0 ** -149, 0.0, 2.0 ** -148, 2.0 ** -149,
+                     2.0 ** -126, big, big, np.inf, 0.0, -0.0])
+    got = L.round_to_f32(vals)
+    assert np.array_equal(got, want)
+    assert np.signbit(got[-1]) and not np.signbit(got[-2])
+    # idempotent on fp32 values; monotone; result within half an ulp
+    a = RNG.standard_normal(5000) * np.exp(RNG.uniform(-80, 80, 5000))
+    r = L.round_to_f32(a)
+    assert np.array_equal(L.round_to_f32(r), r)
+    order = np.argsort(a)
+    assert np.all(np.diff(r[order]) >= 0)
+    m, e = np.frexp(a)
+    half_ulp = np.ldexp(1.0, np.maximum(e - 24, -149) - 1)
+    assert np.all(np.abs(r - a) <= half_ulp)
 
 
 def test_bf16_rounding_matches_torch_on_fp32_values():
@@ -134,22 +158,14 @@ def _contiguous_attention(q, K, V):
 
 
 def _fill_pool(P, nkv, S, d, rng):
-    return rng.standard_normal((P, nkv, S * d)), rng.standard_normal((P, nkv, S * d))
+    """Plain paged K and V pools [page][KV head][slot][dim]."""
+    return rng.standard_normal((P, nkv, S, d)), rng.standard_normal((P, nkv, S, d))
 
 
 def _kv(kp, vp, page, kh, slot, d):
-    """Key and value vectors of one pool slot, addressed through the layout
-    enumerated from the kernel's operand loads (tests/kv_layout.py)."""
-    kmap, vmap = KV.maps(d)
-    return kp[page, kh, kmap[slot]], vp[page, kh, vmap[slot]]
-
-
-def test_pool_layout_offsets_match_operand_enumeration():
-    for d in (32, 64, 128):
-        kmap, vmap = KV.maps(d)
-        s, j = np.meshgrid(np.arange(16), np.arange(d), indexing="ij")
-        assert np.array_equal(L.k_offset(s, j), kmap)
-        assert np.array_equal(L.v_offset(s, j), vmap)
+    """Key and value vectors of one pool slot, read element by element."""
+    return (np.array([kp[page, kh, slot, i] for i in range(d)]),
+            np.array([vp[page, kh, slot, i] for i in range(d)]))
 
 
 def test_paged_attention_equals_contiguous_brute_force():
@@ -230,12 +246,11 @@ def test_kv_append_rebuild_and_sentinel():
             assert np.array_equal(kg, oracle.round_to_bf16(kn[t, kh]))
             assert np.array_equal(vg, oracle.round_to_bf16(vn[t, kh]))
     # every slot no (page table, position) pair names is bit-identical
-    kmap, vmap = KV.maps(d)
     for pg in range(P):
         for sl in range(S):
             if not touched[pg, sl]:
-                assert np.array_equal(kp[pg][:, kmap[sl]], kp0[pg][:, kmap[sl]])
-                assert np.array_equal(vp[pg][:, vmap[sl]], vp0[pg][:, vmap[sl]])
+                assert np.array_equal(kp[pg, :, sl], kp0[pg, :, sl])
+                assert np.array_equal(vp[pg, :, sl], vp0[pg, :, sl])
 
 
 # ---------------------------------------------------------------- whole layer
@@ -298,10 +313,9 @@ def _brute_force_layer(shape, w, batch, kp, vp):
         for kh in range(nkv):
             kv = rot(col[(nq + kh) * d:(nq + kh + 1) * d], p)
             vv = col[(nq + nkv + kh) * d:(nq + nkv + kh + 1) * d]
-            kmap, vmap = KV.maps(d)
             for i in range(d):
-                kp[pg, kh, kmap[p % S, i]] = kv[i]
-                vp[pg, kh, vmap[p % S, i]] = vv[i]
+                kp[pg, kh, p % S, i] = kv[i]
+                vp[pg, kh, p % S, i] = vv[i]
     out = np.zeros((T, H))
     for t in range(T):
         r, p = req_of[t], int(batch["pos"][t])
