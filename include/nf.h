@@ -424,6 +424,33 @@ nf_status nf_gemm_bf16(int32_t M, int32_t N, int32_t K, int32_t mode, const void
                        int64_t ldc, int32_t tile_cfg, int32_t k_splits, int32_t cus, void* stream,
                        int32_t* out_cfg, int32_t* out_splits);
 
+/* Size of the device array that holds nf_gemm_bf16_noalloc's scratch memory. */
+#define NF_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* nf_gemm_bf16 for callers that cannot allocate device memory: code under HIP
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, arithmetic, tile choice and result bits as nf_gemm_bf16, with
+ * three differences:
+ *  - its only scratch memory, the fp32 split-K partial slices (M x N x
+ *    splits x 4 bytes, N doubled for mode 2), lives in a file-scope device
+ *    array of NF_NOALLOC_SCRATCH_BYTES that each GPU the library runs on
+ *    holds from its first call until the process ends; larger needs return
+ *    NF_ERR_OUT_OF_RANGE (choose fewer k_splits or split the problem);
+ *  - it calls no hipMalloc, hipFree or other allocating routine, and does
+ *    not synchronise: it returns once the GEMM is enqueued on `stream`;
+ *  - the weight-streaming configurations (tile_cfg >= 40, which read an
+ *    operand-order copy of B) are NF_ERR_UNSUPPORTED.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams or threads, not ordered by the caller) race on the
+ * partials and give wrong results.  The partial slices are written in full
+ * before they are read, so nothing needs clearing between calls.  The device
+ * address of the array is looked up once per device, on the first call made
+ * with that device current. */
+nf_status nf_gemm_bf16_noalloc(int32_t M, int32_t N, int32_t K, int32_t mode, const void* A, int64_t lda,
+                               const void* B, const void* B2, int64_t ldb, const void* R, int64_t ldr, void* C,
+                               int64_t ldc, int32_t tile_cfg, int32_t k_splits, int32_t cus, void* stream,
+                               int32_t* out_cfg, int32_t* out_splits);
+
 /* ---- errors ---------------------------------------------------------------- */
 const char* nf_last_error(void);
 const char* nf_status_string(nf_status s);

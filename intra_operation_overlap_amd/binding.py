@@ -88,6 +88,8 @@ _SIGS = {
                                     P_i32, P_i32]),
     "nf_gemm_bf16": (i32, [i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, vp,
                            P_i32, P_i32]),
+    "nf_gemm_bf16_noalloc": (i32, [i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, vp,
+                                   P_i32, P_i32]),
     "nf_last_error": (ctypes.c_char_p, []),
     "nf_status_string": (ctypes.c_char_p, [i32]),
 }
@@ -377,6 +379,15 @@ def gemm_bf16(M, N, K, mode, A, lda, B, B2, ldb, R, ldr, C, ldc, tile_cfg=-1, k_
     c, s = i32(), i32()
     check(lib().nf_gemm_bf16(M, N, K, mode, A, lda, B, B2, ldb, R, ldr, C, ldc, tile_cfg, k_splits, cus, stream,
                              ctypes.byref(c), ctypes.byref(s)), "nf_gemm_bf16")
+    return c.value, s.value
+
+
+def gemm_bf16_noalloc(M, N, K, mode, A, lda, B, B2, ldb, R, ldr, C, ldc, tile_cfg=-1, k_splits=0, cus=0,
+                      stream=None):
+    """nf_gemm_bf16_noalloc (enqueue only, no allocation); returns (cfg, splits)."""
+    c, s = i32(), i32()
+    check(lib().nf_gemm_bf16_noalloc(M, N, K, mode, A, lda, B, B2, ldb, R, ldr, C, ldc, tile_cfg, k_splits, cus,
+                                     stream, ctypes.byref(c), ctypes.byref(s)), "nf_gemm_bf16_noalloc")
     return c.value, s.value
 
 

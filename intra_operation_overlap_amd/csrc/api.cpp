@@ -47,6 +47,15 @@ nf_status set_err(nf_status st, const char* fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+nf_status nf::set_error(nf_status st, const char* msg) {
+  g_err = msg;
+  return st;
+}
+
+namespace {
+
 // On a HIP failure the runtime's last-error slot is cleared so that the
 // caller's next unrelated HIP call does not report it again.
 #define HIP_TRY(expr)                                                                     \
