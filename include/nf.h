@@ -122,7 +122,13 @@ typedef enum nf_order {
    * the O-proj/FFN of nano-batch j, so j's attention overlaps j+1's QKV */
   NF_ORDER_PIPELINED = 0,
   /* nano-batch j finishes every operation before j+1 starts */
-  NF_ORDER_SEQUENTIAL = 1
+  NF_ORDER_SEQUENTIAL = 1,
+  /* per GEMM stream, round t issues the front half of nano-batch t, the
+   * O-projection of t-1 and the FFN of t-2: attention(t) runs beside the
+   * O-projection of t-1 and the FFN of t-2, and a collective after an
+   * O-projection (nf_layer_set_allreduce_emulation) beside the next
+   * nano-batch's O-projection */
+  NF_ORDER_DEEP = 2
 } nf_order;
 
 /* Nano-batch plan: count, sizes, operation order and resource split. */
@@ -143,11 +149,15 @@ typedef struct nf_plan {
                                      streams then share those CUs (matrix
                                      cores vs memory pipes).                 */
   int32_t attn_waves_per_cu;      /* 0: one attention workgroup per work item;
-                                     1..16: a persistent attention grid of
-                                     that many single-wave workgroups per CU
-                                     of its budget, each looping over work
-                                     items, so attention leaves room on every
-                                     CU for the GEMM's workgroups            */
+                                     1..16: a persistent attention grid that
+                                     holds that many waves per CU of its
+                                     budget, each workgroup looping over work
+                                     items: four-wave workgroups (33 KB of LDS
+                                     each) for multiples of 4, single-wave
+                                     ones otherwise, so attention leaves
+                                     registers and LDS on every CU for the
+                                     GEMM's workgroups, which then use tiles
+                                     that fit beside it (128 x 128)          */
 } nf_plan;
 
 typedef struct nf_search_opts {
@@ -262,6 +272,26 @@ nf_status nf_kv_offload(nf_kv_pool* pool, const int32_t* pages, int32_t n, void*
  * NF_ERR_HIP. */
 nf_status nf_plan_set(nf_layer* layer, const nf_plan* plan);
 nf_status nf_plan_get(const nf_layer* layer, nf_plan* plan);
+
+/* Emulation of the network-bound operation of a tensor-parallel layer, the
+ * third resource nano-batching overlaps with compute- and memory-bound work
+ * (README "Introduction" on the ossradar Nanoflow page; "The problem
+ * Nanoflow attacks" on the hysenlabs page).  A layer that is one GPU's shard
+ * (row-parallel O and down projections) needs an all-reduce of each of those
+ * outputs across the GPUs; on one GPU it is the identity, and this switch
+ * stands in for it: after the O-projection and after the down projection of
+ * every nano-batch, its [T_j][H] rows make a send leg (to a staging buffer)
+ * and a receive leg (into the buffer the next operation reads) on a third
+ * stream, 2 * T_j * H elements moved per collective -- the per-GPU volume of
+ * a two-phase all-reduce, rounded up from 2 * (7/8) * T_j * H for 8 GPUs.
+ * mode 0: off; 1: both legs on the copy engines (DMA, no compute units); 2:
+ * both legs by a copy kernel of `copy_workgroups` workgroups (a collective
+ * library's CU channels).  The FFN half of a nano-batch waits for its
+ * O-projection's collective, and the step's stream for the last collective;
+ * results are bit-identical to mode 0.  Allocates three [max_tokens][H]
+ * buffers on first use.  Not for stack graphs.  Errors: NF_ERR_INVALID_ARG,
+ * NF_ERR_UNSUPPORTED (hidden not a whole number of 16-byte units), NF_ERR_HIP. */
+nf_status nf_layer_set_allreduce_emulation(nf_layer* layer, int32_t mode, int32_t copy_workgroups);
 
 /* nf_batch_validate: host-only check of a batch (and optionally a plan)
  * against a shape and a pool geometry; makes no HIP call.  It runs the same
@@ -382,10 +412,23 @@ nf_status nf_profile_read(nf_layer* layer, int32_t max_kinds, const char** names
 /* ---- device probes ----------------------------------------------------------
  * Measured peaks of the current device: dense bf16 MFMA TFLOP/s (register-only
  * MFMA chains on every CU) and HBM read GB/s (streaming `bytes` bytes, at
- * least 1 GiB recommended).  nf_probe_cu_map fills xcc[i] with the XCD that
- * CU-mask bit i dispatches to (n = CU count), or -1 for every bit when the
- * expected striping (bit i -> XCD i % 8) could not be confirmed.  A CU mask
- * must leave every XCD at least one CU; the plan's split does. */
+ * least 1 GiB recommended).
+ * nf_probe_cu_map measures which XCD and which CU every CU-mask bit selects
+ * (the partition of the device's units that the plan's CU split relies on,
+ * "How it works" on the bytedragons Nanoflow page): for each aligned group of
+ * 8 mask bits (one CU of every XCD under the runtime's bit i -> XCD i % 8
+ * rule; a mask must leave every XCD a CU) it runs single-wave workgroups on a
+ * stream masked to that group and reads their XCC_ID and the CU field of
+ * HW_ID (bits 15..8: shader engine, array, CU).  xcc[i] receives bit i's XCD
+ * and cu[i] (may be NULL) that CU field; both are -1 for every bit when a
+ * group did not show 8 distinct XCDs with one CU each or an XCD's groups did
+ * not select distinct CUs (the plans then fall back to the striping rule).
+ * Measured once per device and cached.  nf_probe_budget_cus runs the same
+ * probe on a stream masked the way a plan's budget is (CUs first ..
+ * first + count - 1 of every XCD, by the measured map) and returns the
+ * distinct (XCD << 16 | CU field) pairs its workgroups ran on, sorted, in
+ * xcc_cu[0 .. min(*n_out, max) - 1].  Errors: NF_ERR_INVALID_ARG,
+ * NF_ERR_OUT_OF_RANGE (a budget beyond the XCD's CUs), NF_ERR_HIP. */
 nf_status nf_probe_mfma_bf16_tflops(double* tflops);
 nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps);
 /* Average time (ms) of the layer's bf16 GEMM kernel on an M x N x K problem
@@ -401,7 +444,8 @@ nf_status nf_probe_hbm_read_gbps(size_t bytes, double* gbps);
 nf_status nf_probe_gemm_bf16_ms(int32_t M, int32_t N, int32_t K, int32_t mode, int32_t tile_cfg,
                                 int32_t k_splits, int32_t cus, int32_t reps, double* ms,
                                 int32_t* out_cfg, int32_t* out_splits);
-nf_status nf_probe_cu_map(int32_t* xcc, int32_t n);
+nf_status nf_probe_cu_map(int32_t* xcc, int32_t* cu, int32_t n);
+nf_status nf_probe_budget_cus(int32_t first, int32_t count, int32_t* xcc_cu, int32_t max, int32_t* n_out);
 
 /* ---- one GEMM ------------------------------------------------------------------
  * One bf16 GEMM exactly as the layer runs its projections, on caller device

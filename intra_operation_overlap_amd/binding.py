@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libnf.so")
 
 NF_OK, NF_ERR_INVALID_ARG, NF_ERR_OUT_OF_RANGE, NF_ERR_UNSUPPORTED, NF_ERR_NO_PLAN, NF_ERR_HIP = range(6)
 NF_F32, NF_BF16 = 0, 1
-NF_ORDER_PIPELINED, NF_ORDER_SEQUENTIAL = 0, 1
+NF_ORDER_PIPELINED, NF_ORDER_SEQUENTIAL, NF_ORDER_DEEP = 0, 1, 2
 NF_MAX_NANO = 4
 
 i32 = ctypes.c_int32
@@ -67,6 +67,7 @@ _SIGS = {
     "nf_batch_validate": (i32, [ctypes.POINTER(nf_shape), i32, i32, ctypes.POINTER(nf_batch),
                                 ctypes.POINTER(nf_plan)]),
     "nf_layer_step": (i32, [vp, vp, ctypes.POINTER(nf_batch), vp]),
+    "nf_layer_set_allreduce_emulation": (i32, [vp, i32, i32]),
     "nf_stack_step": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(nf_batch), vp]),
     "nf_stack_graph_create": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(nf_batch), vp,
                                     ctypes.POINTER(vp)]),
@@ -83,7 +84,8 @@ _SIGS = {
                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
     "nf_probe_mfma_bf16_tflops": (i32, [ctypes.POINTER(ctypes.c_double)]),
     "nf_probe_hbm_read_gbps": (i32, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_double)]),
-    "nf_probe_cu_map": (i32, [P_i32, i32]),
+    "nf_probe_cu_map": (i32, [P_i32, P_i32, i32]),
+    "nf_probe_budget_cus": (i32, [i32, i32, P_i32, i32, P_i32]),
     "nf_probe_gemm_bf16_ms": (i32, [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double),
                                     P_i32, P_i32]),
     "nf_gemm_bf16": (i32, [i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, vp,
@@ -201,6 +203,10 @@ class Layer:
         p = nf_plan()
         check(lib().nf_plan_get(self.h, ctypes.byref(p)), "nf_plan_get")
         return p
+
+    def set_allreduce_emulation(self, mode: int, copy_workgroups: int = 16) -> None:
+        check(lib().nf_layer_set_allreduce_emulation(self.h, mode, copy_workgroups),
+              "nf_layer_set_allreduce_emulation")
 
     def step(self, pool: "KVPool", hb: HostBatch, stream: int = 0) -> None:
         check(lib().nf_layer_step(self.h, pool.h, ctypes.byref(hb.c), stream), "nf_layer_step")
@@ -359,10 +365,21 @@ def probe_hbm_read_gbps(nbytes: int = 4 << 30) -> float:
     return v.value
 
 
-def probe_cu_map(n: int) -> List[int]:
+def probe_cu_map(n: int):
+    """(xcc, cu): per CU-mask bit, its XCD and its CU field of HW_ID (-1: unknown)."""
     a = np.zeros(n, np.int32)
-    check(lib().nf_probe_cu_map(_i32p(a), n), "nf_probe_cu_map")
-    return a.tolist()
+    c = np.zeros(n, np.int32)
+    check(lib().nf_probe_cu_map(_i32p(a), _i32p(c), n), "nf_probe_cu_map")
+    return a.tolist(), c.tolist()
+
+
+def probe_budget_cus(first: int, count: int, max_pairs: int = 1024) -> List[tuple]:
+    """Distinct (XCD, CU field) pairs a stream masked to CUs first..first+count-1
+    of every XCD ran on."""
+    a = np.zeros(max_pairs, np.int32)
+    n = i32()
+    check(lib().nf_probe_budget_cus(first, count, _i32p(a), max_pairs, ctypes.byref(n)), "nf_probe_budget_cus")
+    return [(int(v) >> 16, int(v) & 0xFFFF) for v in a[:min(n.value, max_pairs)]]
 
 
 def probe_gemm_bf16_ms(M, N, K, mode=0, tile_cfg=-1, k_splits=0, cus=256, reps=20):

@@ -109,11 +109,18 @@ struct nf_layer {
   nf_weights w{};
   int device = 0;
   int n_cus = 0, n_xcd = 8, cus_per_xcd = 32;
-  std::vector<int> xcc_of_bit;                  // CU-mask bit -> XCD (measured)
+  std::vector<int> xcc_of_bit;                  // CU-mask bit -> XCD (measured; -1 unknown)
   nf_plan plan{};
   std::map<std::pair<int, int>, StreamPair> pairs;   // by (GEMM CUs, attention CUs) per XCD
   hipEvent_t ev_app[NF_MAX_NANO] = {}, ev_att[NF_MAX_NANO] = {};
   hipEvent_t ev_start = nullptr, ev_g = nullptr, ev_a = nullptr;
+  // emulated tensor-parallel all-reduce of the O and down projections
+  // (nf_layer_set_allreduce_emulation): mode 0 off, 1 copy engines, 2 a copy
+  // kernel of ar_wgs workgroups; on stream sc, with these events
+  int ar_mode = 0, ar_wgs = 16;
+  hipStream_t sc = nullptr;
+  hipEvent_t ev_o[NF_MAX_NANO] = {}, ev_co[NF_MAX_NANO] = {}, ev_d[NF_MAX_NANO] = {}, ev_cd[NF_MAX_NANO] = {};
+  DevBuf x1r, ypre, ar_stage;   // the all-reduced x1, the down output before its all-reduce, the send leg
   DevBuf h, qkv, q_rot, attn, x1, h2, act, y;
   DevBuf r_idx, r_w, r_perm, r_inv, r_off;
   DevBuf splitk, part_o, part_ml, meta, cos_sin;
@@ -178,51 +185,95 @@ void release(DevBuf& b) {
 }
 
 // --------------------------------------------------------------- CU masks
+struct CuMap {
+  std::vector<int> xcc;   // CU-mask bit -> XCD, -1 unknown
+  std::vector<int> cu;    // CU-mask bit -> hardware CU inside its XCD: HW_ID bits 15..8 (SE, SH, CU), -1 unknown
+};
 std::mutex g_map_mu;
-std::map<int, std::vector<int>> g_xcc_maps;     // device -> bit -> XCD
+std::map<int, CuMap> g_cu_maps;     // by device
 
-// Which XCD each CU-mask bit lands on.  The driver stripes mask bits over
-// the XCDs (bit i -> XCD i % n_xcd, CU i / n_xcd within it), and a mask must
-// leave every XCD at least one CU (workgroups are dealt to XCDs round-robin
-// whatever the mask).  The striping is checked with a stream masked to bits
-// 0 .. n_xcd-1 -- one CU per XCD if striped -- running many single-wave
-// workgroups that report their XCC_ID: every XCD must show up.  If it does
-// not, the bits stay -1 (unknown) and splits still use the striped guess.
-nf_status measure_cu_map(int device, int n_cus, int n_xcd, std::vector<int>& out) {
-  std::lock_guard<std::mutex> lk(g_map_mu);
-  auto it = g_xcc_maps.find(device);
-  if (it != g_xcc_maps.end()) {
-    out = it->second;
-    return NF_OK;
-  }
-  constexpr int kBlocks = 256;
-  std::vector<int> map(n_cus, -1);
-  const int words = (n_cus + 31) / 32;
-  std::vector<uint32_t> mask(words, 0u);
-  for (int bit = 0; bit < n_xcd && bit < n_cus; ++bit) mask[bit / 32] |= 1u << (bit % 32);
+// Runs the identity probe on a stream masked to `mask`; returns the distinct
+// (XCC_ID, HW_ID CU field) pairs its workgroups reported.
+nf_status probe_mask(const std::vector<uint32_t>& mask, std::vector<std::pair<int, int>>& seen) {
+  constexpr int kBlocks = 512;
+  seen.clear();
   uint32_t* d_id = nullptr;
   HIP_TRY(hipMalloc(&d_id, 2 * kBlocks * sizeof(uint32_t)));
   hipStream_t st = nullptr;
-  hipError_t e = hipExtStreamCreateWithCUMask(&st, words, mask.data());
   std::vector<uint32_t> h_id(2 * kBlocks, 0xFFFFFFFFu);
+  hipError_t e = hipExtStreamCreateWithCUMask(&st, (uint32_t)mask.size(), mask.data());
   if (e == hipSuccess) {
     e = probe_hwid(d_id, kBlocks, st);
     if (e == hipSuccess) e = hipMemcpyAsync(h_id.data(), d_id, h_id.size() * 4, hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     (void)hipStreamDestroy(st);
   }
-  (void)hipGetLastError();
   (void)hipFree(d_id);
-  if (e == hipSuccess) {
-    std::vector<int> seen(16, 0);
-    for (int b = 0; b < kBlocks; ++b) seen[h_id[2 * b + 1] & 0xF] = 1;
-    int n_seen = 0;
-    for (int x = 0; x < 16; ++x) n_seen += seen[x];
-    if (n_seen == n_xcd)
-      for (int bit = 0; bit < n_cus; ++bit) map[bit] = bit % n_xcd;
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(NF_ERR_HIP, "CU-mask probe failed: %s", hipGetErrorString(e));
   }
-  g_xcc_maps[device] = map;
-  out = map;
+  for (int b = 0; b < kBlocks; ++b) {
+    const std::pair<int, int> id((int)(h_id[2 * b + 1] & 0xF), (int)((h_id[2 * b] >> 8) & 0xFF));
+    if (std::find(seen.begin(), seen.end(), id) == seen.end()) seen.push_back(id);
+  }
+  std::sort(seen.begin(), seen.end());
+  return NF_OK;
+}
+
+// Which XCD and which CU each CU-mask bit selects, measured.  The runtime
+// deals mask bits to the XCDs in turn (bit i to XCD i % n_xcd), and every XCD
+// must keep at least one CU of a mask, since workgroups are dealt to the XCDs
+// round-robin whatever the mask.  So the probe masks are the aligned groups
+// of n_xcd bits {n_xcd c .. n_xcd c + n_xcd - 1}, which hold one CU of every
+// XCD under that rule: many single-wave workgroups run on each and report
+// XCC_ID and the CU field of HW_ID (shader engine, array, CU).  The map is
+// accepted when every group shows n_xcd distinct XCDs with one CU each and,
+// per XCD, the groups select distinct CUs; bit n_xcd c + x is then CU c of
+// XCD x.  Otherwise every bit stays -1 and budgets use the striping guess.
+nf_status measure_cu_map(int device, int n_cus, int n_xcd, CuMap& out) {
+  std::lock_guard<std::mutex> lk(g_map_mu);
+  auto it = g_cu_maps.find(device);
+  if (it != g_cu_maps.end()) {
+    out = it->second;
+    return NF_OK;
+  }
+  CuMap m;
+  m.xcc.assign(n_cus, -1);
+  m.cu.assign(n_cus, -1);
+  const int words = (n_cus + 31) / 32, groups = n_cus / n_xcd;
+  bool ok = n_cus % n_xcd == 0 && groups > 0;
+  std::vector<std::vector<int>> per_xcd(n_xcd);
+  std::vector<std::pair<int, int>> seen;
+  for (int c = 0; ok && c < groups; ++c) {
+    std::vector<uint32_t> mask(words, 0u);
+    for (int x = 0; x < n_xcd; ++x) {
+      const int bit = c * n_xcd + x;
+      mask[bit / 32] |= 1u << (bit % 32);
+    }
+    nf_status st = probe_mask(mask, seen);
+    if (st != NF_OK) return st;
+    ok = (int)seen.size() == n_xcd;
+    for (int x = 0; ok && x < n_xcd; ++x) {
+      ok = seen[x].first == x;            // sorted: XCD x, exactly one CU
+      if (ok) {
+        m.xcc[c * n_xcd + x] = x;
+        m.cu[c * n_xcd + x] = seen[x].second;
+        per_xcd[x].push_back(seen[x].second);
+      }
+    }
+  }
+  for (int x = 0; ok && x < n_xcd; ++x) {
+    std::vector<int> v = per_xcd[x];
+    std::sort(v.begin(), v.end());
+    ok = std::adjacent_find(v.begin(), v.end()) == v.end();
+  }
+  if (!ok) {
+    m.xcc.assign(n_cus, -1);
+    m.cu.assign(n_cus, -1);
+  }
+  g_cu_maps[device] = m;
+  out = m;
   return NF_OK;
 }
 
@@ -251,8 +302,10 @@ nf_status get_pair(nf_layer* L, int g, int a, StreamPair& out) {
     return NF_OK;
   }
   if ((g || ab) && L->xcc_of_bit.empty()) {
-    nf_status st = measure_cu_map(L->device, L->n_cus, L->n_xcd, L->xcc_of_bit);
+    CuMap cm;
+    nf_status st = measure_cu_map(L->device, L->n_cus, L->n_xcd, cm);
     if (st != NF_OK) return st;
+    L->xcc_of_bit = cm.xcc;
   }
   StreamPair p;
   std::vector<uint32_t> m;
@@ -351,7 +404,7 @@ hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s, int* parti
     prof_end(L, kind, s);
     return e;
   }
-  GemmPlan gp = gemm_choose(g, c.gemm_cus);
+  GemmPlan gp = gemm_choose(g, c.gemm_cus, c.attn_waves_per_cu > 0);
   if (partials) {
     *partials = gemm_partials(g, gp);
     g.defer_reduce = *partials > 1;
@@ -366,7 +419,7 @@ hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s, int* parti
 
 size_t gemm_ws_need(const StepCtx& c, GemmArgs g) {
   if (c.L->s.dtype == NF_F32) return 0;
-  return gemm_workspace_bytes(g, gemm_choose(g, c.gemm_cus));
+  return gemm_workspace_bytes(g, gemm_choose(g, c.gemm_cus, c.attn_waves_per_cu > 0));
 }
 
 // GEMM descriptors of nano-batch [t0, t1)
@@ -402,8 +455,9 @@ NanoGemms nano_gemms(const StepCtx& c, int j, int t0, int t1) {
     GemmArgs& d = n.down;
     d.A = ptr(L->act, (int64_t)t0 * F, dt); d.lda = F;
     d.B = L->w.w_down; d.ldb = F; d.Bp = L->wp_down.p;
-    d.C = (char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt); d.ldc = H;
-    d.R = ptr(L->x1, (int64_t)t0 * H, dt); d.ldr = H;
+    d.C = L->ar_mode ? ptr(L->ypre, (int64_t)t0 * H, dt) : (char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt);
+    d.ldc = H;
+    d.R = ptr(L->ar_mode ? L->x1r : L->x1, (int64_t)t0 * H, dt); d.ldr = H;
     d.M = Tj; d.N = H; d.K = F; d.mode = GEMM_RESIDUAL;
   } else {
     const int32_t* off = (const int32_t*)L->r_off.p + j * (s.n_experts + 1);
@@ -446,7 +500,7 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
   // ride on the QKV GEMM when it takes the LDS-pipelined path, beside its
   // tiles; otherwise on the RMSNorm before it.
   const bool meta_in_gemm = c.mc_pending && dt == NF_BF16 && c.mc.n16 * 16 > (64 << 10) && [&] {
-    const int cfg = gemm_choose(g.qkv, c.gemm_cus).cfg;
+    const int cfg = gemm_choose(g.qkv, c.gemm_cus, c.attn_waves_per_cu > 0).cfg;
     return cfg >= 10 && cfg <= 30 && g.qkv.K % 64 == 0;
   }();
   prof_begin(L, K_NORM1, s);
@@ -507,7 +561,7 @@ nf_status issue_attention(StepCtx& c, int j, hipStream_t s) {
   a.nq = sh.n_q_heads; a.nkv = sh.n_kv_heads; a.d = sh.head_dim; a.page_size = c.P->page_size;
   a.scale = (float)(1.0 / std::sqrt((double)sh.head_dim));
   a.variant = c.attn_variant;
-  a.max_blocks = c.attn_waves_per_cu > 0 ? c.attn_waves_per_cu * c.attn_cus : 0;
+  a.max_blocks = c.attn_waves_per_cu > 0 ? c.attn_waves_per_cu * c.attn_cus / (c.attn_variant == 1 ? 4 : 1) : 0;
   prof_begin(L, K_ATTN, s);
   HIP_STEP(attention(sh.dtype, a, s));
   prof_end(L, K_ATTN, s);
@@ -519,25 +573,68 @@ nf_status issue_attention(StepCtx& c, int j, hipStream_t s) {
   return NF_OK;
 }
 
-nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
+// Emulated all-reduce of rows [t0, t0 + Tj) of a [T][H] buffer: a send leg
+// (src -> the staging buffer) and a receive leg (staging -> dst) on stream
+// sc, on the copy engines (mode 1) or a copy kernel of ar_wgs workgroups
+// (mode 2).  On one GPU the tensor-parallel all-reduce is the identity, so
+// dst receives src's bits.
+nf_status issue_allreduce(nf_layer* L, const void* src, void* dst, int64_t t0, int64_t Tj, hipStream_t sc) {
+  const size_t eb = dtype_bytes(L->s.dtype);
+  const size_t off = (size_t)t0 * L->s.hidden * eb, bytes = (size_t)Tj * L->s.hidden * eb;
+  char* stage = (char*)L->ar_stage.p + off;
+  if (L->ar_mode == 1) {
+    HIP_TRY(hipMemcpyAsync(stage, (const char*)src + off, bytes, hipMemcpyDeviceToDeviceNoCU, sc));
+    HIP_TRY(hipMemcpyAsync((char*)dst + off, stage, bytes, hipMemcpyDeviceToDeviceNoCU, sc));
+  } else {
+    HIP_TRY(copy_rows((const char*)src + off, stage, bytes, L->ar_wgs, sc));
+    HIP_TRY(copy_rows(stage, (char*)dst + off, bytes, L->ar_wgs, sc));
+  }
+  return NF_OK;
+}
+
+// O-projection of nano-batch j on stream s: x1 = x + attn W_o^T and, where
+// the split-K reduce fuses with it, h2 = RMSNorm(x1) (*normed = true).  With
+// the all-reduce emulation the reduce is not fused: x1 then goes through the
+// all-reduce to x1r, which the FFN half reads.
+nf_status issue_oproj(StepCtx& c, int j, hipStream_t s, bool* normed) {
+  nf_layer* L = c.L;
+  const nf_shape& sh = L->s;
+  const NanoWork& nw = L->work.nanos[j];
+  const int t0 = nw.t0, Tj = nw.t1 - nw.t0, dt = sh.dtype, H = sh.hidden;
+  *normed = false;
+  if (Tj == 0) return NF_OK;
+  NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
+  const bool fuse = dt == NF_BF16 && H % 8 == 0 && !L->ar_mode;
+  int o_parts = 1;
+  HIP_STEP(run_gemm(c, g.o, K_OPROJ, s, fuse ? &o_parts : nullptr));
+  if (o_parts > 1) {            // O-projection split-K reduce + residual + FFN norm in one kernel
+    prof_begin(L, K_NORM2, s);
+    HIP_STEP(residual_rmsnorm_partials((const float*)L->splitk.p, H, (int64_t)Tj * H, o_parts, g.o.R, g.o.ldr,
+                                       g.o.C, g.o.ldc, L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
+                                       sh.rms_eps, s));
+    prof_end(L, K_NORM2, s);
+    *normed = true;
+  }
+  return NF_OK;
+}
+
+// FFN half of nano-batch j on stream s: h2 = RMSNorm(x1) unless the O half
+// fused it, then the SwiGLU FFN or the experts, out = x1 + FFN(h2) (with the
+// all-reduce emulation: x1r in, ypre out).
+nf_status issue_ffn(StepCtx& c, int j, hipStream_t s, bool normed) {
   nf_layer* L = c.L;
   const nf_shape& sh = L->s;
   const NanoWork& nw = L->work.nanos[j];
   const int t0 = nw.t0, Tj = nw.t1 - nw.t0, dt = sh.dtype, H = sh.hidden;
   if (Tj == 0) return NF_OK;
   NanoGemms g = nano_gemms(c, j, nw.t0, nw.t1);
-  const bool fuse = dt == NF_BF16 && H % 8 == 0;
-  int o_parts = 1;
-  HIP_STEP(run_gemm(c, g.o, K_OPROJ, s, fuse ? &o_parts : nullptr));
-  prof_begin(L, K_NORM2, s);
-  if (o_parts > 1)              // O-projection split-K reduce + residual + FFN norm in one kernel
-    HIP_STEP(residual_rmsnorm_partials((const float*)L->splitk.p, H, (int64_t)Tj * H, o_parts, g.o.R, g.o.ldr,
-                                       g.o.C, g.o.ldc, L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
-                                       sh.rms_eps, s));
-  else
-    HIP_STEP(rmsnorm(dt, ptr(L->x1, (int64_t)t0 * H, dt), L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
+  const DevBuf& x1 = L->ar_mode ? L->x1r : L->x1;
+  if (!normed) {
+    prof_begin(L, K_NORM2, s);
+    HIP_STEP(rmsnorm(dt, ptr(x1, (int64_t)t0 * H, dt), L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
                      sh.rms_eps, s));
-  prof_end(L, K_NORM2, s);
+    prof_end(L, K_NORM2, s);
+  }
   if (sh.n_experts == 1) {
     HIP_STEP(run_gemm(c, g.gu, K_GATEUP, s));
     HIP_STEP(run_gemm(c, g.down, K_DOWN, s));
@@ -563,9 +660,11 @@ nf_status issue_back(StepCtx& c, int j, hipStream_t s) {
   prof_begin(L, K_MOE_DOWN, s);
   HIP_STEP(gemm_bf16(g.moe_down, gemm_choose(g.moe_down, c.gemm_cus), L->splitk.p, s));
   prof_end(L, K_MOE_DOWN, s);
+  void* dst = L->ar_mode ? (void*)ptr(L->ypre, (int64_t)t0 * H, dt)
+                         : (void*)((char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt));
   prof_begin(L, K_COMBINE, s);
-  HIP_STEP(moe_combine(dt, ptr(L->x1, (int64_t)t0 * H, dt), (const float*)L->y.p + (int64_t)t0 * k * H,
-                       r.w, r.inv, (char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt), Tj, H, k, s));
+  HIP_STEP(moe_combine(dt, ptr(x1, (int64_t)t0 * H, dt), (const float*)L->y.p + (int64_t)t0 * k * H, r.w, r.inv,
+                       dst, Tj, H, k, s));
   prof_end(L, K_COMBINE, s);
   return NF_OK;
 }
@@ -601,6 +700,7 @@ struct LayerRun {
   nf_batch b{};
   StepCtx c{};
   int count = 0;
+  bool normed[NF_MAX_NANO] = {};   // the O half of nano-batch j also wrote h2
 };
 
 // Everything of one layer's step before its launches: the checks, the
@@ -638,8 +738,9 @@ nf_status prepare_layer(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_
   // attention work items: a four-wave workgroup each (fastest when attention
   // has the whole chip), or one wave each (many short items) when the plan
   // asks for a persistent attention grid that leaves room for GEMM waves
-  c.attn_variant = L->attn_variant >= 0 ? L->attn_variant : (c.attn_waves_per_cu > 0 ? 0 : 1);
-  if (c.attn_waves_per_cu > 0) c.attn_variant = 0;
+  // bounded residency: multiples of four waves per CU run as persistent
+  // four-wave workgroups, other counts as persistent single waves
+  c.attn_variant = L->attn_variant >= 0 ? L->attn_variant : (c.attn_waves_per_cu % 4 == 0 ? 1 : 0);
   const bool wave_items = L->s.dtype == NF_BF16 && L->s.head_dim == 128 && c.attn_variant == 0;
   build_work(L->s, *b, plan, P->page_size, wave_items ? 8 * c.attn_cus : 2 * c.attn_cus, 8,
              wave_items ? 32 : 0, L->work);
@@ -721,15 +822,23 @@ nf_status prepare_layer(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_
 // runtime, so only the necessary ones are issued: attention(j) waits for
 // RoPE/append(j), the O-projection of j waits for attention(j).  The last of
 // those also orders every attention kernel before the end of the step on the
-// GEMM stream.
+// GEMM stream.  With the all-reduce emulation a third stream carries the
+// collectives: the all-reduce of nano-batch j's O-projection waits for that
+// GEMM and its FFN half waits for the all-reduce; the caller's stream waits
+// for the last collective.
 struct Streams {
-  bool two = false;
-  hipStream_t caller = nullptr, sg = nullptr, sa = nullptr;
+  bool two = false, comm = false;
+  hipStream_t caller = nullptr, sg = nullptr, sa = nullptr, sc = nullptr;
 };
 
 nf_status open_streams(nf_layer* L, const nf_plan& plan, hipStream_t caller, Streams& S) {
   S.two = plan.n_streams == 2;
   S.caller = S.sg = S.sa = caller;
+  S.comm = L->ar_mode != 0;
+  if (S.comm) {
+    if (!L->sc) HIP_TRY(hipStreamCreateWithFlags(&L->sc, hipStreamNonBlocking));
+    S.sc = L->sc;
+  }
   if (!S.two) return NF_OK;
   StreamPair pr;
   nf_status st = get_pair(L, plan.gemm_cus_per_xcd, plan.attn_cus_per_xcd, pr);
@@ -747,6 +856,10 @@ nf_status close_streams(nf_layer* L, const Streams& S) {
   if (S.two && S.sg != S.caller) {
     HIP_TRY(hipEventRecord(L->ev_g, S.sg));
     HIP_TRY(hipStreamWaitEvent(S.caller, L->ev_g, 0));
+  }
+  if (S.comm) {
+    HIP_TRY(hipEventRecord(L->ev_a, S.sc));
+    HIP_TRY(hipStreamWaitEvent(S.caller, L->ev_a, 0));
   }
   return NF_OK;
 }
@@ -766,10 +879,44 @@ nf_status issue_front_attn(LayerRun& r, const Streams& S, int j) {
   return NF_OK;
 }
 
+// O half of nano-batch j once its attention is done; with the all-reduce
+// emulation its x1 rows then go through the collective on the third stream.
+nf_status issue_o_after_attn(LayerRun& r, const Streams& S, int j) {
+  nf_layer* L = r.L;
+  if (S.two) HIP_TRY(hipStreamWaitEvent(S.sg, L->ev_att[j], 0));
+  nf_status st = issue_oproj(r.c, j, S.sg, &r.normed[j]);
+  if (st != NF_OK || !L->ar_mode) return st;
+  const NanoWork& nw = L->work.nanos[j];
+  if (nw.t1 == nw.t0) return NF_OK;
+  HIP_TRY(hipEventRecord(L->ev_o[j], S.sg));
+  HIP_TRY(hipStreamWaitEvent(S.sc, L->ev_o[j], 0));
+  if ((st = issue_allreduce(L, L->x1.p, L->x1r.p, nw.t0, nw.t1 - nw.t0, S.sc)) != NF_OK) return st;
+  HIP_TRY(hipEventRecord(L->ev_co[j], S.sc));
+  return NF_OK;
+}
+
+// FFN half of nano-batch j (after its O half on the same stream); with the
+// all-reduce emulation it first waits for the O-projection's collective and
+// its output rows go through the collective into the batch's out.
+nf_status issue_ffn_after_o(LayerRun& r, const Streams& S, int j) {
+  nf_layer* L = r.L;
+  const NanoWork& nw = L->work.nanos[j];
+  const bool live = nw.t1 > nw.t0;
+  if (L->ar_mode && live) HIP_TRY(hipStreamWaitEvent(S.sg, L->ev_co[j], 0));
+  nf_status st = issue_ffn(r.c, j, S.sg, r.normed[j]);
+  if (st != NF_OK || !L->ar_mode || !live) return st;
+  HIP_TRY(hipEventRecord(L->ev_d[j], S.sg));
+  HIP_TRY(hipStreamWaitEvent(S.sc, L->ev_d[j], 0));
+  if ((st = issue_allreduce(L, L->ypre.p, r.c.b->out, nw.t0, nw.t1 - nw.t0, S.sc)) != NF_OK) return st;
+  HIP_TRY(hipEventRecord(L->ev_cd[j], S.sc));
+  return NF_OK;
+}
+
 // back (O-projection, norm, FFN or experts) of nano-batch j
 nf_status issue_back_after_attn(LayerRun& r, const Streams& S, int j) {
-  if (S.two) HIP_TRY(hipStreamWaitEvent(S.sg, r.L->ev_att[j], 0));
-  return issue_back(r.c, j, S.sg);
+  nf_status st = issue_o_after_attn(r, S, j);
+  if (st != NF_OK) return st;
+  return issue_ffn_after_o(r, S, j);
 }
 
 // one layer's launches in the plan's order
@@ -780,6 +927,13 @@ nf_status issue_layer(LayerRun& r, const Streams& S, int order) {
     for (int j = 0; j < r.count; ++j) {
       if (j + 1 < r.count && (st = issue_front_attn(r, S, j + 1)) != NF_OK) return st;
       if ((st = issue_back_after_attn(r, S, j)) != NF_OK) return st;
+    }
+  } else if (order == NF_ORDER_DEEP) {
+    // round t: front of t, O half of t - 1, FFN half of t - 2
+    for (int t = 0; t < r.count + 2; ++t) {
+      if (t < r.count && (st = issue_front_attn(r, S, t)) != NF_OK) return st;
+      if (t >= 1 && t - 1 < r.count && (st = issue_o_after_attn(r, S, t - 1)) != NF_OK) return st;
+      if (t >= 2 && (st = issue_ffn_after_o(r, S, t - 2)) != NF_OK) return st;
     }
   } else {
     for (int j = 0; j < r.count; ++j) {
@@ -835,9 +989,10 @@ nf_status check_stack(nf_layer* const* layers, nf_kv_pool* const* pools, int n, 
       if (layers[m] == layers[l]) return set_err(NF_ERR_INVALID_ARG, "stack: layer %d appears twice", l);
     const nf_shape &s0 = layers[0]->s, &sl = layers[l]->s;
     if (sl.hidden != s0.hidden || sl.dtype != s0.dtype || sl.max_tokens != s0.max_tokens ||
-        sl.n_experts != s0.n_experts || layers[l]->device != layers[0]->device)
+        sl.n_experts != s0.n_experts || layers[l]->device != layers[0]->device ||
+        layers[l]->ar_mode != layers[0]->ar_mode)
       return set_err(NF_ERR_INVALID_ARG, "stack: layer %d differs from layer 0 in hidden size, dtype, "
-                     "max_tokens, experts or device", l);
+                     "max_tokens, experts, device or all-reduce emulation", l);
   }
   return NF_OK;
 }
@@ -1021,6 +1176,11 @@ void nf_layer_destroy(nf_layer* L) {
   }
   for (hipEvent_t e : {L->ev_start, L->ev_g, L->ev_a})
     if (e) (void)hipEventDestroy(e);
+  for (int j = 0; j < NF_MAX_NANO; ++j)
+    for (hipEvent_t e : {L->ev_o[j], L->ev_co[j], L->ev_d[j], L->ev_cd[j]})
+      if (e) (void)hipEventDestroy(e);
+  if (L->sc) (void)hipStreamDestroy(L->sc);
+  for (DevBuf* b : {&L->x1r, &L->ypre, &L->ar_stage}) release(*b);
   for (auto& r : L->recs) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
@@ -1151,6 +1311,27 @@ nf_status nf_plan_get(const nf_layer* L, nf_plan* p) {
   return NF_OK;
 }
 
+nf_status nf_layer_set_allreduce_emulation(nf_layer* L, int32_t mode, int32_t copy_workgroups) {
+  if (!L || mode < 0 || mode > 2 || (mode == 2 && (copy_workgroups < 1 || copy_workgroups > 4096)))
+    return set_err(NF_ERR_INVALID_ARG, "nf_layer_set_allreduce_emulation: bad argument");
+  if (mode == 0) {
+    L->ar_mode = 0;
+    return NF_OK;
+  }
+  if (L->s.dtype == NF_F32 ? L->s.hidden % 4 : L->s.hidden % 8)
+    return set_err(NF_ERR_UNSUPPORTED, "nf_layer_set_allreduce_emulation: rows must be whole 16-byte units");
+  HIP_TRY(hipSetDevice(L->device));
+  const size_t bytes = (size_t)L->s.max_tokens * L->s.hidden * dtype_bytes(L->s.dtype);
+  for (DevBuf* b : {&L->x1r, &L->ypre, &L->ar_stage}) HIP_TRY(ensure(*b, bytes));
+  for (int j = 0; j < NF_MAX_NANO; ++j)
+    for (hipEvent_t* e : {&L->ev_o[j], &L->ev_co[j], &L->ev_d[j], &L->ev_cd[j]})
+      if (!*e) HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  if (!L->sc) HIP_TRY(hipStreamCreateWithFlags(&L->sc, hipStreamNonBlocking));
+  L->ar_mode = mode;
+  L->ar_wgs = mode == 2 ? copy_workgroups : L->ar_wgs;
+  return NF_OK;
+}
+
 nf_status nf_layer_step(nf_layer* L, nf_kv_pool* P, const nf_batch* b, void* stream) {
   if (!L || !P || !b) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: null argument");
   if (P->layer != L) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: pool belongs to another layer");
@@ -1191,8 +1372,11 @@ nf_status nf_stack_graph_create(nf_layer* const* layers, nf_kv_pool* const* pool
   if (plan.n_streams == 2 && (plan.gemm_cus_per_xcd || plan.attn_cus_per_xcd))
     return set_err(NF_ERR_UNSUPPORTED, "nf_stack_graph_create: a graph does not keep a stream's CU mask; "
                    "use a plan without a CU split");
-  for (int l = 0; l < n_layers; ++l)
+  for (int l = 0; l < n_layers; ++l) {
     if (layers[l]->prof) return set_err(NF_ERR_UNSUPPORTED, "nf_stack_graph_create: per-kernel timing is on");
+    if (layers[l]->ar_mode)
+      return set_err(NF_ERR_UNSUPPORTED, "nf_stack_graph_create: the all-reduce emulation is on");
+  }
   if (batch->n_tokens == 0) return set_err(NF_ERR_INVALID_ARG, "nf_stack_graph_create: empty batch");
   hipStream_t s = (hipStream_t)stream;
   // one eager step first: every buffer, stream and event the step needs
@@ -1316,16 +1500,42 @@ nf_status nf_profile_read(nf_layer* L, int32_t max_kinds, const char** names, in
   return NF_OK;
 }
 
-nf_status nf_probe_cu_map(int32_t* xcc, int32_t n) {
+nf_status nf_probe_cu_map(int32_t* xcc, int32_t* cu, int32_t n) {
   if (!xcc || n <= 0) return set_err(NF_ERR_INVALID_ARG, "nf_probe_cu_map: bad argument");
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   hipDeviceProp_t prop;
   HIP_TRY(hipGetDeviceProperties(&prop, dev));
-  std::vector<int> map;
+  CuMap map;
   nf_status st = measure_cu_map(dev, prop.multiProcessorCount, 8, map);
   if (st != NF_OK) return st;
-  for (int i = 0; i < n; ++i) xcc[i] = i < (int)map.size() ? map[i] : -1;
+  for (int i = 0; i < n; ++i) {
+    xcc[i] = i < (int)map.xcc.size() ? map.xcc[i] : -1;
+    if (cu) cu[i] = i < (int)map.cu.size() ? map.cu[i] : -1;
+  }
+  return NF_OK;
+}
+
+nf_status nf_probe_budget_cus(int32_t first, int32_t count, int32_t* xcc_cu, int32_t max, int32_t* n_out) {
+  if (!xcc_cu || !n_out || max <= 0 || first < 0 || count <= 0)
+    return set_err(NF_ERR_INVALID_ARG, "nf_probe_budget_cus: bad argument");
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  const int n_cus = prop.multiProcessorCount, n_xcd = 8, per = std::max(1, n_cus / n_xcd);
+  if (first + count > per)
+    return set_err(NF_ERR_OUT_OF_RANGE, "nf_probe_budget_cus: CUs %d..%d of an XCD with %d", first, first + count - 1,
+                   per);
+  CuMap map;
+  nf_status st = measure_cu_map(dev, n_cus, n_xcd, map);
+  if (st != NF_OK) return st;
+  std::vector<uint32_t> mask;
+  make_mask(map.xcc, n_xcd, first, first + count, mask);
+  std::vector<std::pair<int, int>> seen;
+  if ((st = probe_mask(mask, seen)) != NF_OK) return st;
+  *n_out = (int32_t)seen.size();
+  for (int i = 0; i < (int)seen.size() && i < max; ++i) xcc_cu[i] = (seen[i].first << 16) | seen[i].second;
   return NF_OK;
 }
 

@@ -216,15 +216,12 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int64_t qoff, int grp,
 // Held to three waves per SIMD (160 registers, no spills; uncapped it takes
 // 192 and fits two): long-context grids of thousands of items keep a third
 // wave's page loads in flight per SIMD.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_bf16_d128_kernel(AttnArgs a) {
-  __shared__ float m_s[4 * ROWS], l_s[4 * ROWS];
-  __shared__ float O_s[4 * ROWS * DH];
-
-  // workgroup w takes KV head w % nkv of item w / nkv: the heads of one item
-  // (the same pages, adjacent blocks in the pool) are dispatched together,
-  // and the longest items' heads all go first
-  const AttnItem it = a.items[blockIdx.x / a.nkv];
-  const int kh = blockIdx.x % a.nkv;
+__device__ __forceinline__ void item4(const AttnArgs& a, int w, float* m_s, float* l_s, float* O_s) {
+  // work w takes KV head w % nkv of item w / nkv: the heads of one item (the
+  // same pages, adjacent blocks in the pool) are dispatched together, and the
+  // longest items' heads all go first
+  const AttnItem it = a.items[w / a.nkv];
+  const int kh = w % a.nkv;
   const int G = a.nq / a.nkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15;        // row index of the S^T / O^T column this lane holds
@@ -260,6 +257,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     for (int i = 0; i < 4; ++i) O_s[(wave * ROWS + col) * DH + 16 * b + 4 * grp + i] = st.o[b][i];
   __syncthreads();
   finish_item<bf16>(a, it, G, kh, m_s, l_s, O_s);
+}
+
+// One workgroup per work item, or, with a capped grid, each workgroup walks
+// the work list with a stride of the grid (a persistent grid that holds a
+// fixed number of workgroups per CU and so leaves the rest of the CU's LDS
+// and registers to a concurrent GEMM).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_bf16_d128_kernel(AttnArgs a) {
+  __shared__ float m_s[4 * ROWS], l_s[4 * ROWS];
+  __shared__ float O_s[4 * ROWS * DH];
+  const int n_work = a.n_items * a.nkv;
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+    item4(a, w, m_s, l_s, O_s);
+    __syncthreads();                 // the next item reuses the LDS
+  }
 }
 
 // ---------------------------------------------------------------- one wave per item
@@ -437,7 +448,9 @@ hipError_t attention(int dtype, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_items, a.nkv);
   if (dtype == 1 && a.d == 128 && a.page_size == 16) {
     if (a.variant == 1) {
-      launch(attn_bf16_d128_kernel, a.n_items * a.nkv, 256, 0, s, a);
+      int blocks = a.n_items * a.nkv;
+      if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
+      launch(attn_bf16_d128_kernel, blocks, 256, 0, s, a);
     } else {
       int blocks = a.n_items * a.nkv;
       if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;

@@ -1061,7 +1061,7 @@ int stream_splits(const GemmArgs& a, int cfg, int cus) {
 }
 }  // namespace
 
-GemmPlan gemm_choose(const GemmArgs& a, int cus) {
+GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident) {
   GemmPlan p;
   if (cus <= 0) cus = 256;
   if (a.Bp) {                   // packed weights: stream them for expert groups
@@ -1103,7 +1103,7 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   // K >= 8192, when split-K brings them there with >= 2048 of K per piece
   // (shorter K, or fewer tiles: 128 x 128 tiles, whose split partials the
   // consumers reduce more cheaply)
-  if (p.cfg == 14 && a.K >= 2048) {
+  if (p.cfg == 14 && a.K >= 2048 && !coresident) {
     const int64_t t256 = (int64_t)((M + 255) / 256) * n_tiles_of(a, 256);
     const int64_t enough = (3 * (int64_t)cus + 3) / 4;
     int ks = 0;
@@ -1128,7 +1128,7 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus) {
   // 1024 x 4096 x 4096 O projection and its FFN norm 56 -> 45 us (no split-K
   // partials to reduce), the 512 x 6144 x 4096 QKV with RoPE 45 -> 41 us; with
   // fewer tiles (160 or 128 for 256 CUs) the split 128 x 128 tiles were faster
-  if (p.cfg == 14 && a.K >= 1024) {
+  if (p.cfg == 14 && a.K >= 1024 && !coresident) {
     const int64_t t128 = (int64_t)((M + 127) / 128) * n_tiles_of(a, 128);
     if (4 * t128 >= 3 * (int64_t)cus && t128 <= cus) {
       p.cfg = 13;

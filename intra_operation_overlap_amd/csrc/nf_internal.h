@@ -80,8 +80,11 @@ struct GemmPlan {
 };
 
 // Chooses a tile configuration and split-K for a problem given the number of
-// CUs its stream may use.
-GemmPlan gemm_choose(const GemmArgs& a, int cus);
+// CUs its stream may use.  `coresident`: attention waves share every CU with
+// the GEMM, so only tiles that leave registers and LDS for them are chosen
+// (128 x 128 tiles, two workgroups per CU: 146 registers per lane and 64 KB
+// of LDS each, against the 512 registers per SIMD lane and 160 KB of a CU).
+GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident = false);
 // Workspace bytes the split-K path needs for this problem/plan.
 size_t gemm_workspace_bytes(const GemmArgs& a, const GemmPlan& p);
 // Called between the main kernel and the split-K reduce (phase 1) so callers
@@ -153,7 +156,7 @@ struct AttnArgs {
   int nq, nkv, d, page_size;
   float scale;
   int variant = 0;          // bf16 d=128: 0 one wave per item, 1 four waves per item
-  int max_blocks = 0;       // variant 0: > 0 caps the grid; each wave then loops over items
+  int max_blocks = 0;       // > 0 caps the grid (workgroups); each then loops over items
 };
 hipError_t attention(int dtype, const AttnArgs& a, hipStream_t s);
 hipError_t attention_merge(int dtype, const AttnArgs& a, hipStream_t s);
@@ -180,6 +183,8 @@ hipError_t kv_convert(int dtype, void* k_pool, void* v_pool, const int32_t* page
 // copies pool pages pages[0..n) (K and V, block_bytes each) to dst_k / dst_v in list order
 hipError_t kv_gather(const void* k_pool, const void* v_pool, const int32_t* pages, int n, int64_t block_bytes,
                      void* dst_k, void* dst_v, hipStream_t s);
+// copy of `bytes` (multiple of 16, 16-byte aligned) by a kernel of `wgs` workgroups
+hipError_t copy_rows(const void* src, void* dst, size_t bytes, int wgs, hipStream_t s);
 // the inverse: block i of src_k / src_v to pool page pages[i] (pages distinct)
 hipError_t kv_scatter(void* k_pool, void* v_pool, const int32_t* pages, int n, int64_t block_bytes, const void* src_k,
                       const void* src_v, hipStream_t s);

@@ -290,6 +290,14 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(const u32x4* __restrict_
   for (int64_t i = threadIdx.x; i < blk16; i += 256) dst[i] = __builtin_nontemporal_load(src + i);
 }
 
+// Plain copy of n16 16-byte units with a grid of few workgroups (the copy
+// kernel of the emulated all-reduce).
+__global__ __launch_bounds__(256) void copy_rows_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 // Inverse of kv_gather_kernel: block i of src_k / src_v back to pool page
 // pages[i] (pages distinct).
 __global__ __launch_bounds__(256) void kv_scatter_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
@@ -343,6 +351,13 @@ hipError_t kv_convert(int dtype, void* k_pool, void* v_pool, const int32_t* page
   else
     launch(kv_convert_kernel<uint32_t>, dim3((unsigned)grid), 256, 0, s, (uint32_t*)k_pool, (uint32_t*)v_pool, pages,
            n, nkv, d, (uint32_t*)k_rm, (uint32_t*)v_rm, to_pool ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t copy_rows(const void* src, void* dst, size_t bytes, int wgs, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  if (bytes % 16 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15) || wgs <= 0) return hipErrorInvalidValue;
+  launch(copy_rows_kernel, wgs, 256, 0, s, (const u32x4*)src, (u32x4*)dst, (int64_t)(bytes / 16));
   return hipGetLastError();
 }
 

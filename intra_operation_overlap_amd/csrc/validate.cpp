@@ -125,7 +125,7 @@ nf_status check_batch(const nf_shape& s, int64_t n_pages, int page_size, const n
 nf_status check_plan(const nf_plan& p, int cus_per_xcd, std::string& err) {
   if (p.count < 1 || p.count > NF_MAX_NANO)
     return fail(err, NF_ERR_INVALID_ARG, "plan: count %d outside 1..%d", p.count, NF_MAX_NANO);
-  if (p.order != NF_ORDER_PIPELINED && p.order != NF_ORDER_SEQUENTIAL)
+  if (p.order != NF_ORDER_PIPELINED && p.order != NF_ORDER_SEQUENTIAL && p.order != NF_ORDER_DEEP)
     return fail(err, NF_ERR_INVALID_ARG, "plan: unknown order %d", p.order);
   if (p.n_streams != 1 && p.n_streams != 2)
     return fail(err, NF_ERR_INVALID_ARG, "plan: n_streams must be 1 or 2");

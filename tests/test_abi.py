@@ -208,3 +208,14 @@ def test_kv_pool_import_export_reject_bad_arguments_before_launching():
         assert fn(ctypes.c_void_p(8), pages, -1, 1, 1, None) == B.NF_ERR_INVALID_ARG
         assert fn(ctypes.c_void_p(8), pages, 2, None, 1, None) == B.NF_ERR_INVALID_ARG
         assert fn(ctypes.c_void_p(8), None, 2, 1, None, None) == B.NF_ERR_INVALID_ARG
+
+
+def test_cu_map_probes_reject_bad_arguments_before_launching():
+    L = B.lib()
+    buf = (ctypes.c_int32 * 8)()
+    n = ctypes.c_int32()
+    assert L.nf_probe_cu_map(None, None, 8) == B.NF_ERR_INVALID_ARG
+    assert L.nf_probe_cu_map(buf, None, 0) == B.NF_ERR_INVALID_ARG
+    assert L.nf_probe_budget_cus(0, 4, None, 8, ctypes.byref(n)) == B.NF_ERR_INVALID_ARG
+    assert L.nf_probe_budget_cus(-1, 4, buf, 8, ctypes.byref(n)) == B.NF_ERR_INVALID_ARG
+    assert L.nf_probe_budget_cus(0, 0, buf, 8, ctypes.byref(n)) == B.NF_ERR_INVALID_ARG

@@ -65,7 +65,26 @@ def test_device_probes_are_plausible():
     GH.log(f"bf16 MFMA {tf:.0f} TFLOP/s, HBM read {gbps:.0f} GB/s")
     assert 500 < tf < 3000
     assert 1000 < gbps < 9000
-    xcc = B.probe_cu_map(256)
-    assert len(set(xcc)) == 8 and all(0 <= x < 8 for x in xcc)
     ms, cfg, splits = B.probe_gemm_bf16_ms(256, 1024, 1024, 0, -1, 0, 256, 3)
     assert ms > 0 and cfg >= 0 and splits >= 1
+
+
+def test_cu_mask_map_is_measured_and_budgets_land_on_their_cus():
+    """Every CU-mask bit maps to a distinct (XCD, CU); a plan-style budget of
+    CUs [first, first + count) per XCD runs exactly on the CUs the map names."""
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    xcc, cu = B.probe_cu_map(n)
+    GH.log(f"CU map: xcc {xcc[:16]}..., cu {cu[:16]}...")
+    assert all(0 <= x < 8 for x in xcc) and all(c >= 0 for c in cu)
+    pairs = list(zip(xcc, cu))
+    assert len(set(pairs)) == n
+    assert all(xcc.count(x) == n // 8 for x in range(8))
+    per = n // 8
+    for first, count in ((0, 16), (16, 16), (0, 24), (24, 8), (per - 4, 4)):
+        want = sorted({(xcc[b], cu[b]) for b in range(n) if first <= b // 8 < first + count})
+        got = B.probe_budget_cus(first, count)
+        assert got == want, (first, count)
+        assert len({x for x, _ in got}) == 8
+    with pytest.raises(B.NfError) as e:
+        B.probe_budget_cus(per - 2, 4)
+    assert e.value.status == B.NF_ERR_OUT_OF_RANGE

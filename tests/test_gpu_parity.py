@@ -29,11 +29,17 @@ def _plans_for(T):
         "k3_sequential_masked8": B.make_plan(3, [T // 3, T // 3, T - 2 * (T // 3)], order=B.NF_ORDER_SEQUENTIAL,
                                              n_streams=2, gemm_cus_per_xcd=8),
         "k4_masked24": B.make_plan(4, [T // 4] * 3 + [T - 3 * (T // 4)], n_streams=2, gemm_cus_per_xcd=24),
+        "k3_deep_two_streams": B.make_plan(3, [T // 3, T // 3, T - 2 * (T // 3)], order=B.NF_ORDER_DEEP,
+                                           n_streams=2),
         # persistent one-wave attention grids (split page ranges + merge)
         "k1_attn_waves1": B.make_plan(1, [T], n_streams=2, attn_waves_per_cu=1),
         "k2_attn_waves4": B.make_plan(2, [half, T - half], n_streams=2, attn_waves_per_cu=4),
         "k2_attn_waves1_masked16": B.make_plan(2, [half, T - half], n_streams=2, gemm_cus_per_xcd=16,
                                                attn_waves_per_cu=1),
+        # grids far smaller than the work list: every workgroup loops
+        "k2_attn_waves4_on2cus": B.make_plan(2, [half, T - half], n_streams=2, attn_cus_per_xcd=2,
+                                             attn_waves_per_cu=4),
+        "k1_attn_waves2_on2cus": B.make_plan(1, [T], n_streams=2, attn_cus_per_xcd=2, attn_waves_per_cu=2),
     }
 
 
@@ -153,7 +159,9 @@ def test_plan_invariance_bit_exact(small):
     outs = []
     for plan in (B.make_plan(2, [30, T - 30]),
                  B.make_plan(2, [30, T - 30], order=B.NF_ORDER_SEQUENTIAL),
-                 B.make_plan(2, [30, T - 30], n_streams=2)):
+                 B.make_plan(2, [30, T - 30], n_streams=2),
+                 B.make_plan(2, [30, T - 30], order=B.NF_ORDER_DEEP, n_streams=2),
+                 B.make_plan(2, [30, T - 30], order=B.NF_ORDER_DEEP)):
         small.layer.set_plan(plan)
         k0, v0 = small.k.clone(), small.v.clone()
         GH.run_step(small)
