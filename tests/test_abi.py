@@ -219,3 +219,15 @@ def test_cu_map_probes_reject_bad_arguments_before_launching():
     assert L.nf_probe_budget_cus(0, 4, None, 8, ctypes.byref(n)) == B.NF_ERR_INVALID_ARG
     assert L.nf_probe_budget_cus(-1, 4, buf, 8, ctypes.byref(n)) == B.NF_ERR_INVALID_ARG
     assert L.nf_probe_budget_cus(0, 0, buf, 8, ctypes.byref(n)) == B.NF_ERR_INVALID_ARG
+
+
+def test_binding_has_every_name_the_gpu_tests_and_bench_use():
+    """The GPU tests skip on a machine without a GPU; their use of the binding
+    is checked here so a missing name fails on the CPU first."""
+    names = set()
+    for f in ("tests/test_gpu_parity.py", "tests/test_gpu_collective.py", "tests/test_gpu_api.py",
+              "tests/test_gpu_stack.py", "tests/test_gpu_offload.py", "tests/test_gpu_gemm.py",
+              "tests/test_zz_no_alloc.py", "tests/gpu_harness.py", "bench.py", "__graft_entry__.py"):
+        names |= set(re.findall(r"\bB\.([A-Za-z_][A-Za-z0-9_]*)", open(os.path.join(ROOT, f)).read()))
+    missing = sorted(n for n in names if not hasattr(B, n))
+    assert not missing, missing
