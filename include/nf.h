@@ -362,29 +362,79 @@ nf_status nf_graph_launch(nf_graph* graph, void* stream);
 /* Waits for the device, then frees the graph and its metadata buffers. */
 void nf_graph_destroy(nf_graph* graph);
 
+/* ---- plan model ------------------------------------------------------------
+ * The event-graph step-time model the plan search ranks candidates with.  A
+ * step is four operations per nano-batch j -- F (RMSNorm, QKV, RoPE/append),
+ * A (attention), O (O-projection with the FFN norm), N (gate/up and down) --
+ * in the plan's issue order on one stream, or with A on a second stream.
+ * Each nano-batch runs F -> A -> O -> N; a dependency across streams costs
+ * wait_us.  Solo durations: front_us / oproj_us / ffn_us per launch at the
+ * nano-batch sizes tokens[0 .. n_points-1] (ascending), interpolated
+ * piecewise linearly (proportionally for one point); attention
+ * attn_base_us + attn_us_per_page * (work items x KV pages of the
+ * nano-batch); gap_us added per operation.  While both streams run, the GEMM
+ * side progresses at 1 / slow_gemm and attention at 1 / slow_attn of its
+ * solo rate (interference of concurrent operations, the consideration the
+ * codewithpapers abstract names for the search).  The plan search measures
+ * these inputs on the device; nf_plan_predict evaluates the model alone on
+ * the host (no HIP call) for a plan and batch: *us = predicted step time.
+ * Errors: NF_ERR_INVALID_ARG (null argument, n_points outside
+ * 1..NF_PROFILE_POINTS), any nf_batch_validate error of the plan on the
+ * batch's token count. */
+#define NF_PROFILE_POINTS 8
+typedef struct nf_plan_profile {
+  int32_t n_points;
+  double tokens[NF_PROFILE_POINTS];
+  double front_us[NF_PROFILE_POINTS];
+  double oproj_us[NF_PROFILE_POINTS];
+  double ffn_us[NF_PROFILE_POINTS];
+  double attn_base_us, attn_us_per_page;
+  double gap_us;
+  double slow_gemm, slow_attn, wait_us;
+} nf_plan_profile;
+nf_status nf_plan_predict(const nf_plan_profile* prof, const nf_shape* shape, const nf_plan* plan,
+                          const nf_batch* batch, double* us);
+
 /* ---- plan search -----------------------------------------------------------
  * Profile-driven choice of the plan for this batch.  It stands in for the
  * automatic search of nano-batch number, size, order and resource split in
- * the abstract on the codewithpapers NanoFlow page, whose four dimensions the
- * "Search Space" card of the do-not-panic NanoFlow page lists, and for the
- * Gurobi-based solver of the ossradar Nanoflow page.  The candidates are the unsplit plan and, for every
- * count 2..opts->max_count, equal and attention-balanced sizes, each on one
- * stream and on two streams with several (GEMM, attention) CU budgets and
- * attention residency limits.  After three untimed steps of the unsplit
- * plan, every candidate is timed on this batch for two steps; the `top_k`
- * fastest, and the unsplit plan, are timed again with `warmup` + `reps` steps
- * and the fastest of those is kept.  Runs steps on this batch (so it writes
- * batch->out); the pool pages holding the batch's new positions are copied
- * aside before the first step and copied back before returning, so the pool
- * ends bit-identical to how it was (it is not read-only while the search
- * runs: nothing else may use it meanwhile).  Synchronises `stream`, sets the
- * chosen plan on the layer and returns it in *out.  `times_ms`, if not NULL, receives {measured ms per step of the
- * chosen plan, number of candidates}.  An empty batch returns the unsplit
- * plan without running anything.  Errors: NF_ERR_INVALID_ARG for a null
- * argument, any error of nf_layer_step. */
+ * the abstract on the codewithpapers NanoFlow page (which has the search
+ * weigh the interference of concurrent operations), whose four dimensions
+ * the "Search Space" card of the do-not-panic NanoFlow page lists, and for
+ * the Gurobi-based solver of the ossradar Nanoflow page:
+ *  1. solo profiles: the batch run as 1..opts->max_count equal nano-batches
+ *     on one stream with every kernel timed, giving the nf_plan_profile
+ *     inputs (front, O-projection and FFN durations per nano-batch size,
+ *     attention per KV page unit, the per-operation gap);
+ *  2. interference: for each two-stream resource split -- all CUs to both
+ *     sides; attention held to 8 or 4 waves per CU; 16 + 16, 24 + 8 and
+ *     20 + 12 CUs per XCD -- two equal nano-batches run overlapped once,
+ *     giving that split's co-run slowdowns and cross-stream wait;
+ *  3. every candidate is predicted with the model of nf_plan_predict:
+ *     counts 1..max_count; sizes equal, attention-balanced, in 64-token
+ *     steps (two nano-batches), quarter / half / quarter (three), and the
+ *     decode requests apart from a trailing prefill chunk; the pipelined and
+ *     deep orders on two streams for each split, and one stream;
+ *  4. the `top_k` best predictions and the unsplit plan are timed with
+ *     `warmup` + `reps` steps, and the fastest is kept.
+ * Runs steps on this batch (so it writes batch->out); the pool pages holding
+ * the batch's new positions are copied aside before the first step and
+ * copied back before returning, so the pool ends bit-identical to how it was
+ * (it is not read-only while the search runs: nothing else may use it
+ * meanwhile).  Synchronises `stream`, sets the chosen plan on the layer and
+ * returns it in *out.  `times_ms`, if not NULL, receives {measured ms per
+ * step of the chosen plan, number of candidates predicted}.
+ * nf_plan_search_report returns the plans the last search on this layer ran
+ * (the calibration runs, then the timed candidates) with their predicted and
+ * measured ms per step: *n = their number, the first min(n, max) copied to
+ * the arrays (each may be NULL).  An empty batch returns the unsplit plan
+ * without running anything.  Errors: NF_ERR_INVALID_ARG for a null argument,
+ * NF_ERR_UNSUPPORTED with per-kernel timing on, any error of nf_layer_step. */
 nf_status nf_plan_search(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch,
                          const nf_search_opts* opts, nf_plan* out, double* times_ms,
                          void* stream);
+nf_status nf_plan_search_report(const nf_layer* layer, int32_t max, nf_plan* plans, double* predicted_ms,
+                                double* measured_ms, int32_t* n);
 
 /* ---- intermediates ----------------------------------------------------------
  * Device pointer and row stride (elements) of an intermediate of the last

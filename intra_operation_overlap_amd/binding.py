@@ -50,6 +50,17 @@ class nf_plan(ctypes.Structure):
                 ("gemm_cus_per_xcd", i32), ("attn_cus_per_xcd", i32), ("attn_waves_per_cu", i32)]
 
 
+NF_PROFILE_POINTS = 8
+
+
+class nf_plan_profile(ctypes.Structure):
+    _fields_ = [("n_points", i32), ("tokens", ctypes.c_double * NF_PROFILE_POINTS),
+                ("front_us", ctypes.c_double * NF_PROFILE_POINTS), ("oproj_us", ctypes.c_double * NF_PROFILE_POINTS),
+                ("ffn_us", ctypes.c_double * NF_PROFILE_POINTS), ("attn_base_us", ctypes.c_double),
+                ("attn_us_per_page", ctypes.c_double), ("gap_us", ctypes.c_double), ("slow_gemm", ctypes.c_double),
+                ("slow_attn", ctypes.c_double), ("wait_us", ctypes.c_double)]
+
+
 class nf_search_opts(ctypes.Structure):
     _fields_ = [("max_count", i32), ("warmup", i32), ("reps", i32), ("top_k", i32)]
 
@@ -78,6 +89,10 @@ _SIGS = {
     "nf_graph_destroy": (None, [vp]),
     "nf_plan_search": (i32, [vp, vp, ctypes.POINTER(nf_batch), ctypes.POINTER(nf_search_opts),
                              ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double), vp]),
+    "nf_plan_search_report": (i32, [vp, i32, ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
+    "nf_plan_predict": (i32, [ctypes.POINTER(nf_plan_profile), ctypes.POINTER(nf_shape), ctypes.POINTER(nf_plan),
+                              ctypes.POINTER(nf_batch), ctypes.POINTER(ctypes.c_double)]),
     "nf_layer_intermediate": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64)]),
     "nf_profile_enable": (i32, [vp, i32, ctypes.c_char_p]),
     "nf_profile_read": (i32, [vp, i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
@@ -219,6 +234,15 @@ class Layer:
                                    stream), "nf_plan_search")
         return p, (t[0], t[1])
 
+    def search_report(self, max_entries: int = 64):
+        """[(plan dict, predicted ms, measured ms)] of the last plan search."""
+        plans = (nf_plan * max_entries)()
+        pr = (ctypes.c_double * max_entries)()
+        me = (ctypes.c_double * max_entries)()
+        n = i32()
+        check(lib().nf_plan_search_report(self.h, max_entries, plans, pr, me, ctypes.byref(n)), "nf_plan_search_report")
+        return [(plan_dict(plans[i]), pr[i], me[i]) for i in range(min(n.value, max_entries))]
+
     def intermediate(self, which: int):
         ptr, stride = vp(), i64()
         check(lib().nf_layer_intermediate(self.h, which, ctypes.byref(ptr), ctypes.byref(stride)),
@@ -344,6 +368,14 @@ def kv_pool_export(pool: KVPool, k_dst, v_dst, pages=None, stream: int = 0) -> N
     a = None if pages is None else np.ascontiguousarray(np.asarray(pages, np.int32))
     check(lib().nf_kv_pool_export(pool.h, _i32p(a) if a is not None else None, n, k_dst.data_ptr(),
                                   v_dst.data_ptr(), stream), "nf_kv_pool_export")
+
+
+def plan_predict(profile: nf_plan_profile, shape: nf_shape, plan: nf_plan, hb: HostBatch) -> float:
+    """nf_plan_predict: the model's step time (microseconds), host only."""
+    us = ctypes.c_double()
+    check(lib().nf_plan_predict(ctypes.byref(profile), ctypes.byref(shape), ctypes.byref(plan), ctypes.byref(hb.c),
+                                ctypes.byref(us)), "nf_plan_predict")
+    return us.value
 
 
 def kv_pool_bytes(shape: nf_shape, n_pages: int, page_size: int):

@@ -104,6 +104,12 @@ size_t dtype_bytes(int dt) { return dt == NF_BF16 ? 2 : 4; }
 
 }  // namespace
 
+// a plan the last search timed: its predicted and measured ms per step
+struct SearchEntry {
+  nf_plan plan;
+  double predicted_ms, measured_ms;
+};
+
 struct nf_layer {
   nf_shape s{};
   nf_weights w{};
@@ -143,6 +149,7 @@ struct nf_layer {
   StepWork work;
   int last_T = 0;
   int attn_variant = -1;   // bf16 d=128 attention kernel: -1 chosen per step, 0 one-wave items, 1 four-wave items
+  std::vector<SearchEntry> search_report;   // the last plan search's timed plans
 };
 
 struct nf_kv_pool {
@@ -1622,15 +1629,26 @@ nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf
 
 // =============================================================== plan search
 // Profile-driven search over the four plan dimensions (count, sizes, order,
-// CU split) for one batch; replaces the pages' MILP-based parameter search
-// ("Search Space 4D" card on the do-not-panic NanoFlow page; Gurobi note on
-// the ossradar page).  Every candidate is timed on the device with this batch.
+// resource split) for one batch; it replaces the pages' MILP-based parameter
+// search ("Search Space 4D" card on the do-not-panic NanoFlow page; Gurobi
+// note on the ossradar page) and, like it, weighs the interference of
+// concurrent operations (abstract on the codewithpapers page).
+//  1. Solo profiles: the batch split into 1..max_count equal nano-batches on
+//     one stream, every kernel timed; per nano-batch size, the front (norm,
+//     QKV, RoPE), O-projection and FFN durations, and attention as a linear
+//     function of its KV page units.
+//  2. Interference: per two-stream resource split (GEMM / attention CUs per
+//     XCD, attention residency), one overlapped run of two equal nano-batches
+//     gives the co-run slowdown of each side and the cost of a cross-stream
+//     wait.
+//  3. The event-graph model (plan_model.cpp) predicts every candidate: counts
+//     1..max_count; sizes equal, attention-balanced, 64-token steps for two,
+//     quarter / half / quarter for three, decode requests apart from a
+//     prefill chunk; pipelined and deep orders; each resource split, and one
+//     stream.
+//  4. The top_k predictions and the unsplit plan are timed on the device;
+//     the fastest is kept.
 namespace {
-
-struct Cand {
-  nf_plan plan;
-  double ms = 0;
-};
 
 // Nano-batch boundaries that balance attention work (KV pages) plus GEMM rows.
 void balanced_sizes(const nf_batch* b, int count, int32_t* sizes) {
@@ -1655,7 +1673,49 @@ void balanced_sizes(const nf_batch* b, int count, int32_t* sizes) {
   }
 }
 
+// operation class of a kernel kind: 0 front, 1 attention, 2 O half, 3 FFN
+int kind_class(int k) {
+  switch (k) {
+    case K_NORM1: case K_QKV: case K_QKV_RED: case K_ROPE: return 0;
+    case K_ATTN: case K_MERGE: return 1;
+    case K_OPROJ: case K_OPROJ_RED: case K_NORM2: return 2;
+    default: return 3;
+  }
+}
+
+nf_plan make_plan(int count, const int32_t* sizes, int order, int streams, int g, int a, int w) {
+  nf_plan p{};
+  p.count = count;
+  for (int j = 0; j < count; ++j) p.sizes[j] = sizes[j];
+  p.order = order;
+  p.n_streams = streams;
+  p.gemm_cus_per_xcd = g;
+  p.attn_cus_per_xcd = a;
+  p.attn_waves_per_cu = w;
+  return p;
+}
+
+bool same_plan(const nf_plan& x, const nf_plan& y) {
+  if (x.count != y.count || x.order != y.order || x.n_streams != y.n_streams ||
+      x.gemm_cus_per_xcd != y.gemm_cus_per_xcd || x.attn_cus_per_xcd != y.attn_cus_per_xcd ||
+      x.attn_waves_per_cu != y.attn_waves_per_cu)
+    return false;
+  for (int j = 0; j < x.count; ++j)
+    if (x.sizes[j] != y.sizes[j]) return false;
+  return true;
+}
+
+struct Split {
+  int g, a, w;
+};
+// two-stream resource splits: every CU to both sides; attention held to 8 or
+// 4 waves per CU (persistent four-wave workgroups, GEMM tiles that fit beside
+// them); CU partitions per XCD
+const Split kSplits[] = {{0, 0, 0}, {0, 0, 8}, {0, 0, 4}, {16, 16, 0}, {24, 8, 0}, {20, 12, 0}};
+constexpr int kNSplits = sizeof(kSplits) / sizeof(kSplits[0]);
+
 }  // namespace
+
 
 extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_search_opts* o,
                                     nf_plan* out, double* times_ms, void* stream) {
@@ -1667,36 +1727,13 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
   opts.top_k = std::max(1, opts.top_k);
   hipStream_t s = (hipStream_t)stream;
   const int T = b->n_tokens;
+  const nf_plan unsplit = make_plan(1, &T, NF_ORDER_PIPELINED, 1, 0, 0, 0);
   if (T == 0) {
     *out = nf_plan{1, {0, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0, 0, 0};
     L->plan = *out;
     return NF_OK;
   }
-
-  // candidate grid over the four plan dimensions
-  std::vector<Cand> cands;
-  const nf_plan base{1, {T, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0, 0, 0};
-  cands.push_back({base});
-  struct Split { int g, a, w; };
-  const Split splits[] = {{0, 0, 0}, {0, 0, 4}, {0, 24, 0}, {16, 16, 0}, {20, 12, 0}, {24, 8, 0}};
-  for (int k = 2; k <= opts.max_count && k <= T; ++k) {
-    nf_plan eq = base, bal = base;
-    eq.count = bal.count = k;
-    for (int j = 0; j < k; ++j) eq.sizes[j] = T / k + (j < T % k ? 1 : 0);
-    balanced_sizes(b, k, bal.sizes);
-    for (const nf_plan& pz : {eq, bal}) {
-      cands.push_back({pz});                      // split, one stream
-      for (const Split& sp : splits) {
-        if (sp.g >= L->cus_per_xcd || sp.a >= L->cus_per_xcd) continue;
-        nf_plan c = pz;
-        c.n_streams = 2;
-        c.gemm_cus_per_xcd = sp.g;
-        c.attn_cus_per_xcd = sp.a;
-        c.attn_waves_per_cu = sp.w;
-        cands.push_back({c});
-      }
-    }
-  }
+  if (L->prof) return set_err(NF_ERR_UNSUPPORTED, "nf_plan_search: per-kernel timing is on");
 
   // The candidates are timed on this batch, whose steps write K/V into the
   // pool pages holding its new positions.  Those pages are saved first and
@@ -1719,79 +1756,234 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
   const size_t list_bytes = ((saved.size() * 4) + 255) & ~(size_t)255;
   struct Backup {
     void* p = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
     ~Backup() {
       if (p) (void)hipFree(p);
+      if (e0) (void)hipEventDestroy(e0);
+      if (e1) (void)hipEventDestroy(e1);
     }
-  } backup;
+  } bk;
   HIP_TRY(hipSetDevice(L->device));
-  HIP_TRY(hipMalloc(&backup.p, list_bytes + 2 * saved.size() * (size_t)P->block_bytes));
-  int32_t* d_saved = (int32_t*)backup.p;
-  char* bk = (char*)backup.p + list_bytes;
-  char* bv = bk + saved.size() * (size_t)P->block_bytes;
+  HIP_TRY(hipMalloc(&bk.p, list_bytes + 2 * saved.size() * (size_t)P->block_bytes));
+  int32_t* d_saved = (int32_t*)bk.p;
+  char* bkk = (char*)bk.p + list_bytes;
+  char* bkv = bkk + saved.size() * (size_t)P->block_bytes;
   HIP_TRY(hipMemcpyAsync(d_saved, saved.data(), saved.size() * 4, hipMemcpyHostToDevice, s));
-  HIP_TRY(kv_gather(P->k, P->v, d_saved, (int)saved.size(), P->block_bytes, bk, bv, s));
-  auto restore = [&]() -> hipError_t {
-    hipError_t e = kv_scatter(P->k, P->v, d_saved, (int)saved.size(), P->block_bytes, bk, bv, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    return e;
-  };
+  HIP_TRY(kv_gather(P->k, P->v, d_saved, (int)saved.size(), P->block_bytes, bkk, bkv, s));
+  HIP_TRY(hipEventCreate(&bk.e0));
+  HIP_TRY(hipEventCreate(&bk.e1));
+  const bool verbose = std::getenv("NF_SEARCH_VERBOSE") != nullptr;
 
-  hipEvent_t e0, e1;
-  HIP_TRY(hipEventCreate(&e0));
-  HIP_TRY(hipEventCreate(&e1));
-  auto measure = [&](Cand& c, int warm, int reps) -> nf_status {
+  // ms per step of `plan`: `warm` untimed steps, then `reps` between events
+  auto measure = [&](const nf_plan& plan, int warm, int reps, double& ms) -> nf_status {
     nf_status st = NF_OK;
-    for (int w = 0; w < warm && st == NF_OK; ++w) st = step_impl(L, P, b, s, c.plan);
+    for (int w = 0; w < warm && st == NF_OK; ++w) st = step_impl(L, P, b, s, plan);
     if (st != NF_OK) return st;
-    HIP_TRY(hipEventRecord(e0, s));
-    for (int r = 0; r < reps && st == NF_OK; ++r) st = step_impl(L, P, b, s, c.plan);
-    HIP_TRY(hipEventRecord(e1, s));
-    HIP_TRY(hipEventSynchronize(e1));
+    HIP_TRY(hipEventRecord(bk.e0, s));
+    for (int r = 0; r < reps && st == NF_OK; ++r) st = step_impl(L, P, b, s, plan);
+    HIP_TRY(hipEventRecord(bk.e1, s));
+    HIP_TRY(hipEventSynchronize(bk.e1));
     if (st != NF_OK) return st;
-    float ms = 0;
-    HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
-    c.ms = ms / reps;
+    float t = 0;
+    HIP_TRY(hipEventElapsedTime(&t, bk.e0, bk.e1));
+    ms = t / reps;
     return NF_OK;
   };
-  // stage 1: every candidate, briefly (after a few steps of the unsplit plan,
-  // so that the first candidate does not pay for clocks ramping up or
-  // first-use allocations); stage 2: the top_k and the unsplit plan again,
-  // longer
+  // per-step microseconds of each operation class over `reps` profiled steps
+  auto classes = [&](const nf_plan& plan, int reps, double* cls) -> nf_status {
+    nf_status st = nf_profile_enable(L, 1, nullptr);
+    for (int r = 0; r < reps && st == NF_OK; ++r) st = step_impl(L, P, b, s, plan);
+    if (st != NF_OK) {
+      (void)nf_profile_enable(L, 0, nullptr);
+      return st;
+    }
+    for (auto& rec : L->recs) {
+      HIP_TRY(hipEventSynchronize(rec.b));
+      float ms = 0;
+      HIP_TRY(hipEventElapsedTime(&ms, rec.a, rec.b));
+      L->prof_ms[rec.kind] += ms;
+    }
+    for (int c = 0; c < 4; ++c) cls[c] = 0;
+    for (int k = 0; k < K_COUNT; ++k) cls[kind_class(k)] += L->prof_ms[k] * 1e3 / reps;
+    return nf_profile_enable(L, 0, nullptr);
+  };
+
   nf_status st = NF_OK;
-  {
-    Cand warm{base};
-    st = measure(warm, 3, 1);
-  }
-  for (Cand& c : cands) {
+  nf_plan_profile prof{};
+  std::vector<SearchEntry> report, timed;      // calibration runs; candidates timed in step 4
+  std::vector<std::pair<nf_plan, double>> preds;
+  do {
+    // 1. solo profiles on one stream
+    double gap_sum = 0;
+    int gap_n = 0;
+    std::vector<std::pair<double, double>> att;     // (page units per nano-batch, us per launch)
+    const int kmax = std::min(opts.max_count, T);
+    prof.n_points = kmax;
+    double solo2[4] = {0, 0, 0, 0};
+    for (int k = 1; k <= kmax && st == NF_OK; ++k) {
+      int32_t sz[NF_MAX_NANO];
+      for (int j = 0; j < k; ++j) sz[j] = T / k + (j < T % k ? 1 : 0);
+      const nf_plan pl = make_plan(k, sz, NF_ORDER_SEQUENTIAL, 1, 0, 0, 0);
+      double ms = 0, cls[4];
+      if ((st = measure(pl, k == 1 ? 3 : 1, 3, ms)) != NF_OK) break;
+      if ((st = classes(pl, 2, cls)) != NF_OK) break;
+      const int i = kmax - k;                  // ascending nano-batch size
+      prof.tokens[i] = (double)T / k;
+      prof.front_us[i] = cls[0] / k;
+      prof.oproj_us[i] = cls[2] / k;
+      prof.ffn_us[i] = cls[3] / k;
+      if (k == 2) std::copy(cls, cls + 4, solo2);
+      double units[NF_MAX_NANO];
+      attn_page_units(L->s, *b, pl, units);
+      double u = 0;
+      for (int j = 0; j < k; ++j) u += units[j];
+      att.push_back({u / k, cls[1] / k});
+      gap_sum += std::max(0.0, ms * 1e3 - (cls[0] + cls[1] + cls[2] + cls[3])) / (4.0 * k);
+      ++gap_n;
+    }
     if (st != NF_OK) break;
-    st = measure(c, 1, 2);
-  }
-  std::vector<Cand> top;
-  if (st == NF_OK) {
-    const Cand unsplit = cands[0];
-    std::stable_sort(cands.begin(), cands.end(), [](const Cand& x, const Cand& y) { return x.ms < y.ms; });
-    top.assign(cands.begin(), cands.begin() + std::min<size_t>(cands.size(), opts.top_k));
-    bool has_unsplit = false;
-    for (const Cand& c : top) has_unsplit = has_unsplit || (c.plan.count == 1 && c.plan.n_streams == 1);
-    if (!has_unsplit) top.push_back(unsplit);
-    for (Cand& c : top) {
-      const double quick = c.ms;
-      if ((st = measure(c, opts.warmup, opts.reps)) != NF_OK) break;
-      if (std::getenv("NF_SEARCH_VERBOSE")) {
-        const nf_plan& q = c.plan;
-        std::fprintf(stderr,
-                     "nf search: count %d sizes %d/%d/%d/%d streams %d cus/xcd gemm %2d attn %2d waves %d -> %.3f ms "
-                     "(first pass %.3f)\n",
-                     q.count, q.sizes[0], q.sizes[1], q.sizes[2], q.sizes[3], q.n_streams, q.gemm_cus_per_xcd,
-                     q.attn_cus_per_xcd, q.attn_waves_per_cu, c.ms, quick);
+    prof.gap_us = gap_n ? gap_sum / gap_n : 0;
+    if (att.size() >= 2) {          // least squares: us = base + slope * units
+      double sx = 0, sy = 0, sxx = 0, sxy = 0;
+      for (auto& q : att) {
+        sx += q.first;
+        sy += q.second;
+        sxx += q.first * q.first;
+        sxy += q.first * q.second;
+      }
+      const double n = (double)att.size(), den = n * sxx - sx * sx;
+      prof.attn_us_per_page = den > 0 ? std::max(0.0, (n * sxy - sx * sy) / den) : 0;
+      prof.attn_base_us = std::max(0.0, (sy - prof.attn_us_per_page * sx) / n);
+    } else {
+      prof.attn_base_us = 0;
+      prof.attn_us_per_page = att[0].first > 0 ? att[0].second / att[0].first : 0;
+    }
+    prof.slow_gemm = prof.slow_attn = 1;
+    prof.wait_us = 0;
+    if (verbose)
+      std::fprintf(stderr, "nf search: solo fronts %.1f..%.1f us, attention %.2f + %.5f us/page unit, gap %.1f us\n",
+                   prof.front_us[0], prof.front_us[kmax - 1], prof.attn_base_us, prof.attn_us_per_page,
+                   prof.gap_us);
+
+    // 2. interference per two-stream resource split
+    nf_plan_profile calib[kNSplits];
+    bool calib_ok[kNSplits] = {};
+    if (kmax >= 2) {
+      int32_t sz2[2] = {T - T / 2, T / 2};
+      for (int c = 0; c < kNSplits && st == NF_OK; ++c) {
+        const Split& sp = kSplits[c];
+        if (sp.g >= L->cus_per_xcd || sp.a >= L->cus_per_xcd) continue;
+        const nf_plan pl = make_plan(2, sz2, NF_ORDER_PIPELINED, 2, sp.g, sp.a, sp.w);
+        double ms = 0, cls[4];
+        if ((st = measure(pl, 1, 3, ms)) != NF_OK) break;
+        if ((st = classes(pl, 2, cls)) != NF_OK) break;
+        nf_plan_profile q = prof;
+        q.slow_attn = std::max(1.0, solo2[1] > 0 ? cls[1] / solo2[1] : 1.0);
+        const double g_ov = cls[0] + cls[2] + cls[3], g_solo = solo2[0] + solo2[2] + solo2[3];
+        const double frac = cls[1] > 0 ? std::min(0.95, std::max(0.0, (g_ov - g_solo) / cls[1])) : 0.0;
+        q.slow_gemm = 1.0 / (1.0 - frac);
+        double tok[2] = {(double)sz2[0], (double)sz2[1]}, units[NF_MAX_NANO];
+        attn_page_units(L->s, *b, pl, units);
+        const double pred0 = predict_plan_us(q, pl, tok, units);
+        q.wait_us = std::isfinite(pred0) ? std::max(0.0, (ms * 1e3 - pred0) / 4.0) : 0.0;
+        calib[c] = q;
+        calib_ok[c] = true;
+        report.push_back({pl, predict_plan_us(q, pl, tok, units) * 1e-3, ms});
+        if (verbose)
+          std::fprintf(stderr, "nf search: split gemm %d attn %d waves %d: slowdown gemm %.2f attn %.2f, wait %.1f us "
+                       "(two nano-batches %.3f ms)\n", sp.g, sp.a, sp.w, q.slow_gemm, q.slow_attn, q.wait_us, ms);
       }
     }
-  }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
+    if (st != NF_OK) break;
+
+    // 3. candidates, predicted
+    std::vector<std::vector<int32_t>> sizes;
+    auto add_sizes = [&](std::vector<int32_t> v) {
+      int64_t sum = 0;
+      for (int32_t x : v) {
+        if (x <= 0) return;
+        sum += x;
+      }
+      if (sum != T || (int)v.size() > kmax) return;
+      for (auto& w : sizes)
+        if (w == v) return;
+      sizes.push_back(v);
+    };
+    add_sizes({T});
+    // the decode requests apart from a trailing prefill chunk
+    int dec = 0;
+    for (int r = 0; r < b->n_requests; ++r)
+      if (b->req_q_len[r] == 1) dec = b->req_q_start[r] + 1;
+    const bool chunk_last = b->n_requests > 0 && b->req_q_len[b->n_requests - 1] > 1 && dec > 0 &&
+                            dec == b->req_q_start[b->n_requests - 1];
+    for (int k = 2; k <= kmax; ++k) {
+      std::vector<int32_t> eq(k), bal(k);
+      for (int j = 0; j < k; ++j) eq[j] = T / k + (j < T % k ? 1 : 0);
+      balanced_sizes(b, k, bal.data());
+      add_sizes(eq);
+      add_sizes(bal);
+      if (chunk_last) {
+        std::vector<int32_t> v(k);
+        const int nd = k - 1;
+        for (int j = 0; j < nd; ++j) v[j] = dec / nd + (j < dec % nd ? 1 : 0);
+        v[k - 1] = T - dec;
+        add_sizes(v);
+      }
+    }
+    if (kmax >= 2)
+      for (int f = 64; f < T; f += 64) add_sizes({f, T - f});
+    if (kmax >= 3) {
+      const int q = std::max(64, 64 * ((T / 4 + 32) / 64));
+      add_sizes({q, T - 2 * q, q});
+    }
+    for (auto& v : sizes) {
+      const int k = (int)v.size();
+      double tok[NF_MAX_NANO], units[NF_MAX_NANO];
+      for (int j = 0; j < k; ++j) tok[j] = v[j];
+      const nf_plan one = make_plan(k, v.data(), NF_ORDER_SEQUENTIAL, 1, 0, 0, 0);
+      attn_page_units(L->s, *b, one, units);
+      preds.push_back({k == 1 ? unsplit : one, predict_plan_us(prof, one, tok, units)});
+      if (k == 1) continue;
+      for (int c = 0; c < kNSplits; ++c) {
+        if (!calib_ok[c]) continue;
+        for (int order : {NF_ORDER_PIPELINED, NF_ORDER_DEEP}) {
+          const nf_plan pl = make_plan(k, v.data(), order, 2, kSplits[c].g, kSplits[c].a, kSplits[c].w);
+          preds.push_back({pl, predict_plan_us(calib[c], pl, tok, units)});
+        }
+      }
+    }
+    std::stable_sort(preds.begin(), preds.end(), [](const std::pair<nf_plan, double>& x,
+                                                    const std::pair<nf_plan, double>& y) { return x.second < y.second; });
+
+    // 4. the best predictions and the unsplit plan, timed
+    std::vector<std::pair<nf_plan, double>> top;
+    for (auto& pr : preds) {
+      if ((int)top.size() >= opts.top_k) break;
+      top.push_back(pr);
+    }
+    bool has_unsplit = false;
+    for (auto& t : top) has_unsplit = has_unsplit || same_plan(t.first, unsplit);
+    if (!has_unsplit)
+      for (auto& pr : preds)
+        if (same_plan(pr.first, unsplit)) top.push_back(pr);
+    for (auto& t : top) {
+      double ms = 0;
+      if ((st = measure(t.first, opts.warmup, opts.reps, ms)) != NF_OK) break;
+      timed.push_back({t.first, t.second * 1e-3, ms});
+      if (verbose) {
+        const nf_plan& q = t.first;
+        std::fprintf(stderr, "nf search: count %d sizes %d/%d/%d/%d order %d streams %d cus/xcd gemm %2d attn %2d "
+                     "waves %d: predicted %.3f ms, measured %.3f ms\n", q.count, q.sizes[0], q.sizes[1], q.sizes[2],
+                     q.sizes[3], q.order, q.n_streams, q.gemm_cus_per_xcd, q.attn_cus_per_xcd, q.attn_waves_per_cu,
+                     t.second * 1e-3, ms);
+      }
+    }
+  } while (false);
+
   {
     const std::string step_err = g_err;
-    const hipError_t re = restore();
+    hipError_t re = kv_scatter(P->k, P->v, d_saved, (int)saved.size(), P->block_bytes, bkk, bkv, s);
+    if (re == hipSuccess) re = hipStreamSynchronize(s);
     if (re != hipSuccess) {
       (void)hipGetLastError();
       return set_err(NF_ERR_HIP, "nf_plan_search: restoring the pool's pages failed: %s", hipGetErrorString(re));
@@ -1799,15 +1991,48 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
     g_err = step_err;
   }
   if (st != NF_OK) return st;
-  int best = 0;
-  for (size_t i = 1; i < top.size(); ++i)
-    if (top[i].ms < top[best].ms) best = (int)i;
+  // the fastest of the timed candidates (the calibration runs used fewer steps)
+  int best = -1;
+  for (size_t i = 0; i < timed.size(); ++i)
+    if (best < 0 || timed[i].measured_ms < timed[best].measured_ms) best = (int)i;
+  if (best < 0) return set_err(NF_ERR_NO_PLAN, "nf_plan_search: no candidate was timed");
   if (times_ms) {
-    times_ms[0] = top[best].ms;
-    times_ms[1] = cands.empty() ? 0 : (double)cands.size();
+    times_ms[0] = timed[best].measured_ms;
+    times_ms[1] = (double)preds.size();
   }
-  L->plan = top[best].plan;
-  *out = top[best].plan;
+  L->plan = timed[best].plan;
+  *out = timed[best].plan;
+  report.insert(report.end(), timed.begin(), timed.end());
+  L->search_report = report;
+  return NF_OK;
+}
+
+extern "C" nf_status nf_plan_search_report(const nf_layer* L, int32_t max, nf_plan* plans, double* predicted_ms,
+                                           double* measured_ms, int32_t* n) {
+  if (!L || !n || max < 0) return set_err(NF_ERR_INVALID_ARG, "nf_plan_search_report: bad argument");
+  const std::vector<SearchEntry>& r = L->search_report;
+  *n = (int32_t)r.size();
+  for (int i = 0; i < (int)r.size() && i < max; ++i) {
+    if (plans) plans[i] = r[i].plan;
+    if (predicted_ms) predicted_ms[i] = r[i].predicted_ms;
+    if (measured_ms) measured_ms[i] = r[i].measured_ms;
+  }
+  return NF_OK;
+}
+
+extern "C" nf_status nf_plan_predict(const nf_plan_profile* prof, const nf_shape* shape, const nf_plan* plan,
+                                     const nf_batch* batch, double* us) {
+  if (!prof || !shape || !plan || !batch || !us || prof->n_points < 1 || prof->n_points > NF_PROFILE_POINTS)
+    return set_err(NF_ERR_INVALID_ARG, "nf_plan_predict: bad argument");
+  std::string err;
+  nf_status st = check_plan(*plan, 32, err);
+  if (st == NF_OK) st = check_plan_batch(*plan, batch->n_tokens, err);
+  if (st != NF_OK) return set_err(st, "%s", err.c_str());
+  double tok[NF_MAX_NANO], units[NF_MAX_NANO];
+  const int k = plan->count;
+  for (int j = 0; j < k; ++j) tok[j] = (k == 1 && plan->sizes[0] == 0) ? batch->n_tokens : plan->sizes[j];
+  attn_page_units(*shape, *batch, *plan, units);
+  *us = predict_plan_us(*prof, *plan, tok, units);
   return NF_OK;
 }
 

@@ -10,6 +10,9 @@
 
 namespace nf {
 
+// Stores `msg` as the calling thread's nf_last_error() text; returns st.
+nf_status set_error(nf_status st, const char* msg);
+
 // One attention work item: query tokens tok0 .. tok0+ntok-1 of request `req`,
 // keys of its logical pages page_begin .. page_end-1; the result goes straight
 // to the attention output (partial < 0) or to partial slot `partial`.
@@ -58,5 +61,11 @@ nf_status check_plan_batch(const nf_plan& p, int n_tokens, std::string& err);
 // pages (0: no cap).  Split pieces write partials merged by a later kernel.
 void build_work(const nf_shape& s, const nf_batch& b, const nf_plan& p, int page_size, int target_items,
                 int min_split_pages, int max_item_pages, StepWork& w);
+
+// Step-time model of a plan (plan_model.cpp).  tokens[j] / pages[j]: the
+// tokens and the attention page units (work items x KV pages) of nano-batch j.
+double predict_plan_us(const nf_plan_profile& p, const nf_plan& plan, const double* tokens, const double* pages);
+// Attention page units of each nano-batch of `plan` on batch `b`.
+void attn_page_units(const nf_shape& sh, const nf_batch& b, const nf_plan& plan, double* units);
 
 }  // namespace nf

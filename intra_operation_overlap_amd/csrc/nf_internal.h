@@ -8,9 +8,6 @@
 
 namespace nf {
 
-// Stores `msg` as the calling thread's nf_last_error() text; returns st.
-nf_status set_error(nf_status st, const char* msg);
-
 // Kernel timing without marker packets: when the calling thread's timer holds
 // two events, the next kernel launched through launch() records its own start
 // and end into them (hipExtLaunchKernel), and the timer is cleared.

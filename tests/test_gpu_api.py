@@ -36,6 +36,11 @@ def test_plan_search_returns_a_valid_plan_that_matches_the_oracle(small):
     assert 1 <= plan.count <= 3 and sum(list(plan.sizes)[:plan.count]) == T
     assert ms > 0 and n_cands >= 1
     assert B.plan_dict(small.layer.get_plan()) == B.plan_dict(plan)
+    rep = small.layer.search_report()
+    GH.log("search report: " + "; ".join(f"{d} predicted {p:.3f} measured {m:.3f}" for d, p, m in rep))
+    assert any(d == B.plan_dict(plan) for d, _, _ in rep)
+    assert all(p > 0 and m > 0 for _, p, m in rep)
+    assert min(m for d, _, m in rep if d == B.plan_dict(plan)) == pytest.approx(ms)
     _full_check(small, "searched", plan)
 
 

@@ -1,0 +1,93 @@
+"""The plan search's step-time model (nf_plan_predict, host only) against
+timelines worked out by hand: one stream adds every operation; two streams
+follow the dependency chain F -> A -> O -> N of each nano-batch, pay the
+cross-stream wait on A's and O's inputs, and progress at the co-run rates
+while both run."""
+import numpy as np
+import pytest
+
+from intra_operation_overlap_amd import binding as B
+from intra_operation_overlap_amd import workload as W
+
+
+def _profile(front=10.0, oproj=5.0, ffn=30.0, attn=50.0, gap=0.0, slow_g=1.0, slow_a=1.0, wait=0.0):
+    p = B.nf_plan_profile()
+    p.n_points = 2
+    p.tokens[0], p.tokens[1] = 1.0, 100000.0
+    for arr, v in ((p.front_us, front), (p.oproj_us, oproj), (p.ffn_us, ffn)):
+        arr[0] = arr[1] = v            # flat in the nano-batch size
+    p.attn_base_us, p.attn_us_per_page = attn, 0.0
+    p.gap_us, p.slow_gemm, p.slow_attn, p.wait_us = gap, slow_g, slow_a, wait
+    return p
+
+
+def _setup():
+    wl = W.WORKLOADS["c1"]
+    batch = W.make_batch(wl)
+    shape = B.make_shape(wl.shape, 64, 512)
+    return batch, shape, B.HostBatch(batch, 0x1000, 0x2000)
+
+
+def _predict(p, plan):
+    _, shape, hb = _setup()
+    return B.plan_predict(p, shape, plan, hb)
+
+
+def test_one_stream_adds_every_operation():
+    T = 16
+    assert _predict(_profile(gap=1.0), B.make_plan(1, [T])) == pytest.approx(10 + 50 + 5 + 30 + 4)
+    for order in (B.NF_ORDER_PIPELINED, B.NF_ORDER_SEQUENTIAL, B.NF_ORDER_DEEP):
+        assert _predict(_profile(), B.make_plan(2, [8, 8], order=order)) == pytest.approx(2 * 95)
+        assert _predict(_profile(), B.make_plan(4, [4, 4, 4, 4], order=order)) == pytest.approx(4 * 95)
+
+
+def test_two_streams_pipelined_critical_path():
+    plan = B.make_plan(2, [8, 8], n_streams=2)
+    # F0 0-10; A0 10-60 beside F1 10-20; O0 60-65; N0 65-95; A1 60-110; O1 110-115; N1 115-145
+    assert _predict(_profile(), plan) == pytest.approx(145)
+    # a 3 us wait on each cross-stream edge: A0 13-63, O0 66-71, N0 71-101, A1 63-113, O1 116-121, N1 121-151
+    assert _predict(_profile(wait=3.0), plan) == pytest.approx(151)
+
+
+def test_two_streams_co_run_rates():
+    # both sides at half speed while both run:
+    # F0 0-10; F1 beside A0 10-30 (A0 has 40 left); A0 30-70; O0 beside A1 70-80 (A1 45 left);
+    # N0 beside A1 80-140 (A1 15 left); A1 140-155; O1 155-160; N1 160-190
+    plan = B.make_plan(2, [8, 8], n_streams=2)
+    assert _predict(_profile(slow_g=2.0, slow_a=2.0), plan) == pytest.approx(190)
+
+
+def test_deep_order_two_streams():
+    # two: G issues F0 | F1 O0 | O1 N0 | N1
+    # F0 0-10; F1 10-20; A0 10-60; O0 60-65; A1 60-110; O1 110-115; N0 115-145; N1 145-175
+    plan = B.make_plan(2, [8, 8], order=B.NF_ORDER_DEEP, n_streams=2)
+    assert _predict(_profile(), plan) == pytest.approx(175)
+    # three: G issues F0 | F1 O0 | F2 O1 N0 | O2 N1 | N2 with A on its own stream
+    # F0 0-10; F1 10-20; A0 10-60; O0 60-65; F2 65-75; A1 60-110; O1 110-115; N0 115-145;
+    # A2 110-160; O2 160-165; N1 165-195; N2 195-225
+    plan3 = B.make_plan(3, [6, 5, 5], order=B.NF_ORDER_DEEP, n_streams=2)
+    assert _predict(_profile(), plan3) == pytest.approx(225)
+
+
+def test_sizes_interpolate_and_attention_follows_page_units():
+    batch, shape, hb = _setup()
+    p = _profile()
+    p.tokens[0], p.tokens[1] = 8.0, 16.0
+    p.front_us[0], p.front_us[1] = 10.0, 30.0           # 20 us more per 8 tokens
+    p.attn_base_us, p.attn_us_per_page = 0.0, 1.0
+    # decode requests: one work item each, over the pages holding positions 0..pos0
+    units = sum((int(batch.req_pos0[r]) + 16) // 16 for r in range(batch.n_requests))
+    got = B.plan_predict(p, shape, B.make_plan(1, [16]), hb)
+    assert got == pytest.approx(30 + units + 5 + 30)
+    got12 = B.plan_predict(p, shape, B.make_plan(2, [12, 4]), hb)
+    assert got12 == pytest.approx((20 + 5 + 30) + (0 + 5 + 30) + units)   # 4 tokens: extrapolated to 0, floored
+
+
+def test_predict_rejects_bad_arguments():
+    batch, shape, hb = _setup()
+    p = _profile()
+    p.n_points = 0
+    with pytest.raises(B.NfError):
+        B.plan_predict(p, shape, B.make_plan(1, [16]), hb)
+    with pytest.raises(B.NfError):
+        B.plan_predict(_profile(), shape, B.make_plan(2, [8, 9]), hb)
