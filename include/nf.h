@@ -313,6 +313,55 @@ nf_status nf_batch_validate(const nf_shape* shape, int32_t n_pages, int32_t page
  * one layer must not overlap on different host threads. */
 nf_status nf_layer_step(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch, void* stream);
 
+/* ---- serving loop ----------------------------------------------------------
+ * The asynchronous CPU control flow around nf_layer_step: batch formation,
+ * KV page management and retirement of finished requests, which the ossradar
+ * Nanoflow README ("Introduction") measures at over a tenth of inference time
+ * when done in step with the device, and which the hysenlabs page ("The
+ * failure modes the design accepts") has the host run one iteration ahead.
+ * A loop owns a layer's pool pages (all of them, through a free list) and
+ * serves requests added with nf_loop_add_request: rows_in holds the input row
+ * of each position 0 .. max_len-1 (the prompt, then the rows fed back for
+ * generated positions), rows_out receives the layer's output row for every
+ * position processed (both device [max_len][H] in the layer dtype,
+ * 16-byte aligned, caller-owned, valid until the loop is destroyed).  Each
+ * iteration schedules one token per request past its prompt and then chunks
+ * of prompts (at most max_prefill_tokens prompt tokens, max_tokens in all),
+ * runs the layer with its plan (its nano-batch count spread evenly over the
+ * batch), copies the outputs and writes, per token, whether out[t][0] >
+ * eos_threshold into pinned host memory.  A position at or past
+ * prompt_len - 1 whose flag is set ends its request, as does its last
+ * position.  Requests are admitted in order once the free pages hold their
+ * whole max_len.  async = 1: iteration i + 1 is formed (pages allocated) and
+ * launched before iteration i's flags are read, and requests that ended at i
+ * retire when i + 2 is formed (one more token each, counted as wasted);
+ * async = 0: the flags are read after every iteration.  nf_loop_run returns
+ * when every request has ended; nf_loop_request_length gives the number of
+ * positions up to and including a request's end (-1 while it runs).  The
+ * layer must be dense; calls on one loop must not overlap, nor steps on its
+ * layer and pool.  Errors: NF_ERR_INVALID_ARG, NF_ERR_OUT_OF_RANGE (a request
+ * longer than the pool), NF_ERR_HIP, any error of nf_layer_step. */
+typedef struct nf_loop nf_loop;
+typedef struct nf_loop_opts {
+  int32_t max_tokens;           /* tokens per iteration, 1 .. layer max_tokens */
+  int32_t max_prefill_tokens;   /* prompt tokens per iteration                  */
+  int32_t async;                /* 1: read flags one iteration late           */
+  float eos_threshold;          /* a position ends its request when out[t][0] > this */
+} nf_loop_opts;
+typedef struct nf_loop_stats {
+  int32_t iterations, finished;
+  int64_t tokens;               /* token positions processed                 */
+  int64_t wasted_tokens;        /* of those, after their request had ended    */
+  double host_us;               /* host time forming, launching, retiring     */
+  double wall_us;               /* wall time of nf_loop_run                   */
+} nf_loop_stats;
+nf_status nf_loop_create(nf_layer* layer, nf_kv_pool* pool, const nf_loop_opts* opts, nf_loop** out);
+nf_status nf_loop_add_request(nf_loop* loop, int32_t prompt_len, int32_t max_len, const void* rows_in,
+                              void* rows_out, int32_t* id);
+nf_status nf_loop_run(nf_loop* loop, void* stream, nf_loop_stats* stats);
+nf_status nf_loop_request_length(const nf_loop* loop, int32_t id, int32_t* length);
+void nf_loop_destroy(nf_loop* loop);   /* waits for the device */
+
 /* ---- multi-layer step -------------------------------------------------------
  * Runs layers[0..n_layers-1] in order on one batch, each with its own KV pool
  * (pools[l] created for layers[l]): batch->x is layer 0's input, each layer

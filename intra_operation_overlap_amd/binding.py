@@ -61,6 +61,15 @@ class nf_plan_profile(ctypes.Structure):
                 ("slow_attn", ctypes.c_double), ("wait_us", ctypes.c_double)]
 
 
+class nf_loop_opts(ctypes.Structure):
+    _fields_ = [("max_tokens", i32), ("max_prefill_tokens", i32), ("async_", i32), ("eos_threshold", ctypes.c_float)]
+
+
+class nf_loop_stats(ctypes.Structure):
+    _fields_ = [("iterations", i32), ("finished", i32), ("tokens", i64), ("wasted_tokens", i64),
+                ("host_us", ctypes.c_double), ("wall_us", ctypes.c_double)]
+
+
 class nf_search_opts(ctypes.Structure):
     _fields_ = [("max_count", i32), ("warmup", i32), ("reps", i32), ("top_k", i32)]
 
@@ -84,6 +93,11 @@ _SIGS = {
                                     ctypes.POINTER(vp)]),
     "nf_graph_launch": (i32, [vp, vp]),
     "nf_kv_offload": (i32, [vp, P_i32, i32, vp, vp, vp]),
+    "nf_loop_create": (i32, [vp, vp, ctypes.POINTER(nf_loop_opts), ctypes.POINTER(vp)]),
+    "nf_loop_add_request": (i32, [vp, i32, i32, vp, vp, P_i32]),
+    "nf_loop_run": (i32, [vp, vp, ctypes.POINTER(nf_loop_stats)]),
+    "nf_loop_request_length": (i32, [vp, i32, P_i32]),
+    "nf_loop_destroy": (None, [vp]),
     "nf_kv_pool_import": (i32, [vp, P_i32, i32, vp, vp, vp]),
     "nf_kv_pool_export": (i32, [vp, P_i32, i32, vp, vp, vp]),
     "nf_graph_destroy": (None, [vp]),
@@ -302,6 +316,46 @@ class KVPool:
     def close(self):
         if self.h:
             lib().nf_kv_pool_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Loop:
+    """nf_loop over a layer and a pool (the requests' row tensors are kept referenced)."""
+
+    def __init__(self, layer: Layer, pool: KVPool, max_tokens: int, max_prefill_tokens: int, async_: bool,
+                 eos_threshold: float):
+        self._keep = [layer, pool]
+        h = vp()
+        o = nf_loop_opts(max_tokens, max_prefill_tokens, 1 if async_ else 0, eos_threshold)
+        check(lib().nf_loop_create(layer.h, pool.h, ctypes.byref(o), ctypes.byref(h)), "nf_loop_create")
+        self.h = h
+
+    def add(self, prompt_len: int, rows_in, rows_out) -> int:
+        self._keep += [rows_in, rows_out]
+        rid = i32()
+        check(lib().nf_loop_add_request(self.h, prompt_len, int(rows_in.shape[0]), rows_in.data_ptr(),
+                                        rows_out.data_ptr(), ctypes.byref(rid)), "nf_loop_add_request")
+        return rid.value
+
+    def run(self, stream: int = 0) -> dict:
+        st = nf_loop_stats()
+        check(lib().nf_loop_run(self.h, stream, ctypes.byref(st)), "nf_loop_run")
+        return {k: getattr(st, k) for k, _ in nf_loop_stats._fields_}
+
+    def length(self, rid: int) -> int:
+        n = i32()
+        check(lib().nf_loop_request_length(self.h, rid, ctypes.byref(n)), "nf_loop_request_length")
+        return n.value
+
+    def close(self):
+        if self.h:
+            lib().nf_loop_destroy(self.h)
             self.h = None
 
     def __del__(self):

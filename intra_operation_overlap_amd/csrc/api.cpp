@@ -1339,6 +1339,21 @@ nf_status nf_layer_set_allreduce_emulation(nf_layer* L, int32_t mode, int32_t co
   return NF_OK;
 }
 
+}  // extern "C"
+
+const nf_shape* nf::layer_shape(const nf_layer* L) { return &L->s; }
+nf_plan nf::layer_plan(const nf_layer* L) { return L->plan; }
+int32_t nf::pool_pages(const nf_kv_pool* P) { return P->n_pages; }
+nf_status nf::layer_step_with_plan(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t s, const nf_plan& plan) {
+  if (P->layer != L) return set_err(NF_ERR_INVALID_ARG, "step: pool belongs to another layer");
+  std::string err;
+  nf_status st = check_plan(plan, L->cus_per_xcd, err);
+  if (st != NF_OK) return set_err(st, "%s", err.c_str());
+  return step_impl(L, P, b, s, plan);
+}
+
+extern "C" {
+
 nf_status nf_layer_step(nf_layer* L, nf_kv_pool* P, const nf_batch* b, void* stream) {
   if (!L || !P || !b) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: null argument");
   if (P->layer != L) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: pool belongs to another layer");

@@ -30,6 +30,13 @@ inline void launch(void (*k)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, h
   }
 }
 
+// Accessors for the serving loop (api.cpp).
+const nf_shape* layer_shape(const nf_layer* L);
+nf_plan layer_plan(const nf_layer* L);
+int32_t pool_pages(const nf_kv_pool* P);
+// nf_layer_step with an explicit plan (validated against the batch)
+nf_status layer_step_with_plan(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t s, const nf_plan& plan);
+
 // ---------------------------------------------------------------- GEMM
 // C[M][N] = epilogue(A[M][K] . B[N][K]^T): both operands K-contiguous.
 enum GemmMode : int {
@@ -180,6 +187,11 @@ hipError_t kv_convert(int dtype, void* k_pool, void* v_pool, const int32_t* page
 // copies pool pages pages[0..n) (K and V, block_bytes each) to dst_k / dst_v in list order
 hipError_t kv_gather(const void* k_pool, const void* v_pool, const int32_t* pages, int n, int64_t block_bytes,
                      void* dst_k, void* dst_v, hipStream_t s);
+// serving loop: x[t] = row at src[t]; then *dst[t] = out[t] and flag[t] =
+// (out[t][0] > thr) (src, dst, flag: host-mapped pinned memory)
+hipError_t loop_gather(const uint64_t* src, void* x, int T, int64_t row_bytes, hipStream_t s);
+hipError_t loop_scatter(int dtype, const void* out, const uint64_t* dst, int T, int H, float thr, int32_t* flag,
+                        hipStream_t s);
 // copy of `bytes` (multiple of 16, 16-byte aligned) by a kernel of `wgs` workgroups
 hipError_t copy_rows(const void* src, void* dst, size_t bytes, int wgs, hipStream_t s);
 // the inverse: block i of src_k / src_v to pool page pages[i] (pages distinct)

@@ -298,6 +298,26 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const u32x4* __restrict_
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Serving loop: row t of x comes from the device address src[t] (rows of
+// `row16` 16-byte units); row t of `out` goes to dst[t]; flag[t] = 1 when
+// out[t][0] > thr.  src, dst and flag are host-mapped pinned memory.
+__global__ __launch_bounds__(256) void loop_gather_kernel(const uint64_t* __restrict__ src, u32x4* __restrict__ x,
+                                                          int row16) {
+  const u32x4* s = (const u32x4*)src[blockIdx.x];
+  u32x4* d = x + (int64_t)blockIdx.x * row16;
+  for (int i = threadIdx.x; i < row16; i += 256) d[i] = s[i];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void loop_scatter_kernel(const u32x4* __restrict__ out, const uint64_t* __restrict__ dst,
+                                                           int row16, int H, float thr, int32_t* __restrict__ flag) {
+  const u32x4* s = out + (int64_t)blockIdx.x * row16;
+  u32x4* d = (u32x4*)dst[blockIdx.x];
+  for (int i = threadIdx.x; i < row16; i += 256) d[i] = s[i];
+  if (threadIdx.x == 0) flag[blockIdx.x] = to_f32(((const T*)s)[0]) > thr ? 1 : 0;
+  (void)H;
+}
+
 // Inverse of kv_gather_kernel: block i of src_k / src_v back to pool page
 // pages[i] (pages distinct).
 __global__ __launch_bounds__(256) void kv_scatter_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
@@ -358,6 +378,25 @@ hipError_t copy_rows(const void* src, void* dst, size_t bytes, int wgs, hipStrea
   if (bytes == 0) return hipSuccess;
   if (bytes % 16 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15) || wgs <= 0) return hipErrorInvalidValue;
   launch(copy_rows_kernel, wgs, 256, 0, s, (const u32x4*)src, (u32x4*)dst, (int64_t)(bytes / 16));
+  return hipGetLastError();
+}
+
+hipError_t loop_gather(const uint64_t* src, void* x, int T, int64_t row_bytes, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (row_bytes % 16) return hipErrorInvalidValue;
+  launch(loop_gather_kernel, T, 256, 0, s, src, (u32x4*)x, (int)(row_bytes / 16));
+  return hipGetLastError();
+}
+
+hipError_t loop_scatter(int dtype, const void* out, const uint64_t* dst, int T, int H, float thr, int32_t* flag,
+                        hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t row_bytes = (int64_t)H * (dtype == 1 ? 2 : 4);
+  if (row_bytes % 16) return hipErrorInvalidValue;
+  if (dtype == 1)
+    launch(loop_scatter_kernel<bf16>, T, 256, 0, s, (const u32x4*)out, dst, (int)(row_bytes / 16), H, thr, flag);
+  else
+    launch(loop_scatter_kernel<float>, T, 256, 0, s, (const u32x4*)out, dst, (int)(row_bytes / 16), H, thr, flag);
   return hipGetLastError();
 }
 

@@ -231,3 +231,16 @@ def test_binding_has_every_name_the_gpu_tests_and_bench_use():
         names |= set(re.findall(r"\bB\.([A-Za-z_][A-Za-z0-9_]*)", open(os.path.join(ROOT, f)).read()))
     missing = sorted(n for n in names if not hasattr(B, n))
     assert not missing, missing
+
+
+def test_loop_rejects_bad_arguments_before_launching():
+    L = B.lib()
+    o = B.nf_loop_opts(16, 16, 1, 10.0)
+    h = ctypes.c_void_p()
+    assert L.nf_loop_create(None, None, ctypes.byref(o), ctypes.byref(h)) == B.NF_ERR_INVALID_ARG
+    rid = ctypes.c_int32()
+    assert L.nf_loop_add_request(None, 4, 8, 16, 16, ctypes.byref(rid)) == B.NF_ERR_INVALID_ARG
+    assert L.nf_loop_run(None, None, None) == B.NF_ERR_INVALID_ARG
+    n = ctypes.c_int32()
+    assert L.nf_loop_request_length(None, 0, ctypes.byref(n)) == B.NF_ERR_INVALID_ARG
+    L.nf_loop_destroy(None)
