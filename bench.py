@@ -1,20 +1,30 @@
 """Decoder-layer step throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c2|c3|c5]
 
 One step = one nf_layer_step of the whole layer (norm, QKV, RoPE + paged KV
 append, decode/prefill attention, O-proj, norm, FFN or experts) over one batch
-of seeded synthetic inputs that are resident in HBM before timing starts.
-Prints one JSON line: throughput (tokens/s), the fraction of the
-compute-bound optimum (peaks measured in this run), the roofline of the
-dominant kernel (its duration measured with HIP events on its own stream
-during the timed steps), the step time with cold caches (a 512 MiB scratch
-read before each step), a stack of --stack layers of the same shape
-(nf_stack_step eager and as a HIP graph: unsplit, two nano-batches one
-after the other, and two nano-batches on two streams pipelined across
-layers; time per layer), the KV offload of an eighth of the requests to
-pinned host memory alone and beside steps (nf_kv_offload), the host time to
-enqueue one step, and the CPU oracle timed on a bounded sample.
+of seeded synthetic inputs that are resident in HBM before timing starts.  The
+default workload is c4 (the Llama-2-70B 1/8 tensor-parallel shard, 1536
+decode requests + a 512-token prefill chunk, 2048 tokens); the plan is chosen
+by the library's plan search.  Prints one JSON line:
+  - value: tokens/s over K steps with cold caches (a 512 MiB scratch read
+    before each step, outside the step's events); warm_cache: the same K
+    steps back to back;
+  - the fraction of the compute-bound optimum (peaks measured in this run);
+  - roofline of the dominant kernel (its duration measured with HIP events on
+    its own stream during K cold steps; HBM traffic from the committed
+    counter summary when its sources are unchanged);
+  - comparisons: unsplit, two nano-batches in sequence, two on two streams,
+    and the searched plan; search: what the search predicted and measured;
+  - a stack of --stack layers (eager and as a HIP graph; unsplit, split in
+    sequence, split pipelined across layers) and the single-layer graph;
+  - the emulated tensor-parallel all-reduce (copy engines, third stream),
+    with and without, unsplit and overlapped;
+  - the serving loop, synchronous vs asynchronous control flow, with the
+    host's share of each iteration;
+  - the KV offload to pinned host memory alone and beside steps, the host
+    time to enqueue one step, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -103,6 +113,9 @@ def main():
                     help="also time a stack of this many layers of the workload's shape (nf_stack_step, eager "
                          "and as a HIP graph; unsplit and two nano-batches pipelined across layers); 0: skip")
     ap.add_argument("--traffic", default=None, help="text file with the rocprofv3 FETCH/WRITE bytes per launch")
+    ap.add_argument("--no-allreduce", action="store_true",
+                    help="skip the emulated tensor-parallel all-reduce measurement")
+    ap.add_argument("--no-loop", action="store_true", help="skip the serving-loop measurement (sync vs async)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 5 times (counter calibration) and exit")
     args = ap.parse_args()
@@ -178,6 +191,7 @@ def main():
         return sum(times) / n, times[n // 2]
 
     comparisons, comparisons_warm = {}, {}
+    search = None
     half = [T - T // 2, T // 2]
     baselines = (("sequential_unsplit_ms", B.make_plan(1, [T])),
                  ("sequential_split2_ms", B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL)),
@@ -195,8 +209,17 @@ def main():
         layer.set_plan(plan)
     else:
         log("plan search")
+        t_search = time.perf_counter()
         plan, (best_ms, n_cands) = layer.search(pool, hb, max_count=4, warmup=2, reps=5, stream=sp)
-        log(f"searched plan {B.plan_dict(plan)} ({best_ms:.3f} ms, {int(n_cands)} candidates)")
+        t_search = time.perf_counter() - t_search
+        log(f"searched plan {B.plan_dict(plan)} ({best_ms:.3f} ms, {int(n_cands)} candidates predicted, "
+            f"{t_search:.2f} s)")
+        rep = layer.search_report()
+        search = {"candidates_predicted": int(n_cands), "seconds": round(t_search, 3),
+                  "timed": [{"plan": d, "predicted_ms": round(pr, 4), "measured_ms": round(me, 4)}
+                            for d, pr, me in rep]}
+        errs = [abs(pr - me) / me for _, pr, me in rep if me > 0]
+        search["median_abs_rel_error"] = round(sorted(errs)[len(errs) // 2], 4) if errs else None
         # the baselines the searched plan is compared with: the unsplit step,
         # two nano-batches one after the other on one stream, and the same two
         # nano-batches overlapped on two streams without CU masks; cold
@@ -305,6 +328,18 @@ def main():
         stack = stack_measure(args.stack, wl, batch, layer, pool, acts, plan, sp)
         layer.set_plan(plan)
 
+    single_graph = graph_single_layer(layer, pool, hb, plan, sp, ms_warm)
+
+    allreduce = None
+    if not args.no_allreduce and s.n_experts == 1:
+        allreduce = allreduce_measure(layer, pool, hb, T, sp)
+        layer.set_plan(plan)
+
+    loop = None
+    if not args.no_loop and s.n_experts == 1:
+        loop = loop_measure(wl, layer, sp)
+        layer.set_plan(plan)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, batch, weights, acts, k_plain, v_plain)
@@ -339,11 +374,153 @@ def main():
         line["comparisons"]["caches"] = "cold"
         line["comparisons_warm"] = {k: round(v, 5) for k, v in comparisons_warm.items()}
     line["host"] = host
+    if single_graph is not None:
+        line["single_layer_graph"] = single_graph
+    if search is not None:
+        line["search"] = search
+    if allreduce is not None:
+        line["allreduce_emulation"] = allreduce
+    if loop is not None:
+        line["serving_loop"] = loop
     if offload is not None:
         line["kv_offload"] = offload
     if stack is not None:
         line["stack"] = stack
     print(json.dumps(line), flush=True)
+
+
+def graph_single_layer(layer, pool, hb, plan, sp, step_ms, steps=20):
+    """The single-layer step recorded as a HIP graph (a one-layer stack):
+    time per replay and host time to launch one replay."""
+    import torch
+    from intra_operation_overlap_amd import binding as B
+    if plan.n_streams == 2 and (plan.gemm_cus_per_xcd or plan.attn_cus_per_xcd):
+        return None
+    g = B.StackGraph([layer], [pool], hb, sp)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        g.launch(sp)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    h0 = time.perf_counter()
+    for _ in range(steps):
+        g.launch(sp)
+    host = (time.perf_counter() - h0) / steps * 1e6
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    hs = []
+    for _ in range(10):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        g.launch(sp)
+        hs.append((time.perf_counter() - h0) * 1e6)
+    torch.cuda.synchronize()
+    g.close()
+    res = {"ms_per_step": round(ms, 5), "eager_ms_per_step": round(step_ms, 5),
+           "host_launch_us_idle": round(sorted(hs)[5], 1), "host_us_per_step_in_loop": round(host, 1)}
+    log(f"single-layer graph: {ms * 1e3:.1f} us per step (eager {step_ms * 1e3:.1f}), launch {res['host_launch_us_idle']} us")
+    return res
+
+
+def allreduce_measure(layer, pool, hb, T, sp, steps=20):
+    """The network-bound third resource, emulated on one GPU: after the
+    O-projection and the down projection of every nano-batch, its rows make a
+    send and a receive leg (2 x T_j x H elements) on a third stream, on the
+    copy engines (nf_layer_set_allreduce_emulation mode 1).  Times the
+    unsplit step with and without it, and overlapped plans with it (warm
+    caches, events around `steps` steps)."""
+    import torch
+    from intra_operation_overlap_amd import binding as B
+    stream = torch.cuda.current_stream()
+
+    def timed():
+        for _ in range(3):
+            layer.step(pool, hb, sp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            layer.step(pool, hb, sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    half = [T - T // 2, T // 2]
+    plans = {"unsplit": B.make_plan(1, [T]),
+             "split2_sequential": B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL),
+             "split2_pipelined_two_streams": B.make_plan(2, half, n_streams=2),
+             "split2_deep_two_streams": B.make_plan(2, half, order=B.NF_ORDER_DEEP, n_streams=2),
+             "split2_deep_one_stream": B.make_plan(2, half, order=B.NF_ORDER_DEEP)}
+    res = {"mode": "copy engines", "bytes_per_step": None, "ms_per_step": {}}
+    layer.set_allreduce_emulation(0)
+    layer.set_plan(plans["unsplit"])
+    res["ms_per_step"]["unsplit_without_allreduce"] = round(timed(), 5)
+    layer.set_allreduce_emulation(1)
+    for name, p in plans.items():
+        layer.set_plan(p)
+        res["ms_per_step"][name] = round(timed(), 5)
+    layer.set_allreduce_emulation(0)
+    H = layer.shape.hidden
+    res["bytes_per_step"] = 2 * 2 * 2 * T * H * (2 if layer.shape.dtype == B.NF_BF16 else 4)
+    log("all-reduce emulation: " + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in res["ms_per_step"].items()))
+    return res
+
+
+def loop_measure(wl, layer, sp, n_requests=96):
+    """The serving loop (nf_loop_*) on the bench's layer and a pool of its
+    own: requests with prompts of 64-512 tokens and 16-64 generated
+    positions, a third of them ended early by an end marker in an input row,
+    2048 tokens and 512 prompt tokens per iteration; synchronous control flow
+    (flags read after every iteration) against asynchronous (iteration i + 1
+    launched before i's flags are read).  Each variant runs twice; the second
+    run is reported."""
+    import torch
+    from intra_operation_overlap_amd import binding as B
+    s = wl.shape
+    rng = np.random.Generator(np.random.PCG64(17))
+    reqs = []
+    top = min(512, int(layer.shape.max_pos) - 65)
+    for i in range(n_requests):
+        prompt = int(rng.integers(min(64, top), top + 1))
+        max_len = prompt + int(rng.integers(16, 65))
+        g = torch.Generator(device="cuda")
+        g.manual_seed(17000 + i)
+        rows = torch.randn(max_len, s.hidden, generator=g, device="cuda").to(torch.bfloat16)
+        if i % 3 == 0:
+            rows[int(rng.integers(prompt, max_len - 1)), 0] = 200.0
+        reqs.append((prompt, rows))
+    need = sum(-(-r.shape[0] // 16) for _, r in reqs)
+    n_pages = need // 2                                   # about half the requests fit at once
+    kp = torch.zeros(n_pages, s.n_kv_heads, 16, s.head_dim, dtype=torch.bfloat16, device="cuda")
+    pool = B.KVPool.from_plain(layer, kp, kp, sp)
+    del kp
+    max_tokens = min(2048, int(layer.shape.max_tokens))
+    layer.set_plan(B.make_plan(1, [0]))
+    out = {}
+    for name, async_ in (("sync", False), ("async", True)):
+        for rep in range(2):
+            loop = B.Loop(layer, pool, max_tokens, 512, async_, 100.0)
+            outs = [torch.empty_like(r) for _, r in reqs]
+            for (prompt, rows), o in zip(reqs, outs):
+                loop.add(prompt, rows, o)
+            st = loop.run(sp)
+            torch.cuda.synchronize()
+            loop.close()
+        it = max(1, st["iterations"])
+        out[name] = {"iterations": st["iterations"], "tokens": st["tokens"], "wasted_tokens": st["wasted_tokens"],
+                     "wall_ms": round(st["wall_us"] / 1e3, 3), "wall_us_per_iteration": round(st["wall_us"] / it, 1),
+                     "host_us_per_iteration": round(st["host_us"] / it, 1),
+                     "host_share_of_wall": round(st["host_us"] / st["wall_us"], 4),
+                     "tokens_per_s": round(st["tokens"] / (st["wall_us"] * 1e-6), 1)}
+        log(f"serving loop {name}: {st['iterations']} iterations, {st['wall_us'] / 1e3:.1f} ms, host "
+            f"{st['host_us'] / it:.1f} us per iteration ({100 * st['host_us'] / st['wall_us']:.1f}% of wall), "
+            f"{st['wasted_tokens']} wasted tokens")
+    pool.close()
+    out["requests"] = n_requests
+    out["pool_pages"] = n_pages
+    return out
 
 
 def offload_measure(batch, layer, pool, k_pool, hb, sp, step_ms, reps=10):
