@@ -1,7 +1,8 @@
 """The KV pool's block layout, built by enumerating the attention kernel's
 operand loads (as the boundary documents them): lane l of a 16-byte load
 of 32-dim chunk c carries 8 elements.  Used by tests to address pool slots;
-deliberately written differently from the oracle's closed-form offsets."""
+written from the lane layout of the instructions, independently of the
+library's closed-form offsets; a GPU test checks pool import against it."""
 import numpy as np
 
 
