@@ -259,11 +259,20 @@ __device__ __forceinline__ void item4(const AttnArgs& a, int w, float* m_s, floa
   finish_item<bf16>(a, it, G, kh, m_s, l_s, O_s);
 }
 
-// One workgroup per work item, or, with a capped grid, each workgroup walks
-// the work list with a stride of the grid (a persistent grid that holds a
-// fixed number of workgroups per CU and so leaves the rest of the CU's LDS
-// and registers to a concurrent GEMM).
+// One workgroup per work item.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_bf16_d128_kernel(AttnArgs a) {
+  __shared__ float m_s[4 * ROWS], l_s[4 * ROWS];
+  __shared__ float O_s[4 * ROWS * DH];
+  item4(a, blockIdx.x, m_s, l_s, O_s);
+}
+
+// A capped grid: each workgroup walks the work list with a stride of the grid
+// (a persistent grid that holds a fixed number of workgroups per CU and so
+// leaves the rest of the CU's LDS and registers to a concurrent GEMM).  The
+// loop keeps its bounds and the item index live across the item, which needs
+// 172 registers: held to three waves per SIMD it spilled to scratch, so it
+// runs at two (plans bound it to one or two workgroups per CU anyway).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_d128_loop_kernel(AttnArgs a) {
   __shared__ float m_s[4 * ROWS], l_s[4 * ROWS];
   __shared__ float O_s[4 * ROWS * DH];
   const int n_work = a.n_items * a.nkv;
@@ -448,9 +457,11 @@ hipError_t attention(int dtype, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_items, a.nkv);
   if (dtype == 1 && a.d == 128 && a.page_size == 16) {
     if (a.variant == 1) {
-      int blocks = a.n_items * a.nkv;
-      if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
-      launch(attn_bf16_d128_kernel, blocks, 256, 0, s, a);
+      const int blocks = a.n_items * a.nkv;
+      if (a.max_blocks > 0 && blocks > a.max_blocks)
+        launch(attn_bf16_d128_loop_kernel, a.max_blocks, 256, 0, s, a);
+      else
+        launch(attn_bf16_d128_kernel, blocks, 256, 0, s, a);
     } else {
       int blocks = a.n_items * a.nkv;
       if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
