@@ -145,7 +145,10 @@ def main():
     out = torch.empty_like(acts["x"])
     T = batch.n_tokens
     layer = B.Layer(s, weights, T, int(batch.pos.max()) + 1)
-    stream = torch.cuda.current_stream()
+    # a stream of the bench's own: the null stream would synchronise
+    # implicitly with the library's CU-masked (blocking) streams
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
     sp = stream.cuda_stream
     pool = B.KVPool.from_plain(layer, k_plain, v_plain, sp)
     hb = B.HostBatch(batch, acts["x"].data_ptr(), out.data_ptr(),

@@ -851,7 +851,12 @@ nf_status open_streams(nf_layer* L, const nf_plan& plan, hipStream_t caller, Str
   nf_status st = get_pair(L, plan.gemm_cus_per_xcd, plan.attn_cus_per_xcd, pr);
   if (st != NF_OK) return st;
   S.sa = pr.a;
-  if (plan.gemm_cus_per_xcd) {
+  // CU-masked streams are blocking streams, which the null stream
+  // synchronises with implicitly: GEMM work left on a null caller stream
+  // would wait for the attention stream's earlier launches and hold back its
+  // later ones, serialising the two sides.  The GEMM side then runs on the
+  // pair's own (non-blocking, or masked) stream, as under a GEMM budget.
+  if (plan.gemm_cus_per_xcd || caller == nullptr) {
     S.sg = pr.g;
     HIP_TRY(hipEventRecord(L->ev_start, caller));
     HIP_TRY(hipStreamWaitEvent(S.sg, L->ev_start, 0));
