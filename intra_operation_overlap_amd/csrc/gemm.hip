@@ -1109,6 +1109,20 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident) {
     int ks = 0;
     if (t256 >= enough) {
       ks = 1;
+    } else if (const int64_t t12 = (int64_t)((M + 127) / 128) * n_tiles_of(a, 256), t13 = (int64_t)((M + 127) / 128) * n_tiles_of(a, 128);
+               (a.K < 8192 || a.mode == GEMM_SWIGLU) &&
+               ((t12 >= enough && t12 <= cus) || (t13 >= enough && t13 <= cus))) {
+      // a grid of 128-row tiles that fills one round runs unsplit, with no
+      // partials to write and reduce: 128 x 256 (configuration 12) before
+      // 128 x 128 (13).  Inside the step: the Llama-3-8B QKV of 1024 tokens
+      // 74 -> 55 us; the Llama-2-70B-shard gate/up of 1024 and 512 tokens
+      // (whose split partials are twice as wide) alone 109 us against 118
+      // plus a reduce, and 64 against 70 plus a reduce.  Long-K projections
+      // keep the split 256 x 256 tiles (the 1024-token Llama-3-8B down
+      // projection: 117 us split, 134 as 128 x 128 tiles).
+      p.cfg = (t12 >= enough && t12 <= cus) ? 12 : 13;
+      p.k_splits = 1;
+      return p;
     } else if (a.K >= 8192) {
       for (int k = 2; k <= 8 && a.K / k >= 2048; k *= 2)
         if (t256 * k >= enough) {
