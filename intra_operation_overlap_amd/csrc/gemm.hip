@@ -1136,6 +1136,21 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident) {
       return p;
     }
   }
+  // A long-K projection to a narrow output (the Llama-2-70B-shard QKV:
+  // 2048 x 1280 x 8192) has too few 256 x 256 tiles even split four ways;
+  // 128 x 256 tiles split until they fill one round run it in 61 us inside
+  // the step against 73-75 for split 128 x 128 tiles (the partials go to the
+  // RoPE kernel, which reduces them)
+  if (p.cfg == 14 && a.K >= 8192 && !coresident && a.mode == GEMM_STORE) {
+    const int64_t t12 = (int64_t)((M + 127) / 128) * n_tiles_of(a, 256);
+    const int64_t enough = (3 * (int64_t)cus + 3) / 4;
+    for (int k = 2; k <= 4; ++k)
+      if (t12 * k >= enough && t12 * k <= cus) {
+        p.cfg = 12;
+        p.k_splits = k;
+        return p;
+      }
+  }
   // 128 x 128 tiles that fill one round on the CUs (at least three quarters
   // of them) run unsplit, one workgroup per CU with three stages and the
   // refill spread over the MFMAs (configuration 13).  Inside the step: the
