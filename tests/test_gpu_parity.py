@@ -112,8 +112,9 @@ def test_small_bf16_prefill_from_zero_and_g8():
 
 # Seeded shape sweep: GQA groups 1, 2 and 8, hidden not a multiple of 64 (the
 # GEMMs' non-pipelined configurations), ragged FFN widths, prefill chunks from
-# position 0 and mid-context, a decode-only batch with long contexts, and an
-# fp32 layer with head_dim 64 (the generic attention kernel).
+# position 0 and mid-context, a decode-only batch with long contexts, contexts
+# of 6K-16K tokens, and an fp32 layer with head_dim 64 (the generic attention
+# kernel).
 SWEEP = {
     "g1_prefill_from_0": W.Workload("sw_g1", W.Shape(hidden=256, n_q_heads=8, n_kv_heads=8, head_dim=128, ffn=344,
                                                      dtype="bf16", rope_theta=1e4),
@@ -124,6 +125,11 @@ SWEEP = {
     "g8_long_decode": W.Workload("sw_g8", W.Shape(hidden=1024, n_q_heads=16, n_kv_heads=2, head_dim=128, ffn=1000,
                                                   dtype="bf16", rope_theta=1e6),
                                  n_decode=50, ctx_range=(1, 700), prefill=None, seed=103),
+    # contexts of 6K-16K tokens: long items split into page ranges whose
+    # partials several merge items combine, and a prefill chunk deep in context
+    "g4_long_context": W.Workload("sw_long", W.Shape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=688,
+                                                     dtype="bf16", rope_theta=1e6),
+                                  n_decode=5, ctx_range=(6000, 16000), prefill=(9000, 40), seed=105),
     "fp32_d64": W.Workload("sw_f32", W.Shape(hidden=384, n_q_heads=6, n_kv_heads=2, head_dim=64, ffn=520,
                                              dtype="f32", rope_theta=1e4),
                            n_decode=12, ctx_range=(1, 150), prefill=(10, 27), seed=104),
@@ -171,6 +177,35 @@ def test_plan_invariance_bit_exact(small):
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert torch.equal(a, b)
+
+
+def test_caller_stream_kind_does_not_change_results(small):
+    """Two-stream plans give the same bits on the null stream (whose implicit
+    synchronisation with the blocking CU-masked streams the executor steps
+    around) and on a non-blocking caller stream."""
+    T = small.batch.n_tokens
+    half = [T // 2, T - T // 2]
+    side = torch.cuda.Stream()
+    for plan in (B.make_plan(2, half, n_streams=2),
+                 B.make_plan(2, half, n_streams=2, attn_cus_per_xcd=24),
+                 B.make_plan(2, half, n_streams=2, gemm_cus_per_xcd=16, attn_cus_per_xcd=16),
+                 B.make_plan(2, half, order=B.NF_ORDER_DEEP, n_streams=2, gemm_cus_per_xcd=20)):
+        small.layer.set_plan(plan)
+        outs = []
+        for s in (None, side):
+            k0, v0 = small.k.clone(), small.v.clone()
+            torch.cuda.synchronize()
+            if s is None:
+                GH.run_step(small)
+            else:
+                with torch.cuda.stream(s):
+                    GH.run_step(small)
+            torch.cuda.synchronize()
+            outs.append((small.out.clone(), small.k.clone(), small.v.clone()))
+            small.k.copy_(k0)
+            small.v.copy_(v0)
+        for a, b in zip(*outs):
+            assert torch.equal(a, b), B.plan_dict(plan)
 
 
 def test_repeated_steps_are_idempotent(small):
