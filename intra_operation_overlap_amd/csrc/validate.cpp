@@ -77,14 +77,14 @@ nf_status check_batch(const nf_shape& s, int64_t n_pages, int page_size, const n
   if (s.n_experts > 1 && !b.router_logits)
     return fail(err, NF_ERR_INVALID_ARG, "batch: router_logits required for a mixture-of-experts layer");
   if (b.page_indptr[0] != 0) return fail(err, NF_ERR_INVALID_ARG, "batch: page_indptr[0] must be 0");
-  int expect_start = 0;
+  int64_t expect_start = 0;           // 64-bit: a huge q_len must not wrap past the bound check
   for (int r = 0; r < R; ++r) {
     const int qs = b.req_q_start[r], ql = b.req_q_len[r], p0 = b.req_pos0[r];
     if (ql < 0 || p0 < 0)
       return fail(err, NF_ERR_INVALID_ARG, "batch: request %d has negative q_len or pos0", r);
     if (qs != expect_start)
-      return fail(err, NF_ERR_INVALID_ARG, "batch: request %d starts at token %d, expected %d", r, qs,
-                  expect_start);
+      return fail(err, NF_ERR_INVALID_ARG, "batch: request %d starts at token %d, expected %lld", r, qs,
+                  (long long)expect_start);
     expect_start += ql;
     if (expect_start > T)
       return fail(err, NF_ERR_INVALID_ARG, "batch: requests cover more than %d tokens", T);
@@ -103,7 +103,8 @@ nf_status check_batch(const nf_shape& s, int64_t n_pages, int page_size, const n
                   (long long)have, (long long)need);
   }
   if (expect_start != T)
-    return fail(err, NF_ERR_INVALID_ARG, "batch: requests cover %d tokens, batch has %d", expect_start, T);
+    return fail(err, NF_ERR_INVALID_ARG, "batch: requests cover %lld tokens, batch has %d", (long long)expect_start,
+                T);
   const int64_t nnz = b.page_indptr[R];
   std::vector<int32_t> owner((size_t)n_pages, -1);
   for (int r = 0; r < R; ++r) {

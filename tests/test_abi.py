@@ -86,6 +86,10 @@ def test_validate_rejects_bad_batches():
     bad = _copy(batch)
     bad.req_q_start[1] = 2
     assert _validate(shape, bad) == B.NF_ERR_INVALID_ARG
+    # a q_len so large that a 32-bit running token count would wrap
+    bad = _copy(batch)
+    bad.req_q_len[1] = 2 ** 31 - 1
+    assert _validate(shape, bad) == B.NF_ERR_INVALID_ARG
     # out aliasing x
     assert _validate(shape, batch, x=0x1000, out=0x1000) == B.NF_ERR_INVALID_ARG
     # unsupported page size
