@@ -310,7 +310,13 @@ nf_status nf_batch_validate(const nf_shape* shape, int32_t n_pages, int32_t page
  * after the step completes.  Asynchronous to the host; host arrays of the
  * batch may be reused once the call returns.  Writes batch->out, the pool
  * slots of the batch's new positions and the layer's workspace.  Calls on
- * one layer must not overlap on different host threads. */
+ * one layer must not overlap on different host threads.  Errors: those of
+ * nf_batch_validate (nothing launched), NF_ERR_HIP; after a HIP failure
+ * partway through the launches the call waits for what it had enqueued
+ * before returning, and the next step runs as if none had failed.  For tests
+ * of these paths, NF_FAULT=after:<n> in the environment makes the n-th
+ * checked HIP call of the next nf_layer_step / nf_stack_step report failure
+ * without being made. */
 nf_status nf_layer_step(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch, void* stream);
 
 /* ---- serving loop ----------------------------------------------------------

@@ -56,10 +56,35 @@ nf_status nf::set_error(nf_status st, const char* msg) {
 
 namespace {
 
+// Host-side fault injection for tests of the error paths: with NF_FAULT set
+// to "after:<n>" when nf_layer_step or nf_stack_step is called, the n-th
+// (from 0) checked HIP call inside that call is not made and reports
+// failure instead, once.  No device work is touched: the call is skipped.
+thread_local int g_fault_at = -1;
+thread_local int g_fault_seen = 0;
+
+struct FaultScope {
+  FaultScope() {
+    g_fault_at = -1;
+    g_fault_seen = 0;
+    const char* v = std::getenv("NF_FAULT");
+    if (v && std::strncmp(v, "after:", 6) == 0) g_fault_at = std::atoi(v + 6);
+  }
+  ~FaultScope() { g_fault_at = -1; }
+};
+
+bool fault_now() {
+  if (g_fault_at < 0) return false;
+  if (g_fault_seen++ != g_fault_at) return false;
+  g_fault_at = -1;
+  return true;
+}
+
 // On a HIP failure the runtime's last-error slot is cleared so that the
 // caller's next unrelated HIP call does not report it again.
 #define HIP_TRY(expr)                                                                     \
   do {                                                                                    \
+    if (fault_now()) return set_err(NF_ERR_HIP, "%s not made: injected failure (NF_FAULT)", #expr); \
     hipError_t e_ = (expr);                                                               \
     if (e_ != hipSuccess) {                                                               \
       (void)hipGetLastError();                                                            \
@@ -322,11 +347,18 @@ nf_status get_pair(nf_layer* L, int g, int a, StreamPair& out) {
     make_mask(L->xcc_of_bit, L->n_xcd, 0, g, m);
     HIP_TRY(hipExtStreamCreateWithCUMask(&p.g, (uint32_t)m.size(), m.data()));
   }
-  if (ab == 0) {
-    HIP_TRY(hipStreamCreateWithFlags(&p.a, hipStreamNonBlocking));
-  } else {
-    make_mask(L->xcc_of_bit, L->n_xcd, L->cus_per_xcd - ab, L->cus_per_xcd, m);
-    HIP_TRY(hipExtStreamCreateWithCUMask(&p.a, (uint32_t)m.size(), m.data()));
+  nf_status st = [&]() -> nf_status {
+    if (ab == 0) {
+      HIP_TRY(hipStreamCreateWithFlags(&p.a, hipStreamNonBlocking));
+    } else {
+      make_mask(L->xcc_of_bit, L->n_xcd, L->cus_per_xcd - ab, L->cus_per_xcd, m);
+      HIP_TRY(hipExtStreamCreateWithCUMask(&p.a, (uint32_t)m.size(), m.data()));
+    }
+    return NF_OK;
+  }();
+  if (st != NF_OK) {            // the first stream is not kept: destroy it
+    (void)hipStreamDestroy(p.g);
+    return st;
   }
   L->pairs[key] = p;
   out = p;
@@ -489,6 +521,7 @@ NanoGemms nano_gemms(const StepCtx& c, int j, int t0, int t1) {
 
 #define HIP_STEP(expr)                                                                      \
   do {                                                                                      \
+    if (fault_now()) return set_err(NF_ERR_HIP, "%s not made: injected failure (NF_FAULT)", #expr); \
     hipError_t e_ = (expr);                                                                 \
     if (e_ != hipSuccess)                                                                   \
       return set_err(NF_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));           \
@@ -864,6 +897,21 @@ nf_status open_streams(nf_layer* L, const nf_plan& plan, hipStream_t caller, Str
   return NF_OK;
 }
 
+// After a failure partway through enqueuing a step: wait for what was
+// enqueued (each launch went out with its dependencies in place), so that no
+// kernel of the failed step still reads the metadata staging or the
+// workspace when the caller goes on.  Errors here are ignored: the step's own
+// error is the one reported.
+void drain_after_error(const Streams& S) {
+  const hipStream_t all[4] = {S.caller, S.sg, S.sa, S.sc};
+  for (int i = 0; i < 4; ++i) {
+    bool seen = false;
+    for (int k = 0; k < i; ++k) seen = seen || all[k] == all[i];
+    if (!seen && (i == 0 || all[i])) (void)hipStreamSynchronize(all[i]);
+  }
+  (void)hipGetLastError();
+}
+
 nf_status close_streams(nf_layer* L, const Streams& S) {
   if (S.two && S.sg != S.caller) {
     HIP_TRY(hipEventRecord(L->ev_g, S.sg));
@@ -985,9 +1033,11 @@ nf_status step_impl(nf_layer* L, nf_kv_pool* P, const nf_batch* b, hipStream_t c
   nf_status st = prepare_layer(L, P, b, plan, nullptr, r);
   if (st != NF_OK || r.count == 0) return st;
   Streams S;
-  if ((st = open_streams(L, plan, caller, S)) != NF_OK) return st;
-  if ((st = issue_layer(r, S, plan.order)) != NF_OK) return st;
-  return close_streams(L, S);
+  if ((st = open_streams(L, plan, caller, S)) == NF_OK && (st = issue_layer(r, S, plan.order)) == NF_OK &&
+      (st = close_streams(L, S)) == NF_OK)
+    return NF_OK;
+  drain_after_error(S);
+  return st;
 }
 
 // Checks of a multi-layer step's arguments (no HIP call).
@@ -1035,9 +1085,11 @@ nf_status stack_impl(nf_layer* const* layers, nf_kv_pool* const* pools, int n, c
   nf_status st = prepare_stack(layers, pools, n, b, nullptr, runs);
   if (st != NF_OK || runs[0].count == 0) return st;
   Streams S;
-  if ((st = open_streams(layers[0], layers[0]->plan, caller, S)) != NF_OK) return st;
-  if ((st = issue_stack(runs, S, layers[0]->plan.order)) != NF_OK) return st;
-  return close_streams(layers[0], S);
+  if ((st = open_streams(layers[0], layers[0]->plan, caller, S)) == NF_OK &&
+      (st = issue_stack(runs, S, layers[0]->plan.order)) == NF_OK && (st = close_streams(layers[0], S)) == NF_OK)
+    return NF_OK;
+  drain_after_error(S);
+  return st;
 }
 
 }  // namespace
@@ -1362,6 +1414,7 @@ extern "C" {
 nf_status nf_layer_step(nf_layer* L, nf_kv_pool* P, const nf_batch* b, void* stream) {
   if (!L || !P || !b) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: null argument");
   if (P->layer != L) return set_err(NF_ERR_INVALID_ARG, "nf_layer_step: pool belongs to another layer");
+  FaultScope fault;
   return step_impl(L, P, b, (hipStream_t)stream, L->plan);
 }
 
@@ -1369,6 +1422,7 @@ nf_status nf_stack_step(nf_layer* const* layers, nf_kv_pool* const* pools, int32
                         void* stream) {
   nf_status st = check_stack(layers, pools, n_layers, batch);
   if (st != NF_OK) return st;
+  FaultScope fault;
   return stack_impl(layers, pools, n_layers, batch, (hipStream_t)stream);
 }
 
