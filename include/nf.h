@@ -192,7 +192,12 @@ typedef struct nf_graph nf_graph;
  * merge) or four-wave workgroups (1); by default four-wave workgroups run
  * unless the plan bounds the attention waves per CU.  NF_SEARCH_VERBOSE
  * prints each plan the search re-times; NF_PROBE_VERBOSE prints the MFMA
- * probe's rate per shape (both to stderr). */
+ * probe's rate per shape (both to stderr).  NF_GEMM_OVERRIDE=
+ * "M,N,K,mode=cfg:splits;..." (read once per process) forces LDS-pipelined
+ * configuration cfg (10..30) and the K split on every dense bf16 GEMM of that
+ * shape and mode (0 plain, 1 residual, 2 SwiGLU), for timing configurations
+ * inside the step; results then differ from the default choice by rounding
+ * only. */
 nf_status nf_layer_create(const nf_shape* shape, const nf_weights* w, nf_layer** out);
 void nf_layer_destroy(nf_layer* layer);   /* waits for the layer's streams */
 

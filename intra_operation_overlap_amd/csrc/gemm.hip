@@ -16,7 +16,11 @@
 // XCD-aware: the dispatcher deals workgroups round-robin over the 8 XCDs, so
 // each XCD is handed a contiguous range of tiles (M fastest) and the weight
 // rows of one N tile stay in one XCD's L2.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
+#include <vector>
 
 #include "nf_device.h"
 #include "nf_internal.h"
@@ -1061,9 +1065,42 @@ int stream_splits(const GemmArgs& a, int cfg, int cus) {
 }
 }  // namespace
 
+// Tuning knob for timing tile configurations inside the step:
+// NF_GEMM_OVERRIDE="M,N,K,mode=cfg:splits;..." makes every dense GEMM of that
+// shape and mode run LDS-pipelined configuration cfg (10..30) with the given
+// K split.  Read once per process; shapes the configuration cannot take
+// (K not a multiple of 64, grouped GEMMs) keep the regular choice.
+struct GemmOverride {
+  int M, N, K, mode, cfg, splits;
+};
+
+const std::vector<GemmOverride>& gemm_overrides() {
+  static const std::vector<GemmOverride> table = [] {
+    std::vector<GemmOverride> t;
+    const char* v = std::getenv("NF_GEMM_OVERRIDE");
+    while (v && *v) {
+      GemmOverride o{};
+      if (std::sscanf(v, "%d,%d,%d,%d=%d:%d", &o.M, &o.N, &o.K, &o.mode, &o.cfg, &o.splits) == 6 && o.cfg >= 10 &&
+          o.cfg <= 30 && o.splits >= 1)
+        t.push_back(o);
+      v = std::strchr(v, ';');
+      if (v) ++v;
+    }
+    return t;
+  }();
+  return table;
+}
+
 GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident) {
   GemmPlan p;
   if (cus <= 0) cus = 256;
+  if (!a.group_off && !a.Bp && a.K % 64 == 0)
+    for (const GemmOverride& o : gemm_overrides())
+      if (o.M == a.M && o.N == a.N && o.K == a.K && o.mode == a.mode) {
+        p.cfg = o.cfg;
+        p.k_splits = std::min(o.splits, a.K / 64);
+        return p;
+      }
   if (a.Bp) {                   // packed weights: stream them for expert groups
     // (measured: for dense decode-sized M the pipelined LDS kernel below is
     // faster, so configurations 40..43 are chosen only on request; on the
@@ -1103,6 +1140,17 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident) {
   // K >= 8192, when split-K brings them there with >= 2048 of K per piece
   // (shorter K, or fewer tiles: 128 x 128 tiles, whose split partials the
   // consumers reduce more cheaply)
+  // Short K (1024..2047) takes them only when they fill exactly one round:
+  // the Llama-2-70B-shard O projection (2048 x 8192 x 1024) 53.3 -> 50.2 us
+  // inside the step against 128 x 128 tiles (three alternating runs).
+  if (p.cfg == 14 && a.K >= 1024 && a.K < 2048 && !coresident) {
+    const int64_t t256 = (int64_t)((M + 255) / 256) * n_tiles_of(a, 256);
+    if (4 * t256 >= 3 * (int64_t)cus && t256 <= cus) {
+      p.cfg = 10;
+      p.k_splits = 1;
+      return p;
+    }
+  }
   if (p.cfg == 14 && a.K >= 2048 && !coresident) {
     const int64_t t256 = (int64_t)((M + 255) / 256) * n_tiles_of(a, 256);
     const int64_t enough = (3 * (int64_t)cus + 3) / 4;
