@@ -1185,14 +1185,15 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident) {
     }
   }
   // A long-K projection to a narrow output (the Llama-2-70B-shard QKV:
-  // 2048 x 1280 x 8192) has too few 256 x 256 tiles even split four ways;
-  // 128 x 256 tiles split until they fill one round run it in 61 us inside
-  // the step against 73-75 for split 128 x 128 tiles (the partials go to the
-  // RoPE kernel, which reduces them)
+  // 1280 x 8192) has too few 256 x 256 tiles even split four ways; 128 x 256
+  // tiles split until they fill one round (at least 1024 of K per piece) run
+  // it inside the step in 61 us at 2048 tokens (3 pieces) against 73-75 for
+  // split 128 x 128 tiles, and in 2 x 32 us at 1024 tokens (5 pieces) against
+  // 2 x 45 (the partials go to the RoPE kernel, which reduces them)
   if (p.cfg == 14 && a.K >= 8192 && !coresident && a.mode == GEMM_STORE) {
     const int64_t t12 = (int64_t)((M + 127) / 128) * n_tiles_of(a, 256);
     const int64_t enough = (3 * (int64_t)cus + 3) / 4;
-    for (int k = 2; k <= 4; ++k)
+    for (int k = 2; k <= 8 && a.K / k >= 1024; ++k)
       if (t12 * k >= enough && t12 * k <= cus) {
         p.cfg = 12;
         p.k_splits = k;
