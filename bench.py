@@ -219,9 +219,11 @@ def main():
             f"{t_search:.2f} s)")
         rep = layer.search_report()
         search = {"candidates_predicted": int(n_cands), "seconds": round(t_search, 3),
+                  "calibration": [{"plan": d, "measured_ms": round(me, 4)} for d, pr, me, cal in rep if cal],
                   "timed": [{"plan": d, "predicted_ms": round(pr, 4), "measured_ms": round(me, 4)}
-                            for d, pr, me in rep]}
-        errs = [abs(pr - me) / me for _, pr, me in rep if me > 0]
+                            for d, pr, me, cal in rep if not cal]}
+        # over the candidates the model ranked (the calibration runs are fitted)
+        errs = [abs(pr - me) / me for _, pr, me, cal in rep if me > 0 and not cal]
         search["median_abs_rel_error"] = round(sorted(errs)[len(errs) // 2], 4) if errs else None
         # the baselines the searched plan is compared with: the unsplit step,
         # two nano-batches one after the other on one stream, and the same two

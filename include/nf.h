@@ -435,7 +435,10 @@ void nf_graph_destroy(nf_graph* graph);
  * nano-batch); gap_us added per operation.  While both streams run, the GEMM
  * side progresses at 1 / slow_gemm and attention at 1 / slow_attn of its
  * solo rate (interference of concurrent operations, the consideration the
- * codewithpapers abstract names for the search).  The plan search measures
+ * codewithpapers abstract names for the search).  scale_gemm / scale_attn
+ * (values <= 0 read as 1) multiply every duration of that side whether or
+ * not the other runs: the cost of a CU budget, which confines a side also
+ * when it runs alone.  The plan search measures
  * these inputs on the device; nf_plan_predict evaluates the model alone on
  * the host (no HIP call) for a plan and batch: *us = predicted step time.
  * Errors: NF_ERR_INVALID_ARG (null argument, n_points outside
@@ -451,6 +454,7 @@ typedef struct nf_plan_profile {
   double attn_base_us, attn_us_per_page;
   double gap_us;
   double slow_gemm, slow_attn, wait_us;
+  double scale_gemm, scale_attn;
 } nf_plan_profile;
 nf_status nf_plan_predict(const nf_plan_profile* prof, const nf_shape* shape, const nf_plan* plan,
                           const nf_batch* batch, double* us);
@@ -486,15 +490,16 @@ nf_status nf_plan_predict(const nf_plan_profile* prof, const nf_shape* shape, co
  * step of the chosen plan, number of candidates predicted}.
  * nf_plan_search_report returns the plans the last search on this layer ran
  * (the calibration runs, then the timed candidates) with their predicted and
- * measured ms per step: *n = their number, the first min(n, max) copied to
- * the arrays (each may be NULL).  An empty batch returns the unsplit plan
+ * measured ms per step, and calibration[i] = 1 for a calibration run (whose
+ * cross-stream wait was fitted to make the model meet it) else 0: *n = their
+ * number, the first min(n, max) copied to the arrays (each may be NULL).  An empty batch returns the unsplit plan
  * without running anything.  Errors: NF_ERR_INVALID_ARG for a null argument,
  * NF_ERR_UNSUPPORTED with per-kernel timing on, any error of nf_layer_step. */
 nf_status nf_plan_search(nf_layer* layer, nf_kv_pool* pool, const nf_batch* batch,
                          const nf_search_opts* opts, nf_plan* out, double* times_ms,
                          void* stream);
 nf_status nf_plan_search_report(const nf_layer* layer, int32_t max, nf_plan* plans, double* predicted_ms,
-                                double* measured_ms, int32_t* n);
+                                double* measured_ms, int32_t* calibration, int32_t* n);
 
 /* ---- intermediates ----------------------------------------------------------
  * Device pointer and row stride (elements) of an intermediate of the last

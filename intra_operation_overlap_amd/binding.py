@@ -58,7 +58,8 @@ class nf_plan_profile(ctypes.Structure):
                 ("front_us", ctypes.c_double * NF_PROFILE_POINTS), ("oproj_us", ctypes.c_double * NF_PROFILE_POINTS),
                 ("ffn_us", ctypes.c_double * NF_PROFILE_POINTS), ("attn_base_us", ctypes.c_double),
                 ("attn_us_per_page", ctypes.c_double), ("gap_us", ctypes.c_double), ("slow_gemm", ctypes.c_double),
-                ("slow_attn", ctypes.c_double), ("wait_us", ctypes.c_double)]
+                ("slow_attn", ctypes.c_double), ("wait_us", ctypes.c_double), ("scale_gemm", ctypes.c_double),
+                ("scale_attn", ctypes.c_double)]
 
 
 class nf_loop_opts(ctypes.Structure):
@@ -104,7 +105,7 @@ _SIGS = {
     "nf_plan_search": (i32, [vp, vp, ctypes.POINTER(nf_batch), ctypes.POINTER(nf_search_opts),
                              ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double), vp]),
     "nf_plan_search_report": (i32, [vp, i32, ctypes.POINTER(nf_plan), ctypes.POINTER(ctypes.c_double),
-                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
     "nf_plan_predict": (i32, [ctypes.POINTER(nf_plan_profile), ctypes.POINTER(nf_shape), ctypes.POINTER(nf_plan),
                               ctypes.POINTER(nf_batch), ctypes.POINTER(ctypes.c_double)]),
     "nf_layer_intermediate": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64)]),
@@ -249,13 +250,15 @@ class Layer:
         return p, (t[0], t[1])
 
     def search_report(self, max_entries: int = 64):
-        """[(plan dict, predicted ms, measured ms)] of the last plan search."""
+        """[(plan dict, predicted ms, measured ms, calibration run?)] of the last plan search."""
         plans = (nf_plan * max_entries)()
         pr = (ctypes.c_double * max_entries)()
         me = (ctypes.c_double * max_entries)()
+        cal = (i32 * max_entries)()
         n = i32()
-        check(lib().nf_plan_search_report(self.h, max_entries, plans, pr, me, ctypes.byref(n)), "nf_plan_search_report")
-        return [(plan_dict(plans[i]), pr[i], me[i]) for i in range(min(n.value, max_entries))]
+        check(lib().nf_plan_search_report(self.h, max_entries, plans, pr, me, cal, ctypes.byref(n)),
+              "nf_plan_search_report")
+        return [(plan_dict(plans[i]), pr[i], me[i], bool(cal[i])) for i in range(min(n.value, max_entries))]
 
     def intermediate(self, which: int):
         ptr, stride = vp(), i64()

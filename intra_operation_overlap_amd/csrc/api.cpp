@@ -133,6 +133,7 @@ size_t dtype_bytes(int dt) { return dt == NF_BF16 ? 2 : 4; }
 struct SearchEntry {
   nf_plan plan;
   double predicted_ms, measured_ms;
+  bool calibration = false;     // a run the model's inputs were fitted to
 };
 
 struct nf_layer {
@@ -1849,12 +1850,13 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
   const bool verbose = std::getenv("NF_SEARCH_VERBOSE") != nullptr;
 
   // ms per step of `plan`: `warm` untimed steps, then `reps` between events
-  auto measure = [&](const nf_plan& plan, int warm, int reps, double& ms) -> nf_status {
+  auto measure = [&](const nf_plan& plan, int warm, int reps, double& ms, const nf_batch* bb = nullptr) -> nf_status {
+    if (!bb) bb = b;
     nf_status st = NF_OK;
-    for (int w = 0; w < warm && st == NF_OK; ++w) st = step_impl(L, P, b, s, plan);
+    for (int w = 0; w < warm && st == NF_OK; ++w) st = step_impl(L, P, bb, s, plan);
     if (st != NF_OK) return st;
     HIP_TRY(hipEventRecord(bk.e0, s));
-    for (int r = 0; r < reps && st == NF_OK; ++r) st = step_impl(L, P, b, s, plan);
+    for (int r = 0; r < reps && st == NF_OK; ++r) st = step_impl(L, P, bb, s, plan);
     HIP_TRY(hipEventRecord(bk.e1, s));
     HIP_TRY(hipEventSynchronize(bk.e1));
     if (st != NF_OK) return st;
@@ -1864,9 +1866,10 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
     return NF_OK;
   };
   // per-step microseconds of each operation class over `reps` profiled steps
-  auto classes = [&](const nf_plan& plan, int reps, double* cls) -> nf_status {
+  auto classes = [&](const nf_plan& plan, int reps, double* cls, const nf_batch* bb = nullptr) -> nf_status {
+    if (!bb) bb = b;
     nf_status st = nf_profile_enable(L, 1, nullptr);
-    for (int r = 0; r < reps && st == NF_OK; ++r) st = step_impl(L, P, b, s, plan);
+    for (int r = 0; r < reps && st == NF_OK; ++r) st = step_impl(L, P, bb, s, plan);
     if (st != NF_OK) {
       (void)nf_profile_enable(L, 0, nullptr);
       return st;
@@ -1882,17 +1885,45 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
     return nf_profile_enable(L, 0, nullptr);
   };
 
+  // Per-kernel timing adds event packets around every kernel, so a profiled
+  // step's class times can sum past the same step timed plainly; they are
+  // scaled down to the plain step time (one stream: the step is their sum
+  // plus the gaps between launches).
+  auto fit_classes = [](double* cls, double ms) {
+    const double total = cls[0] + cls[1] + cls[2] + cls[3];
+    if (total > ms * 1e3 && total > 0)
+      for (int c = 0; c < 4; ++c) cls[c] *= ms * 1e3 / total;
+  };
+
   nf_status st = NF_OK;
   nf_plan_profile prof{};
   std::vector<SearchEntry> report, timed;      // calibration runs; candidates timed in step 4
   std::vector<std::pair<nf_plan, double>> preds;
   do {
+    // the device settles first (clocks, caches): the first steps after idle
+    // run slower than the ones the candidates are timed with later
+    {
+      double ms = 0;
+      if ((st = measure(unsplit, 10, 1, ms)) != NF_OK) break;
+    }
     // 1. solo profiles on one stream
     double gap_sum = 0;
     int gap_n = 0;
     std::vector<std::pair<double, double>> att;     // (page units per nano-batch, us per launch)
     const int kmax = std::min(opts.max_count, T);
-    prof.n_points = kmax;
+    // a prefix of the batch's requests of about T/8 tokens adds the profile
+    // point below the smallest equal split, where weight-bound GEMMs stop
+    // scaling with the tokens
+    nf_batch pre = *b;
+    pre.n_requests = 0;
+    pre.n_tokens = 0;
+    for (int r = 0; r < b->n_requests && pre.n_tokens < T / 8; ++r) {
+      pre.n_requests = r + 1;
+      pre.n_tokens = b->req_q_start[r] + b->req_q_len[r];
+    }
+    const bool small = kmax >= 2 && pre.n_tokens > 0 && 2 * pre.n_tokens <= T / kmax;
+    const int base = small ? 1 : 0;
+    prof.n_points = kmax + base;
     double solo2[4] = {0, 0, 0, 0};
     for (int k = 1; k <= kmax && st == NF_OK; ++k) {
       int32_t sz[NF_MAX_NANO];
@@ -1901,12 +1932,14 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
       double ms = 0, cls[4];
       if ((st = measure(pl, k == 1 ? 3 : 1, 3, ms)) != NF_OK) break;
       if ((st = classes(pl, 2, cls)) != NF_OK) break;
-      const int i = kmax - k;                  // ascending nano-batch size
+      // the co-run ratios below compare profiled runs with profiled runs
+      if (k == 2) std::copy(cls, cls + 4, solo2);
+      fit_classes(cls, ms);
+      const int i = base + kmax - k;           // ascending nano-batch size
       prof.tokens[i] = (double)T / k;
       prof.front_us[i] = cls[0] / k;
       prof.oproj_us[i] = cls[2] / k;
       prof.ffn_us[i] = cls[3] / k;
-      if (k == 2) std::copy(cls, cls + 4, solo2);
       double units[NF_MAX_NANO];
       attn_page_units(L->s, *b, pl, units);
       double u = 0;
@@ -1916,6 +1949,21 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
       ++gap_n;
     }
     if (st != NF_OK) break;
+    if (small) {
+      const int32_t one = pre.n_tokens;
+      const nf_plan pl = make_plan(1, &one, NF_ORDER_SEQUENTIAL, 1, 0, 0, 0);
+      double ms = 0, cls[4];
+      if ((st = measure(pl, 1, 3, ms, &pre)) != NF_OK) break;
+      if ((st = classes(pl, 2, cls, &pre)) != NF_OK) break;
+      fit_classes(cls, ms);
+      prof.tokens[0] = pre.n_tokens;
+      prof.front_us[0] = cls[0];
+      prof.oproj_us[0] = cls[2];
+      prof.ffn_us[0] = cls[3];
+      double units[NF_MAX_NANO];
+      attn_page_units(L->s, pre, pl, units);
+      att.push_back({units[0], cls[1]});
+    }
     prof.gap_us = gap_n ? gap_sum / gap_n : 0;
     if (att.size() >= 2) {          // least squares: us = base + slope * units
       double sx = 0, sy = 0, sxx = 0, sxy = 0;
@@ -1936,7 +1984,7 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
     prof.wait_us = 0;
     if (verbose)
       std::fprintf(stderr, "nf search: solo fronts %.1f..%.1f us, attention %.2f + %.5f us/page unit, gap %.1f us\n",
-                   prof.front_us[0], prof.front_us[kmax - 1], prof.attn_base_us, prof.attn_us_per_page,
+                   prof.front_us[0], prof.front_us[prof.n_points - 1], prof.attn_base_us, prof.attn_us_per_page,
                    prof.gap_us);
 
     // 2. interference per two-stream resource split
@@ -1952,20 +2000,38 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
         if ((st = measure(pl, 1, 3, ms)) != NF_OK) break;
         if ((st = classes(pl, 2, cls)) != NF_OK) break;
         nf_plan_profile q = prof;
-        q.slow_attn = std::max(1.0, solo2[1] > 0 ? cls[1] / solo2[1] : 1.0);
         const double g_ov = cls[0] + cls[2] + cls[3], g_solo = solo2[0] + solo2[2] + solo2[3];
-        const double frac = cls[1] > 0 ? std::min(0.95, std::max(0.0, (g_ov - g_solo) / cls[1])) : 0.0;
-        q.slow_gemm = 1.0 / (1.0 - frac);
+        if (sp.g || sp.a) {
+          // a CU budget confines each side also while it runs alone: its
+          // durations scale throughout, with no further co-run slowdown
+          q.scale_gemm = g_solo > 0 ? std::max(0.5, g_ov / g_solo) : 1.0;
+          q.scale_attn = solo2[1] > 0 ? std::max(0.5, cls[1] / solo2[1]) : 1.0;
+        } else {
+          // unmasked, the sides slow each other only while both run
+          q.slow_attn = std::max(1.0, solo2[1] > 0 ? cls[1] / solo2[1] : 1.0);
+          const double frac = cls[1] > 0 ? std::min(0.95, std::max(0.0, (g_ov - g_solo) / cls[1])) : 0.0;
+          q.slow_gemm = 1.0 / (1.0 - frac);
+        }
         double tok[2] = {(double)sz2[0], (double)sz2[1]}, units[NF_MAX_NANO];
         attn_page_units(L->s, *b, pl, units);
-        const double pred0 = predict_plan_us(q, pl, tok, units);
-        q.wait_us = std::isfinite(pred0) ? std::max(0.0, (ms * 1e3 - pred0) / 4.0) : 0.0;
+        // the cross-stream wait that makes the model meet the measured step
+        // (the prediction grows with the wait; bisection over 0..500 us)
+        double lo = 0, hi = 500;
+        q.wait_us = 0;
+        if (predict_plan_us(q, pl, tok, units) < ms * 1e3) {
+          for (int it = 0; it < 40; ++it) {
+            q.wait_us = 0.5 * (lo + hi);
+            (predict_plan_us(q, pl, tok, units) < ms * 1e3 ? lo : hi) = q.wait_us;
+          }
+          q.wait_us = 0.5 * (lo + hi);
+        }
         calib[c] = q;
         calib_ok[c] = true;
-        report.push_back({pl, predict_plan_us(q, pl, tok, units) * 1e-3, ms});
+        report.push_back({pl, predict_plan_us(q, pl, tok, units) * 1e-3, ms, true});
         if (verbose)
-          std::fprintf(stderr, "nf search: split gemm %d attn %d waves %d: slowdown gemm %.2f attn %.2f, wait %.1f us "
-                       "(two nano-batches %.3f ms)\n", sp.g, sp.a, sp.w, q.slow_gemm, q.slow_attn, q.wait_us, ms);
+          std::fprintf(stderr, "nf search: split gemm %d attn %d waves %d: slowdown gemm %.2f attn %.2f, scale gemm %.2f "
+                       "attn %.2f, wait %.1f us (two nano-batches %.3f ms)\n", sp.g, sp.a, sp.w, q.slow_gemm,
+                       q.slow_attn, q.scale_gemm, q.scale_attn, q.wait_us, ms);
       }
     }
     if (st != NF_OK) break;
@@ -2082,7 +2148,7 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
 }
 
 extern "C" nf_status nf_plan_search_report(const nf_layer* L, int32_t max, nf_plan* plans, double* predicted_ms,
-                                           double* measured_ms, int32_t* n) {
+                                           double* measured_ms, int32_t* calibration, int32_t* n) {
   if (!L || !n || max < 0) return set_err(NF_ERR_INVALID_ARG, "nf_plan_search_report: bad argument");
   const std::vector<SearchEntry>& r = L->search_report;
   *n = (int32_t)r.size();
@@ -2090,6 +2156,7 @@ extern "C" nf_status nf_plan_search_report(const nf_layer* L, int32_t max, nf_pl
     if (plans) plans[i] = r[i].plan;
     if (predicted_ms) predicted_ms[i] = r[i].predicted_ms;
     if (measured_ms) measured_ms[i] = r[i].measured_ms;
+    if (calibration) calibration[i] = r[i].calibration ? 1 : 0;
   }
   return NF_OK;
 }

@@ -13,7 +13,9 @@
 // its KV pages).  While both streams run an operation, the GEMM side
 // progresses at 1 / slow_gemm and attention at 1 / slow_attn of its solo
 // rate: the co-run interference, calibrated per resource split from one
-// overlapped run.  The simulation advances from event to event (an operation
+// overlapped run.  Under a CU budget a side is confined whether or not the
+// other runs, so its durations are scaled by scale_gemm / scale_attn
+// throughout.  The simulation advances from event to event (an operation
 // finishing, or one becoming ready) and returns the makespan.
 #include <algorithm>
 #include <cmath>
@@ -68,6 +70,7 @@ void attn_page_units(const nf_shape& sh, const nf_batch& b, const nf_plan& plan,
 double predict_plan_us(const nf_plan_profile& p, const nf_plan& plan, const double* tokens, const double* pages) {
   const int k = std::max(1, std::min(plan.count, NF_MAX_NANO));
   const bool two = plan.n_streams == 2;
+  const double sc_g = p.scale_gemm > 0 ? p.scale_gemm : 1.0, sc_a = p.scale_attn > 0 ? p.scale_attn : 1.0;
   std::vector<Op> ops;
   std::vector<std::vector<int>> queue(2);
   int f[NF_MAX_NANO], a[NF_MAX_NANO], o[NF_MAX_NANO], nn[NF_MAX_NANO];
@@ -77,10 +80,10 @@ double predict_plan_us(const nf_plan_profile& p, const nf_plan& plan, const doub
       ops.push_back(Op{stream, std::max(0.0, us) + p.gap_us});
       return (int)ops.size() - 1;
     };
-    f[j] = add(0, interp(p, p.front_us, tj));
-    a[j] = add(two ? 1 : 0, p.attn_base_us + p.attn_us_per_page * pages[j]);
-    o[j] = add(0, interp(p, p.oproj_us, tj));
-    nn[j] = add(0, interp(p, p.ffn_us, tj));
+    f[j] = add(0, sc_g * interp(p, p.front_us, tj));
+    a[j] = add(two ? 1 : 0, sc_a * (p.attn_base_us + p.attn_us_per_page * pages[j]));
+    o[j] = add(0, sc_g * interp(p, p.oproj_us, tj));
+    nn[j] = add(0, sc_g * interp(p, p.ffn_us, tj));
     ops[a[j]].dep = f[j];
     ops[o[j]].dep = a[j];
   }

@@ -57,6 +57,22 @@ def test_two_streams_co_run_rates():
     assert _predict(_profile(slow_g=2.0, slow_a=2.0), plan) == pytest.approx(190)
 
 
+def test_budget_scales_apply_whether_or_not_the_other_side_runs():
+    # one stream: every GEMM-side duration x2, attention x3
+    p = _profile()
+    p.scale_gemm, p.scale_attn = 2.0, 3.0
+    assert _predict(p, B.make_plan(1, [16])) == pytest.approx(2 * (10 + 5 + 30) + 3 * 50)
+    # two streams, GEMM side x2 (F 20, O 10, N 60), attention unscaled, no co-run slowdown:
+    # F0 0-20; F1 20-40; A0 20-70; O0 70-80; N0 80-140; A1 70-120; O1 140-150; N1 150-210
+    p = _profile()
+    p.scale_gemm = 2.0
+    assert _predict(p, B.make_plan(2, [8, 8], n_streams=2)) == pytest.approx(210)
+    # zero reads as one
+    p = _profile()
+    p.scale_gemm = p.scale_attn = 0.0
+    assert _predict(p, B.make_plan(1, [16])) == pytest.approx(95)
+
+
 def test_deep_order_two_streams():
     # two: G issues F0 | F1 O0 | O1 N0 | N1
     # F0 0-10; F1 10-20; A0 10-60; O0 60-65; A1 60-110; O1 110-115; N0 115-145; N1 145-175
