@@ -148,6 +148,22 @@ def test_shape_sweep_parity(case):
         _full_check(S, f"{case} k1 attn_waves1", B.make_plan(1, [T], n_streams=2, attn_waves_per_cu=1))
 
 
+def test_degenerate_batches_parity():
+    """A single token at position 0 (one key, one page slot); decode tokens on
+    the last slot of a page and the first slot of the next; a prefill chunk of
+    exactly one page from position 0."""
+    shape = W.Shape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=688, dtype="bf16", rope_theta=1e4)
+    one = GH.setup(W.Workload("one_tok", shape, n_decode=1, ctx_range=(0, 0), prefill=None, seed=111))
+    _full_check(one, "one token k1", B.make_plan(1, [1]))
+    _full_check(one, "one token two streams attn_waves1", B.make_plan(1, [1], n_streams=2, attn_waves_per_cu=1))
+    edges = GH.setup(W.Workload("page_edges", shape, n_decode=6, ctx_range=(15, 16), prefill=(0, 16), seed=112))
+    T = edges.batch.n_tokens
+    assert set(edges.batch.pos[:6].tolist()) <= {15, 16} and edges.batch.req_q_len[-1] == 16
+    _full_check(edges, "page edges k1", B.make_plan(1, [T]))
+    _full_check(edges, "page edges k2", B.make_plan(2, [6, T - 6], n_streams=2))
+    _full_check(edges, "page edges k2 attn_waves4", B.make_plan(2, [6, T - 6], n_streams=2, attn_waves_per_cu=4))
+
+
 def test_split_k_small_batch_parity():
     """Decode-sized nano-batches take the split-K GEMM path (fused reduction)."""
     wl = W.Workload("splitk", W.Shape(hidden=2048, n_q_heads=8, n_kv_heads=4, head_dim=128, ffn=1536,
