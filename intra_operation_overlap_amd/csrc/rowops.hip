@@ -190,6 +190,78 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   v[kv_v_off(slot, j + half)] = v1;
 }
 
+// bf16 form with four rotation pairs per thread (j .. j+3 and their partners
+// j+d/2 ..): 16-byte partial loads, 8-byte stores, and one block of
+// 2048 / d heads per token, so a token's heads go out in one round of loads
+// rather than one 4-byte load per thread.  Same arithmetic per element as
+// rope_append_kernel (partials summed in slice order, then the rotation).
+__global__ __launch_bounds__(256) void rope_append_bf16x4_kernel(RopeAppendArgs a) {
+  const int t = blockIdx.x;
+  const int d = a.d, half = d / 2, tph = half / 4;       // threads per head
+  const int head = blockIdx.y * (256 / tph) + threadIdx.x / tph;
+  const int j = 4 * (threadIdx.x % tph);
+  if (head >= a.nq + 2 * a.nkv) return;
+  const int p = a.pos[t];
+  const int r = a.tok_req[t];
+  const int ncols = (a.nq + 2 * a.nkv) * d;
+  float x0[4], x1[4];
+  bf16x4 v0, v1;
+  if (a.splits > 1) {
+    const float* P = a.part + (int64_t)t * a.part_ld + (int64_t)head * d + j;
+    const f32x4 s0 = sum_slices<f32x4>(P, a.zstride, a.splits);
+    const f32x4 s1 = sum_slices<f32x4>(P + half, a.zstride, a.splits);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v0[e] = (bf16)s0[e];
+      v1[e] = (bf16)s1[e];
+    }
+    bf16* out = (bf16*)a.qkv + (int64_t)t * ncols + (int64_t)head * d;
+    *(bf16x4*)(out + j) = v0;
+    *(bf16x4*)(out + j + half) = v1;
+  } else {
+    const bf16* row = (const bf16*)a.qkv + (int64_t)t * ncols + (int64_t)head * d;
+    v0 = *(const bf16x4*)(row + j);
+    v1 = *(const bf16x4*)(row + j + half);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x0[e] = (float)v0[e];
+    x1[e] = (float)v1[e];
+  }
+  if (head < a.nq + a.nkv) {
+    const f32x4* cs = (const f32x4*)((const float2*)a.cos_sin + (int64_t)p * half + j);
+    const f32x4 c01 = cs[0], c23 = cs[1];
+    const float cx[4] = {c01[0], c01[2], c23[0], c23[2]}, cy[4] = {c01[1], c01[3], c23[1], c23[3]};
+    bf16x4 y0, y1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y0[e] = (bf16)(x0[e] * cx[e] - x1[e] * cy[e]);
+      y1[e] = (bf16)(x0[e] * cy[e] + x1[e] * cx[e]);
+    }
+    if (head < a.nq) {
+      bf16* q = (bf16*)a.q_rot + (int64_t)t * a.nq * d + (int64_t)head * d;
+      *(bf16x4*)(q + j) = y0;
+      *(bf16x4*)(q + j + half) = y1;
+      return;
+    }
+    const int page = a.page_indices[a.page_indptr[r] + p / a.page_size];
+    const int slot = p % a.page_size;
+    bf16* k = (bf16*)a.k_pool + ((int64_t)page * a.nkv + (head - a.nq)) * a.page_size * d;
+    // dims j .. j+3 lie in one run of 8 of the K block order, so contiguously
+    *(bf16x4*)(k + kv_k_off(slot, j)) = y0;
+    *(bf16x4*)(k + kv_k_off(slot, j + half)) = y1;
+    return;
+  }
+  const int page = a.page_indices[a.page_indptr[r] + p / a.page_size];
+  const int slot = p % a.page_size;
+  bf16* v = (bf16*)a.v_pool + ((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * a.page_size * d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[kv_v_off(slot, j + e)] = v0[e];
+    v[kv_v_off(slot, j + half + e)] = v1[e];
+  }
+}
+
 // ---------------------------------------------------------------- MoE router
 // Single 256-thread block.  Top-k per token (larger logit first; equal logits
 // keep the lower expert index first), gate weights = softmax over the chosen
@@ -448,10 +520,12 @@ hipError_t rope_append(int dtype, const RopeAppendArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int hpb = 256 / (a.d / 2);                      // head_dim in [32, 256]: 2..16 heads per block
   const dim3 grid(a.T, (a.nq + 2 * a.nkv + hpb - 1) / hpb);
-  if (dtype == 1)
-    launch(rope_append_kernel<bf16>, grid, 256, 0, s, a);
-  else
+  if (dtype == 1) {
+    const int hpb4 = 2048 / a.d;                         // four pairs per thread: 8..64 heads per block
+    launch(rope_append_bf16x4_kernel, dim3(a.T, (a.nq + 2 * a.nkv + hpb4 - 1) / hpb4), 256, 0, s, a);
+  } else {
     launch(rope_append_kernel<float>, grid, 256, 0, s, a);
+  }
   return hipGetLastError();
 }
 
