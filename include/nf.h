@@ -466,14 +466,18 @@ nf_status nf_plan_predict(const nf_plan_profile* prof, const nf_shape* shape, co
  * weigh the interference of concurrent operations), whose four dimensions
  * the "Search Space" card of the do-not-panic NanoFlow page lists, and for
  * the Gurobi-based solver of the ossradar Nanoflow page:
- *  1. solo profiles: the batch run as 1..opts->max_count equal nano-batches
- *     on one stream with every kernel timed, giving the nf_plan_profile
- *     inputs (front, O-projection and FFN durations per nano-batch size,
- *     attention per KV page unit, the per-operation gap);
+ *  1. solo profiles: after ten settling steps, the batch run as
+ *     1..opts->max_count equal nano-batches, and a prefix of its requests of
+ *     about T/8 tokens, on one stream with every kernel timed, giving the
+ *     nf_plan_profile inputs (front, O-projection and FFN durations per
+ *     nano-batch size, attention per KV page unit, the per-operation gap),
+ *     scaled to the same steps timed without per-kernel events;
  *  2. interference: for each two-stream resource split -- all CUs to both
- *     sides; attention held to 8 or 4 waves per CU; 16 + 16, 24 + 8 and
- *     20 + 12 CUs per XCD -- two equal nano-batches run overlapped once,
- *     giving that split's co-run slowdowns and cross-stream wait;
+ *     sides; attention held to 8 or 4 waves per CU; GEMM + attention CUs per
+ *     XCD of 28 + 4, 24 + 8, 20 + 12, 16 + 16, 12 + 20 and 8 + 24 -- two equal
+ *     nano-batches run overlapped once, giving that split's co-run slowdowns
+ *     (unmasked) or per-side scale factors (CU budgets), and the cross-stream
+ *     wait fitted so that the model meets the run;
  *  3. every candidate is predicted with the model of nf_plan_predict:
  *     counts 1..max_count; sizes equal, attention-balanced, in 64-token
  *     steps (two nano-batches), quarter / half / quarter (three), and the

@@ -1785,8 +1785,9 @@ struct Split {
 };
 // two-stream resource splits: every CU to both sides; attention held to 8 or
 // 4 waves per CU (persistent four-wave workgroups, GEMM tiles that fit beside
-// them); CU partitions per XCD
-const Split kSplits[] = {{0, 0, 0}, {0, 0, 8}, {0, 0, 4}, {16, 16, 0}, {24, 8, 0}, {20, 12, 0}};
+// them); CU partitions per XCD from 28 + 4 to 8 + 24
+const Split kSplits[] = {{0, 0, 0}, {0, 0, 8}, {0, 0, 4}, {28, 4, 0}, {24, 8, 0}, {20, 12, 0},
+                         {16, 16, 0}, {12, 20, 0}, {8, 24, 0}};
 constexpr int kNSplits = sizeof(kSplits) / sizeof(kSplits[0]);
 
 }  // namespace
