@@ -488,6 +488,15 @@ constexpr int stage_rows(int bm, int fit) {
   return 0;
 }
 
+// f(integral_constant<int, U>) for U = B .. N - 1, in order
+template <int B, int N, class F>
+__device__ __forceinline__ void unroll_n(F&& f) {
+  if constexpr (B < N) {
+    f(std::integral_constant<int, B>{});
+    unroll_n<B + 1, N>(f);
+  }
+}
+
 // wait until at most `after` slabs issued after the current one are pending
 // (each slab is X loads of this thread, and loads retire in order)
 template <class C, int A = C::STAGES - 2>
@@ -694,24 +703,33 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
     for (int s = 0; s < L; ++s)
 #pragma unroll
       for (int r = 0; r < NR; ++r) read1(smem, s, r);
-    for (int kt = 0; kt < nk; ++kt) {
-      const char* cur = smem + (kt % C::STAGES) * C::SLAB;
-      const char* nxt = smem + ((kt + 1) % C::STAGES) * C::SLAB;
+    // Slab kt lives in stage buffer U = kt % STAGES.  The loop is unrolled by
+    // STAGES so that U is a constant in each copy: every fragment address is
+    // then a per-lane register plus an immediate offset, where a run-time
+    // buffer index cost vector adds for every read of every slab.
+    auto slab = [&](int kt, auto u_c) {
+      constexpr int U = decltype(u_c)::value;
+      const char* cur = smem + U * C::SLAB;
+      const char* nxt = smem + ((U + 1) % C::STAGES) * C::SLAB;
 #pragma unroll
       for (int s = 0; s < KS - L; ++s) step(s, cur, s + L, 0, 0, 0, 0, false);
       // every wave holds this slab's last fragments and slab kt + 1 has landed
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<(C::STAGES - 2) * C::X>();
       barrier_lds();
-      const int t = kt + C::STAGES, buf = kt % C::STAGES;
+      const int t = kt + C::STAGES;
       const bool real = t < nk;
 #pragma unroll
       for (int s = KS - L; s < KS; ++s) {
         // the next slab's first k-steps (after the last slab these reads go unused)
         const int first = s == KS - L;
-        step(s, nxt, s + L - KS, first ? D_FIRST : D_REST, first ? 0 : D_FIRST + (s - KS + L - 1) * D_REST, t, buf, real);
+        step(s, nxt, s + L - KS, first ? D_FIRST : D_REST, first ? 0 : D_FIRST + (s - KS + L - 1) * D_REST, t, U, real);
       }
-    }
+    };
+    for (int kt = 0; kt < nk; kt += C::STAGES)
+      unroll_n<0, C::STAGES>([&](auto u) {
+        if (kt + decltype(u)::value < nk) slab(kt + decltype(u)::value, u);
+      });
     wait_vmcnt<0>();                     // the empty loads too: none may land during the epilogue
   };
   // Burst refills: the slab's loads are issued together right after the
