@@ -273,8 +273,13 @@ nf_status nf_kv_offload(nf_kv_pool* pool, const int32_t* pages, int32_t n, void*
  * streams (partitioning a device's functional units: "How it works" on the
  * bytedragons Nanoflow page).  It validates count, order, streams and CU
  * split against the device (sizes are checked against each batch at step
- * time) and (re)creates the CU-masked streams.  Errors: NF_ERR_INVALID_ARG, NF_ERR_OUT_OF_RANGE,
- * NF_ERR_HIP. */
+ * time) and creates the plan's CU-masked stream pair if it does not exist.
+ * Masked pairs belong to the device, not the layer: every layer on a device
+ * shares them, at most two stay alive, and the least recently used one is
+ * drained and destroyed when a third budget is needed (each masked stream
+ * holds a hardware queue; dozens of them slowed masked steps severalfold).
+ * They live until the process ends.  Errors: NF_ERR_INVALID_ARG,
+ * NF_ERR_OUT_OF_RANGE, NF_ERR_HIP. */
 nf_status nf_plan_set(nf_layer* layer, const nf_plan* plan);
 nf_status nf_plan_get(const nf_layer* layer, nf_plan* plan);
 
