@@ -105,7 +105,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--plan", default="auto",
                     help="auto (workload default / search), k1 (unsplit), overlap2 (two nano-batches on two "
-                         "streams), or overlap2:G:A (the same with G GEMM and A attention CUs per XCD)")
+                         "streams), overlap2:G:A (the same with G GEMM and A attention CUs per XCD), lanes2 (two "
+                         "nano-batches, each on a lane of its own) or lanes2:G:A")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the KV-offload measurement (nf_kv_offload alone and beside steps)")
@@ -198,11 +199,13 @@ def main():
     half = [T - T // 2, T // 2]
     baselines = (("sequential_unsplit_ms", B.make_plan(1, [T])),
                  ("sequential_split2_ms", B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL)),
-                 ("overlapped_split2_two_streams_ms", B.make_plan(2, half, n_streams=2)))
-    if args.plan.startswith("overlap2"):
+                 ("overlapped_split2_two_streams_ms", B.make_plan(2, half, n_streams=2)),
+                 ("overlapped_split2_lanes_ms", B.make_plan(2, half, order=B.NF_ORDER_LANES, n_streams=2)))
+    if args.plan.startswith("overlap2") or args.plan.startswith("lanes2"):
         parts = args.plan.split(":")
         g, a = (int(parts[1]), int(parts[2])) if len(parts) == 3 else (0, 0)
-        plan = B.make_plan(2, half, n_streams=2, gemm_cus_per_xcd=g, attn_cus_per_xcd=a)
+        order = B.NF_ORDER_LANES if parts[0] == "lanes2" else B.NF_ORDER_PIPELINED
+        plan = B.make_plan(2, half, order=order, n_streams=2, gemm_cus_per_xcd=g, attn_cus_per_xcd=a)
         layer.set_plan(plan)
     elif args.plan == "k1" or wl.plan_sizes == (T,):
         plan = B.make_plan(1, [T])
@@ -640,7 +643,8 @@ def stack_measure(n, wl, batch, layer0, pool0, acts, main_plan, sp, steps=10):
     half = [T - T // 2, T // 2]
     for name, plan in (("unsplit", B.make_plan(1, [T])),
                        ("split2_sequential", B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL)),
-                       ("overlap2_pipelined", B.make_plan(2, half, n_streams=2))):
+                       ("overlap2_pipelined", B.make_plan(2, half, n_streams=2)),
+                       ("lanes2", B.make_plan(2, half, order=B.NF_ORDER_LANES, n_streams=2))):
         for L in layers:
             L.set_plan(plan)
         res[f"{name}_eager"] = timed(lambda: B.stack_step(layers, pools, hb, sp))

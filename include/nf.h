@@ -128,7 +128,20 @@ typedef enum nf_order {
    * O-projection of t-1 and the FFN of t-2, and a collective after an
    * O-projection (nf_layer_set_allreduce_emulation) beside the next
    * nano-batch's O-projection */
-  NF_ORDER_DEEP = 2
+  NF_ORDER_DEEP = 2,
+  /* n_streams == 2 only: two lanes.  Nano-batch j runs every operation of
+   * its own (front, attention, O-projection, FFN) on stream j mod 2, so one
+   * lane's attention shares the chip with the other lane's GEMMs as each
+   * kernel frees CUs.  Lane 1 starts once nano-batch 0's front is done (one
+   * wait); the attention of a nano-batch j >= 2 whose first request began
+   * in an earlier nano-batch (a prefill chunk cut by the plan) also waits
+   * for the front of nano-batch j - 1, which appended keys it reads; the
+   * caller's stream joins both lanes at the end (one wait).  Each lane's GEMMs take
+   * their tiles for the lane's share of the chip: its CU budget under a CU
+   * split (gemm_cus_per_xcd for lane 0, the attention budget for lane 1),
+   * else half the CUs, so that a lane's GEMM of half the tokens keeps full-K
+   * 256 x 256 tiles instead of split-K ones sized for the whole chip. */
+  NF_ORDER_LANES = 3
 } nf_order;
 
 /* Nano-batch plan: count, sizes, operation order and resource split. */

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libnf.so")
 
 NF_OK, NF_ERR_INVALID_ARG, NF_ERR_OUT_OF_RANGE, NF_ERR_UNSUPPORTED, NF_ERR_NO_PLAN, NF_ERR_HIP = range(6)
 NF_F32, NF_BF16 = 0, 1
-NF_ORDER_PIPELINED, NF_ORDER_SEQUENTIAL, NF_ORDER_DEEP = 0, 1, 2
+NF_ORDER_PIPELINED, NF_ORDER_SEQUENTIAL, NF_ORDER_DEEP, NF_ORDER_LANES = 0, 1, 2, 3
 NF_MAX_NANO = 4
 
 i32 = ctypes.c_int32

@@ -146,6 +146,7 @@ struct nf_layer {
   std::map<std::pair<int, int>, StreamPair> pairs;   // unmasked two-stream pair (masked ones: g_pairs)
   hipEvent_t ev_app[NF_MAX_NANO] = {}, ev_att[NF_MAX_NANO] = {};
   hipEvent_t ev_start = nullptr, ev_g = nullptr, ev_a = nullptr;
+  hipEvent_t ev_lane = nullptr;                 // end of lane 1 (lanes order)
   // emulated tensor-parallel all-reduce of the O and down projections
   // (nf_layer_set_allreduce_emulation): mode 0 off, 1 copy engines, 2 a copy
   // kernel of ar_wgs workgroups; on stream sc, with these events
@@ -156,6 +157,7 @@ struct nf_layer {
   DevBuf h, qkv, q_rot, attn, x1, h2, act, y;
   DevBuf r_idx, r_w, r_perm, r_inv, r_off;
   DevBuf splitk, part_o, part_ml, meta, cos_sin;
+  DevBuf splitk_lane1;                          // lane 1's split-K partials (lanes order)
   DevBuf stack_out;                             // this layer's output inside a multi-layer step
   // expert weights in MFMA operand order for the weight-streaming kernels
   // (bf16 mixture-of-experts layers; empty otherwise)
@@ -488,6 +490,11 @@ struct StepCtx {
   const AttnItem* items;
   const MergeItem* merges;
   int gemm_cus, attn_cus;
+  // lanes order: nano-batch j runs on lane j % 2, whose GEMMs choose tiles
+  // for lane_cus[j % 2] CUs and keep their split-K partials apart
+  bool lanes;
+  int lane;                // lane of the nano-batch being issued
+  int lane_cus[2];
   int attn_waves_per_cu;
   int attn_variant;        // 0: one-wave work items (any grid), 1: four-wave workgroups
   // the step's metadata copy rides on the first front's RMSNorm; the event
@@ -498,6 +505,14 @@ struct StepCtx {
 };
 
 char* ptr(const DevBuf& b, int64_t elems, int dt) { return (char*)b.p + elems * (int64_t)dtype_bytes(dt); }
+
+// CUs the GEMMs of the nano-batch being issued choose their tiles for, and
+// the split-K workspace they write
+int gemm_cus_of(const StepCtx& c) { return c.lanes ? c.lane_cus[c.lane] : c.gemm_cus; }
+// GEMM tiles that fit beside a bounded attention grid on the same CUs (not
+// for lanes: there the other lane's attention takes the CUs a GEMM leaves)
+bool coresident(const StepCtx& c) { return c.attn_waves_per_cu > 0 && !c.lanes; }
+DevBuf& splitk_of(const StepCtx& c) { return c.lanes && c.lane ? c.L->splitk_lane1 : c.L->splitk; }
 
 // `partials` != nullptr: when the GEMM splits K, its reduce is left to the
 // consumer, and *partials receives the slice count (1: C was written).
@@ -510,7 +525,7 @@ hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s, int* parti
     prof_end(L, kind, s);
     return e;
   }
-  GemmPlan gp = gemm_choose(g, c.gemm_cus, c.attn_waves_per_cu > 0);
+  GemmPlan gp = gemm_choose(g, gemm_cus_of(c), coresident(c));
   if (partials) {
     *partials = gemm_partials(g, gp);
     g.defer_reduce = *partials > 1;
@@ -518,14 +533,14 @@ hipError_t run_gemm(StepCtx& c, GemmArgs& g, int kind, hipStream_t s, int* parti
   Prof pctx{L, kind, s};
   LaunchHook hook{prof_hook_fn, &pctx};
   prof_begin(L, kind, s);
-  hipError_t e = gemm_bf16(g, gp, L->splitk.p, s, L->prof ? &hook : nullptr);
+  hipError_t e = gemm_bf16(g, gp, splitk_of(c).p, s, L->prof ? &hook : nullptr);
   prof_end(L, pctx.kind, s);
   return e;
 }
 
 size_t gemm_ws_need(const StepCtx& c, GemmArgs g) {
   if (c.L->s.dtype == NF_F32) return 0;
-  return gemm_workspace_bytes(g, gemm_choose(g, c.gemm_cus, c.attn_waves_per_cu > 0));
+  return gemm_workspace_bytes(g, gemm_choose(g, gemm_cus_of(c), coresident(c)));
 }
 
 // GEMM descriptors of nano-batch [t0, t1)
@@ -607,7 +622,7 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
   // ride on the QKV GEMM when it takes the LDS-pipelined path, beside its
   // tiles; otherwise on the RMSNorm before it.
   const bool meta_in_gemm = c.mc_pending && dt == NF_BF16 && c.mc.n16 * 16 > (64 << 10) && [&] {
-    const int cfg = gemm_choose(g.qkv, c.gemm_cus, c.attn_waves_per_cu > 0).cfg;
+    const int cfg = gemm_choose(g.qkv, gemm_cus_of(c), coresident(c)).cfg;
     return cfg >= 10 && cfg <= 30 && g.qkv.K % 64 == 0;
   }();
   prof_begin(L, K_NORM1, s);
@@ -625,7 +640,7 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
   RopeAppendArgs r;
   const int Nqkv = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim;
   if (qkv_parts > 1) {          // RoPE reduces the split-K partials itself
-    r.part = (const float*)L->splitk.p;
+    r.part = (const float*)splitk_of(c).p;
     r.part_ld = Nqkv;
     r.zstride = (int64_t)Tj * Nqkv;
     r.splits = qkv_parts;
@@ -716,7 +731,7 @@ nf_status issue_oproj(StepCtx& c, int j, hipStream_t s, bool* normed) {
   HIP_STEP(run_gemm(c, g.o, K_OPROJ, s, fuse ? &o_parts : nullptr));
   if (o_parts > 1) {            // O-projection split-K reduce + residual + FFN norm in one kernel
     prof_begin(L, K_NORM2, s);
-    HIP_STEP(residual_rmsnorm_partials((const float*)L->splitk.p, H, (int64_t)Tj * H, o_parts, g.o.R, g.o.ldr,
+    HIP_STEP(residual_rmsnorm_partials((const float*)splitk_of(c).p, H, (int64_t)Tj * H, o_parts, g.o.R, g.o.ldr,
                                        g.o.C, g.o.ldc, L->w.ffn_norm, ptr(L->h2, (int64_t)t0 * H, dt), Tj, H,
                                        sh.rms_eps, s));
     prof_end(L, K_NORM2, s);
@@ -762,10 +777,10 @@ nf_status issue_ffn(StepCtx& c, int j, hipStream_t s, bool normed) {
   // grouped: the tile choice depends on the mean rows per expert; the
   // streaming kernels may split K (partials in the split-K workspace)
   prof_begin(L, K_MOE_GATEUP, s);
-  HIP_STEP(gemm_bf16(g.moe_gu, gemm_choose(g.moe_gu, c.gemm_cus), L->splitk.p, s));
+  HIP_STEP(gemm_bf16(g.moe_gu, gemm_choose(g.moe_gu, gemm_cus_of(c)), splitk_of(c).p, s));
   prof_end(L, K_MOE_GATEUP, s);
   prof_begin(L, K_MOE_DOWN, s);
-  HIP_STEP(gemm_bf16(g.moe_down, gemm_choose(g.moe_down, c.gemm_cus), L->splitk.p, s));
+  HIP_STEP(gemm_bf16(g.moe_down, gemm_choose(g.moe_down, gemm_cus_of(c)), splitk_of(c).p, s));
   prof_end(L, K_MOE_DOWN, s);
   void* dst = L->ar_mode ? (void*)ptr(L->ypre, (int64_t)t0 * H, dt)
                          : (void*)((char*)c.b->out + (int64_t)t0 * H * dtype_bytes(dt));
@@ -841,6 +856,10 @@ nf_status prepare_layer(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_
   c.b = &r.b;
   c.gemm_cus = gsplit ? gsplit * L->n_xcd : L->n_cus;
   c.attn_cus = asplit ? asplit * L->n_xcd : L->n_cus;
+  c.lanes = two && plan.order == NF_ORDER_LANES;
+  c.lane = 0;
+  c.lane_cus[0] = gsplit ? c.gemm_cus : std::max(1, L->n_cus / 2);
+  c.lane_cus[1] = asplit ? c.attn_cus : std::max(1, L->n_cus / 2);
   c.attn_waves_per_cu = two ? plan.attn_waves_per_cu : 0;
   // attention work items: a four-wave workgroup each (fastest when attention
   // has the whole chip), or one wave each (many short items) when the plan
@@ -855,15 +874,19 @@ nf_status prepare_layer(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_
   r.count = (int)w.nanos.size();
 
   // workspace the GEMMs and the split attention items need (before any launch)
-  size_t ws = 0;
+  size_t ws[2] = {0, 0};
   for (int j = 0; j < r.count; ++j) {
+    c.lane = c.lanes ? j % 2 : 0;
     NanoGemms g = nano_gemms(c, j, w.nanos[j].t0, w.nanos[j].t1);
+    size_t& need = ws[c.lane];
     if (L->s.n_experts == 1)
-      for (const GemmArgs* a : {&g.qkv, &g.o, &g.gu, &g.down}) ws = std::max(ws, gemm_ws_need(c, *a));
+      for (const GemmArgs* a : {&g.qkv, &g.o, &g.gu, &g.down}) need = std::max(need, gemm_ws_need(c, *a));
     else
-      for (const GemmArgs* a : {&g.qkv, &g.o, &g.moe_gu, &g.moe_down}) ws = std::max(ws, gemm_ws_need(c, *a));
+      for (const GemmArgs* a : {&g.qkv, &g.o, &g.moe_gu, &g.moe_down}) need = std::max(need, gemm_ws_need(c, *a));
   }
-  HIP_TRY(ensure(L->splitk, ws));
+  c.lane = 0;
+  HIP_TRY(ensure(L->splitk, ws[0]));
+  if (ws[1]) HIP_TRY(ensure(L->splitk_lane1, ws[1]));
   const size_t n_part = (size_t)std::max(1, w.n_partials) * L->s.n_kv_heads * 16;
   HIP_TRY(ensure(L->part_o, n_part * L->s.head_dim * sizeof(float)));
   HIP_TRY(ensure(L->part_ml, n_part * 2 * sizeof(float)));
@@ -935,6 +958,7 @@ nf_status prepare_layer(nf_layer* L, nf_kv_pool* P, const nf_batch* b, const nf_
 // for the last collective.
 struct Streams {
   bool two = false, comm = false;
+  bool lanes = false;            // nano-batch j on lane j % 2 (sg, sa)
   hipStream_t caller = nullptr, sg = nullptr, sa = nullptr, sc = nullptr;
   int held_dev = -1;             // a held masked pair (released here)
   hipStream_t held = nullptr;
@@ -948,6 +972,7 @@ struct Streams {
 
 nf_status open_streams(nf_layer* L, const nf_plan& plan, hipStream_t caller, Streams& S) {
   S.two = plan.n_streams == 2;
+  S.lanes = S.two && plan.order == NF_ORDER_LANES;
   S.caller = S.sg = S.sa = caller;
   S.comm = L->ar_mode != 0;
   if (S.comm) {
@@ -993,6 +1018,10 @@ void drain_after_error(const Streams& S) {
 }
 
 nf_status close_streams(nf_layer* L, const Streams& S) {
+  if (S.lanes) {                 // lane 1 joins the caller (lane 0 below)
+    HIP_TRY(hipEventRecord(L->ev_lane, S.sa));
+    HIP_TRY(hipStreamWaitEvent(S.caller, L->ev_lane, 0));
+  }
   if (S.two && S.sg != S.caller) {
     HIP_TRY(hipEventRecord(L->ev_g, S.sg));
     HIP_TRY(hipStreamWaitEvent(S.caller, L->ev_g, 0));
@@ -1004,9 +1033,33 @@ nf_status close_streams(nf_layer* L, const Streams& S) {
   return NF_OK;
 }
 
+// The stream the GEMM side of nano-batch j goes to, and that of its
+// attention; with lanes both are lane j % 2 and the context is set to it.
+hipStream_t gemm_stream(LayerRun& r, const Streams& S, int j) {
+  r.c.lane = S.lanes ? j % 2 : 0;
+  return S.lanes && j % 2 ? S.sa : S.sg;
+}
+
 // front (norm, QKV, RoPE/append) of nano-batch j and its attention
 nf_status issue_front_attn(LayerRun& r, const Streams& S, int j) {
   nf_layer* L = r.L;
+  if (S.lanes) {                 // the whole nano-batch on its lane
+    const hipStream_t s = gemm_stream(r, S, j);
+    // lane 1 starts after nano-batch 0's front, whose RMSNorm also carries
+    // the step's metadata copy that every lane reads
+    if (j == 1) HIP_TRY(hipStreamWaitEvent(s, L->ev_app[0], 0));
+    nf_status st = issue_front(r.c, j, s);
+    if (st != NF_OK) return st;
+    if (j + 1 < r.count) HIP_TRY(hipEventRecord(L->ev_app[j], s));
+    // A request whose tokens began in an earlier nano-batch (a prefill chunk
+    // cut by the plan) attends to keys that the fronts before j appended; the
+    // last of them ran on the other lane (earlier ones on either lane are
+    // ordered before it or before this launch)
+    const NanoWork& nw = L->work.nanos[j];
+    if (j >= 2 && nw.t1 > nw.t0 && r.b.req_q_start[L->work.tok_req[nw.t0]] < nw.t0)
+      HIP_TRY(hipStreamWaitEvent(s, L->ev_app[j - 1], 0));
+    return issue_attention(r.c, j, s);
+  }
   nf_status st = issue_front(r.c, j, S.sg);
   if (st != NF_OK) return st;
   if (S.two) {
@@ -1023,12 +1076,13 @@ nf_status issue_front_attn(LayerRun& r, const Streams& S, int j) {
 // emulation its x1 rows then go through the collective on the third stream.
 nf_status issue_o_after_attn(LayerRun& r, const Streams& S, int j) {
   nf_layer* L = r.L;
-  if (S.two) HIP_TRY(hipStreamWaitEvent(S.sg, L->ev_att[j], 0));
-  nf_status st = issue_oproj(r.c, j, S.sg, &r.normed[j]);
+  const hipStream_t sg = gemm_stream(r, S, j);
+  if (S.two && !S.lanes) HIP_TRY(hipStreamWaitEvent(sg, L->ev_att[j], 0));
+  nf_status st = issue_oproj(r.c, j, sg, &r.normed[j]);
   if (st != NF_OK || !L->ar_mode) return st;
   const NanoWork& nw = L->work.nanos[j];
   if (nw.t1 == nw.t0) return NF_OK;
-  HIP_TRY(hipEventRecord(L->ev_o[j], S.sg));
+  HIP_TRY(hipEventRecord(L->ev_o[j], sg));
   HIP_TRY(hipStreamWaitEvent(S.sc, L->ev_o[j], 0));
   if ((st = issue_allreduce(L, L->x1.p, L->x1r.p, nw.t0, nw.t1 - nw.t0, S.sc)) != NF_OK) return st;
   HIP_TRY(hipEventRecord(L->ev_co[j], S.sc));
@@ -1042,10 +1096,11 @@ nf_status issue_ffn_after_o(LayerRun& r, const Streams& S, int j) {
   nf_layer* L = r.L;
   const NanoWork& nw = L->work.nanos[j];
   const bool live = nw.t1 > nw.t0;
-  if (L->ar_mode && live) HIP_TRY(hipStreamWaitEvent(S.sg, L->ev_co[j], 0));
-  nf_status st = issue_ffn(r.c, j, S.sg, r.normed[j]);
+  const hipStream_t sg = gemm_stream(r, S, j);
+  if (L->ar_mode && live) HIP_TRY(hipStreamWaitEvent(sg, L->ev_co[j], 0));
+  nf_status st = issue_ffn(r.c, j, sg, r.normed[j]);
   if (st != NF_OK || !L->ar_mode || !live) return st;
-  HIP_TRY(hipEventRecord(L->ev_d[j], S.sg));
+  HIP_TRY(hipEventRecord(L->ev_d[j], sg));
   HIP_TRY(hipStreamWaitEvent(S.sc, L->ev_d[j], 0));
   if ((st = issue_allreduce(L, L->ypre.p, r.c.b->out, nw.t0, nw.t1 - nw.t0, S.sc)) != NF_OK) return st;
   HIP_TRY(hipEventRecord(L->ev_cd[j], S.sc));
@@ -1062,6 +1117,15 @@ nf_status issue_back_after_attn(LayerRun& r, const Streams& S, int j) {
 // one layer's launches in the plan's order
 nf_status issue_layer(LayerRun& r, const Streams& S, int order) {
   nf_status st;
+  if (S.lanes) {
+    // in nano-batch order, each on its lane: every event a launch waits for
+    // (the front of the nano-batch before it) is recorded before the wait
+    for (int j = 0; j < r.count; ++j) {
+      if ((st = issue_front_attn(r, S, j)) != NF_OK) return st;
+      if ((st = issue_back_after_attn(r, S, j)) != NF_OK) return st;
+    }
+    return NF_OK;
+  }
   if (order == NF_ORDER_PIPELINED) {
     if ((st = issue_front_attn(r, S, 0)) != NF_OK) return st;
     for (int j = 0; j < r.count; ++j) {
@@ -1291,6 +1355,7 @@ nf_status nf_layer_create(const nf_shape* s, const nf_weights* w, nf_layer** out
   if (hipEventCreateWithFlags(&L->ev_start, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&L->ev_g, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&L->ev_a, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&L->ev_lane, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&L->stage_ev[0], hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&L->stage_ev[1], hipEventDisableTiming) != hipSuccess)
     return fail(set_err(NF_ERR_HIP, "event creation failed"));
@@ -1307,7 +1372,7 @@ void nf_layer_destroy(nf_layer* L) {
     if (kv.second.a) (void)hipStreamDestroy(kv.second.a);
   }
   for (DevBuf* b : {&L->h, &L->qkv, &L->q_rot, &L->attn, &L->x1, &L->h2, &L->act, &L->y, &L->r_idx, &L->r_w,
-                    &L->r_perm, &L->r_inv, &L->r_off, &L->splitk, &L->part_o, &L->part_ml, &L->meta, &L->cos_sin,
+                    &L->r_perm, &L->r_inv, &L->r_off, &L->splitk, &L->splitk_lane1, &L->part_o, &L->part_ml, &L->meta, &L->cos_sin,
                     &L->wp_qkv, &L->wp_o, &L->wp_gu, &L->wp_down, &L->stack_out})
     release(*b);
   for (int i = 0; i < 2; ++i) {
@@ -1318,7 +1383,7 @@ void nf_layer_destroy(nf_layer* L) {
     if (L->ev_app[j]) (void)hipEventDestroy(L->ev_app[j]);
     if (L->ev_att[j]) (void)hipEventDestroy(L->ev_att[j]);
   }
-  for (hipEvent_t e : {L->ev_start, L->ev_g, L->ev_a})
+  for (hipEvent_t e : {L->ev_start, L->ev_g, L->ev_a, L->ev_lane})
     if (e) (void)hipEventDestroy(e);
   for (int j = 0; j < NF_MAX_NANO; ++j)
     for (hipEvent_t e : {L->ev_o[j], L->ev_co[j], L->ev_d[j], L->ev_cd[j]})
@@ -2170,6 +2235,12 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
           const nf_plan pl = make_plan(k, v.data(), order, 2, kSplits[c].g, kSplits[c].a, kSplits[c].w);
           preds.push_back({pl, predict_plan_us(calib[c], pl, tok, units)});
         }
+      }
+      // two lanes without CU masks, with the co-run rates of the unmasked
+      // calibration (kSplits[0])
+      if (calib_ok[0]) {
+        const nf_plan pl = make_plan(k, v.data(), NF_ORDER_LANES, 2, 0, 0, 0);
+        preds.push_back({pl, predict_plan_us(calib[0], pl, tok, units)});
       }
     }
     std::stable_sort(preds.begin(), preds.end(), [](const std::pair<nf_plan, double>& x,

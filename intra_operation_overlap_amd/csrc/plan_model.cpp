@@ -17,6 +17,14 @@
 // other runs, so its durations are scaled by scale_gemm / scale_attn
 // throughout.  The simulation advances from event to event (an operation
 // finishing, or one becoming ready) and returns the makespan.
+//
+// With the lanes order each stream is a lane that runs whole nano-batches
+// (j on lane j mod 2), lane 1 starting after F_0, and the caller waiting for
+// both lanes.  The co-run rates then follow the classes of the two running
+// operations: attention beside a GEMM-side operation as above; two
+// operations of the same class share the chip, each at half its solo rate
+// (a lane's GEMMs take tiles for half the chip, so their solo durations from
+// whole-chip profiles stand for the pair).
 #include <algorithm>
 #include <cmath>
 #include <vector>
@@ -38,7 +46,8 @@ double interp(const nf_plan_profile& p, const double* y, double tokens) {
 }
 
 struct Op {
-  int stream;        // 0 GEMM side, 1 attention
+  int stream;        // 0 GEMM side (or lane 0), 1 attention (or lane 1)
+  bool attn;         // attention (else a GEMM-side operation)
   double work;       // solo microseconds left
   int dep = -1;      // index of the operation this one waits for (-1: none)
   double ready = 0;  // time its dependency (plus a cross-stream wait) allowed it
@@ -70,20 +79,22 @@ void attn_page_units(const nf_shape& sh, const nf_batch& b, const nf_plan& plan,
 double predict_plan_us(const nf_plan_profile& p, const nf_plan& plan, const double* tokens, const double* pages) {
   const int k = std::max(1, std::min(plan.count, NF_MAX_NANO));
   const bool two = plan.n_streams == 2;
+  const bool lanes = two && plan.order == NF_ORDER_LANES;
   const double sc_g = p.scale_gemm > 0 ? p.scale_gemm : 1.0, sc_a = p.scale_attn > 0 ? p.scale_attn : 1.0;
   std::vector<Op> ops;
   std::vector<std::vector<int>> queue(2);
   int f[NF_MAX_NANO], a[NF_MAX_NANO], o[NF_MAX_NANO], nn[NF_MAX_NANO];
   for (int j = 0; j < k; ++j) {
     const double tj = tokens[j];
-    auto add = [&](int stream, double us) {
-      ops.push_back(Op{stream, std::max(0.0, us) + p.gap_us});
+    auto add = [&](int stream, bool at, double us) {
+      ops.push_back(Op{stream, at, std::max(0.0, us) + p.gap_us});
       return (int)ops.size() - 1;
     };
-    f[j] = add(0, sc_g * interp(p, p.front_us, tj));
-    a[j] = add(two ? 1 : 0, sc_a * (p.attn_base_us + p.attn_us_per_page * pages[j]));
-    o[j] = add(0, sc_g * interp(p, p.oproj_us, tj));
-    nn[j] = add(0, sc_g * interp(p, p.ffn_us, tj));
+    const int ln = lanes ? j % 2 : 0;
+    f[j] = add(ln, false, sc_g * interp(p, p.front_us, tj));
+    a[j] = add(lanes ? ln : (two ? 1 : 0), true, sc_a * (p.attn_base_us + p.attn_us_per_page * pages[j]));
+    o[j] = add(ln, false, sc_g * interp(p, p.oproj_us, tj));
+    nn[j] = add(ln, false, sc_g * interp(p, p.ffn_us, tj));
     ops[a[j]].dep = f[j];
     ops[o[j]].dep = a[j];
   }
@@ -95,7 +106,11 @@ double predict_plan_us(const nf_plan_profile& p, const nf_plan& plan, const doub
     if (two) queue[1].push_back(a[j]);
     else g.push_back(a[j]);
   };
-  if (plan.order == NF_ORDER_PIPELINED) {
+  if (lanes) {
+    for (int j = 0; j < k; ++j)
+      for (int op : {f[j], a[j], o[j], nn[j]}) queue[j % 2].push_back(op);
+    if (k > 1) ops[f[1]].dep = f[0];
+  } else if (plan.order == NF_ORDER_PIPELINED) {
     front(0);
     for (int j = 0; j < k; ++j) {
       if (j + 1 < k) front(j + 1);
@@ -151,8 +166,13 @@ double predict_plan_us(const nf_plan_profile& p, const nf_plan& plan, const doub
     const bool both = running[0] >= 0 && running[1] >= 0;
     double rate[2] = {1.0, 1.0};
     if (both) {
-      rate[0] = 1.0 / slow_g;
-      rate[1] = 1.0 / slow_a;
+      const bool a0 = ops[running[0]].attn, a1 = ops[running[1]].attn;
+      if (a0 == a1) {
+        rate[0] = rate[1] = 0.5;
+      } else {
+        rate[0] = a0 ? 1.0 / slow_a : 1.0 / slow_g;
+        rate[1] = a1 ? 1.0 / slow_a : 1.0 / slow_g;
+      }
     }
     // next event: a running op finishing, or a waiting op becoming ready
     double dt = INFINITY;
@@ -184,7 +204,8 @@ double predict_plan_us(const nf_plan_profile& p, const nf_plan& plan, const doub
     if (op.done < 0) return INFINITY;    // cannot happen for a valid order
     end = std::max(end, op.done);
   }
-  return end;
+  // the caller's stream joins lane 1
+  return lanes && k > 1 ? end + p.wait_us : end;
 }
 
 }  // namespace nf

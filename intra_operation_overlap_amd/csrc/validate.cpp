@@ -126,10 +126,13 @@ nf_status check_batch(const nf_shape& s, int64_t n_pages, int page_size, const n
 nf_status check_plan(const nf_plan& p, int cus_per_xcd, std::string& err) {
   if (p.count < 1 || p.count > NF_MAX_NANO)
     return fail(err, NF_ERR_INVALID_ARG, "plan: count %d outside 1..%d", p.count, NF_MAX_NANO);
-  if (p.order != NF_ORDER_PIPELINED && p.order != NF_ORDER_SEQUENTIAL && p.order != NF_ORDER_DEEP)
+  if (p.order != NF_ORDER_PIPELINED && p.order != NF_ORDER_SEQUENTIAL && p.order != NF_ORDER_DEEP &&
+      p.order != NF_ORDER_LANES)
     return fail(err, NF_ERR_INVALID_ARG, "plan: unknown order %d", p.order);
   if (p.n_streams != 1 && p.n_streams != 2)
     return fail(err, NF_ERR_INVALID_ARG, "plan: n_streams must be 1 or 2");
+  if (p.order == NF_ORDER_LANES && p.n_streams != 2)
+    return fail(err, NF_ERR_INVALID_ARG, "plan: the lanes order needs two streams");
   if (p.gemm_cus_per_xcd < 0 || p.gemm_cus_per_xcd >= cus_per_xcd)
     return fail(err, NF_ERR_OUT_OF_RANGE, "plan: gemm_cus_per_xcd %d outside 0..%d", p.gemm_cus_per_xcd,
                 cus_per_xcd - 1);

@@ -147,8 +147,8 @@ nf_plan random_plan(int T) {
   }
   if (coin(0.1)) p.sizes[uni(0, k - 1)] += uni(-2, 2);
   if (p.count == 1 && coin(0.3)) p.sizes[0] = 0;          // "the whole batch"
-  p.order = uni(0, 2);
-  if (coin(0.05)) p.order = uni(-1, 4);
+  p.order = uni(0, 3);
+  if (coin(0.05)) p.order = uni(-1, 5);
   p.n_streams = uni(1, 2);
   p.gemm_cus_per_xcd = coin(0.5) ? 0 : uni(0, 32);
   p.attn_cus_per_xcd = coin(0.5) ? 0 : uni(0, 32);

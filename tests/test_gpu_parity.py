@@ -40,6 +40,16 @@ def _plans_for(T):
         "k2_attn_waves4_on2cus": B.make_plan(2, [half, T - half], n_streams=2, attn_cus_per_xcd=2,
                                              attn_waves_per_cu=4),
         "k1_attn_waves2_on2cus": B.make_plan(1, [T], n_streams=2, attn_cus_per_xcd=2, attn_waves_per_cu=2),
+        # lanes: nano-batch j on stream j % 2, each lane's GEMMs tiled for half
+        # the chip (own split-K partials), under CU budgets, with a bounded
+        # attention grid, and with three nano-batches (two share lane 0)
+        "k2_lanes": B.make_plan(2, [half, T - half], order=B.NF_ORDER_LANES, n_streams=2),
+        "k2_lanes_masked16": B.make_plan(2, [half, T - half], order=B.NF_ORDER_LANES, n_streams=2,
+                                         gemm_cus_per_xcd=16, attn_cus_per_xcd=16),
+        "k2_lanes_attn_waves8": B.make_plan(2, [half, T - half], order=B.NF_ORDER_LANES, n_streams=2,
+                                            attn_waves_per_cu=8),
+        "k3_lanes": B.make_plan(3, [T // 3, T // 3, T - 2 * (T // 3)], order=B.NF_ORDER_LANES, n_streams=2),
+        "k4_lanes": B.make_plan(4, [T // 4] * 3 + [T - 3 * (T // 4)], order=B.NF_ORDER_LANES, n_streams=2),
     }
 
 
@@ -382,6 +392,9 @@ def test_mixed_full_size_sampled(wl_name):
     _sampled_check(S, _sample_requests(S.batch, 16, seed=4), w_np)
     S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], n_streams=2, attn_waves_per_cu=4))
     _sampled_check(S, _sample_requests(S.batch, 8, seed=5), w_np)
+    # two lanes, each tiling its GEMMs for half the chip
+    S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], order=B.NF_ORDER_LANES, n_streams=2))
+    _sampled_check(S, _sample_requests(S.batch, 8, seed=6), w_np)
 
 
 # ---------------------------------------------------------------- mixture of experts
@@ -420,7 +433,8 @@ def test_small_moe_full_parity():
     S = GH.setup(SMALL_MOE)
     T = S.batch.n_tokens
     for name, plan in (("k1", B.make_plan(1, [T])),
-                       ("k3", B.make_plan(3, [33, 33, T - 66], n_streams=2, gemm_cus_per_xcd=16))):
+                       ("k3", B.make_plan(3, [33, 33, T - 66], n_streams=2, gemm_cus_per_xcd=16)),
+                       ("k3_lanes", B.make_plan(3, [33, 33, T - 66], order=B.NF_ORDER_LANES, n_streams=2))):
         _full_check(S, name, plan)
         sizes = list(plan.sizes)[:plan.count]
         t0 = 0

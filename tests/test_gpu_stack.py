@@ -90,6 +90,7 @@ def _plans(T):
         "k3_two_streams_pipelined": B.make_plan(3, [T // 3, T // 3, T - 2 * (T // 3)], n_streams=2),
         "k2_masked16": B.make_plan(2, [half, T - half], n_streams=2, gemm_cus_per_xcd=16),
         "k2_sequential_one_stream": B.make_plan(2, [half, T - half], order=B.NF_ORDER_SEQUENTIAL),
+        "k2_lanes": B.make_plan(2, [half, T - half], order=B.NF_ORDER_LANES, n_streams=2),
     }
 
 
@@ -198,7 +199,7 @@ def test_stack_rejects_repeated_layer_and_foreign_pool(bf16_stack):
     assert e.value.status == B.NF_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("plan_name", ["k1", "k2_two_streams_pipelined"])
+@pytest.mark.parametrize("plan_name", ["k1", "k2_two_streams_pipelined", "k2_lanes"])
 def test_graph_replays_equal_eager_step(bf16_stack, plan_name):
     st = bf16_stack
     T = st.batch.n_tokens

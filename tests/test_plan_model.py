@@ -107,3 +107,24 @@ def test_predict_rejects_bad_arguments():
         B.plan_predict(p, shape, B.make_plan(1, [16]), hb)
     with pytest.raises(B.NfError):
         B.plan_predict(_profile(), shape, B.make_plan(2, [8, 9]), hb)
+
+
+def test_lanes_share_the_chip_by_operation_class():
+    plan = B.make_plan(2, [8, 8], order=B.NF_ORDER_LANES, n_streams=2)
+    # F0 0-10; F1 beside A0 10-20; A0 beside A1 at half rate each 20-100 (A1 10 left);
+    # O0 beside A1 100-105; N0 beside A1 105-110 (25 left); O1 beside N0 at half rate 110-120
+    # (N0 20 left); N1 beside N0 at half rate 120-160 (N1 10 left); N1 alone 160-170
+    assert _predict(_profile(), plan) == pytest.approx(170)
+    # attention beside a GEMM-side operation at the calibrated rates (half here):
+    # F1 beside A0 10-30 (A0 40 left); A0 beside A1 30-110 (A1 10 left); O0 beside A1 110-120;
+    # N0 beside A1 120-130 (N0 25 left); O1 beside N0 130-140 (N0 20 left);
+    # N1 beside N0 140-180 (N1 10 left); N1 alone 180-190
+    assert _predict(_profile(slow_g=2.0, slow_a=2.0), plan) == pytest.approx(190)
+    # a 7 us wait before lane 1 starts and before the caller joins it:
+    # A0 alone 10-17 (43 left); F1 beside A0 17-27 (33 left); A0 beside A1 27-93 (A1 17 left);
+    # O0 beside A1 93-98; N0 beside A1 98-110 (18 left); O1 beside N0 110-120 (13 left);
+    # N1 beside N0 120-146 (N1 17 left); N1 alone 146-163; join 170
+    assert _predict(_profile(wait=7.0), plan) == pytest.approx(170)
+    # one nano-batch: one lane, no join
+    assert _predict(_profile(wait=7.0), B.make_plan(1, [16], order=B.NF_ORDER_LANES, n_streams=2)) == \
+        pytest.approx(95)
