@@ -533,6 +533,14 @@ nf_status nf_plan_search_report(const nf_layer* layer, int32_t max, nf_plan* pla
 nf_status nf_layer_intermediate(const nf_layer* layer, int32_t which, const void** dev_ptr,
                                 int64_t* row_stride);
 
+/* nf_layer_debug_capture: per-stage parity access.  q_rot, attn, x1 and act
+ * are the step's own working buffers, so keeping them costs the step nothing
+ * and capture is on from nf_layer_create.  With on == 0 the library makes no
+ * promise about them: nf_layer_intermediate refuses every index with
+ * NF_ERR_UNSUPPORTED until capture is switched on again (the next step then
+ * refills them).  No device work; NF_ERR_INVALID_ARG for a null layer. */
+nf_status nf_layer_debug_capture(nf_layer* layer, int32_t on);
+
 /* ---- per-kernel timing ------------------------------------------------------
  * When on, every kernel launch of a step (or only those of kind `only_kind`,
  * if not NULL) records the kernel's own start and end timestamps into a pair

@@ -109,6 +109,7 @@ _SIGS = {
     "nf_plan_predict": (i32, [ctypes.POINTER(nf_plan_profile), ctypes.POINTER(nf_shape), ctypes.POINTER(nf_plan),
                               ctypes.POINTER(nf_batch), ctypes.POINTER(ctypes.c_double)]),
     "nf_layer_intermediate": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64)]),
+    "nf_layer_debug_capture": (i32, [vp, i32]),
     "nf_profile_enable": (i32, [vp, i32, ctypes.c_char_p]),
     "nf_profile_read": (i32, [vp, i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
@@ -265,6 +266,9 @@ class Layer:
         check(lib().nf_layer_intermediate(self.h, which, ctypes.byref(ptr), ctypes.byref(stride)),
               "nf_layer_intermediate")
         return ptr.value, stride.value
+
+    def debug_capture(self, on: bool) -> None:
+        check(lib().nf_layer_debug_capture(self.h, 1 if on else 0), "nf_layer_debug_capture")
 
     def profile_enable(self, on: bool, only_kind: Optional[str] = None) -> None:
         check(lib().nf_profile_enable(self.h, 1 if on else 0, only_kind.encode() if only_kind else None),

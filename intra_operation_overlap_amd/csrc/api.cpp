@@ -177,6 +177,7 @@ struct nf_layer {
   StepWork work;
   int last_T = 0;
   int attn_variant = -1;   // bf16 d=128 attention kernel: -1 chosen per step, 0 one-wave items, 1 four-wave items
+  bool debug_capture = true;   // nf_layer_intermediate answers (nf_layer_debug_capture)
   std::vector<SearchEntry> search_report;   // the last plan search's timed plans
 };
 
@@ -1660,6 +1661,8 @@ nf_status nf_graph_launch(nf_graph* g, void* stream) {
 
 nf_status nf_layer_intermediate(const nf_layer* L, int32_t which, const void** dev, int64_t* stride) {
   if (!L || !dev || !stride) return set_err(NF_ERR_INVALID_ARG, "nf_layer_intermediate: null argument");
+  if (!L->debug_capture)
+    return set_err(NF_ERR_UNSUPPORTED, "nf_layer_intermediate: capture is off (nf_layer_debug_capture)");
   const nf_shape& s = L->s;
   const int64_t nqd = (int64_t)s.n_q_heads * s.head_dim;
   switch (which) {
@@ -1675,6 +1678,12 @@ nf_status nf_layer_intermediate(const nf_layer* L, int32_t which, const void** d
     default: return set_err(NF_ERR_INVALID_ARG, "nf_layer_intermediate: unknown index %d", which);
   }
   if (!*dev) return set_err(NF_ERR_INVALID_ARG, "nf_layer_intermediate: %d not held by this layer", which);
+  return NF_OK;
+}
+
+nf_status nf_layer_debug_capture(nf_layer* L, int32_t on) {
+  if (!L) return set_err(NF_ERR_INVALID_ARG, "nf_layer_debug_capture: null layer");
+  L->debug_capture = on != 0;
   return NF_OK;
 }
 

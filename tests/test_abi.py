@@ -248,3 +248,10 @@ def test_loop_rejects_bad_arguments_before_launching():
     n = ctypes.c_int32()
     assert L.nf_loop_request_length(None, 0, ctypes.byref(n)) == B.NF_ERR_INVALID_ARG
     L.nf_loop_destroy(None)
+
+
+def test_debug_capture_and_intermediate_reject_null_layers():
+    L = B.lib()
+    assert L.nf_layer_debug_capture(None, 1) == B.NF_ERR_INVALID_ARG
+    ptr, stride = ctypes.c_void_p(), ctypes.c_int64()
+    assert L.nf_layer_intermediate(None, 0, ctypes.byref(ptr), ctypes.byref(stride)) == B.NF_ERR_INVALID_ARG

@@ -99,3 +99,16 @@ def test_cu_mask_map_is_measured_and_budgets_land_on_their_cus():
     with pytest.raises(B.NfError) as e:
         B.probe_budget_cus(per - 2, 4)
     assert e.value.status == B.NF_ERR_OUT_OF_RANGE
+
+
+def test_debug_capture_switches_the_intermediates_off_and_on(small):
+    """With capture off nf_layer_intermediate refuses every index; switched on
+    again, the next step's q_rot / attn / x1 / act are readable and match the
+    oracle."""
+    small.layer.debug_capture(False)
+    for which in (0, 1, 2, 3):
+        with pytest.raises(B.NfError) as e:
+            small.layer.intermediate(which)
+        assert e.value.status == B.NF_ERR_UNSUPPORTED
+    small.layer.debug_capture(True)
+    _full_check(small, "capture_on", B.make_plan(1, [small.batch.n_tokens]))
