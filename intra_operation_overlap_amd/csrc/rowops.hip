@@ -64,6 +64,11 @@ __device__ __forceinline__ float block_sum_sq(float ss) {
   return tot;
 }
 
+// 16-byte chunks a thread keeps in registers between the sum of squares and
+// the output (rows up to RN_HELD * RN_THREADS * 8 elements); longer rows read
+// their chunks again.  The order of the sum is the same either way.
+constexpr int RN_HELD = 4;
+
 __global__ __launch_bounds__(RN_THREADS) void rmsnorm_bf16x8_kernel(const bf16* __restrict__ x,
                                                              const bf16* __restrict__ g,
                                                              bf16* __restrict__ y, int H, float eps, MetaCopy mc,
@@ -74,6 +79,34 @@ __global__ __launch_bounds__(RN_THREADS) void rmsnorm_bf16x8_kernel(const bf16* 
   const bf16x8* gr = (const bf16x8*)g;
   bf16x8* yr = (bf16x8*)(y + row * H);
   const int n8 = H / 8;
+  if (n8 <= RN_HELD * RN_THREADS) {
+    // every chunk of the row is loaded once, all loads issued before the sum
+    bf16x8 v[RN_HELD];
+#pragma unroll
+    for (int k = 0; k < RN_HELD; ++k) {
+      const int i = threadIdx.x + k * RN_THREADS;
+      if (i < n8) v[k] = xr[i];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < RN_HELD; ++k)
+      if (threadIdx.x + k * RN_THREADS < n8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += (float)v[k][e] * (float)v[k][e];
+      }
+    const float inv = rsqrtf(block_sum_sq(ss) / (float)H + eps);
+#pragma unroll
+    for (int k = 0; k < RN_HELD; ++k) {
+      const int i = threadIdx.x + k * RN_THREADS;
+      if (i >= n8) break;
+      const bf16x8 w = gr[i];
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[k][e] * inv * (float)w[e]);
+      yr[i] = o;
+    }
+    return;
+  }
   float ss = 0.f;
   for (int i = threadIdx.x; i < n8; i += RN_THREADS) {
     const bf16x8 v = xr[i];
@@ -103,6 +136,44 @@ __global__ __launch_bounds__(RN_THREADS) void residual_rmsnorm_partials_kernel(
   const float* P = part + row * part_ld;
   const bf16x8* xr = (const bf16x8*)(x + row * ldx);
   bf16x8* x1r = (bf16x8*)(x1 + row * ldx1);
+  if (n8 <= RN_HELD * RN_THREADS) {
+    // x1 stays in registers for the norm (same sums, same order)
+    bf16x8 o[RN_HELD];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < RN_HELD; ++k) {
+      const int i = threadIdx.x + k * RN_THREADS;
+      if (i >= n8) break;
+      const f32x4 lo = sum_slices<f32x4>(P + 8 * i, zstride, splits);
+      const f32x4 hi = sum_slices<f32x4>(P + 8 * i + 4, zstride, splits);
+      const bf16x8 r = xr[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float a0 = lo[e], a1 = hi[e];
+        a0 += (float)r[e];
+        a1 += (float)r[e + 4];
+        o[k][e] = (bf16)a0;
+        o[k][e + 4] = (bf16)a1;
+      }
+      x1r[i] = o[k];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += (float)o[k][e] * (float)o[k][e];
+    }
+    const float inv = rsqrtf(block_sum_sq(ss) / (float)H + eps);
+    const bf16x8* gr = (const bf16x8*)g;
+    bf16x8* yr = (bf16x8*)(y + row * H);
+#pragma unroll
+    for (int k = 0; k < RN_HELD; ++k) {
+      const int i = threadIdx.x + k * RN_THREADS;
+      if (i >= n8) break;
+      const bf16x8 w = gr[i];
+      bf16x8 q;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = (bf16)((float)o[k][e] * inv * (float)w[e]);
+      yr[i] = q;
+    }
+    return;
+  }
   float ss = 0.f;
   for (int i = threadIdx.x; i < n8; i += RN_THREADS) {
     const f32x4 lo = sum_slices<f32x4>(P + 8 * i, zstride, splits);
@@ -204,6 +275,10 @@ __global__ __launch_bounds__(256) void rope_append_bf16x4_kernel(RopeAppendArgs 
   const int p = a.pos[t];
   const int r = a.tok_req[t];
   const int ncols = (a.nq + 2 * a.nkv) * d;
+  // K and V heads: the pool page of this position, looked up before any
+  // store (the compiler would otherwise keep these loads behind the stores
+  // below, which it cannot tell apart from the page table)
+  const int page = head >= a.nq ? a.page_indices[a.page_indptr[r] + p / a.page_size] : 0;
   float x0[4], x1[4];
   bf16x4 v0, v1;
   if (a.splits > 1) {
@@ -244,7 +319,6 @@ __global__ __launch_bounds__(256) void rope_append_bf16x4_kernel(RopeAppendArgs 
       *(bf16x4*)(q + j + half) = y1;
       return;
     }
-    const int page = a.page_indices[a.page_indptr[r] + p / a.page_size];
     const int slot = p % a.page_size;
     bf16* k = (bf16*)a.k_pool + ((int64_t)page * a.nkv + (head - a.nq)) * a.page_size * d;
     // dims j .. j+3 lie in one run of 8 of the K block order, so contiguously
@@ -252,7 +326,6 @@ __global__ __launch_bounds__(256) void rope_append_bf16x4_kernel(RopeAppendArgs 
     *(bf16x4*)(k + kv_k_off(slot, j + half)) = y1;
     return;
   }
-  const int page = a.page_indices[a.page_indptr[r] + p / a.page_size];
   const int slot = p % a.page_size;
   bf16* v = (bf16*)a.v_pool + ((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * a.page_size * d;
 #pragma unroll
