@@ -30,6 +30,7 @@ def _plans(T):
         "k3_deep": B.make_plan(3, t3, order=B.NF_ORDER_DEEP, n_streams=2),
         "k3_deep_one_stream": B.make_plan(3, t3, order=B.NF_ORDER_DEEP),
         "k2_masked16_waves4": B.make_plan(2, [h, T - h], n_streams=2, gemm_cus_per_xcd=16, attn_waves_per_cu=4),
+        "k3_lanes": B.make_plan(3, t3, order=B.NF_ORDER_LANES, n_streams=2),
     }
 
 

@@ -215,7 +215,10 @@ def test_caller_stream_kind_does_not_change_results(small):
     for plan in (B.make_plan(2, half, n_streams=2),
                  B.make_plan(2, half, n_streams=2, attn_cus_per_xcd=24),
                  B.make_plan(2, half, n_streams=2, gemm_cus_per_xcd=16, attn_cus_per_xcd=16),
-                 B.make_plan(2, half, order=B.NF_ORDER_DEEP, n_streams=2, gemm_cus_per_xcd=20)):
+                 B.make_plan(2, half, order=B.NF_ORDER_DEEP, n_streams=2, gemm_cus_per_xcd=20),
+                 B.make_plan(2, half, order=B.NF_ORDER_LANES, n_streams=2),
+                 B.make_plan(3, [28, 28, T - 56], order=B.NF_ORDER_LANES, n_streams=2, gemm_cus_per_xcd=16,
+                             attn_cus_per_xcd=16)):
         small.layer.set_plan(plan)
         outs = []
         for s in (None, side):
