@@ -842,8 +842,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
       constexpr int RP = stage_rows(C::BM, FIT);          // rows per pass
       static_assert(RP >= 32 && C::BM % RP == 0, "staging");
       constexpr int CH = BNO / 8;                          // 16-byte output chunks per row
-      // Residual chunks of a pass are loaded one pass ahead (the first right
-      // after the k loop), so their latency hides behind the previous pass.
+      // Residual chunks are loaded two passes ahead (the first two passes'
+      // right after the k loop, into registers the operand fragments held),
+      // so a pass's loads have two passes to land.
       constexpr int NPASS = C::BM / RP, PER = RP * CH / 256;
       static_assert(RP * CH % 256 == 0, "chunks per thread");
       bf16x8 res[F32S ? NPASS : 1][F32S ? PER : 1];
@@ -858,7 +859,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
           }
         }
       };
-      load_res(0);
+      constexpr int AHEAD = NPASS < 2 ? NPASS : 2;
+#pragma unroll
+      for (int pass = 0; pass < AHEAD; ++pass) load_res(pass);
 #pragma unroll
       for (int pass = 0; pass < NPASS; ++pass) {
         __syncthreads();                                   // LDS free (slabs, or the previous pass)
@@ -887,7 +890,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(KParams p) {
           }
         }
         __syncthreads();
-        if (pass + 1 < NPASS) load_res(pass + 1);
+        if (pass + AHEAD < NPASS) load_res(pass + AHEAD);
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
           const int idx = threadIdx.x + e * 256;
