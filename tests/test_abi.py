@@ -107,6 +107,10 @@ def test_validate_rejects_capacity_and_plan_errors():
     assert _validate(shape, batch, plan=B.make_plan(5, [4, 4, 4, 4])) == B.NF_ERR_INVALID_ARG
     assert _validate(shape, batch, plan=B.make_plan(1, [16], n_streams=1, gemm_cus_per_xcd=8)) == B.NF_ERR_INVALID_ARG
     assert _validate(shape, batch, plan=B.make_plan(1, [16], n_streams=2, gemm_cus_per_xcd=32)) == B.NF_ERR_OUT_OF_RANGE
+    # lanes need two streams; an unknown order is refused
+    assert _validate(shape, batch, plan=B.make_plan(2, [8, 8], order=B.NF_ORDER_LANES)) == B.NF_ERR_INVALID_ARG
+    assert _validate(shape, batch, plan=B.make_plan(2, [8, 8], order=B.NF_ORDER_LANES, n_streams=2)) == B.NF_OK
+    assert _validate(shape, batch, plan=B.make_plan(2, [8, 8], order=4, n_streams=2)) == B.NF_ERR_INVALID_ARG
 
 
 def test_validate_rejects_gemm_operands_over_4gib():

@@ -483,3 +483,8 @@ def test_c5_full_size_sampled():
     S.layer.set_plan(B.make_plan(1, [T]))
     _sampled_check(S, _sample_requests(S.batch, 8, seed=4), w_np)
     _route_check(S, 0, T, 0)
+    # two lanes: each lane's expert GEMMs with split-K partials of its own
+    S.layer.set_plan(B.make_plan(2, [T // 2, T - T // 2], order=B.NF_ORDER_LANES, n_streams=2))
+    _sampled_check(S, _sample_requests(S.batch, 6, seed=7), w_np)
+    _route_check(S, 0, T // 2, 0)
+    _route_check(S, T // 2, T, 1)
