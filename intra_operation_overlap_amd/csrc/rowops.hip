@@ -339,8 +339,10 @@ __global__ __launch_bounds__(256) void rope_append_bf16x4_kernel(RopeAppendArgs 
 // Single 256-thread block.  Top-k per token (larger logit first; equal logits
 // keep the lower expert index first), gate weights = softmax over the chosen
 // logits, then a stable counting sort of assignment ids t*k+s by expert:
-// per-thread contiguous ranges are counted, scanned per expert across threads,
-// then scattered in order, so perm is deterministic.
+// per-thread contiguous ranges are counted, scanned per expert across threads
+// (shuffle scans within each wave, then the totals of the earlier waves), then
+// scattered in order, each thread advancing its own row of the table, so perm
+// is deterministic.
 constexpr int ROUTE_THREADS = 256;
 constexpr int ROUTE_MAX_E = 64;
 
@@ -376,14 +378,31 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(RouteArgs a) {
   for (int e = 0; e < E; ++e) cnt[tid][e] = 0;
   for (int i = lo; i < hi; ++i) cnt[tid][a.idx[i]]++;
   __syncthreads();
-  if (tid < E) {                       // exclusive scan over threads, per expert
-    int run = 0;
-    for (int u = 0; u < ROUTE_THREADS; ++u) {
-      const int c = cnt[u][tid];
-      cnt[u][tid] = run;
-      run += c;
+  // exclusive scan over threads of every expert's column: within each wave by
+  // shuffles, then the totals of the waves before it
+  constexpr int NWAVE = ROUTE_THREADS / 64;
+  __shared__ int wsum[NWAVE][ROUTE_MAX_E];
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int e = 0; e < E; ++e) {
+    const int c = cnt[tid][e];
+    int v = c;
+    for (int d = 1; d < 64; d *= 2) {
+      const int u = __shfl_up(v, d, 64);
+      if (lane >= d) v += u;
     }
-    off[tid] = run;                    // total for expert tid (scanned below)
+    cnt[tid][e] = v - c;
+    if (lane == 63) wsum[wv][e] = v;
+  }
+  __syncthreads();
+  for (int e = 0; e < E; ++e) {
+    int base = 0;
+    for (int q = 0; q < wv; ++q) base += wsum[q][e];
+    cnt[tid][e] += base;
+  }
+  if (tid < E) {                       // total for expert tid (scanned below)
+    int tot = 0;
+    for (int q = 0; q < NWAVE; ++q) tot += wsum[q][tid];
+    off[tid] = tot;
   }
   __syncthreads();
   if (tid == 0) {
@@ -398,13 +417,48 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(RouteArgs a) {
     a.offsets[E] = run;
   }
   __syncthreads();
-  int local[ROUTE_MAX_E];
-  for (int e = 0; e < E; ++e) local[e] = 0;
   for (int i = lo; i < hi; ++i) {
     const int e = a.idx[i];
-    const int dst = off[e] + cnt[tid][e] + local[e]++;
+    const int dst = off[e] + cnt[tid][e]++;
     a.perm[dst] = i;
     a.inv[i] = dst;
+  }
+}
+
+// bf16, H % 8 == 0: the same sums over 8-element chunks, every load of a
+// chunk issued before its sum (k <= 8)
+__global__ __launch_bounds__(256) void moe_combine_bf16x8_kernel(const bf16* __restrict__ x1,
+                                                                 const float* __restrict__ y,
+                                                                 const float* __restrict__ w,
+                                                                 const int32_t* __restrict__ inv,
+                                                                 bf16* __restrict__ out, int H, int k) {
+  const int64_t t = blockIdx.x;
+  float ws[8];
+  int64_t rows[8];
+  for (int s = 0; s < k; ++s) {
+    ws[s] = w[t * k + s];
+    rows[s] = (int64_t)inv[t * k + s] * H;
+  }
+  for (int c = threadIdx.x; c < H / 8; c += 256) {
+    const int i = 8 * c;
+    const bf16x8 xv = *(const bf16x8*)(x1 + t * H + i);
+    f32x4 lo[8], hi[8];
+    for (int s = 0; s < k; ++s) {
+      lo[s] = *(const f32x4*)(y + rows[s] + i);
+      hi[s] = *(const f32x4*)(y + rows[s] + i + 4);
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v0 = (float)xv[e], v1 = (float)xv[e + 4];
+      for (int s = 0; s < k; ++s) {
+        v0 += ws[s] * lo[s][e];
+        v1 += ws[s] * hi[s][e];
+      }
+      o[e] = (bf16)v0;
+      o[e + 4] = (bf16)v1;
+    }
+    *(bf16x8*)(out + t * H + i) = o;
   }
 }
 
@@ -613,7 +667,8 @@ hipError_t moe_combine(int dtype, const void* x1, const float* y, const float* w
                        void* out, int T, int H, int k, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 1)
-    launch(moe_combine_kernel<bf16>, T, 256, 0, s, (const bf16*)x1, y, w, inv, (bf16*)out, H, k);
+    launch(H % 8 == 0 && k <= 8 ? moe_combine_bf16x8_kernel : moe_combine_kernel<bf16>, T, 256, 0, s,
+           (const bf16*)x1, y, w, inv, (bf16*)out, H, k);
   else
     launch(moe_combine_kernel<float>, T, 256, 0, s, (const float*)x1, y, w, inv, (float*)out, H, k);
   return hipGetLastError();
