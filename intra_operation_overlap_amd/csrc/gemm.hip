@@ -1191,6 +1191,11 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident) {
       // projection: 117 us split, 134 as 128 x 128 tiles).
       p.cfg = (t12 >= enough && t12 <= cus) ? 12 : 13;
       p.k_splits = 1;
+      // plain stores (the QKV projection) as 256 x 128 tiles when those fill
+      // the round as well: the 1024-token Llama-3-8B QKV 56.3 -> 53.1 us
+      // inside the step (two alternating runs)
+      const int64_t t11 = (int64_t)((M + 255) / 256) * n_tiles_of(a, 128);
+      if (a.mode == GEMM_STORE && t11 >= enough && t11 <= cus) p.cfg = 11;
       return p;
     } else if (a.K >= 8192) {
       for (int k = 2; k <= 8 && a.K / k >= 2048; k *= 2)
@@ -1211,12 +1216,15 @@ GemmPlan gemm_choose(const GemmArgs& a, int cus, bool coresident) {
   // it inside the step in 61 us at 2048 tokens (3 pieces) against 73-75 for
   // split 128 x 128 tiles, and in 2 x 32 us at 1024 tokens (5 pieces) against
   // 2 x 45 (the partials go to the RoPE kernel, which reduces them)
+  // The same tiles as 256 x 128 (configuration 11) ran it in 53.0 us against
+  // 54.7 (three pieces; two alternating runs inside the step), so the split
+  // is sized on those.
   if (p.cfg == 14 && a.K >= 8192 && !coresident && a.mode == GEMM_STORE) {
-    const int64_t t12 = (int64_t)((M + 127) / 128) * n_tiles_of(a, 256);
+    const int64_t t11 = (int64_t)((M + 255) / 256) * n_tiles_of(a, 128);
     const int64_t enough = (3 * (int64_t)cus + 3) / 4;
     for (int k = 2; k <= 8 && a.K / k >= 1024; ++k)
-      if (t12 * k >= enough && t12 * k <= cus) {
-        p.cfg = 12;
+      if (t11 * k >= enough && t11 * k <= cus) {
+        p.cfg = 11;
         p.k_splits = k;
         return p;
       }
