@@ -345,38 +345,64 @@ __global__ __launch_bounds__(256) void rope_append_bf16x4_kernel(RopeAppendArgs 
 // is deterministic.
 constexpr int ROUTE_THREADS = 256;
 constexpr int ROUTE_MAX_E = 64;
+constexpr int ROUTE_REG_E = 8;        // up to this many experts a token's logits are held in registers
+constexpr int ROUTE_LDS_IDX = 8192;   // up to this many assignments the sort reads them from LDS
 
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(RouteArgs a) {
   __shared__ int cnt[ROUTE_THREADS][ROUTE_MAX_E + 1];
   __shared__ int off[ROUTE_MAX_E + 1];
+  __shared__ int s_idx[ROUTE_LDS_IDX];
   const int tid = threadIdx.x;
   const int E = a.E, k = a.k;
+  const int A = a.T * k;
+  const bool lds_idx = A <= ROUTE_LDS_IDX;
   for (int t = tid; t < a.T; t += ROUTE_THREADS) {
     const float* lg = a.logits + (int64_t)t * E;
     uint64_t taken = 0;
     float sel[8];
-    for (int s = 0; s < k; ++s) {
-      int best = -1;
-      float bv = 0.f;
-      for (int e = 0; e < E; ++e) {
-        if (taken & (1ull << e)) continue;
-        const float v = lg[e];
-        if (best < 0 || v > bv) { best = e; bv = v; }
+    if (E <= ROUTE_REG_E) {
+      // every logit of the token loaded before the selection
+      float v[ROUTE_REG_E];
+#pragma unroll
+      for (int e = 0; e < ROUTE_REG_E; ++e) v[e] = e < E ? lg[e] : 0.f;
+      for (int s = 0; s < k; ++s) {
+        int best = -1;
+        float bv = 0.f;
+#pragma unroll
+        for (int e = 0; e < ROUTE_REG_E; ++e) {
+          if (e >= E || (taken & (1ull << e))) continue;
+          if (best < 0 || v[e] > bv) { best = e; bv = v[e]; }
+        }
+        taken |= 1ull << best;
+        a.idx[t * k + s] = best;
+        if (lds_idx) s_idx[t * k + s] = best;
+        sel[s] = bv;
       }
-      taken |= 1ull << best;
-      a.idx[t * k + s] = best;
-      sel[s] = bv;
+    } else {
+      for (int s = 0; s < k; ++s) {
+        int best = -1;
+        float bv = 0.f;
+        for (int e = 0; e < E; ++e) {
+          if (taken & (1ull << e)) continue;
+          const float v = lg[e];
+          if (best < 0 || v > bv) { best = e; bv = v; }
+        }
+        taken |= 1ull << best;
+        a.idx[t * k + s] = best;
+        if (lds_idx) s_idx[t * k + s] = best;
+        sel[s] = bv;
+      }
     }
     float z = 0.f;
     for (int s = 0; s < k; ++s) z += expf(sel[s] - sel[0]);
     for (int s = 0; s < k; ++s) a.w[t * k + s] = expf(sel[s] - sel[0]) / z;
   }
   __syncthreads();
-  const int A = a.T * k;
+  auto idx_of = [&](int i) { return lds_idx ? s_idx[i] : a.idx[i]; };
   const int per = (A + ROUTE_THREADS - 1) / ROUTE_THREADS;
   const int lo = min(A, tid * per), hi = min(A, lo + per);
   for (int e = 0; e < E; ++e) cnt[tid][e] = 0;
-  for (int i = lo; i < hi; ++i) cnt[tid][a.idx[i]]++;
+  for (int i = lo; i < hi; ++i) cnt[tid][idx_of(i)]++;
   __syncthreads();
   // exclusive scan over threads of every expert's column: within each wave by
   // shuffles, then the totals of the waves before it
@@ -418,7 +444,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(RouteArgs a) {
   }
   __syncthreads();
   for (int i = lo; i < hi; ++i) {
-    const int e = a.idx[i];
+    const int e = idx_of(i);
     const int dst = off[e] + cnt[tid][e]++;
     a.perm[dst] = i;
     a.inv[i] = dst;
