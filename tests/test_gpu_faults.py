@@ -37,7 +37,8 @@ def _plans(T):
     half = [T // 2, T - T // 2]
     return {"k1": B.make_plan(1, [T]),
             "k2_masked": B.make_plan(2, half, n_streams=2, gemm_cus_per_xcd=20, attn_cus_per_xcd=12),
-            "k2_deep": B.make_plan(2, half, order=B.NF_ORDER_DEEP, n_streams=2)}
+            "k2_deep": B.make_plan(2, half, order=B.NF_ORDER_DEEP, n_streams=2),
+            "k3_lanes": B.make_plan(3, [T // 3, T // 3, T - 2 * (T // 3)], order=B.NF_ORDER_LANES, n_streams=2)}
 
 
 def _step_bits(S):
@@ -50,7 +51,7 @@ def _step_bits(S):
     return got, (k0, v0)
 
 
-@pytest.mark.parametrize("plan_name", ["k1", "k2_masked", "k2_deep"])
+@pytest.mark.parametrize("plan_name", ["k1", "k2_masked", "k2_deep", "k3_lanes"])
 def test_every_injected_hip_failure_is_reported_and_recovered(S, plan_name):
     S.layer.set_plan(_plans(S.batch.n_tokens)[plan_name])
     want, _ = _step_bits(S)
