@@ -473,6 +473,9 @@ typedef struct nf_plan_profile {
   double gap_us;
   double slow_gemm, slow_attn, wait_us;
   double scale_gemm, scale_attn;
+  double lane_rate;       /* lanes order: the rate (of its solo rate) at which each of two
+                             operations of one class runs while both lanes run them
+                             (0: one half) */
 } nf_plan_profile;
 nf_status nf_plan_predict(const nf_plan_profile* prof, const nf_shape* shape, const nf_plan* plan,
                           const nf_batch* batch, double* us);
@@ -495,12 +498,14 @@ nf_status nf_plan_predict(const nf_plan_profile* prof, const nf_shape* shape, co
  *     XCD of 28 + 4, 24 + 8, 20 + 12, 16 + 16, 12 + 20 and 8 + 24 -- two equal
  *     nano-batches run overlapped once, giving that split's co-run slowdowns
  *     (unmasked) or per-side scale factors (CU budgets), and the cross-stream
- *     wait fitted so that the model meets the run;
+ *     wait fitted so that the model meets the run; then the same two
+ *     nano-batches as two lanes (NF_ORDER_LANES), which fits the profile's
+ *     lane_rate (and, if that cannot slow the model enough, its wait);
  *  3. every candidate is predicted with the model of nf_plan_predict:
  *     counts 1..max_count; sizes equal, attention-balanced, in 64-token
  *     steps (two nano-batches), quarter / half / quarter (three), and the
  *     decode requests apart from a trailing prefill chunk; the pipelined and
- *     deep orders on two streams for each split, and one stream;
+ *     deep orders on two streams for each split, two lanes, and one stream;
  *  4. the `top_k` best predictions and the unsplit plan are timed with
  *     `warmup` + `reps` steps, and the fastest is kept.
  * Runs steps on this batch (so it writes batch->out); the pool pages holding
@@ -513,7 +518,7 @@ nf_status nf_plan_predict(const nf_plan_profile* prof, const nf_shape* shape, co
  * nf_plan_search_report returns the plans the last search on this layer ran
  * (the calibration runs, then the timed candidates) with their predicted and
  * measured ms per step, and calibration[i] = 1 for a calibration run (whose
- * cross-stream wait was fitted to make the model meet it) else 0: *n = their
+ * cross-stream wait or lane rate was fitted to make the model meet it) else 0: *n = their
  * number, the first min(n, max) copied to the arrays (each may be NULL).  An empty batch returns the unsplit plan
  * without running anything.  Errors: NF_ERR_INVALID_ARG for a null argument,
  * NF_ERR_UNSUPPORTED with per-kernel timing on, any error of nf_layer_step. */

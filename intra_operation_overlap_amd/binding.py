@@ -59,7 +59,7 @@ class nf_plan_profile(ctypes.Structure):
                 ("ffn_us", ctypes.c_double * NF_PROFILE_POINTS), ("attn_base_us", ctypes.c_double),
                 ("attn_us_per_page", ctypes.c_double), ("gap_us", ctypes.c_double), ("slow_gemm", ctypes.c_double),
                 ("slow_attn", ctypes.c_double), ("wait_us", ctypes.c_double), ("scale_gemm", ctypes.c_double),
-                ("scale_attn", ctypes.c_double)]
+                ("scale_attn", ctypes.c_double), ("lane_rate", ctypes.c_double)]
 
 
 class nf_loop_opts(ctypes.Structure):

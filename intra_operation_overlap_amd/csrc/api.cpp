@@ -2189,6 +2189,51 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
       }
     }
     if (st != NF_OK) break;
+    // Two lanes of the same two nano-batches, once: the rate at which two
+    // operations of one class share the chip is fitted so that the model meets
+    // the run (bisection; the prediction falls as the rate rises), on top of
+    // the unmasked split's co-run slowdowns.
+    nf_plan_profile calib_lanes{};
+    bool lanes_ok = false;
+    if (kmax >= 2 && calib_ok[0]) {
+      int32_t sz2[2] = {T - T / 2, T / 2};
+      const nf_plan pl = make_plan(2, sz2, NF_ORDER_LANES, 2, 0, 0, 0);
+      double ms = 0;
+      if ((st = measure(pl, 1, 3, ms)) != NF_OK) break;
+      nf_plan_profile q = calib[0];
+      double tok[2] = {(double)sz2[0], (double)sz2[1]}, units[NF_MAX_NANO];
+      attn_page_units(L->s, *b, pl, units);
+      double lo = 0.25, hi = 1.0;
+      auto pred = [&](double rate) {
+        q.lane_rate = rate;
+        return predict_plan_us(q, pl, tok, units);
+      };
+      if (pred(lo) <= ms * 1e3) {
+        // slower than the slowest rate explains: the cross-stream wait takes
+        // the rest, fitted as for the splits
+        q.lane_rate = lo;
+        double wlo = q.wait_us, whi = q.wait_us + 500;
+        for (int it = 0; it < 40; ++it) {
+          q.wait_us = 0.5 * (wlo + whi);
+          (predict_plan_us(q, pl, tok, units) < ms * 1e3 ? wlo : whi) = q.wait_us;
+        }
+        q.wait_us = whi;
+      } else if (pred(hi) >= ms * 1e3) {
+        q.lane_rate = hi;
+      } else {
+        for (int it = 0; it < 40; ++it) {
+          const double mid = 0.5 * (lo + hi);
+          (pred(mid) > ms * 1e3 ? lo : hi) = mid;
+        }
+        q.lane_rate = 0.5 * (lo + hi);
+      }
+      calib_lanes = q;
+      lanes_ok = true;
+      report.push_back({pl, predict_plan_us(q, pl, tok, units) * 1e-3, ms, true});
+      if (verbose)
+        std::fprintf(stderr, "nf search: two lanes: same-class rate %.3f (two nano-batches %.3f ms)\n", q.lane_rate,
+                     ms);
+    }
 
     // 3. candidates, predicted
     std::vector<std::vector<int32_t>> sizes;
@@ -2246,10 +2291,10 @@ extern "C" nf_status nf_plan_search(nf_layer* L, nf_kv_pool* P, const nf_batch* 
         }
       }
       // two lanes without CU masks, with the co-run rates of the unmasked
-      // calibration (kSplits[0])
-      if (calib_ok[0]) {
+      // calibration (kSplits[0]) and the fitted lane rate
+      if (lanes_ok) {
         const nf_plan pl = make_plan(k, v.data(), NF_ORDER_LANES, 2, 0, 0, 0);
-        preds.push_back({pl, predict_plan_us(calib[0], pl, tok, units)});
+        preds.push_back({pl, predict_plan_us(calib_lanes, pl, tok, units)});
       }
     }
     std::stable_sort(preds.begin(), preds.end(), [](const std::pair<nf_plan, double>& x,

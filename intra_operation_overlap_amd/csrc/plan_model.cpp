@@ -22,9 +22,10 @@
 // (j on lane j mod 2), lane 1 starting after F_0, and the caller waiting for
 // both lanes.  The co-run rates then follow the classes of the two running
 // operations: attention beside a GEMM-side operation as above; two
-// operations of the same class share the chip, each at half its solo rate
-// (a lane's GEMMs take tiles for half the chip, so their solo durations from
-// whole-chip profiles stand for the pair).
+// operations of the same class share the chip, each at lane_rate of its solo
+// rate (one half unless a two-lane calibration run fitted it: a lane's GEMMs
+// take tiles for half the chip, and two lanes' GEMMs lose each other's L2
+// reuse, so the whole-chip profiles only approximate the pair).
 #include <algorithm>
 #include <cmath>
 #include <vector>
@@ -168,7 +169,7 @@ double predict_plan_us(const nf_plan_profile& p, const nf_plan& plan, const doub
     if (both) {
       const bool a0 = ops[running[0]].attn, a1 = ops[running[1]].attn;
       if (a0 == a1) {
-        rate[0] = rate[1] = 0.5;
+        rate[0] = rate[1] = p.lane_rate > 0 ? p.lane_rate : 0.5;
       } else {
         rate[0] = a0 ? 1.0 / slow_a : 1.0 / slow_g;
         rate[1] = a1 ? 1.0 / slow_a : 1.0 / slow_g;

@@ -128,3 +128,21 @@ def test_lanes_share_the_chip_by_operation_class():
     # one nano-batch: one lane, no join
     assert _predict(_profile(wait=7.0), B.make_plan(1, [16], order=B.NF_ORDER_LANES, n_streams=2)) == \
         pytest.approx(95)
+
+
+def test_lane_rate_sets_how_two_same_class_operations_share_the_chip():
+    plan = B.make_plan(2, [8, 8], order=B.NF_ORDER_LANES, n_streams=2)
+    # as the first lanes timeline, with same-class pairs at full rate each:
+    # F0 0-10; F1 beside A0 10-20; A0 beside A1 20-60 (A1 10 left); O0 beside A1 60-65;
+    # N0 beside A1 65-70 (25 left); O1 beside N0 70-75 (20 left); N1 beside N0 75-95 (N1 10 left);
+    # N1 alone 95-105
+    p = _profile()
+    p.lane_rate = 1.0
+    assert _predict(p, plan) == pytest.approx(105)
+    # 0 means one half: the first lanes timeline
+    p.lane_rate = 0.0
+    assert _predict(p, plan) == pytest.approx(170)
+    # the rate only matters for lanes: two streams pipelined are unchanged
+    q = _profile()
+    q.lane_rate = 1.0
+    assert _predict(q, B.make_plan(2, [8, 8], n_streams=2)) == pytest.approx(145)
