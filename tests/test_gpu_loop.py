@@ -99,3 +99,27 @@ def test_async_loop_matches_sync_loop_and_the_oracle():
         assert e <= 2e-2, (r, e)
     pool.close()
     layer.close()
+
+
+def test_loop_under_two_lanes_matches_the_unsplit_loop():
+    """The loop spreads the layer's plan over every batch it forms: under the
+    lanes order (two nano-batches, each on a stream of its own) every request
+    ends at the same position and its rows match the unsplit loop's within the
+    bf16 tolerance (the lanes pick GEMM tiles for half the chip)."""
+    wl = W.Workload("loop_lanes", SHAPE, n_decode=1, ctx_range=(1, 1), prefill=None, seed=96)
+    weights = W.make_weights(wl, "cuda")
+    layer = B.Layer(SHAPE, weights, 96, 128)
+    kp = torch.zeros(64, SHAPE.n_kv_heads, 16, SHAPE.head_dim, dtype=torch.bfloat16, device="cuda")
+    pool = B.KVPool.from_plain(layer, kp, kp, GH.stream())
+    reqs = _requests(20, 11)
+    o_ref, len_ref, st_ref = _run(layer, pool, reqs, True)
+    layer.set_plan(B.make_plan(2, [1, 1], order=B.NF_ORDER_LANES, n_streams=2))
+    o_lanes, len_lanes, st_lanes = _run(layer, pool, reqs, True)
+    GH.log(f"unsplit {st_ref}; lanes {st_lanes}")
+    assert len_lanes == len_ref
+    assert st_lanes["wasted_tokens"] == st_ref["wasted_tokens"]
+    for r, n in enumerate(len_ref):
+        e = GH.normwise(GH.f64(o_lanes[r][:n]), GH.f64(o_ref[r][:n]))
+        assert e <= 2e-2, (r, e)
+    pool.close()
+    layer.close()
