@@ -460,7 +460,10 @@ def allreduce_measure(layer, pool, hb, T, sp, steps=20):
              "split2_sequential": B.make_plan(2, half, order=B.NF_ORDER_SEQUENTIAL),
              "split2_pipelined_two_streams": B.make_plan(2, half, n_streams=2),
              "split2_deep_two_streams": B.make_plan(2, half, order=B.NF_ORDER_DEEP, n_streams=2),
-             "split2_deep_one_stream": B.make_plan(2, half, order=B.NF_ORDER_DEEP)}
+             "split2_deep_one_stream": B.make_plan(2, half, order=B.NF_ORDER_DEEP),
+             "split2_lanes": B.make_plan(2, half, order=B.NF_ORDER_LANES, n_streams=2),
+             "split3_lanes": B.make_plan(3, [T // 3, T // 3, T - 2 * (T // 3)], order=B.NF_ORDER_LANES,
+                                         n_streams=2)}
     res = {"mode": "copy engines", "bytes_per_step": None, "ms_per_step": {}}
     layer.set_allreduce_emulation(0)
     layer.set_plan(plans["unsplit"])

@@ -152,6 +152,8 @@ struct nf_layer {
   // kernel of ar_wgs workgroups; on stream sc, with these events
   int ar_mode = 0, ar_wgs = 16;
   hipStream_t sc = nullptr;
+  hipStream_t sc2 = nullptr;                    // lane 1's collectives (lanes order)
+  hipEvent_t ev_a2 = nullptr;
   hipEvent_t ev_o[NF_MAX_NANO] = {}, ev_co[NF_MAX_NANO] = {}, ev_d[NF_MAX_NANO] = {}, ev_cd[NF_MAX_NANO] = {};
   DevBuf x1r, ypre, ar_stage;   // the all-reduced x1, the down output before its all-reduce, the send leg
   DevBuf h, qkv, q_rot, attn, x1, h2, act, y;
@@ -961,6 +963,7 @@ struct Streams {
   bool two = false, comm = false;
   bool lanes = false;            // nano-batch j on lane j % 2 (sg, sa)
   hipStream_t caller = nullptr, sg = nullptr, sa = nullptr, sc = nullptr;
+  hipStream_t sc2 = nullptr;     // lane 1's collectives (sc unless lanes)
   int held_dev = -1;             // a held masked pair (released here)
   hipStream_t held = nullptr;
   Streams() = default;
@@ -978,7 +981,14 @@ nf_status open_streams(nf_layer* L, const nf_plan& plan, hipStream_t caller, Str
   S.comm = L->ar_mode != 0;
   if (S.comm) {
     if (!L->sc) HIP_TRY(hipStreamCreateWithFlags(&L->sc, hipStreamNonBlocking));
-    S.sc = L->sc;
+    S.sc = S.sc2 = L->sc;
+    // with lanes each lane's collectives go on a stream of their own: on one
+    // stream, in issue order, lane 1's would queue behind all of lane 0's
+    if (S.lanes) {
+      if (!L->sc2) HIP_TRY(hipStreamCreateWithFlags(&L->sc2, hipStreamNonBlocking));
+      if (!L->ev_a2) HIP_TRY(hipEventCreateWithFlags(&L->ev_a2, hipEventDisableTiming));
+      S.sc2 = L->sc2;
+    }
   }
   if (!S.two) return NF_OK;
   StreamPair pr;
@@ -1009,8 +1019,8 @@ nf_status open_streams(nf_layer* L, const nf_plan& plan, hipStream_t caller, Str
 // workspace when the caller goes on.  Errors here are ignored: the step's own
 // error is the one reported.
 void drain_after_error(const Streams& S) {
-  const hipStream_t all[4] = {S.caller, S.sg, S.sa, S.sc};
-  for (int i = 0; i < 4; ++i) {
+  const hipStream_t all[5] = {S.caller, S.sg, S.sa, S.sc, S.sc2};
+  for (int i = 0; i < 5; ++i) {
     bool seen = false;
     for (int k = 0; k < i; ++k) seen = seen || all[k] == all[i];
     if (!seen && (i == 0 || all[i])) (void)hipStreamSynchronize(all[i]);
@@ -1030,9 +1040,16 @@ nf_status close_streams(nf_layer* L, const Streams& S) {
   if (S.comm) {
     HIP_TRY(hipEventRecord(L->ev_a, S.sc));
     HIP_TRY(hipStreamWaitEvent(S.caller, L->ev_a, 0));
+    if (S.sc2 != S.sc) {
+      HIP_TRY(hipEventRecord(L->ev_a2, S.sc2));
+      HIP_TRY(hipStreamWaitEvent(S.caller, L->ev_a2, 0));
+    }
   }
   return NF_OK;
 }
+
+// The stream of nano-batch j's collectives
+hipStream_t comm_stream(const Streams& S, int j) { return S.lanes && j % 2 ? S.sc2 : S.sc; }
 
 // The stream the GEMM side of nano-batch j goes to, and that of its
 // attention; with lanes both are lane j % 2 and the context is set to it.
@@ -1083,10 +1100,11 @@ nf_status issue_o_after_attn(LayerRun& r, const Streams& S, int j) {
   if (st != NF_OK || !L->ar_mode) return st;
   const NanoWork& nw = L->work.nanos[j];
   if (nw.t1 == nw.t0) return NF_OK;
+  const hipStream_t sc = comm_stream(S, j);
   HIP_TRY(hipEventRecord(L->ev_o[j], sg));
-  HIP_TRY(hipStreamWaitEvent(S.sc, L->ev_o[j], 0));
-  if ((st = issue_allreduce(L, L->x1.p, L->x1r.p, nw.t0, nw.t1 - nw.t0, S.sc)) != NF_OK) return st;
-  HIP_TRY(hipEventRecord(L->ev_co[j], S.sc));
+  HIP_TRY(hipStreamWaitEvent(sc, L->ev_o[j], 0));
+  if ((st = issue_allreduce(L, L->x1.p, L->x1r.p, nw.t0, nw.t1 - nw.t0, sc)) != NF_OK) return st;
+  HIP_TRY(hipEventRecord(L->ev_co[j], sc));
   return NF_OK;
 }
 
@@ -1101,10 +1119,11 @@ nf_status issue_ffn_after_o(LayerRun& r, const Streams& S, int j) {
   if (L->ar_mode && live) HIP_TRY(hipStreamWaitEvent(sg, L->ev_co[j], 0));
   nf_status st = issue_ffn(r.c, j, sg, r.normed[j]);
   if (st != NF_OK || !L->ar_mode || !live) return st;
+  const hipStream_t sc = comm_stream(S, j);
   HIP_TRY(hipEventRecord(L->ev_d[j], sg));
-  HIP_TRY(hipStreamWaitEvent(S.sc, L->ev_d[j], 0));
-  if ((st = issue_allreduce(L, L->ypre.p, r.c.b->out, nw.t0, nw.t1 - nw.t0, S.sc)) != NF_OK) return st;
-  HIP_TRY(hipEventRecord(L->ev_cd[j], S.sc));
+  HIP_TRY(hipStreamWaitEvent(sc, L->ev_d[j], 0));
+  if ((st = issue_allreduce(L, L->ypre.p, r.c.b->out, nw.t0, nw.t1 - nw.t0, sc)) != NF_OK) return st;
+  HIP_TRY(hipEventRecord(L->ev_cd[j], sc));
   return NF_OK;
 }
 
@@ -1390,6 +1409,8 @@ void nf_layer_destroy(nf_layer* L) {
     for (hipEvent_t e : {L->ev_o[j], L->ev_co[j], L->ev_d[j], L->ev_cd[j]})
       if (e) (void)hipEventDestroy(e);
   if (L->sc) (void)hipStreamDestroy(L->sc);
+  if (L->sc2) (void)hipStreamDestroy(L->sc2);
+  if (L->ev_a2) (void)hipEventDestroy(L->ev_a2);
   for (DevBuf* b : {&L->x1r, &L->ypre, &L->ar_stage}) release(*b);
   for (auto& r : L->recs) {
     (void)hipEventDestroy(r.a);
