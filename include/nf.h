@@ -195,7 +195,12 @@ typedef struct nf_graph nf_graph;
  * fp32 cos/sin table (angles in fp64).  For bf16 mixture-of-experts layers
  * it also copies the expert weights once into the MFMA operand order of the
  * weight-streaming expert GEMMs (E * 3 * F * H * 2 bytes, owned by the
- * layer), so weights must not change while the layer exists.  The default plan is
+ * layer).  Every bf16 layer (hidden % 8 == 0) also folds the attention
+ * RMSNorm into the QKV projection: it keeps W_qkv with the norm gain applied
+ * to its columns ((nq + 2 nkv) * d * H * 2 bytes, made once, rounded to bf16),
+ * the projection reads the layer input itself, and each row's 1 / RMS scales
+ * q, k and v in RoPE/append.  Weights must therefore not change while the
+ * layer exists.  The default plan is
  * one nano-batch on the caller's stream.  Errors: NF_ERR_INVALID_ARG (null
  * pointers, inconsistent shape), NF_ERR_UNSUPPORTED (head_dim or dtype
  * outside the list above), NF_ERR_HIP (allocation failure).
@@ -210,7 +215,8 @@ typedef struct nf_graph nf_graph;
  * configuration cfg (10..30) and the K split on every dense bf16 GEMM of that
  * shape and mode (0 plain, 1 residual, 2 SwiGLU), for timing configurations
  * inside the step; results then differ from the default choice by rounding
- * only. */
+ * only.  NF_NORM_FOLD=0 keeps the attention RMSNorm as a kernel of its own
+ * (normalised rows, then the QKV GEMM) in layers created afterwards. */
 nf_status nf_layer_create(const nf_shape* shape, const nf_weights* w, nf_layer** out);
 void nf_layer_destroy(nf_layer* layer);   /* waits for the layer's streams */
 
@@ -531,7 +537,9 @@ nf_status nf_plan_search_report(const nf_layer* layer, int32_t max, nf_plan* pla
 /* ---- intermediates ----------------------------------------------------------
  * Device pointer and row stride (elements) of an intermediate of the last
  * step, in the layer dtype: 0 q_rot [T][nq*d], 1 attn [T][nq*d],
- * 2 x1 [T][H], 3 act [T][F] (dense layers), 4 qkv [T][(nq+2nkv)*d].
+ * 2 x1 [T][H], 3 act [T][F] (dense layers), 4 qkv [T][(nq+2nkv)*d] (only
+ * when the QKV GEMM was not split over K; in bf16 layers that fold the
+ * attention RMSNorm, before each row's 1 / RMS is applied).
  * For MoE layers, 5 route_idx int32 [T][top_k], 6 route_w fp32 [T][top_k],
  * 7 route_perm int32 [T*top_k], 8 expert_offsets int32 [E+1] (per
  * nano-batch, at the nano-batch's token offset / top_k-scaled offset). */

@@ -164,6 +164,12 @@ struct nf_layer {
   // expert weights in MFMA operand order for the weight-streaming kernels
   // (bf16 mixture-of-experts layers; empty otherwise)
   DevBuf wp_qkv, wp_o, wp_gu, wp_down;
+  // bf16: the attention RMSNorm folded into the QKV projection.  w_qkv_g
+  // holds W_qkv with the norm gain applied to its columns (made once), the
+  // GEMM reads the layer input itself, and rs holds each row's 1 / RMS, which
+  // RoPE/append applies to q, k and v
+  bool fold_norm1 = false;
+  DevBuf w_qkv_g, rs;
   void* stage[2] = {nullptr, nullptr};       // pinned, coherent host staging
   void* stage_dev[2] = {nullptr, nullptr};   // their device addresses
   size_t stage_bytes[2] = {0, 0};
@@ -560,8 +566,14 @@ NanoGemms nano_gemms(const StepCtx& c, int j, int t0, int t1) {
   const int Tj = t1 - t0, k = s.top_k;
   NanoGemms n;
   GemmArgs& q = n.qkv;
-  q.A = ptr(L->h, (int64_t)t0 * H, dt); q.lda = H;
-  q.B = L->w.w_qkv; q.ldb = H; q.Bp = L->wp_qkv.p;
+  if (L->fold_norm1) {
+    q.A = (const char*)c.b->x + (int64_t)t0 * H * dtype_bytes(dt);
+    q.B = L->w_qkv_g.p;
+  } else {
+    q.A = ptr(L->h, (int64_t)t0 * H, dt);
+    q.B = L->w.w_qkv;
+  }
+  q.lda = H; q.ldb = H; q.Bp = L->wp_qkv.p;
   q.C = ptr(L->qkv, (int64_t)t0 * Nqkv, dt); q.ldc = Nqkv;
   q.M = Tj; q.N = Nqkv; q.K = H; q.mode = GEMM_STORE;
   GemmArgs& o = n.o;
@@ -629,9 +641,12 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
     return cfg >= 10 && cfg <= 30 && g.qkv.K % 64 == 0;
   }();
   prof_begin(L, K_NORM1, s);
-  HIP_STEP(rmsnorm(dt, (const char*)c.b->x + (int64_t)t0 * H * dtype_bytes(dt), L->w.attn_norm,
-                   ptr(L->h, (int64_t)t0 * H, dt), Tj, H, sh.rms_eps, s,
-                   c.mc_pending && !meta_in_gemm ? &c.mc : nullptr));
+  const char* x = (const char*)c.b->x + (int64_t)t0 * H * dtype_bytes(dt);
+  const MetaCopy* mc = c.mc_pending && !meta_in_gemm ? &c.mc : nullptr;
+  if (L->fold_norm1)
+    HIP_STEP(row_rms_scale(x, (float*)L->rs.p + t0, Tj, H, sh.rms_eps, s, mc));
+  else
+    HIP_STEP(rmsnorm(dt, x, L->w.attn_norm, ptr(L->h, (int64_t)t0 * H, dt), Tj, H, sh.rms_eps, s, mc));
   prof_end(L, K_NORM1, s);
   if (meta_in_gemm) g.qkv.meta = c.mc;
   int qkv_parts = 1;
@@ -657,6 +672,7 @@ nf_status issue_front(StepCtx& c, int j, hipStream_t s) {
   r.page_indptr = c.indptr;
   r.page_indices = c.indices;
   r.cos_sin = (const float*)L->cos_sin.p;
+  if (L->fold_norm1) r.row_scale = (const float*)L->rs.p + t0;
   r.T = Tj; r.nq = sh.n_q_heads; r.nkv = sh.n_kv_heads; r.d = sh.head_dim; r.page_size = c.P->page_size;
   prof_begin(L, K_ROPE, s);
   HIP_STEP(rope_append(dt, r, s));
@@ -1331,6 +1347,8 @@ nf_status nf_layer_create(const nf_shape* s, const nf_weights* w, nf_layer** out
   L->cus_per_xcd = std::max(1, L->n_cus / L->n_xcd);
   L->plan = nf_plan{1, {0, 0, 0, 0}, NF_ORDER_PIPELINED, 1, 0, 0, 0};
   if (const char* v = std::getenv("NF_ATTN_VARIANT")) L->attn_variant = std::atoi(v);
+  L->fold_norm1 = s->dtype == NF_BF16 && s->hidden % 8 == 0;
+  if (const char* v = std::getenv("NF_NORM_FOLD")) L->fold_norm1 = L->fold_norm1 && std::atoi(v) != 0;
 
   const int dt = s->dtype;
   const size_t eb = dtype_bytes(dt);
@@ -1341,7 +1359,8 @@ nf_status nf_layer_create(const nf_shape* s, const nf_weights* w, nf_layer** out
     DevBuf* b;
     size_t bytes;
   } allocs[] = {
-      {&L->h, Tm * H * eb},          {&L->qkv, Tm * Nqkv * eb}, {&L->q_rot, Tm * nqd * eb},
+      {&L->h, L->fold_norm1 ? 0 : Tm * H * eb}, {&L->rs, L->fold_norm1 ? (size_t)Tm * 4 : 0},
+      {&L->qkv, Tm * Nqkv * eb},     {&L->q_rot, Tm * nqd * eb},
       {&L->attn, Tm * nqd * eb},     {&L->x1, Tm * H * eb},     {&L->h2, Tm * H * eb},
       {&L->act, Tm * k * F * eb},
   };
@@ -1365,6 +1384,10 @@ nf_status nf_layer_create(const nf_shape* s, const nf_weights* w, nf_layer** out
     }
   if (dt == NF_BF16 && pack_weights(L) != hipSuccess)
     return fail(set_err(NF_ERR_HIP, "weight packing failed"));
+  if (L->fold_norm1 && (ensure(L->w_qkv_g, Nqkv * H * eb) != hipSuccess ||
+                        scale_cols_bf16(L->w.w_qkv, L->w.attn_norm, L->w_qkv_g.p, Nqkv, (int)H, nullptr) != hipSuccess ||
+                        hipDeviceSynchronize() != hipSuccess))
+    return fail(set_err(NF_ERR_HIP, "gain-scaled QKV weight failed"));
   if (ensure(L->cos_sin, cs.size() * 4) != hipSuccess ||
       hipMemcpy(L->cos_sin.p, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
     return fail(set_err(NF_ERR_HIP, "cos/sin table upload failed"));
@@ -1393,7 +1416,7 @@ void nf_layer_destroy(nf_layer* L) {
   }
   for (DevBuf* b : {&L->h, &L->qkv, &L->q_rot, &L->attn, &L->x1, &L->h2, &L->act, &L->y, &L->r_idx, &L->r_w,
                     &L->r_perm, &L->r_inv, &L->r_off, &L->splitk, &L->splitk_lane1, &L->part_o, &L->part_ml, &L->meta, &L->cos_sin,
-                    &L->wp_qkv, &L->wp_o, &L->wp_gu, &L->wp_down, &L->stack_out})
+                    &L->wp_qkv, &L->wp_o, &L->wp_gu, &L->wp_down, &L->w_qkv_g, &L->rs, &L->stack_out})
     release(*b);
   for (int i = 0; i < 2; ++i) {
     if (L->stage[i]) (void)hipHostFree(L->stage[i]);

@@ -137,8 +137,17 @@ struct RopeAppendArgs {
   // `splits` fp32 partial slices (zstride floats apart, row stride part_ld),
   // which this kernel also stores to qkv
   const float* part = nullptr; int64_t part_ld = 0, zstride = 0; int splits = 1;
+  // bf16: the attention RMSNorm folded in.  The QKV GEMM ran on x against
+  // weights with the norm gain applied to their columns; each token's q, k
+  // and v are multiplied by its 1 / RMS (row_scale[t]) before the rotation
+  const float* row_scale = nullptr;
 };
 hipError_t rope_append(int dtype, const RopeAppendArgs& a, hipStream_t s);
+// bf16, H % 8 == 0: s[t] = 1 / sqrt(mean(x[t]^2) + eps), with the sum of
+// squares of rmsnorm (same threads, chunks and order); carries `mc` like rmsnorm
+hipError_t row_rms_scale(const void* x, float* s, int T, int H, float eps, hipStream_t st, const MetaCopy* mc);
+// bf16 [N][K] (K % 8 == 0): out[n][k] = round(w[n][k] * g[k])
+hipError_t scale_cols_bf16(const void* w, const void* g, void* out, int64_t N, int K, hipStream_t s);
 // bf16, H % 8 == 0: x1 = round(sum of `splits` split-K partial slices + x),
 // then y = RMSNorm(x1) * g, in one kernel; bit-identical to the split-K
 // reduce (residual epilogue) followed by rmsnorm.

@@ -123,6 +123,39 @@ __global__ __launch_bounds__(RN_THREADS) void rmsnorm_bf16x8_kernel(const bf16* 
   }
 }
 
+// Each row's 1 / RMS only: the sum of squares exactly as rmsnorm_bf16x8_kernel
+// forms it (same threads, chunks and order), one read of the row.
+__global__ __launch_bounds__(RN_THREADS) void row_rms_scale_kernel(const bf16* __restrict__ x, float* __restrict__ s,
+                                                                   int H, float eps, MetaCopy mc, int rows) {
+  if (meta_copy_block(mc, rows)) return;
+  const int64_t row = blockIdx.x;
+  const bf16x8* xr = (const bf16x8*)(x + row * H);
+  const int n8 = H / 8;
+  float ss = 0.f;
+  if (n8 <= RN_HELD * RN_THREADS) {
+    bf16x8 v[RN_HELD];
+#pragma unroll
+    for (int k = 0; k < RN_HELD; ++k) {
+      const int i = threadIdx.x + k * RN_THREADS;
+      if (i < n8) v[k] = xr[i];
+    }
+#pragma unroll
+    for (int k = 0; k < RN_HELD; ++k)
+      if (threadIdx.x + k * RN_THREADS < n8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += (float)v[k][e] * (float)v[k][e];
+      }
+  } else {
+    for (int i = threadIdx.x; i < n8; i += RN_THREADS) {
+      const bf16x8 v = xr[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += (float)v[e] * (float)v[e];
+    }
+  }
+  const float inv = rsqrtf(block_sum_sq(ss) / (float)H + eps);
+  if (threadIdx.x == 0) s[row] = inv;
+}
+
 // Split-K reduce of the O-projection (residual epilogue) fused with the FFN
 // RMSNorm: x1 = round(sum_z partial_z + x) is stored, then y = RMSNorm(x1) * g.
 // Same thread-to-chunk mapping and summation order as splitk_reduce_kernel
@@ -281,14 +314,15 @@ __global__ __launch_bounds__(256) void rope_append_bf16x4_kernel(RopeAppendArgs 
   const int page = head >= a.nq ? a.page_indices[a.page_indptr[r] + p / a.page_size] : 0;
   float x0[4], x1[4];
   bf16x4 v0, v1;
+  const float sc = a.row_scale ? a.row_scale[t] : 1.f;
   if (a.splits > 1) {
     const float* P = a.part + (int64_t)t * a.part_ld + (int64_t)head * d + j;
     const f32x4 s0 = sum_slices<f32x4>(P, a.zstride, a.splits);
     const f32x4 s1 = sum_slices<f32x4>(P + half, a.zstride, a.splits);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v0[e] = (bf16)s0[e];
-      v1[e] = (bf16)s1[e];
+      v0[e] = (bf16)(s0[e] * sc);
+      v1[e] = (bf16)(s1[e] * sc);
     }
     bf16* out = (bf16*)a.qkv + (int64_t)t * ncols + (int64_t)head * d;
     *(bf16x4*)(out + j) = v0;
@@ -297,6 +331,12 @@ __global__ __launch_bounds__(256) void rope_append_bf16x4_kernel(RopeAppendArgs 
     const bf16* row = (const bf16*)a.qkv + (int64_t)t * ncols + (int64_t)head * d;
     v0 = *(const bf16x4*)(row + j);
     v1 = *(const bf16x4*)(row + j + half);
+    if (a.row_scale)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v0[e] = (bf16)((float)v0[e] * sc);
+        v1[e] = (bf16)((float)v1[e] * sc);
+      }
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -485,6 +525,20 @@ __global__ __launch_bounds__(256) void moe_combine_bf16x8_kernel(const bf16* __r
       o[e + 4] = (bf16)v1;
     }
     *(bf16x8*)(out + t * H + i) = o;
+  }
+}
+
+// out[n][k] = round(w[n][k] * g[k]) for a bf16 [N][K] matrix, 16 bytes per
+// thread and step (K % 8 == 0): weights with a norm gain folded in
+__global__ __launch_bounds__(256) void scale_cols_bf16x8_kernel(const bf16x8* __restrict__ w,
+                                                                const bf16x8* __restrict__ g,
+                                                                bf16x8* __restrict__ out, int64_t n16, int k8) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const bf16x8 v = w[i], s = g[i % k8];
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[e] * (float)s[e]);
+    out[i] = o;
   }
 }
 
@@ -686,6 +740,25 @@ hipError_t moe_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.E > ROUTE_MAX_E || a.k > 8) return hipErrorInvalidValue;
   launch(moe_route_kernel, 1, ROUTE_THREADS, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t row_rms_scale(const void* x, float* s, int T, int H, float eps, hipStream_t st, const MetaCopy* mc) {
+  if (T == 0) return hipSuccess;
+  if (H % 8) return hipErrorInvalidValue;
+  MetaCopy m;
+  if (mc) m = *mc;
+  const int extra = m.n16 > 0 ? (int)std::min<int64_t>((m.n16 + 255) / 256, 64) : 0;
+  launch(row_rms_scale_kernel, T + extra, RN_THREADS, 0, st, (const bf16*)x, s, H, eps, m, T);
+  return hipGetLastError();
+}
+
+hipError_t scale_cols_bf16(const void* w, const void* g, void* out, int64_t N, int K, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (K % 8) return hipErrorInvalidValue;
+  const int64_t n16 = N * K / 8;
+  launch(scale_cols_bf16x8_kernel, (int)std::min<int64_t>((n16 + 255) / 256, 4096), 256, 0, s, (const bf16x8*)w,
+         (const bf16x8*)g, (bf16x8*)out, n16, K / 8);
   return hipGetLastError();
 }
 

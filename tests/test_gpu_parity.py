@@ -184,6 +184,28 @@ def test_split_k_small_batch_parity():
     _full_check(S, "k2_masked", B.make_plan(2, [7, 13], n_streams=2, gemm_cus_per_xcd=20))
 
 
+@pytest.mark.parametrize("wl_name", ["small_bf16", "splitk"])
+def test_attention_norm_kernel_and_fold_both_match_the_oracle(wl_name, monkeypatch):
+    """bf16 layers fold the attention RMSNorm into the QKV projection (gain in
+    the weights, 1 / RMS applied in RoPE/append, also on the split-K
+    partials); NF_NORM_FOLD=0 keeps the norm as a kernel of its own.  Both
+    layers match the oracle, and each other within the bf16 tolerance."""
+    wl = SMALL_BF16 if wl_name == "small_bf16" else W.Workload(
+        "splitk_nofold", W.Shape(hidden=2048, n_q_heads=8, n_kv_heads=4, head_dim=128, ffn=1536, dtype="bf16",
+                                 rope_theta=5e5), n_decode=20, ctx_range=(5, 90), prefill=None, seed=81)
+    outs = []
+    for fold in ("0", "1"):
+        monkeypatch.setenv("NF_NORM_FOLD", fold)
+        S = GH.setup(wl)
+        T = S.batch.n_tokens
+        _full_check(S, f"fold={fold} k1", B.make_plan(1, [T]))
+        outs.append(S.out.clone())
+        _full_check(S, f"fold={fold} k2", B.make_plan(2, [T // 2, T - T // 2], n_streams=2))
+    e = GH.normwise(GH.f64(outs[1]), GH.f64(outs[0]))
+    GH.log(f"  folded vs unfolded {e:.2e}")
+    assert e <= GH.tolerance(wl)
+
+
 def test_plan_invariance_bit_exact(small):
     """Same nano-batch sizes and the same CU budget give bit-identical outputs
     whatever the stream count and operation order."""
