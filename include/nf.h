@@ -537,9 +537,10 @@ nf_status nf_plan_search_report(const nf_layer* layer, int32_t max, nf_plan* pla
 /* ---- intermediates ----------------------------------------------------------
  * Device pointer and row stride (elements) of an intermediate of the last
  * step, in the layer dtype: 0 q_rot [T][nq*d], 1 attn [T][nq*d],
- * 2 x1 [T][H], 3 act [T][F] (dense layers), 4 qkv [T][(nq+2nkv)*d] (only
- * when the QKV GEMM was not split over K; in bf16 layers that fold the
- * attention RMSNorm, before each row's 1 / RMS is applied).
+ * 2 x1 [T][H], 3 act [T][F] (dense layers), 4 qkv [T][(nq+2nkv)*d] (in bf16
+ * layers that fold the attention RMSNorm: with each row's 1 / RMS applied
+ * where the QKV GEMM was split over K, since RoPE/append writes its reduced
+ * sums there, and without it where the GEMM stored them itself).
  * For MoE layers, 5 route_idx int32 [T][top_k], 6 route_w fp32 [T][top_k],
  * 7 route_perm int32 [T*top_k], 8 expert_offsets int32 [E+1] (per
  * nano-batch, at the nano-batch's token offset / top_k-scaled offset). */
